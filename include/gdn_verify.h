@@ -1,0 +1,197 @@
+/*
+ * gdn_verify.h -- C ABI of the MI355X (gfx950) library for speculative
+ * verification through GatedDeltaNet (GDN) recurrent layers with tape-replay
+ * rollback.  Library: libgdnverify.so (hand-written HIP, one GPU).
+ *
+ * The problem, as the pages state it:
+ *  - A GDN layer carries a Conv1D window and a gated delta state per sequence
+ *    and is sequential per token ("Speculative Decoding on GDN Hybrid
+ *    Architectures: A 31-Experiment Investigation", s2.1).
+ *  - During verification every GDN step records an innovation tape: delta
+ *    [B,T,Hv,Dv], key [B,T,Hk,Dk], decay gate [B,T,Hv] and the raw qkv stream
+ *    for the conv window.  On partial acceptance of n of the N drafts the
+ *    pre-verify snapshot is restored and only the accepted steps are replayed
+ *    (state <- g[t] state + delta[t] k[t]^T for t < n), and the conv window is
+ *    rebuilt from the last K-1 accepted raw tokens; cost O(n_accepted), one
+ *    dispatch per layer stack (same page, s4 "Tape-Replay rollback").
+ *  - The accepted length is the longest prefix whose drafts equal the target's
+ *    argmax, and the correction token is the target argmax at the stop
+ *    position (xserv "Phase 25", s2 pseudo-code; colibri "MTP speculative
+ *    decoding", s5: greedy = exact argmax match).
+ *  - A draft tree can be verified by walking the tree through the recurrent
+ *    state (same GDN page, s2.2 update and s8: tree-aware GDN kernels over a
+ *    DDTree).
+ *
+ * Recurrence per (layer, sequence, v-head h), with k-head floor(h*Hk/Hv):
+ *   S_t = a_t S_{t-1} + u_t k_t^T,   u_t = b_t (v_t - a_t S_{t-1} k_t),
+ *   o_t = S_t q_t,   S is Dv x Dk (row-major, Dk fastest).
+ * q, k, v come from a depthwise causal conv (tap K-1 = current token, no bias,
+ * SiLU after when conv_silu != 0) over the qkv stream whose channels are
+ * [q: Hk*Dk | k: Hk*Dk | v: Hv*Dv] (head-major); q and k are then L2
+ * normalised per head, x / sqrt(sum x^2 + l2_eps).
+ *
+ * Conventions for every call:
+ *  - All pointers are DEVICE memory owned by the caller, contiguous, in the
+ *    layouts given below; the library allocates nothing, keeps no state
+ *    between calls and is reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work; none of them synchronises the host.
+ *  - Host-side validation (NULL pointers, sizes, unsupported shapes) returns a
+ *    status before anything is launched.  Data errors only visible on the
+ *    device (n_keep out of range, malformed parent array or path) are reported
+ *    by OR-ing bits into *dev_err (when dev_err != NULL); the affected
+ *    sequence is left untouched.
+ *  - Supported: d_k, d_v in {32, 64, 128}; conv_kernel in 2..8; T in 1..64;
+ *    n_v_heads % n_k_heads == 0; in_dtype F32 or BF16 (x, conv_state, a, b).
+ *    conv_w, S, o and the tape are always fp32.
+ */
+#ifndef GDN_VERIFY_H_
+#define GDN_VERIFY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1, /* NULL pointer, bad size or inconsistent shape */
+  GDN_ERR_UNSUPPORTED = 2, /* valid but not instantiated (e.g. d_k = 96) */
+  GDN_ERR_LAUNCH = 3,      /* the HIP runtime rejected a launch */
+  GDN_ERR_WORKSPACE = 4    /* workspace missing or smaller than required */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Bits OR-ed into *dev_err by device-side checks. */
+#define GDN_DEV_ERR_N_KEEP 1 /* n_keep[b] outside [0, T] */
+#define GDN_DEV_ERR_PARENT 2 /* parent[b][v] outside [-1, v-1] */
+#define GDN_DEV_ERR_PATH 4   /* path entry outside [0, T) or not a child of the previous */
+
+typedef struct {
+  int32_t n_layers;    /* L: leading dimension of every per-layer tensor */
+  int32_t batch;       /* B: sequences */
+  int32_t n_k_heads;   /* Hk */
+  int32_t n_v_heads;   /* Hv, multiple of Hk */
+  int32_t d_k;         /* Dk */
+  int32_t d_v;         /* Dv */
+  int32_t conv_kernel; /* K */
+  int32_t conv_silu;   /* 1: SiLU after the conv, 0: identity */
+  float l2_eps;        /* epsilon inside the q/k L2-norm square root */
+  int32_t in_dtype;    /* gdn_dtype of x, conv_state, a, b */
+} gdn_shape;
+
+/* The innovation tape written by verify and read by rollback (fp32):
+ *   u [L,B,T,Hv,Dv]  innovation u_t (the write strength b_t folded in)
+ *   k [L,B,T,Hk,Dk]  L2-normalised key
+ *   g [L,B,T,Hv]     decay gate a_t
+ * The tape's raw-qkv entry is the verify input x itself (kept by the caller). */
+typedef struct {
+  float* u;
+  float* k;
+  float* g;
+} gdn_tape;
+
+/*
+ * Verify T drafted tokens (a chain) through L GDN layers.
+ *   x          [L,B,T,C]      raw qkv stream, C = 2*Hk*Dk + Hv*Dv (in_dtype)
+ *   conv_state [L,B,K-1,C]    conv window before the chunk (in_dtype), read only
+ *   conv_w     [L,C,K]        depthwise conv weights (fp32)
+ *   a, b       [L,B,T,Hv]     decay and write gates (in_dtype)
+ *   S          [L,B,Hv,Dv,Dk] state before the chunk (fp32), read only: it stays
+ *                             the snapshot that gdn_tape_rollback replays onto
+ *   o          [L,B,T,Hv,Dv]  outputs o_t (fp32)
+ *   tape                      innovation tape for the T tokens
+ * Source: GDN page s2.1 (sequential GDN layer) and s4 (the tape).
+ */
+gdn_status gdn_verify_chunk(const gdn_shape* shape, int32_t T, const void* x,
+                            const void* conv_state, const float* conv_w, const void* a,
+                            const void* b, const float* S, float* o, const gdn_tape* tape,
+                            void* stream);
+
+/*
+ * Verify a draft tree of T nodes (T <= 64) per sequence: node v with parent
+ * p = parent[b][v] (-1 = the committed state; parents precede children) runs
+ * one recurrence step from the state after p, without materialising per-node
+ * states.  Node v's conv window is the last K entries of [conv_state rows,
+ * x of v's ancestors from the root down, x_v].
+ *   parent   [B,T] int32, shared by all L layers
+ *   conv_win [B,T,K] int32 or NULL: index of each window entry, where
+ *            -(K-1)..-1 is conv_state row K-1+idx and 0..T-1 a node
+ *   other arguments as gdn_verify_chunk with T = nodes.
+ * A malformed parent array sets GDN_DEV_ERR_PARENT and leaves that
+ * sequence's outputs unwritten.
+ * Source: GDN page s2.2 and s8 (tree-aware GDN kernels over a draft tree).
+ */
+gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* parent,
+                           const void* x, const void* conv_state, const float* conv_w,
+                           const void* a, const void* b, const float* S, float* o,
+                           const gdn_tape* tape, int32_t* conv_win, int32_t* dev_err,
+                           void* stream);
+
+/*
+ * Greedy acceptance.  logits [B,T+1,V] (F32 or BF16): row 0 is the target's
+ * distribution after the last committed token, row 1+v after draft token /
+ * node v.  argmax takes the lowest index among equal maxima.
+ *   parent == NULL (chain): n_keep[b] = longest prefix with
+ *     draft[b][j] == argmax(row j); path[b] = 0..n-1 then -1.
+ *   parent != NULL (tree): from the root, step to the lowest-index child c
+ *     of the current node with draft[b][c] == argmax(current row), until
+ *     none matches; path[b] = accepted nodes then -1.
+ *   bonus[b] = argmax of the row where the walk stopped (the correction token).
+ * draft [B,T] int32; n_keep [B], path [B,T], bonus [B] int32 outputs.
+ * workspace: device scratch of at least spec_accept_workspace_bytes(B,T,V).
+ * Source: xserv "Phase 25" s2 pseudo-code; colibri "MTP speculative decoding" s5.
+ */
+gdn_status spec_accept_prefix(int32_t B, int32_t T, int32_t V, const int32_t* parent,
+                              const int32_t* draft, const void* logits, int32_t logits_dtype,
+                              int32_t* n_keep, int32_t* path, int32_t* bonus, void* workspace,
+                              size_t workspace_bytes, int32_t* dev_err, void* stream);
+
+/* Bytes of device workspace spec_accept_prefix needs for (B, T, V). */
+size_t spec_accept_workspace_bytes(int32_t B, int32_t T, int32_t V);
+
+/*
+ * Tape-replay rollback of L layers at once: S holds the pre-verify snapshot
+ * on entry and the state after the n = n_keep[b] accepted steps on exit,
+ *   S <- g_{p_{n-1}} ( ... (g_{p_0} S + u_{p_0} k_{p_0}^T) ... ) + u_{p_{n-1}} k_{p_{n-1}}^T
+ * with p_i = path[b][i] (or p_i = i when path == NULL).  n = 0 leaves S
+ * untouched.  Computed in closed form,
+ *   S_n = (prod_i g_{p_i}) S + sum_i (prod_{j>i} g_{p_j}) u_{p_i} k_{p_i}^T,
+ * so the cost is one state pass plus O(n) tape reads and no S-dependent
+ * products.  S [L,B,Hv,Dv,Dk] in/out; tape as written by verify (T entries);
+ * path [B,T] or NULL; n_keep [B].
+ * Source: GDN page s4 (restore snapshot, replay accepted steps, O(n_accepted)).
+ */
+gdn_status gdn_tape_rollback(const gdn_shape* shape, int32_t T, float* S, const gdn_tape* tape,
+                             const int32_t* path, const int32_t* n_keep, int32_t* dev_err,
+                             void* stream);
+
+/*
+ * Conv-window rollback of L layers: the new window holds the last K-1 rows
+ * of [old window rows; x[p_0]; ...; x[p_{n-1}]], i.e. new[j] = row n+j of
+ * that sequence; n = 0 keeps the window.  conv_state [L,B,K-1,C] in/out
+ * (in_dtype); x [L,B,T,C] the verify input; path/n_keep as gdn_tape_rollback.
+ * win_idx [B,K-1] int32 or NULL receives the source of each new row in the
+ * conv index space (-(K-1)..-1 old row K-1+idx, 0..T-1 token / node).
+ * Source: GDN page s4 (conv state rebuilt from the last K-1 raw tokens).
+ */
+gdn_status gdn_conv_state_rollback(const gdn_shape* shape, int32_t T, void* conv_state,
+                                   const void* x, const int32_t* path, const int32_t* n_keep,
+                                   int32_t* win_idx, int32_t* dev_err, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* gdn_status_string(int32_t status);
+
+/* GDN_ABI_VERSION of the built library. */
+int32_t gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_VERIFY_H_ */

@@ -1,0 +1,215 @@
+// gdn_api.cpp -- the C ABI of libgdnverify: host-side validation and dispatch
+// onto the gfx950 kernels.  Declared in include/gdn_verify.h.
+//
+// Every entry point validates its arguments on the host and returns a status
+// before anything is launched; device-detected data errors go to *dev_err.
+// Nothing here allocates, synchronises or keeps state between calls.
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn_kernels.hpp"
+#include "gdn_verify.h"
+
+namespace {
+
+using gdn::ConvRollbackArgs;
+using gdn::RollbackArgs;
+using gdn::VerifyArgs;
+
+constexpr int kMaxT = 64;
+
+bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+// Structural checks shared by every call that takes a gdn_shape.
+gdn_status check_shape(const gdn_shape* s, int32_t T) {
+  if (!s) return GDN_ERR_INVALID_ARG;
+  if (s->n_layers < 1 || s->batch < 1 || s->n_k_heads < 1 || s->n_v_heads < 1)
+    return GDN_ERR_INVALID_ARG;
+  if (s->n_v_heads % s->n_k_heads != 0) return GDN_ERR_INVALID_ARG;
+  if (s->d_k < 1 || s->d_v < 1 || s->conv_kernel < 1) return GDN_ERR_INVALID_ARG;
+  if (T < 1) return GDN_ERR_INVALID_ARG;
+  if (s->in_dtype != GDN_F32 && s->in_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (!(s->l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  if (T > kMaxT) return GDN_ERR_UNSUPPORTED;
+  if (!dim_ok(s->d_k) || !dim_ok(s->d_v) || s->d_k != s->d_v) return GDN_ERR_UNSUPPORTED;
+  if (s->conv_kernel < 2 || s->conv_kernel > 8) return GDN_ERR_UNSUPPORTED;
+  // index arithmetic inside the kernels uses 64-bit offsets, but grid sizes
+  // are 32-bit: keep L*B*Hv within range.
+  const long long heads = static_cast<long long>(s->n_layers) * s->batch * s->n_v_heads;
+  if (heads > (1LL << 26)) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+int channels(const gdn_shape* s) {
+  return 2 * s->n_k_heads * s->d_k + s->n_v_heads * s->d_v;
+}
+
+gdn_status launch_status(hipError_t e) {
+  if (e == hipSuccess) return GDN_OK;
+  if (e == hipErrorInvalidValue) return GDN_ERR_UNSUPPORTED;
+  return GDN_ERR_LAUNCH;
+}
+
+VerifyArgs verify_args(const gdn_shape* s, int32_t T, const void* x, const void* conv_state,
+                       const float* conv_w, const void* a, const void* b, const float* S,
+                       float* o, const gdn_tape* tape) {
+  VerifyArgs v{};
+  v.x = x;
+  v.conv_state = conv_state;
+  v.conv_w = conv_w;
+  v.a = a;
+  v.b = b;
+  v.S = S;
+  v.o = o;
+  v.tu = tape->u;
+  v.tk = tape->k;
+  v.tg = tape->g;
+  v.L = s->n_layers;
+  v.B = s->batch;
+  v.Hk = s->n_k_heads;
+  v.Hv = s->n_v_heads;
+  v.K = s->conv_kernel;
+  v.T = T;
+  v.silu = s->conv_silu ? 1 : 0;
+  v.eps = s->l2_eps;
+  v.C = channels(s);
+  return v;
+}
+
+bool verify_ptrs_ok(const void* x, const void* conv_state, const float* conv_w, const void* a,
+                    const void* b, const float* S, const float* o, const gdn_tape* tape) {
+  return x && conv_state && conv_w && a && b && S && o && tape && tape->u && tape->k && tape->g;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_verify_chunk(const gdn_shape* shape, int32_t T, const void* x,
+                            const void* conv_state, const float* conv_w, const void* a,
+                            const void* b, const float* S, float* o, const gdn_tape* tape,
+                            void* stream) {
+  gdn_status st = check_shape(shape, T);
+  if (st != GDN_OK) return st;
+  if (!verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape)) return GDN_ERR_INVALID_ARG;
+  VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
+  return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* parent,
+                           const void* x, const void* conv_state, const float* conv_w,
+                           const void* a, const void* b, const float* S, float* o,
+                           const gdn_tape* tape, int32_t* conv_win, int32_t* dev_err,
+                           void* stream) {
+  gdn_status st = check_shape(shape, T);
+  if (st != GDN_OK) return st;
+  if (!parent || !verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape))
+    return GDN_ERR_INVALID_ARG;
+  VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
+  v.parent = parent;
+  v.conv_win = conv_win;
+  v.dev_err = dev_err;
+  return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t spec_accept_workspace_bytes(int32_t B, int32_t T, int32_t V) {
+  if (B < 1 || T < 1 || V < 1 || T > kMaxT) return 0;
+  int split = 1, chunk = 1;
+  gdn::accept_split(B, T, V, &split, &chunk);
+  const size_t rows = static_cast<size_t>(B) * (T + 1);
+  return rows * split * (sizeof(float) + sizeof(int32_t)) + 256;
+}
+
+gdn_status spec_accept_prefix(int32_t B, int32_t T, int32_t V, const int32_t* parent,
+                              const int32_t* draft, const void* logits, int32_t logits_dtype,
+                              int32_t* n_keep, int32_t* path, int32_t* bonus, void* workspace,
+                              size_t workspace_bytes, int32_t* dev_err, void* stream) {
+  if (B < 1 || T < 1 || V < 1) return GDN_ERR_INVALID_ARG;
+  if (logits_dtype != GDN_F32 && logits_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (!draft || !logits || !n_keep || !path || !bonus) return GDN_ERR_INVALID_ARG;
+  if (T > kMaxT) return GDN_ERR_UNSUPPORTED;
+  const size_t need = spec_accept_workspace_bytes(B, T, V);
+  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  gdn::AcceptArgs a{};
+  a.logits = logits;
+  a.parent = parent;
+  a.draft = draft;
+  a.n_keep = n_keep;
+  a.path = path;
+  a.bonus = bonus;
+  a.dev_err = dev_err;
+  a.B = B;
+  a.T = T;
+  a.V = V;
+  gdn::accept_split(B, T, V, &a.split, &a.chunk);
+  // 256-byte aligned partial arrays inside the workspace
+  uintptr_t base = (reinterpret_cast<uintptr_t>(workspace) + 255) & ~static_cast<uintptr_t>(255);
+  const size_t n = static_cast<size_t>(B) * (T + 1) * a.split;
+  a.part_val = reinterpret_cast<float*>(base);
+  a.part_idx = reinterpret_cast<int32_t*>(base + n * sizeof(float));
+  return launch_status(gdn::launch_accept(a, logits_dtype, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_tape_rollback(const gdn_shape* shape, int32_t T, float* S, const gdn_tape* tape,
+                             const int32_t* path, const int32_t* n_keep, int32_t* dev_err,
+                             void* stream) {
+  gdn_status st = check_shape(shape, T);
+  if (st != GDN_OK) return st;
+  if (!S || !tape || !tape->u || !tape->k || !tape->g || !n_keep) return GDN_ERR_INVALID_ARG;
+  RollbackArgs r{};
+  r.S = S;
+  r.tu = tape->u;
+  r.tk = tape->k;
+  r.tg = tape->g;
+  r.path = path;
+  r.n_keep = n_keep;
+  r.dev_err = dev_err;
+  r.L = shape->n_layers;
+  r.B = shape->batch;
+  r.Hk = shape->n_k_heads;
+  r.Hv = shape->n_v_heads;
+  r.T = T;
+  return launch_status(gdn::launch_tape_rollback(r, shape->d_k, shape->d_v,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_conv_state_rollback(const gdn_shape* shape, int32_t T, void* conv_state,
+                                   const void* x, const int32_t* path, const int32_t* n_keep,
+                                   int32_t* win_idx, int32_t* dev_err, void* stream) {
+  gdn_status st = check_shape(shape, T);
+  if (st != GDN_OK) return st;
+  if (!conv_state || !x || !n_keep) return GDN_ERR_INVALID_ARG;
+  ConvRollbackArgs c{};
+  c.conv_state = conv_state;
+  c.x = x;
+  c.path = path;
+  c.n_keep = n_keep;
+  c.win_idx = win_idx;
+  c.dev_err = dev_err;
+  c.L = shape->n_layers;
+  c.B = shape->batch;
+  c.K = shape->conv_kernel;
+  c.T = T;
+  c.C = channels(shape);
+  return launch_status(gdn::launch_conv_rollback(c, shape->in_dtype,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+const char* gdn_status_string(int32_t status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+    default: return "GDN_UNKNOWN_STATUS";
+  }
+}
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// gdn_kernels.hpp -- internal launch interface between the C ABI (gdn_api.cpp)
+// and the gfx950 kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn_verify.h"
+
+namespace gdn {
+
+// Chain / tree verify (conv + L2 norm + gated delta rule + tape).
+struct VerifyArgs {
+  const void* x;
+  const void* conv_state;
+  const float* conv_w;
+  const void* a;
+  const void* b;
+  const float* S;
+  float* o;
+  float* tu;
+  float* tk;
+  float* tg;
+  const int32_t* parent;  // [B,T] or nullptr for a chain
+  int32_t* conv_win;      // [B,T,K] or nullptr
+  int32_t* dev_err;       // or nullptr
+  int L, B, Hk, Hv, K, T, silu;
+  float eps;
+  int C;
+};
+
+// Tape-replay rollback.
+struct RollbackArgs {
+  float* S;
+  const float* tu;
+  const float* tk;
+  const float* tg;
+  const int32_t* path;  // [B,T] or nullptr
+  const int32_t* n_keep;
+  int32_t* dev_err;
+  int L, B, Hk, Hv, T;
+};
+
+// Conv-window rollback.
+struct ConvRollbackArgs {
+  void* conv_state;
+  const void* x;
+  const int32_t* path;
+  const int32_t* n_keep;
+  int32_t* win_idx;
+  int32_t* dev_err;
+  int L, B, K, T, C;
+};
+
+// Greedy acceptance.
+struct AcceptArgs {
+  const void* logits;
+  const int32_t* parent;
+  const int32_t* draft;
+  int32_t* n_keep;
+  int32_t* path;
+  int32_t* bonus;
+  int32_t* dev_err;
+  float* part_val;  // [rows, split]
+  int32_t* part_idx;
+  int B, T, V, split, chunk;
+};
+
+// Each returns hipErrorInvalidValue for an uninstantiated combination, else
+// the launch status.  dtype: 0 fp32, 1 bf16.
+hipError_t launch_verify_wy(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
+hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream_t s);
+hipError_t launch_conv_rollback(const ConvRollbackArgs& a, int dtype, hipStream_t s);
+hipError_t launch_accept(const AcceptArgs& a, int dtype, hipStream_t s);
+
+// Accept kernel decomposition shared by the host sizing function and launch.
+void accept_split(int B, int T, int V, int* split, int* chunk);
+
+}  // namespace gdn

@@ -1,0 +1,219 @@
+// k_rollback.hip -- tape-replay rollback of the gated delta state and of the
+// conv window, for gfx950 (GDN page s4, "Tape-Replay rollback").
+//
+// State: the live buffer still holds the pre-verify snapshot S0.  Replaying
+// the accepted steps p_0..p_{n-1} from the tape,
+//   S <- g_{p_i} S + u_{p_i} k_{p_i}^T,
+// unrolls to one closed form,
+//   S_n = w_{-1} S0 + sum_i w_i u_{p_i} k_{p_i}^T,   w_i = prod_{j>i} g_{p_j},
+// so each element costs one read of S0, n fused multiply-adds against the
+// tape, and one write -- no products with the state.  n = 0 returns before
+// touching the state, so the cost is one state pass plus O(n) tape bytes.
+//
+// Layout: one 256-thread workgroup per (layer, seq, v-head, RB-row block);
+// every thread owns 4 float4 of the block, read and written fully coalesced.
+// The block's n tape rows (k: n x Dk, w-scaled u: n x RB) are staged in LDS.
+//
+// Conv window: new row j = row n+j of [old window; x[p_0]; ...; x[p_{n-1}]],
+// copied 16 bytes per thread; all sources are loaded before any store, so
+// the in-place update is safe.
+
+#include "gdn_common.hpp"
+#include "gdn_kernels.hpp"
+
+namespace gdn {
+namespace {
+
+template <int DK, int DV, int TMAX>
+__global__ __launch_bounds__(256) void k_tape_rollback(RollbackArgs p) {
+  constexpr int NT = 256;
+  constexpr int VPT = 4;                        // float4 per thread
+  constexpr int RB0 = NT * VPT * 4 / DK;        // rows that fill the block
+  constexpr int RB = RB0 < DV ? RB0 : DV;
+  constexpr int NRBLK = DV / RB;
+  constexpr int C4 = DK / 4;                    // float4 per row
+  constexpr int NV = RB * C4;                   // float4 in the block
+  static_assert(DV % RB == 0, "row blocks");
+
+  __shared__ float s_k[TMAX * DK];
+  __shared__ float s_u[TMAX * RB];
+  __shared__ float s_w[TMAX];
+  __shared__ int s_pi[TMAX];
+  __shared__ int s_bad;
+
+  const int tid = threadIdx.x;
+  const int rblk = blockIdx.x % NRBLK;
+  const int rest = blockIdx.x / NRBLK;
+  const int hv = rest % p.Hv;
+  const size_t lb = rest / p.Hv;
+  const int bb = static_cast<int>(lb % p.B);
+  const int l = static_cast<int>(lb / p.B);
+  const int T = p.T;
+  const int n = p.n_keep[bb];
+  if (n == 0) return;
+  if (n < 0 || n > T) {
+    if (tid == 0 && p.dev_err && l == 0 && hv == 0 && rblk == 0) atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
+    return;
+  }
+  const int hk = hv / (p.Hv / p.Hk);
+  const int r0 = rblk * RB;
+  float* Sblk = p.S + ((lb * p.Hv + hv) * DV + r0) * static_cast<size_t>(DK);
+
+  // Snapshot loads first; the tape staging below overlaps their latency.
+  floatx4 sv[VPT];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int e = tid + v * NT;
+    if (e < NV) sv[v] = reinterpret_cast<const floatx4*>(Sblk)[e];
+  }
+
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (tid < n) {
+    const int pi = p.path ? p.path[static_cast<size_t>(bb) * T + tid] : tid;
+    if (pi < 0 || pi >= T) s_bad = 1;
+    s_pi[tid] = pi < 0 ? 0 : (pi >= T ? T - 1 : pi);
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0 && p.dev_err && l == 0 && hv == 0 && rblk == 0) atomicOr(p.dev_err, GDN_DEV_ERR_PATH);
+    return;
+  }
+  if (tid < n) {  // w_i = prod_{j>i} g_{p_j}
+    float w = 1.f;
+    for (int j = tid + 1; j < n; ++j) w *= p.tg[(lb * T + s_pi[j]) * p.Hv + hv];
+    s_w[tid] = w;
+  }
+  for (int e = tid; e < n * DK; e += NT) {
+    const int i = e / DK, c = e % DK;
+    s_k[e] = p.tk[((lb * T + s_pi[i]) * p.Hk + hk) * DK + c];
+  }
+  __syncthreads();
+  for (int e = tid; e < n * RB; e += NT) {
+    const int i = e / RB, r = e % RB;
+    s_u[e] = s_w[i] * p.tu[((lb * T + s_pi[i]) * p.Hv + hv) * DV + r0 + r];
+  }
+  __syncthreads();
+  const float gam = s_w[0] * p.tg[(lb * T + s_pi[0]) * p.Hv + hv];
+
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int e = tid + v * NT;
+    if (e < NV) {
+      const int r = e / C4, c = (e % C4) * 4;
+      floatx4 acc = sv[v] * gam;
+      for (int i = 0; i < n; ++i) {
+        const float u = s_u[i * RB + r];
+        const floatx4 k = *reinterpret_cast<const floatx4*>(s_k + i * DK + c);
+        acc[0] = fmaf(u, k[0], acc[0]);
+        acc[1] = fmaf(u, k[1], acc[1]);
+        acc[2] = fmaf(u, k[2], acc[2]);
+        acc[3] = fmaf(u, k[3], acc[3]);
+      }
+      reinterpret_cast<floatx4*>(Sblk)[e] = acc;
+    }
+  }
+}
+
+template <int DK, int DV>
+hipError_t launch_rb(const RollbackArgs& a, hipStream_t s) {
+  constexpr int RB0 = 256 * 4 * 4 / DK;
+  constexpr int RB = RB0 < DV ? RB0 : DV;
+  const long long grid = static_cast<long long>(a.L) * a.B * a.Hv * (DV / RB);
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.T <= 16)
+    hipLaunchKernelGGL((k_tape_rollback<DK, DV, 16>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_tape_rollback<DK, DV, 64>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// 16-byte chunks of channels per thread; KM1 = K-1 window rows.
+template <int ESZ, int KM1>
+__global__ __launch_bounds__(256) void k_conv_rollback(ConvRollbackArgs p) {
+  constexpr int EPC = 16 / ESZ;  // elements per chunk
+  const int tid = threadIdx.x;
+  const size_t lb = blockIdx.x;
+  const int bb = static_cast<int>(lb % p.B);
+  const int l = static_cast<int>(lb / p.B);
+  const int n = p.n_keep[bb];
+  const int T = p.T;
+  const bool first_block = (l == 0 && blockIdx.y == 0);
+  if (n < 0 || n > T) {
+    if (first_block && tid == 0 && p.dev_err) atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
+    return;
+  }
+  int idx[KM1];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < KM1; ++j) {
+    int id = n + j - KM1;  // position in [old rows; accepted rows], minus KM1
+    if (id >= 0 && p.path) {
+      id = p.path[static_cast<size_t>(bb) * T + id];
+      if (id < 0 || id >= T) {
+        bad = true;
+        id = 0;
+      }
+    }
+    idx[j] = id;
+  }
+  if (bad) {
+    if (first_block && tid == 0 && p.dev_err) atomicOr(p.dev_err, GDN_DEV_ERR_PATH);
+    return;
+  }
+  if (p.win_idx && first_block && tid == 0) {
+#pragma unroll
+    for (int j = 0; j < KM1; ++j) p.win_idx[static_cast<size_t>(bb) * KM1 + j] = idx[j];
+  }
+  if (n == 0) return;  // window unchanged
+  const size_t chunk = static_cast<size_t>(blockIdx.y) * 256 + tid;
+  const size_t row_chunks = static_cast<size_t>(p.C) / EPC;
+  if (chunk >= row_chunks) return;
+  const uint4* xs = static_cast<const uint4*>(p.x);
+  uint4* cs = static_cast<uint4*>(p.conv_state);
+  uint4 v[KM1];
+#pragma unroll
+  for (int j = 0; j < KM1; ++j) {
+    const int id = idx[j];
+    v[j] = id < 0 ? cs[(lb * KM1 + (KM1 + id)) * row_chunks + chunk]
+                  : xs[(lb * T + id) * row_chunks + chunk];
+  }
+#pragma unroll
+  for (int j = 0; j < KM1; ++j) cs[(lb * KM1 + j) * row_chunks + chunk] = v[j];
+}
+
+template <int ESZ>
+hipError_t launch_crb(const ConvRollbackArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.K) {
+    case 2: hipLaunchKernelGGL((k_conv_rollback<ESZ, 1>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_conv_rollback<ESZ, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_conv_rollback<ESZ, 3>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((k_conv_rollback<ESZ, 4>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((k_conv_rollback<ESZ, 5>), grid, dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((k_conv_rollback<ESZ, 6>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_conv_rollback<ESZ, 7>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream_t s) {
+  if (dk != dv) return hipErrorInvalidValue;
+  switch (dk) {
+    case 32: return launch_rb<32, 32>(a, s);
+    case 64: return launch_rb<64, 64>(a, s);
+    case 128: return launch_rb<128, 128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_conv_rollback(const ConvRollbackArgs& a, int dtype, hipStream_t s) {
+  const int esz = dtype == 1 ? 2 : 4;
+  const int chunks = a.C * esz / 16;
+  dim3 grid(static_cast<unsigned>(a.L) * a.B, (chunks + 255) / 256);
+  return dtype == 1 ? launch_crb<2>(a, grid, s) : launch_crb<4>(a, grid, s);
+}
+
+}  // namespace gdn

@@ -1,0 +1,109 @@
+"""One speculative round through a GDN layer stack, as calls into the C ABI.
+
+A round is: per layer, verify the drafted chain (or tree) reading the live
+state and conv window as the snapshot; accept the greedy prefix (or tree
+path) from the target logits; then roll the whole stack back in two calls,
+the state by tape replay and the conv window by re-gathering the accepted raw
+rows ("Speculative Decoding on GDN Hybrid Architectures", s4; accept rule:
+xserv "Phase 25", s2).  Nothing in a round synchronises with the host: the
+accepted lengths and paths stay on the device between the calls.
+
+This module only orders the calls and owns the device buffers; all
+arithmetic happens in libgdnverify.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+from . import binding as gb
+
+
+@dataclass
+class RoundBuffers:
+    """Device buffers of one layer stack for chunks / trees of T nodes."""
+    sh: gb.GdnShape
+    T: int
+    V: int
+    tree: bool
+    S: torch.Tensor            # [L,B,Hv,Dv,Dk] live state (= snapshot during verify)
+    conv_state: torch.Tensor   # [L,B,K-1,C] live conv window
+    conv_w: torch.Tensor       # [L,C,K]
+    x: torch.Tensor            # [L,B,T,C] drafted raw qkv (also the tape's qkv entry)
+    a: torch.Tensor            # [L,B,T,Hv]
+    b: torch.Tensor            # [L,B,T,Hv]
+    logits: torch.Tensor       # [B,T+1,V]
+    draft: torch.Tensor        # [B,T] int32
+    parent: Optional[torch.Tensor]  # [B,T] int32 for trees
+    o: torch.Tensor = None
+    tape: gb.Tape = None
+    n_keep: torch.Tensor = None
+    path: torch.Tensor = None
+    bonus: torch.Tensor = None
+    workspace: torch.Tensor = None
+    win_idx: torch.Tensor = None
+    conv_win: Optional[torch.Tensor] = None
+    dev_err: torch.Tensor = None
+    layer_shape: gb.GdnShape = field(init=False)
+
+    def __post_init__(self):
+        sh, T, dev = self.sh, self.T, self.S.device
+        f32 = dict(device=dev, dtype=torch.float32)
+        i32 = dict(device=dev, dtype=torch.int32)
+        if self.o is None:
+            self.o = torch.empty((sh.L, sh.B, T, sh.Hv, sh.Dv), **f32)
+        if self.tape is None:
+            self.tape = gb.Tape.empty(sh, T, dev)
+        self.n_keep = torch.zeros((sh.B,), **i32)
+        self.path = torch.full((sh.B, T), -1, **i32)
+        self.bonus = torch.zeros((sh.B,), **i32)
+        self.workspace = torch.empty((gb.spec_accept_workspace_bytes(sh.B, T, self.V),),
+                                     device=dev, dtype=torch.uint8)
+        self.win_idx = torch.zeros((sh.B, sh.K - 1), **i32)
+        if self.tree and self.conv_win is None:
+            self.conv_win = torch.zeros((sh.B, T, sh.K), **i32)
+        self.dev_err = torch.zeros((1,), **i32)
+        self.layer_shape = gb.GdnShape(1, sh.B, sh.Hk, sh.Hv, sh.Dk, sh.Dv, sh.K, sh.silu,
+                                       sh.eps, sh.dtype)
+
+    def layer_tape(self, l: int) -> gb.Tape:
+        return gb.Tape(self.tape.u[l:l + 1], self.tape.k[l:l + 1], self.tape.g[l:l + 1])
+
+
+def verify_layer(rb: RoundBuffers, l: int, stream=None):
+    """Verify layer l (one C-ABI call; S and conv_state are not written)."""
+    sl = slice(l, l + 1)
+    if rb.tree:
+        gb.gdn_tree_verify(rb.layer_shape, rb.parent, rb.x[sl], rb.conv_state[sl],
+                           rb.conv_w[sl], rb.a[sl], rb.b[sl], rb.S[sl], rb.o[sl],
+                           rb.layer_tape(l), conv_win=rb.conv_win if l == 0 else None,
+                           dev_err=rb.dev_err, stream=stream)
+    else:
+        gb.gdn_verify_chunk(rb.layer_shape, rb.x[sl], rb.conv_state[sl], rb.conv_w[sl],
+                            rb.a[sl], rb.b[sl], rb.S[sl], rb.o[sl], rb.layer_tape(l),
+                            stream=stream)
+
+
+def accept(rb: RoundBuffers, stream=None):
+    gb.spec_accept_prefix(rb.draft, rb.logits, rb.n_keep, rb.path, rb.bonus, rb.workspace,
+                          parent=rb.parent if rb.tree else None, dev_err=rb.dev_err,
+                          stream=stream)
+
+
+def rollback(rb: RoundBuffers, stream=None):
+    """Tape-replay the state and rebuild the conv window for all layers."""
+    path = rb.path if rb.tree else None
+    gb.gdn_tape_rollback(rb.sh, rb.S, rb.tape, rb.n_keep, path=path, dev_err=rb.dev_err,
+                         stream=stream)
+    gb.gdn_conv_state_rollback(rb.sh, rb.conv_state, rb.x, rb.n_keep, path=path,
+                               win_idx=rb.win_idx, dev_err=rb.dev_err, stream=stream)
+
+
+def run_round(rb: RoundBuffers, stream=None):
+    """verify (per layer) -> accept -> rollback, all enqueued on one stream."""
+    for l in range(rb.sh.L):
+        verify_layer(rb, l, stream)
+    accept(rb, stream)
+    rollback(rb, stream)

@@ -1,0 +1,102 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_decode_verify_gdn_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_verify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gb.LIB_PATH):
+        from speculative_decode_verify_gdn_amd import build
+        build.build()
+    return gb.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(gb.EXPORTS) <= set(names), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert gb.abi_version() == 1
+    assert gb.status_string(0) == "GDN_OK"
+    assert gb.status_string(1) == "GDN_ERR_INVALID_ARG"
+    assert gb.status_string(4) == "GDN_ERR_WORKSPACE"
+    assert gb.status_string(99) == "GDN_UNKNOWN_STATUS"
+
+
+def test_workspace_size(lib):
+    assert gb.spec_accept_workspace_bytes(32, 8, 151936) > 32 * 9 * 8
+    assert gb.spec_accept_workspace_bytes(0, 8, 100) == 0
+    assert gb.spec_accept_workspace_bytes(1, 65, 100) == 0
+
+
+def _shape(**kw):
+    d = dict(L=1, B=2, Hk=2, Hv=4, Dk=128, Dv=128, K=4)
+    d.update(kw)
+    return gb.GdnShape(**d).c()
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _verify(shape, T=4, null_x=False):
+    tape = gb._CTape(FAKE.value, FAKE.value, FAKE.value)
+    x = None if null_x else FAKE
+    return gb.lib().gdn_verify_chunk(ctypes.byref(shape), T, x, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, ctypes.byref(tape), None)
+
+
+def test_host_validation_before_launch(lib):
+    assert _verify(_shape(), null_x=True) == gb.GDN_ERR_INVALID_ARG
+    assert _verify(_shape(Hv=3)) == gb.GDN_ERR_INVALID_ARG          # Hv % Hk != 0
+    assert _verify(_shape(), T=0) == gb.GDN_ERR_INVALID_ARG
+    assert _verify(_shape(), T=65) == gb.GDN_ERR_UNSUPPORTED
+    assert _verify(_shape(Dk=96, Dv=96)) == gb.GDN_ERR_UNSUPPORTED
+    assert _verify(_shape(Dk=64, Dv=128)) == gb.GDN_ERR_UNSUPPORTED
+    assert _verify(_shape(K=9)) == gb.GDN_ERR_UNSUPPORTED
+    assert _verify(_shape(B=0)) == gb.GDN_ERR_INVALID_ARG
+    tape = gb._CTape(FAKE.value, FAKE.value, None)
+    assert lib.gdn_tape_rollback(ctypes.byref(_shape()), 4, FAKE, ctypes.byref(tape), None, FAKE,
+                                 None, None) == gb.GDN_ERR_INVALID_ARG
+    assert lib.gdn_conv_state_rollback(ctypes.byref(_shape()), 4, FAKE, FAKE, None, None, None,
+                                       None, None) == gb.GDN_ERR_INVALID_ARG
+    assert lib.gdn_tree_verify(ctypes.byref(_shape()), 4, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, ctypes.byref(gb._CTape(1, 1, 1)), None, None,
+                               None) == gb.GDN_ERR_INVALID_ARG
+    # accept: missing / short workspace, bad dtype
+    assert lib.spec_accept_prefix(2, 4, 100, None, FAKE, FAKE, gb.GDN_BF16, FAKE, FAKE, FAKE,
+                                  FAKE, 8, None, None) == gb.GDN_ERR_WORKSPACE
+    assert lib.spec_accept_prefix(2, 4, 100, None, FAKE, FAKE, 7, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 20, None, None) == gb.GDN_ERR_INVALID_ARG
+    assert lib.spec_accept_prefix(2, 4, 100, None, None, FAKE, gb.GDN_BF16, FAKE, FAKE, FAKE,
+                                  FAKE, 1 << 20, None, None) == gb.GDN_ERR_INVALID_ARG
+
+
+def test_binding_rejects_mismatched_tensors():
+    import torch
+    sh = gb.GdnShape(1, 1, 1, 1, 32, 32, 4, dtype=torch.float32)
+    x = torch.zeros((1, 1, 4, sh.C))
+    with pytest.raises((ValueError, TypeError)):
+        gb._need(x, "x", torch.float32, (1, 1, 5, sh.C))
+    with pytest.raises(TypeError):
+        gb._need(x, "x", torch.bfloat16, (1, 1, 4, sh.C))
+    with pytest.raises(ValueError):  # host tensor
+        gb._need(x, "x", torch.float32, (1, 1, 4, sh.C))
