@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark: speculative rounds through a 30-layer GDN stack on one MI355X.
+
+One step = one speculative round over the whole stack, all on one stream:
+  30 x gdn_verify_chunk (or gdn_tree_verify)  ->  spec_accept_prefix
+  ->  gdn_tape_rollback (all layers)  ->  gdn_conv_state_rollback (all layers)
+with every input already resident in HBM.  The round is captured once per
+input set into a HIP graph and replayed (eager with --eager).
+
+Prints ONE JSON line.  `value` is verified draft tokens per second for the
+30-layer stack (B * T drafted tokens per round / round time).  Extra fields
+give accepted and committed tokens/s, rollback time per round, whole-round
+HBM fraction from the algorithmic byte model, the dominant kernel's roofline
+(measured with HIP events around its launches on the launch stream), and the
+fp64 oracle's throughput on a bounded sample on the host cores.
+
+Workloads (seeded synthetic, Qwen3.6-shaped GDN layers: 16 q/k heads and
+32 v heads of 128, conv kernel 4, bf16 inputs, fp32 state):
+  --config 3 (default)  30 layers, batch 32, N=8 chain, per-position acceptance 0.36
+  --config 4            30 layers, batch 256, N=16 chain, acceptance 0.85
+  --config 5            30 layers, batch 64, 64-node draft trees
+  --config 1 / 2        tiny and one-layer cases (launch-bound; parity cases)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--input-sets", type=int, default=4,
+                    help="distinct pre-generated rounds of drafts/logits cycled through")
+    ap.add_argument("--eager", action="store_true", help="launch without HIP graph capture")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target host time of the oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--sweep-n", action="store_true",
+                    help="also time rollback with every sequence forced to n = 0..T")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------- byte model --
+
+def verify_bytes_per_launch(cfg, B) -> int:
+    """Algorithmic HBM bytes of one verify launch (one layer, B sequences)."""
+    esz = 2 if cfg.dtype == torch.bfloat16 else 4
+    T, C = cfg.T, cfg.C
+    P = cfg.Hv * cfg.Dv * cfg.Dk * 4                     # state read once
+    per_tok = (C * esz                                  # raw qkv row
+               + 2 * cfg.Hv * esz                       # gates a, b
+               + cfg.Hv * cfg.Dv * 4                    # output o
+               + cfg.Hv * cfg.Dv * 4 + cfg.Hk * cfg.Dk * 4 + cfg.Hv * 4)  # tape u, k, g
+    per_seq = P + T * per_tok + (cfg.K - 1) * C * esz  # + conv window read
+    if cfg.is_tree:
+        per_seq += T * 4 + T * cfg.K * 4 // cfg.L       # parent array; conv_win once per stack
+    return B * per_seq + C * cfg.K * 4                  # + conv weights
+
+
+def rollback_bytes(cfg, n_keep: np.ndarray) -> int:
+    """Tape replay: for n >= 1 read + write the state, read n tape entries."""
+    P = cfg.Hv * cfg.Dv * cfg.Dk * 4
+    tape_tok = cfg.Hv * cfg.Dv * 4 + cfg.Hk * cfg.Dk * 4 + cfg.Hv * 4
+    n = n_keep.astype(np.int64)
+    return int(cfg.L * np.sum((n >= 1) * 2 * P + n * tape_tok))
+
+
+def conv_rollback_bytes(cfg, n_keep: np.ndarray) -> int:
+    esz = 2 if cfg.dtype == torch.bfloat16 else 4
+    return int(cfg.L * np.sum(n_keep >= 1) * 2 * (cfg.K - 1) * cfg.C * esz)
+
+
+def accept_bytes(cfg, B) -> int:
+    return B * (cfg.T + 1) * cfg.V * 2 + B * cfg.T * 4 * (2 if cfg.is_tree else 1)
+
+
+# ---------------------------------------------------------------- helpers --
+
+def calib_copy():
+    n = 256 << 20
+    a = torch.empty(n // 4, device="cuda", dtype=torch.float32).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 5}))
+
+
+def build_sets(cfg, n_sets, dev):
+    from speculative_decode_verify_gdn_amd import workload as W
+    base = W.layer_inputs(cfg, 0, dev)
+    sets = []
+    for r in range(n_sets):
+        inp = W.layer_inputs(cfg, r, dev) if r else base
+        acc = W.tree_accept_inputs(cfg, r, dev) if cfg.is_tree else W.chain_accept_inputs(cfg, r, dev)
+        sets.append((inp, acc))
+    return base, sets
+
+
+def oracle_baseline(cfg, seconds: float) -> dict:
+    """Time the fp64 oracle's round on a bounded sample of (layer, sequence)
+    units -- verify, accept, tape and conv rollback for L_s layers of B_s
+    sequences -- and scale to the whole stack: the units are independent and
+    equal in cost, so t_round = t_sample * (L * B) / (L_s * B_s)."""
+    import oracle
+    from speculative_decode_verify_gdn_amd import workload as W
+
+    def one(L_s, B_s):
+        c = cfg.with_(L=L_s, B=B_s)
+        inp = {k: W.to_f64(v) for k, v in W.layer_inputs(c, 0, "cpu").items()}
+        acc = W.tree_accept_inputs(c, 0, "cpu") if c.is_tree else W.chain_accept_inputs(c, 0, "cpu")
+        sh = oracle.Shape(L_s, B_s, c.Hk, c.Hv, c.Dk, c.Dv, c.K, c.silu, c.eps)
+        draft = acc["draft"].numpy()
+        logits = W.to_f64(acc["logits"])
+        parent = acc["parent"].numpy() if c.is_tree else None
+        keys = ("x", "conv_state", "conv_w", "a", "b", "S0")
+        t0 = time.perf_counter()
+        if parent is None:
+            out = oracle.verify_chunk(sh, *[inp[k] for k in keys], want_final=False)
+        else:
+            out = oracle.tree_verify(sh, parent, *[inp[k] for k in keys])
+        n, path, _ = oracle.accept(draft, logits, parent)
+        pth = path if parent is not None else None
+        oracle.tape_rollback(sh, inp["S0"], out["u"], out["k"], out["g"], n, pth)
+        oracle.conv_rollback(sh, inp["conv_state"], inp["x"], n, pth)
+        return time.perf_counter() - t0
+
+    oracle.build(force=False)
+    nthr = max(1, oracle.num_threads())
+    L_s = min(cfg.L, nthr)
+    # fp64 host bytes one sampled sequence needs (state twice, o, u, x, logits)
+    per_seq = L_s * 8 * (2 * cfg.Hv * cfg.Dv * cfg.Dk + 2 * cfg.T * cfg.Hv * cfg.Dv
+                         + cfg.T * cfg.C) + 8 * (cfg.T + 1) * cfg.V
+    b_cap = int(max(1, min(cfg.B, 3e9 // per_seq)))
+    B_s = min(2, b_cap)
+    t = one(L_s, B_s)
+    want = int(B_s * seconds / max(t, 1e-3))
+    if want > B_s:
+        B_s = int(min(b_cap, want))
+        t = one(L_s, B_s)
+    t_round = t * (cfg.L * cfg.B) / (L_s * B_s)
+    return {"value": cfg.B * cfg.T / t_round, "unit": "tokens/s", "cores": nthr,
+            "kind": "oracle",
+            "sample": "fp64 oracle round (verify, accept, tape and conv rollback) on %d layers x "
+                      "%d sequences of the %d x %d workload in %.1f s, scaled by unit count to "
+                      "%.1f s per round" % (L_s, B_s, cfg.L, cfg.B, t, t_round)}
+
+
+# ------------------------------------------------------------------- main --
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU only: this build runs on a single MI355X "
+                         "and has no multi-GPU path (got --gpus %d)\n" % args.gpus)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py needs a GPU\n")
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+
+    from speculative_decode_verify_gdn_amd import binding as gb
+    from speculative_decode_verify_gdn_amd import spec_round as sr
+    from speculative_decode_verify_gdn_amd import workload as W
+    gb.lib()  # fail loudly if the HIP library is missing
+
+    cfg = W.CONFIGS[args.config]
+    dev = "cuda"
+    torch.cuda.empty_cache()
+    base, sets = build_sets(cfg, args.input_sets, dev)
+    S = base["S0"]
+    cs = base["conv_state"]
+    conv_w = base["conv_w"]
+    shared = None
+    rbs = []
+    for inp, acc in sets:
+        rb = sr.RoundBuffers(sh=gb.GdnShape(cfg.L, cfg.B, cfg.Hk, cfg.Hv, cfg.Dk, cfg.Dv, cfg.K,
+                                            cfg.silu, cfg.eps, cfg.dtype),
+                             T=cfg.T, V=cfg.V, tree=cfg.is_tree, S=S, conv_state=cs,
+                             conv_w=conv_w, x=inp["x"], a=inp["a"], b=inp["b"],
+                             logits=acc["logits"], draft=acc["draft"],
+                             parent=acc.get("parent") if cfg.is_tree else None,
+                             o=None if shared is None else shared.o,
+                             tape=None if shared is None else shared.tape)
+        if shared is None:
+            shared = rb
+        rbs.append(rb)
+    stream = torch.cuda.Stream()
+    n_hist = torch.zeros((args.steps, cfg.B), dtype=torch.int32, device=dev)
+
+    graphs = []
+    with torch.cuda.stream(stream):
+        for rb in rbs:  # eager warm-up of every set (also loads code objects)
+            sr.run_round(rb)
+        torch.cuda.synchronize()
+        if not args.eager:
+            for rb in rbs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    sr.run_round(rb)
+                graphs.append(g)
+        torch.cuda.synchronize()
+
+        def step(i):
+            if graphs:
+                graphs[i % len(rbs)].replay()
+            else:
+                sr.run_round(rbs[i % len(rbs)])
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = e0.elapsed_time(e1)
+
+        # Kernel pass: same rounds, eager, HIP events around each launch group
+        # on the launch stream (per-kernel durations; not the headline).
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        v_ms, a_ms, r_ms = [], [], []
+        for i in range(args.steps):
+            rb = rbs[i % len(rbs)]
+            for l in range(cfg.L):
+                s0, s1 = ev(), ev()
+                s0.record(stream)
+                sr.verify_layer(rb, l)
+                s1.record(stream)
+                v_ms.append((s0, s1))
+            s0, s1 = ev(), ev()
+            s0.record(stream)
+            sr.accept(rb)
+            s1.record(stream)
+            a_ms.append((s0, s1))
+            n_hist[i].copy_(rb.n_keep)
+            s0, s1 = ev(), ev()
+            s0.record(stream)
+            sr.rollback(rb)
+            s1.record(stream)
+            r_ms.append((s0, s1))
+        torch.cuda.synchronize()
+    verify_ms = float(np.mean([a.elapsed_time(b) for a, b in v_ms]))
+    accept_ms = float(np.mean([a.elapsed_time(b) for a, b in a_ms]))
+    rollback_ms = float(np.mean([a.elapsed_time(b) for a, b in r_ms]))
+    assert int(shared.dev_err.item()) == 0, "device-side error bits set"
+
+    ms = total_ms / args.steps
+    n_keep = n_hist.cpu().numpy()
+    B, T = cfg.B, cfg.T
+    vb = verify_bytes_per_launch(cfg, B)
+    round_bytes = [cfg.L * vb + accept_bytes(cfg, B) + rollback_bytes(cfg, n_keep[i])
+                   + conv_rollback_bytes(cfg, n_keep[i]) for i in range(args.steps)]
+    mean_round_bytes = float(np.mean(round_bytes))
+    verify_gbs = vb / (verify_ms * 1e-3) / 1e9
+    acc_tok = float(n_keep.sum()) / args.steps
+    out = {
+        "metric": "verified draft tokens/s per 30-layer GDN stack",
+        "value": B * T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.L, "batch": B,
+                   "drafts" if not cfg.is_tree else "tree_nodes": T,
+                   "acceptance": (cfg.p_accept if cfg.law == "bernoulli" else cfg.law),
+                   "k_heads": cfg.Hk, "v_heads": cfg.Hv, "d_k": cfg.Dk, "d_v": cfg.Dv,
+                   "conv_kernel": cfg.K, "inputs": "bf16" if cfg.dtype == torch.bfloat16 else "f32",
+                   "state": "f32", "vocab": cfg.V, "hip_graph": not args.eager,
+                   "input_sets": len(rbs)},
+        "accepted_tokens_per_s": acc_tok / (ms * 1e-3),
+        "committed_tokens_per_s": (acc_tok + B) / (ms * 1e-3),
+        "rollback_us": rollback_ms * 1e3,
+        "round_hbm_frac": mean_round_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "round_algorithmic_bytes": mean_round_bytes,
+        "kernel_ms": {"verify_per_layer": verify_ms, "accept": accept_ms,
+                      "rollback_state_and_conv": rollback_ms},
+        "roofline": {"kernel": "k_verify_wy (gdn_verify_chunk / gdn_tree_verify, one layer)",
+                     "bound": "hbm", "achieved": verify_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": verify_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": vb},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = oracle_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
