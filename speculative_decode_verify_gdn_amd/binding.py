@@ -172,7 +172,7 @@ def _verify_ptrs(sh: GdnShape, T: int, x, conv_state, conv_w, a, b, S, o):
     dt = sh.dtype
     return [_need(x, "x", dt, (sh.L, sh.B, T, sh.C)),
             _need(conv_state, "conv_state", dt, (sh.L, sh.B, sh.K - 1, sh.C)),
-            _need(conv_w, "conv_w", torch.float32, (sh.L, sh.C, sh.K), 4),
+            _need(conv_w, "conv_w", torch.float32, (sh.L, sh.C, sh.K)),
             _need(a, "a", dt, (sh.L, sh.B, T, sh.Hv), 2),
             _need(b, "b", dt, (sh.L, sh.B, T, sh.Hv), 2),
             _need(S, "S", torch.float32, (sh.L, sh.B, sh.Hv, sh.Dv, sh.Dk)),

@@ -9,6 +9,7 @@ namespace gdn {
 constexpr int kWave = 64;  // CDNA wavefront width
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes
 
 // Input element loads: fp32 as is, bf16 (raw uint16 bits) widened exactly.
 __device__ __forceinline__ float ld_in(const float* p, size_t i) { return p[i]; }

@@ -23,6 +23,10 @@
 // ROWS-row block of S); the rows of S are independent recurrences sharing
 // q, k and the gates.  Each wave owns 16-row tiles of S; lane (c16 = lane%16,
 // kk = lane/16) holds S0[row c16][16m + 4kk .. +3] for every 16-column step m.
+// The per-head prologue (conv, L2 norm, Gram on MFMA, the T x T algebra)
+// runs while the state loads are in flight.
+
+#include <stdlib.h>
 
 #include "gdn_common.hpp"
 #include "gdn_kernels.hpp"
@@ -34,39 +38,56 @@ constexpr int kMaxK = 8;
 constexpr int kNT = 256;
 constexpr int kNWave = kNT / kWave;
 
-template <int DK, int DV, int TMAX, int ROWS, typename TIn>
+// Sum over aligned groups of 8 lanes (DPP; every lane gets its group's sum).
+__device__ __forceinline__ float sum8(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+__device__ __forceinline__ float silu(float y) { return y / (1.f + __expf(-y)); }
+
+// Back to the input dtype; exact for values that were widened from it.
+template <typename TIn>
+__device__ __forceinline__ TIn to_in(float v);
+template <>
+__device__ __forceinline__ float to_in<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t to_in<uint16_t>(float v) {
+  return static_cast<uint16_t>(__float_as_uint(v) >> 16);
+}
+
+template <int DK, int DV, int TMAX, int ROWS, int KM, typename TIn>
 struct VerifyLayout {
   static constexpr int KQ_ROWS = 2 * TMAX;  // k rows [0,TMAX), q rows [TMAX,2TMAX)
   static constexpr int KQ_LD = DK + 4;      // +4 floats: conflict-free float4 column reads
   static constexpr int RHS_LD = ROWS + 4;
   static constexpr int CO_LD = TMAX + 1;
   static constexpr int NCH = 2 * DK + ROWS;  // q, k of the k-head; v rows of the block
-  static constexpr int XR = TMAX + kMaxK - 1;
-  static constexpr int COEF_BYTES = 3 * TMAX * CO_LD * 4;
-  static constexpr int STAGE_FULL = XR * NCH * (int)sizeof(TIn);
-  static constexpr int STAGE_CAP = COEF_BYTES > 48 * 1024 ? COEF_BYTES : 48 * 1024;
-  // channels staged per pass (multiple of 64 unless everything fits)
-  static constexpr int CHK = STAGE_FULL <= STAGE_CAP
-                                 ? NCH
-                                 : ((STAGE_CAP / (XR * (int)sizeof(TIn))) / 64) * 64;
-  static constexpr int STAGE_BYTES = XR * CHK * (int)sizeof(TIn);
+  static constexpr int XR = TMAX + KM - 1;
+  // Raw conv inputs [old window rows; node rows] x [q | k | v-rows], staged
+  // with 16-byte loads; CPR = 16-byte chunks per row.
+  static constexpr int CPR = NCH * (int)sizeof(TIn) / 16;
+  static constexpr int STAGE_BYTES = XR * CPR * 16;
+  static constexpr int COEF_BYTES = 3 * TMAX * CO_LD * 4;  // [A;Oc] then [M2;Oc], and Ti
   static constexpr int U1_BYTES = STAGE_BYTES > COEF_BYTES ? STAGE_BYTES : COEF_BYTES;
-  static constexpr int KQ_BYTES = KQ_ROWS * KQ_LD * 4;
-  static constexpr int RHS_BYTES = TMAX * RHS_LD * 4;
-  static_assert(CHK >= 64, "staging chunk too small");
+  static constexpr int TOTAL = 2 * TMAX * KQ_LD * 4 + TMAX * RHS_LD * 4 + U1_BYTES + TMAX * 56 + 16;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget of one workgroup exceeded");
 };
 
-template <int DK, int DV, int TMAX, int ROWS, typename TIn>
+template <int DK, int DV, int TMAX, int ROWS, int KC, typename TIn>
 __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
-  using LY = VerifyLayout<DK, DV, TMAX, ROWS, TIn>;
+  constexpr int KM = KC > 0 ? KC : kMaxK;  // unroll bound of the conv taps
+  using LY = VerifyLayout<DK, DV, TMAX, ROWS, KM, TIn>;
   constexpr int KQ_LD = LY::KQ_LD, RHS_LD = LY::RHS_LD, CO_LD = LY::CO_LD;
-  constexpr int NCH = LY::NCH, CHK = LY::CHK;
+  constexpr int NCH = LY::NCH;
   constexpr int NRB = LY::KQ_ROWS / 16;
   constexpr int NTILE = ROWS / 16;
   constexpr int TPW = (NTILE + kNWave - 1) / kNWave;
   constexpr int MSTEPS = DK / 16;
   constexpr int NRBLK = DV / ROWS;
-  static_assert(ROWS % 16 == 0 && DV % ROWS == 0 && TMAX % 8 == 0, "tiling");
+  static_assert(ROWS % 16 == 0 && DV % ROWS == 0 && TMAX % 8 == 0 && TMAX <= 64, "tiling");
 
   __shared__ __align__(16) float s_kq[LY::KQ_ROWS * KQ_LD];
   __shared__ __align__(16) float s_rhs[TMAX * RHS_LD];        // v, then RHS
@@ -76,10 +97,8 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   __shared__ int s_par[TMAX];
   __shared__ int s_widx[TMAX * kMaxK];
   __shared__ int s_bad;
-  TIn* s_x = reinterpret_cast<TIn*>(s_u1);                      // [XR][CHK]
-  float* s_A = reinterpret_cast<float*>(s_u1);                  // [TMAX][CO_LD], later M2
-  float* s_Oc = s_A + TMAX * CO_LD;
-  float* s_Ti = s_Oc + TMAX * CO_LD;
+  float* s_G = reinterpret_cast<float*>(s_u1);  // [2TMAX][CO_LD]: KK then A (-> M2); QK then Oc
+  float* s_Ti = s_G + 2 * TMAX * CO_LD;         // [TMAX][CO_LD]
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -100,9 +119,71 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   const int hv = hk * G + g;
   const int r0 = rblk * ROWS;
   const int T = p.T;
-  const int K = p.K;
+  const int K = KC > 0 ? KC : p.K;
+  const bool tree = p.parent != nullptr;
 
-  // (1) State loads first: their HBM latency overlaps everything up to MFMA.
+  // (1) Issue every load up front, small inputs first and the state last.
+  //     Vector-memory loads return in order, so the prologue below waits only
+  //     for the small loads while the 64 KiB of state stay in flight.
+  const TIn* x = static_cast<const TIn*>(p.x);
+  const TIn* cs = static_cast<const TIn*>(p.conv_state);
+  const float* cw = p.conv_w + static_cast<size_t>(l) * p.C * K;
+  const TIn* xcol = x + lb * T * p.C;
+  const TIn* ccol = cs + lb * (K - 1) * p.C;
+  auto chan = [&](int c) {
+    return c < DK ? hk * DK + c
+                  : (c < 2 * DK ? p.Hk * DK + hk * DK + (c - DK)
+                                : 2 * p.Hk * DK + hv * DV + r0 + (c - 2 * DK));
+  };
+  // Every load below is unconditional, from a clamped always-valid address,
+  // with the value selected afterwards: a load under a branch makes the
+  // compiler wait for it at the join, which would serialise the prologue.
+  const int tq = tid < T ? tid : 0;
+  const int* par_ptr = tree ? p.parent + static_cast<size_t>(bb) * T + tq
+                            : reinterpret_cast<const int*>(p.S);
+  const int par_raw = *par_ptr;
+  const size_t gi = (lb * T + tq) * p.Hv + hv;
+  const float ga_ld = ld_in(static_cast<const TIn*>(p.a), gi);
+  const float gb_ld = ld_in(static_cast<const TIn*>(p.b), gi);
+  // Raw conv inputs: rows [old window; nodes] x channels [q | k | v-rows],
+  // each row three contiguous segments, fetched as 16-byte chunks.
+  constexpr int CPR = LY::CPR;
+  constexpr int EPC = 16 / (int)sizeof(TIn);  // elements per chunk
+  constexpr int XRR = TMAX + KM - 1;
+  constexpr int NRAW = (XRR * CPR + kNT - 1) / kNT;
+  const int nrows = K - 1 + T;
+  u32x4 raw[NRAW];
+#pragma unroll
+  for (int q = 0; q < NRAW; ++q) {
+    const int e = tid + q * kNT;
+    const int row = e / CPR, chunk = e % CPR;
+    const int rr = row < nrows ? row : nrows - 1;
+    const int c = chunk * EPC;  // first channel of the chunk
+    const TIn* base = rr < K - 1 ? ccol + static_cast<size_t>(rr) * p.C
+                                 : xcol + static_cast<size_t>(rr - (K - 1)) * p.C;
+    raw[q] = *reinterpret_cast<const u32x4*>(base + chan(c));
+  }
+  // conv weights of this thread's channels (one float4 when K == 4)
+  constexpr int NSLOT = (NCH + kNT - 1) / kNT;
+  float w[NSLOT][KM];
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    const int c = tid + sl * kNT;
+    const bool live = c < NCH;
+    const int ch = chan(live ? c : 0);
+    if (KC == 4) {
+      const floatx4 wv = *reinterpret_cast<const floatx4*>(cw + static_cast<size_t>(ch) * 4);
+#pragma unroll
+      for (int j = 0; j < KM; ++j) w[sl][j] = live ? wv[j] : 0.f;
+    } else {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const int jj = j < K ? j : 0;
+        const float wv = cw[static_cast<size_t>(ch) * K + jj];
+        w[sl][j] = (live && j < K) ? wv : 0.f;
+      }
+    }
+  }
   floatx4 sreg[TPW][MSTEPS];
   const float* S_head = p.S + (lb * p.Hv + hv) * static_cast<size_t>(DV * DK);
 #pragma unroll
@@ -111,8 +192,7 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
     if (tile < NTILE) {
       const float* rp = S_head + static_cast<size_t>(r0 + tile * 16 + c16) * DK + 4 * kk;
 #pragma unroll
-      for (int m = 0; m < MSTEPS; ++m)
-        sreg[tt][m] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(rp + 16 * m));
+      for (int m = 0; m < MSTEPS; ++m) sreg[tt][m] = *reinterpret_cast<const floatx4*>(rp + 16 * m);
     }
   }
 
@@ -120,15 +200,14 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   if (tid == 0) s_bad = 0;
   __syncthreads();
   if (tid < T) {
-    int pv = p.parent ? p.parent[static_cast<size_t>(bb) * T + tid] : tid - 1;
+    int pv = tree ? par_raw : tid - 1;
     if (pv < -1 || pv >= tid) {
       s_bad = 1;
       pv = -1;
     }
     s_par[tid] = pv;
-    const size_t gi = (lb * T + tid) * p.Hv + hv;
-    s_ga[tid] = ld_in(static_cast<const TIn*>(p.a), gi);
-    s_gb[tid] = ld_in(static_cast<const TIn*>(p.b), gi);
+    s_ga[tid] = ga_ld;
+    s_gb[tid] = gb_ld;
   }
   __syncthreads();
   if (s_bad) {
@@ -147,10 +226,6 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
         s_widx[tid * kMaxK + j] = --old;
       }
     }
-    // gamma_t: product of a over the node and all its ancestors
-    float gm = 1.f;
-    for (int c = tid; c >= 0; c = s_par[c]) gm *= s_ga[c];
-    s_gam[tid] = gm;
   }
   if (tid == 0) {
     for (int v = 0; v < T; ++v) {
@@ -164,32 +239,19 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
       p.conv_win[static_cast<size_t>(bb) * T * K + e] = s_widx[(e / K) * kMaxK + (e % K)];
   }
 
-  // (3) Conv + SiLU of this block's q, k and v channels for every node:
-  //     stage the raw rows [old window; x of all nodes] in LDS with one wide
-  //     burst of independent loads, then convolve out of LDS.
-  const TIn* x = static_cast<const TIn*>(p.x);
-  const TIn* cs = static_cast<const TIn*>(p.conv_state);
-  const int nrows = K - 1 + T;
-  for (int c0 = 0; c0 < NCH; c0 += CHK) {
-    const int nc = NCH - c0 < CHK ? NCH - c0 : CHK;
-    for (int e = tid; e < nrows * nc; e += kNT) {
-      const int row = e / nc, cl = e % nc, c = c0 + cl;
-      const int ch = c < DK ? hk * DK + c
-                            : (c < 2 * DK ? p.Hk * DK + hk * DK + (c - DK)
-                                          : 2 * p.Hk * DK + hv * DV + r0 + (c - 2 * DK));
-      s_x[row * CHK + cl] = row < K - 1 ? cs[(lb * (K - 1) + row) * p.C + ch]
-                                        : x[(lb * T + (row - (K - 1))) * p.C + ch];
-    }
-    __syncthreads();
-    for (int cl = tid; cl < nc; cl += kNT) {
-      const int c = c0 + cl;
-      const int ch = c < DK ? hk * DK + c
-                            : (c < 2 * DK ? p.Hk * DK + hk * DK + (c - DK)
-                                          : 2 * p.Hk * DK + hv * DV + r0 + (c - 2 * DK));
-      float w[kMaxK];
+  // (3) Conv + SiLU out of the staged raw block, one thread per channel.
+  u32x4* s_raw = reinterpret_cast<u32x4*>(s_u1);  // [XRR][CPR]
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j)
-        w[j] = j < K ? p.conv_w[(static_cast<size_t>(l) * p.C + ch) * K + j] : 0.f;
+  for (int q = 0; q < NRAW; ++q) {
+    const int e = tid + q * kNT;
+    if (e < nrows * CPR) s_raw[e] = raw[q];
+  }
+  __syncthreads();
+  const TIn* s_rawe = reinterpret_cast<const TIn*>(s_u1);  // element view [XRR][NCH]
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    const int c = tid + sl * kNT;
+    if (c < NCH) {
       float* dst;
       int ld;
       if (c < DK) {
@@ -202,73 +264,176 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
         dst = s_rhs + (c - 2 * DK);
         ld = RHS_LD;
       }
-      for (int t = 0; t < TMAX; ++t) {
-        float y = 0.f;
-        if (t < T) {
+      if (!tree) {
+        // chain: the window of token t is raw rows t .. t+K-1
+#pragma unroll 4
+        for (int t = 0; t < TMAX; ++t) {
+          float y = 0.f;
+          if (t < T) {
 #pragma unroll
-          for (int j = 0; j < kMaxK; ++j)
-            if (j < K)
-              y = fmaf(w[j], ld_in(s_x, (s_widx[t * kMaxK + j] + K - 1) * CHK + cl), y);
-          if (p.silu) y = y / (1.f + __expf(-y));
+            for (int j = 0; j < KM; ++j)
+              if (KC > 0 || j < K) y = fmaf(w[sl][j], ld_in(s_rawe, (t + j) * NCH + c), y);
+            if (p.silu) y = silu(y);
+          }
+          dst[t * ld] = y;
         }
-        dst[t * ld] = y;
+      } else {
+#pragma unroll 4
+        for (int t = 0; t < TMAX; ++t) {
+          float y = 0.f;
+          if (t < T) {
+#pragma unroll
+            for (int j = 0; j < KM; ++j)
+              if (KC > 0 || j < K)
+                y = fmaf(w[sl][j], ld_in(s_rawe, (s_widx[t * kMaxK + j] + K - 1) * NCH + c), y);
+            if (p.silu) y = silu(y);
+          }
+          dst[t * ld] = y;
+        }
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
-  // (4) L2-normalise the 2T vectors (k rows then q rows), one wave per vector.
-  for (int vi = wave; vi < 2 * T; vi += kNWave) {
-    float* r = s_kq + (vi < T ? vi : TMAX + vi - T) * KQ_LD;
+  // (4) L2-normalise the 2T vectors (k rows, q rows): 8 lanes per vector.
+  for (int v0 = 0; v0 < 2 * T; v0 += kNT / 8) {
+    const int vi = v0 + tid / 8, sub = tid % 8;
+    const bool ok = vi < 2 * T;
+    floatx4* r = reinterpret_cast<floatx4*>(s_kq + (vi < T ? vi : TMAX + vi - T) * KQ_LD);
+    floatx4 e[DK / 32];
     float ss = 0.f;
-    for (int e = lane; e < DK; e += kWave) ss = fmaf(r[e], r[e], ss);
-    ss = wave_sum(ss);
+#pragma unroll
+    for (int q = 0; q < DK / 32; ++q) {
+      e[q] = ok ? r[sub + 8 * q] : floatx4{0.f, 0.f, 0.f, 0.f};
+      ss = fmaf(e[q][0], e[q][0], fmaf(e[q][1], e[q][1], fmaf(e[q][2], e[q][2], fmaf(e[q][3], e[q][3], ss))));
+    }
+    ss = sum8(ss);
     const float inv = 1.f / sqrtf(ss + p.eps);
-    for (int e = lane; e < DK; e += kWave) r[e] *= inv;
+    if (ok) {
+#pragma unroll
+      for (int q = 0; q < DK / 32; ++q) r[sub + 8 * q] = e[q] * inv;
+    }
   }
   __syncthreads();
 
   // Tape k: written once per k-head (first v-head of the group, first row block).
   if (g == 0 && rblk == 0) {
-    for (int e = tid; e < T * DK; e += kNT) {
-      const int t = e / DK, c = e % DK;
-      p.tk[((lb * T + t) * p.Hk + hk) * DK + c] = s_kq[t * KQ_LD + c];
+    for (int e = tid; e < T * (DK / 4); e += kNT) {
+      const int t = e / (DK / 4), c4 = e % (DK / 4);
+      reinterpret_cast<floatx4*>(p.tk + ((lb * T + t) * p.Hk + hk) * DK)[c4] =
+          reinterpret_cast<const floatx4*>(s_kq + t * KQ_LD)[c4];
     }
   }
 
-  // (5) Coefficients A (proper ancestors) and Oc (ancestors + self), dense
-  //     TMAX x TMAX with zeros elsewhere; one thread per (t, i) pair.
-  for (int e = tid; e < TMAX * TMAX; e += kNT) {
-    const int t = e / TMAX, i = e % TMAX;
-    float av = 0.f, ov = 0.f;
-    if (t < T && i <= t && (i == t || ((s_anc[t] >> i) & 1ull))) {
-      float gm = 1.f;  // Gamma[t,i]: product of a from t up to, not including, i
-      for (int c = t; c != i; c = s_par[c]) gm *= s_ga[c];
-      const floatx4* kt = reinterpret_cast<const floatx4*>(s_kq + t * KQ_LD);
-      const floatx4* ki = reinterpret_cast<const floatx4*>(s_kq + i * KQ_LD);
-      const floatx4* qt = reinterpret_cast<const floatx4*>(s_kq + (TMAX + t) * KQ_LD);
-      floatx4 dk = {0.f, 0.f, 0.f, 0.f}, dq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-      for (int c = 0; c < DK / 4; ++c) {
-        const floatx4 kiv = ki[c];
-        const floatx4 ktv = kt[c];
-        const floatx4 qtv = qt[c];
+  // (5) Gram [K;Q] K^T on MFMA: G[r][i] = (k or q)_r . k_i, r < 2TMAX, i < TMAX.
+  {
+    constexpr int NCT = (TMAX + 15) / 16;
+    for (int job = wave; job < NRB * NCT; job += kNWave) {
+      const int rb = job / NCT, ct = job % NCT;
+      const bool live = !(TMAX >= 16 && (rb * 16) % TMAX >= T) && ct * 16 < T;
+      if (!live) continue;
+      floatx4 gacc = {0.f, 0.f, 0.f, 0.f};
+      const float* arow = s_kq + (rb * 16 + c16) * KQ_LD + 4 * kk;
+      const float* brow = s_kq + (ct * 16 + c16) * KQ_LD + 4 * kk;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          dk[h] = fmaf(ktv[h], kiv[h], dk[h]);
-          dq[h] = fmaf(qtv[h], kiv[h], dq[h]);
+      for (int m = 0; m < MSTEPS; ++m) {
+        const floatx4 av = *reinterpret_cast<const floatx4*>(arow + 16 * m);
+        const floatx4 bv = *reinterpret_cast<const floatx4*>(brow + 16 * m);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) gacc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[h], bv[h], gacc, 0, 0, 0);
+      }
+      const int col = ct * 16 + c16;
+      if (col < TMAX) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_G[(rb * 16 + 4 * kk + r) * CO_LD + col] = gacc[r];
+      }
+    }
+  }
+  __syncthreads();
+
+  // (6) A and Oc in place of the Gram rows, gamma: one thread per node walks
+  //     its ancestor path accumulating Gamma.
+  if (tid < TMAX) {
+    const int t = tid;
+    float* arow = s_G + t * CO_LD;
+    float* orow = s_G + (TMAX + t) * CO_LD;
+    const unsigned long long anc = t < T ? s_anc[t] : 0ull;
+    for (int i = 0; i < TMAX; ++i) {
+      const bool is_anc = (anc >> i) & 1ull;
+      if (!is_anc) arow[i] = 0.f;
+      if (!is_anc && (i != t || t >= T)) orow[i] = 0.f;
+    }
+    if (t < T) {
+      const float bt = s_gb[t];
+      float gm = 1.f;
+      int cur = t;
+      for (;;) {
+        gm *= s_ga[cur];
+        const int nxt = s_par[cur];
+        if (nxt < 0) break;
+        arow[nxt] = bt * gm * arow[nxt];
+        orow[nxt] = gm * orow[nxt];
+        cur = nxt;
+      }
+      s_gam[t] = gm;
+    }
+  }
+
+  __syncthreads();  // A, Oc, gamma complete
+
+  // (7) Ti = (I + A)^-1 by columns (forward substitution, thread j = column).
+  if (tid < TMAX) {
+    const int j = tid;
+    if (TMAX <= 16) {
+      float xc[TMAX];
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        float v = (t == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int a = 0; a < t; ++a) v = fmaf(-s_G[t * CO_LD + a], xc[a], v);
+        xc[t] = (t < T && j < T) ? v : 0.f;
+        s_Ti[t * CO_LD + j] = xc[t];
+      }
+    } else {
+      for (int t = 0; t < TMAX; ++t) {
+        float v = 0.f;
+        if (t < T && j < T) {
+          if (t == j) {
+            v = 1.f;
+          } else if (t > j) {
+            for (unsigned long long mm = s_anc[t] & ~((1ull << j) - 1ull); mm; mm &= mm - 1) {
+              const int a = __builtin_ctzll(mm);
+              v = fmaf(-s_G[t * CO_LD + a], s_Ti[a * CO_LD + j], v);
+            }
+          }
+        }
+        s_Ti[t * CO_LD + j] = v;
+      }
+    }
+  }
+  __syncthreads();  // Ti complete
+
+  // (8) M2 = Oc Ti (support: ancestors-or-self), written over A.
+  for (int e = tid; e < TMAX * TMAX; e += kNT) {
+    const int t = e / TMAX, s = e % TMAX;
+    float mv = 0.f;
+    if (t < T && s <= t) {
+      const float* orow = s_G + (TMAX + t) * CO_LD;
+      mv = orow[t] * s_Ti[t * CO_LD + s];
+      if (TMAX <= 16) {
+        for (int a = s; a < t; ++a) mv = fmaf(orow[a], s_Ti[a * CO_LD + s], mv);
+      } else {
+        for (unsigned long long mm = s_anc[t] & ~((1ull << s) - 1ull); mm; mm &= mm - 1) {
+          const int a = __builtin_ctzll(mm);
+          mv = fmaf(orow[a], s_Ti[a * CO_LD + s], mv);
         }
       }
-      const float kdot = (dk[0] + dk[1]) + (dk[2] + dk[3]);
-      const float qdot = (dq[0] + dq[1]) + (dq[2] + dq[3]);
-      av = i == t ? 0.f : s_gb[t] * gm * kdot;
-      ov = gm * qdot;
     }
-    s_A[t * CO_LD + i] = av;
-    s_Oc[t * CO_LD + i] = ov;
+    s_G[t * CO_LD + s] = mv;
   }
+  __syncthreads();
 
-  // (6) [K;Q] S0^T on fp32 MFMA (16x16x4): A from LDS, B from registers.
+  // (9) [K;Q] S0^T on fp32 MFMA (16x16x4): A from LDS, B from registers.
   floatx4 acc1[TPW][NRB];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt)
@@ -292,29 +457,9 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
       }
     }
   }
-  __syncthreads();  // A and Oc complete
 
-  // (7) Ti = (I + A)^-1, one thread per column j (forward substitution).
-  if (tid < TMAX) {
-    const int j = tid;
-    for (int t = 0; t < TMAX; ++t) {
-      float xv = 0.f;
-      if (t < T && j < T) {
-        if (t == j) {
-          xv = 1.f;
-        } else if (t > j) {
-          const unsigned long long m = s_anc[t] & ~((1ull << j) - 1ull);
-          for (unsigned long long mm = m; mm; mm &= mm - 1) {
-            const int a = __builtin_ctzll(mm);
-            xv = fmaf(-s_A[t * CO_LD + a], s_Ti[a * CO_LD + j], xv);
-          }
-        }
-      }
-      s_Ti[t * CO_LD + j] = xv;
-    }
-  }
   // RHS_t[i] = b_t (v_t[i] - gamma_t W[t][i]) from the W rows of acc1, in place
-  // of v in s_rhs; padding rows become 0.
+  // of v; padding rows become 0.
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int tile = wave + tt * kNWave;
@@ -332,26 +477,10 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
       }
     }
   }
-  __syncthreads();  // Ti and RHS complete
+  __syncthreads();  // RHS complete
 
-  // (8) M2 = Oc Ti (support: ancestors-or-self), written over A.
-  for (int e = tid; e < TMAX * TMAX; e += kNT) {
-    const int t = e / TMAX, s = e % TMAX;
-    float mv = 0.f;
-    if (t < T && s <= t) {
-      mv = s_Oc[t * CO_LD + t] * s_Ti[t * CO_LD + s];
-      const unsigned long long m = s_anc[t] & ~((1ull << s) - 1ull);
-      for (unsigned long long mm = m; mm; mm &= mm - 1) {
-        const int a = __builtin_ctzll(mm);
-        mv = fmaf(s_Oc[t * CO_LD + a], s_Ti[a * CO_LD + s], mv);
-      }
-    }
-    s_A[t * CO_LD + s] = mv;
-  }
-  __syncthreads();
-
-  // (9) [Ti; M2] RHS on MFMA: rows [0,TMAX) give U, rows [TMAX,2TMAX) give
-  //     M2 RHS, in the same lanes as the Q S0^T rows of acc1.
+  // (10) [Ti; M2] RHS on MFMA: rows [0,TMAX) give U, rows [TMAX,2TMAX) give
+  //      M2 RHS, in the same lanes as the Q S0^T rows of acc1.
   floatx4 acc2[TPW][NRB];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt)
@@ -361,7 +490,7 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   for (int rb = 0; rb < NRB; ++rb) {
     if (TMAX >= 16 && (rb * 16) % TMAX >= T) continue;
     const int arow = rb * 16 + c16;
-    const float* amat = arow < TMAX ? s_Ti + arow * CO_LD : s_A + (arow - TMAX) * CO_LD;
+    const float* amat = arow < TMAX ? s_Ti + arow * CO_LD : s_G + (arow - TMAX) * CO_LD;
 #pragma unroll
     for (int st = 0; st < TMAX / 4; ++st) {
       if (st * 4 >= T) break;
@@ -377,7 +506,7 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
     }
   }
 
-  // (10) Outputs straight from registers: u rows and o = gamma Z + M2 RHS.
+  // (11) Outputs straight from registers: u rows and o = gamma Z + M2 RHS.
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int tile = wave + tt * kNWave;
@@ -402,21 +531,42 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   }
 }
 
+template <int DK, int DV, int TMAX, int ROWS, typename TIn>
+hipError_t launch_k(const VerifyArgs& a, int grid, hipStream_t s) {
+  if (a.K == 4)
+    hipLaunchKernelGGL((k_verify_wy<DK, DV, TMAX, ROWS, 4, TIn>), dim3(grid), dim3(kNT), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_verify_wy<DK, DV, TMAX, ROWS, 0, TIn>), dim3(grid), dim3(kNT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, int ROWS, typename TIn>
+hipError_t launch_t(const VerifyArgs& a, hipStream_t s);
+
+// fp32 inputs at T > 32 with 128-dim heads use 32-row blocks to stay in LDS.
+template <int DK, int DV, int ROWS, typename TIn>
+constexpr int rows_for_long() {
+  return (sizeof(TIn) == 4 && DV == 128) ? 32 : ROWS;
+}
+
 template <int DK, int DV, int ROWS, typename TIn>
 hipError_t launch_t(const VerifyArgs& a, hipStream_t s) {
   const int nsub = (a.Hv / a.Hk) * (DV / ROWS);
   const int n_units = a.L * a.B * a.Hk;
   const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * nsub;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.T <= 8)
-    hipLaunchKernelGGL((k_verify_wy<DK, DV, 8, ROWS, TIn>), dim3(grid), dim3(kNT), 0, s, a);
-  else if (a.T <= 16)
-    hipLaunchKernelGGL((k_verify_wy<DK, DV, 16, ROWS, TIn>), dim3(grid), dim3(kNT), 0, s, a);
-  else if (a.T <= 32)
-    hipLaunchKernelGGL((k_verify_wy<DK, DV, 32, ROWS, TIn>), dim3(grid), dim3(kNT), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_verify_wy<DK, DV, 64, ROWS, TIn>), dim3(grid), dim3(kNT), 0, s, a);
-  return hipGetLastError();
+  if (a.T <= 8) return launch_k<DK, DV, 8, ROWS, TIn>(a, static_cast<int>(grid), s);
+  if (a.T <= 16) return launch_k<DK, DV, 16, ROWS, TIn>(a, static_cast<int>(grid), s);
+  if (a.T <= 32) return launch_k<DK, DV, 32, ROWS, TIn>(a, static_cast<int>(grid), s);
+  constexpr int RL = rows_for_long<DK, DV, ROWS, TIn>();
+  if constexpr (RL != ROWS) {
+    const int nsub2 = (a.Hv / a.Hk) * (DV / RL);
+    const long long grid2 = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * nsub2;
+    if (grid2 > 0x7fffffffLL) return hipErrorInvalidValue;
+    return launch_k<DK, DV, 64, RL, TIn>(a, static_cast<int>(grid2), s);
+  } else {
+    return launch_k<DK, DV, 64, ROWS, TIn>(a, static_cast<int>(grid), s);
+  }
 }
 
 template <typename TIn>
@@ -425,7 +575,13 @@ hipError_t launch_d(const VerifyArgs& a, int dk, int dv, hipStream_t s) {
   switch (dk) {
     case 32: return launch_t<32, 32, 32, TIn>(a, s);
     case 64: return launch_t<64, 64, 64, TIn>(a, s);
-    case 128: return launch_t<128, 128, 64, TIn>(a, s);
+    case 128: {
+      static const int rows = [] {
+        const char* e = getenv("GDN_VERIFY_ROWS");
+        return e ? atoi(e) : 128;
+      }();
+      return rows == 64 ? launch_t<128, 128, 64, TIn>(a, s) : launch_t<128, 128, 128, TIn>(a, s);
+    }
     default: return hipErrorInvalidValue;
   }
 }
