@@ -10,6 +10,32 @@ constexpr int kWave = 64;  // CDNA wavefront width
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Split 8 fp32 values into bf16 high parts and bf16 residuals, x ~ hi + lo
+// with |x - hi - lo| <= 2^-18 |x| (both roundings to nearest even).
+__device__ __forceinline__ void split_bf16x8(const floatx4& a, const floatx4& b, bf16x8& hi,
+                                             bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 ha = static_cast<__bf16>(a[e]);
+    const __bf16 hb = static_cast<__bf16>(b[e]);
+    hi[e] = ha;
+    hi[e + 4] = hb;
+    lo[e] = static_cast<__bf16>(a[e] - static_cast<float>(ha));
+    lo[e + 4] = static_cast<__bf16>(b[e] - static_cast<float>(hb));
+  }
+}
+
+// fp32-accurate product on bf16 MFMA (16x16x32): acc += A B with each
+// operand split hi + lo and the lo*lo term dropped (relative error ~1e-5).
+__device__ __forceinline__ floatx4 mfma_bf16x3(const bf16x8& ahi, const bf16x8& alo,
+                                               const bf16x8& bhi, const bf16x8& blo, floatx4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bhi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, blo, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc, 0, 0, 0);
+  return acc;
+}
 
 // Input element loads: fp32 as is, bf16 (raw uint16 bits) widened exactly.
 __device__ __forceinline__ float ld_in(const float* p, size_t i) { return p[i]; }

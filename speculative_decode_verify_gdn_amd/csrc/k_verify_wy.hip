@@ -433,7 +433,17 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   }
   __syncthreads();
 
-  // (9) [K;Q] S0^T on fp32 MFMA (16x16x4): A from LDS, B from registers.
+  // (9) [K;Q] S0^T on bf16 MFMA (16x16x32) with every operand split into a
+  //     bf16 high part and a bf16 residual (three products, fp32 accumulate).
+  //     Step s contracts the 32 columns {32s + 16h + 4kk + e}: the two float4
+  //     this lane holds for m = 2s, 2s+1, and the matching k/q columns.
+  constexpr int KSTEPS = DK / 32;
+  bf16x8 shi[TPW][KSTEPS], slo[TPW][KSTEPS];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      split_bf16x8(sreg[tt][2 * ks], sreg[tt][2 * ks + 1], shi[tt][ks], slo[tt][ks]);
   floatx4 acc1[TPW][NRB];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt)
@@ -442,22 +452,18 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     if (TMAX >= 16 && (rb * 16) % TMAX >= T) continue;  // all-padding block
+    const float* arow = s_kq + (rb * 16 + c16) * KQ_LD + 4 * kk;
 #pragma unroll
-    for (int m = 0; m < MSTEPS; ++m) {
-      const floatx4 av =
-          *reinterpret_cast<const floatx4*>(s_kq + (rb * 16 + c16) * KQ_LD + 16 * m + 4 * kk);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      bf16x8 ahi, alo;
+      split_bf16x8(*reinterpret_cast<const floatx4*>(arow + 32 * ks),
+                   *reinterpret_cast<const floatx4*>(arow + 32 * ks + 16), ahi, alo);
 #pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        if (wave + tt * kNWave < NTILE) {
-#pragma unroll
-          for (int h = 0; h < 4; ++h)
-            acc1[tt][rb] =
-                __builtin_amdgcn_mfma_f32_16x16x4f32(av[h], sreg[tt][m][h], acc1[tt][rb], 0, 0, 0);
-        }
-      }
+      for (int tt = 0; tt < TPW; ++tt)
+        if (wave + tt * kNWave < NTILE)
+          acc1[tt][rb] = mfma_bf16x3(ahi, alo, shi[tt][ks], slo[tt][ks], acc1[tt][rb]);
     }
   }
-
   // RHS_t[i] = b_t (v_t[i] - gamma_t W[t][i]) from the W rows of acc1, in place
   // of v; padding rows become 0.
 #pragma unroll
