@@ -24,21 +24,23 @@
 namespace gdn {
 namespace {
 
-template <int DK, int DV, int TMAX>
+template <int DK, int DV>
 __global__ __launch_bounds__(256) void k_tape_rollback(RollbackArgs p) {
   constexpr int NT = 256;
-  constexpr int VPT = 4;                        // float4 per thread
-  constexpr int RB0 = NT * VPT * 4 / DK;        // rows that fill the block
+  constexpr int VPT = 4;                  // float4 per thread
+  constexpr int RB0 = NT * VPT * 4 / DK;  // rows that fill the block
   constexpr int RB = RB0 < DV ? RB0 : DV;
   constexpr int NRBLK = DV / RB;
-  constexpr int C4 = DK / 4;                    // float4 per row
-  constexpr int NV = RB * C4;                   // float4 in the block
-  static_assert(DV % RB == 0, "row blocks");
+  constexpr int C4 = DK / 4;              // float4 per row
+  constexpr int NV = RB * C4;             // float4 in the block
+  constexpr int CH = 16;                  // tape entries staged per chunk
+  constexpr int TM = 64;                  // longest tape
+  static_assert(DV % RB == 0 && NV <= NT * VPT, "row blocks");
 
-  __shared__ float s_k[TMAX * DK];
-  __shared__ float s_u[TMAX * RB];
-  __shared__ float s_w[TMAX];
-  __shared__ int s_pi[TMAX];
+  __shared__ __align__(16) float s_k[CH * DK];
+  __shared__ float s_u[CH * RB];
+  __shared__ float s_w[TM];
+  __shared__ int s_pi[TM];
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
@@ -59,12 +61,12 @@ __global__ __launch_bounds__(256) void k_tape_rollback(RollbackArgs p) {
   const int r0 = rblk * RB;
   float* Sblk = p.S + ((lb * p.Hv + hv) * DV + r0) * static_cast<size_t>(DK);
 
-  // Snapshot loads first; the tape staging below overlaps their latency.
+  // Snapshot loads first (unconditional: every thread owns VPT float4).
   floatx4 sv[VPT];
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int e = tid + v * NT;
-    if (e < NV) sv[v] = reinterpret_cast<const floatx4*>(Sblk)[e];
+    sv[v] = reinterpret_cast<const floatx4*>(Sblk)[e < NV ? e : 0];
   }
 
   if (tid == 0) s_bad = 0;
@@ -84,34 +86,43 @@ __global__ __launch_bounds__(256) void k_tape_rollback(RollbackArgs p) {
     for (int j = tid + 1; j < n; ++j) w *= p.tg[(lb * T + s_pi[j]) * p.Hv + hv];
     s_w[tid] = w;
   }
-  for (int e = tid; e < n * DK; e += NT) {
-    const int i = e / DK, c = e % DK;
-    s_k[e] = p.tk[((lb * T + s_pi[i]) * p.Hk + hk) * DK + c];
-  }
-  __syncthreads();
-  for (int e = tid; e < n * RB; e += NT) {
-    const int i = e / RB, r = e % RB;
-    s_u[e] = s_w[i] * p.tu[((lb * T + s_pi[i]) * p.Hv + hv) * DV + r0 + r];
-  }
   __syncthreads();
   const float gam = s_w[0] * p.tg[(lb * T + s_pi[0]) * p.Hv + hv];
+  floatx4 acc[VPT];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) acc[v] = sv[v] * gam;
 
+  for (int i0 = 0; i0 < n; i0 += CH) {
+    const int nc = n - i0 < CH ? n - i0 : CH;
+    if (i0 > 0) __syncthreads();  // previous chunk consumed
+    for (int e = tid; e < nc * C4; e += NT) {
+      const int i = e / C4, c4 = e % C4;
+      reinterpret_cast<floatx4*>(s_k)[e] =
+          reinterpret_cast<const floatx4*>(p.tk + ((lb * T + s_pi[i0 + i]) * p.Hk + hk) * DK)[c4];
+    }
+    for (int e = tid; e < nc * RB; e += NT) {
+      const int i = e / RB, r = e % RB;
+      s_u[e] = s_w[i0 + i] * p.tu[((lb * T + s_pi[i0 + i]) * p.Hv + hv) * DV + r0 + r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int e = tid + v * NT;
+      const int r = (e % NV) / C4, c = (e % C4) * 4;
+      for (int i = 0; i < nc; ++i) {
+        const float u = s_u[i * RB + r];
+        const floatx4 k = *reinterpret_cast<const floatx4*>(s_k + i * DK + c);
+        acc[v][0] = fmaf(u, k[0], acc[v][0]);
+        acc[v][1] = fmaf(u, k[1], acc[v][1]);
+        acc[v][2] = fmaf(u, k[2], acc[v][2]);
+        acc[v][3] = fmaf(u, k[3], acc[v][3]);
+      }
+    }
+  }
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int e = tid + v * NT;
-    if (e < NV) {
-      const int r = e / C4, c = (e % C4) * 4;
-      floatx4 acc = sv[v] * gam;
-      for (int i = 0; i < n; ++i) {
-        const float u = s_u[i * RB + r];
-        const floatx4 k = *reinterpret_cast<const floatx4*>(s_k + i * DK + c);
-        acc[0] = fmaf(u, k[0], acc[0]);
-        acc[1] = fmaf(u, k[1], acc[1]);
-        acc[2] = fmaf(u, k[2], acc[2]);
-        acc[3] = fmaf(u, k[3], acc[3]);
-      }
-      reinterpret_cast<floatx4*>(Sblk)[e] = acc;
-    }
+    if (e < NV) reinterpret_cast<floatx4*>(Sblk)[e] = acc[v];
   }
 }
 
@@ -120,11 +131,8 @@ hipError_t launch_rb(const RollbackArgs& a, hipStream_t s) {
   constexpr int RB0 = 256 * 4 * 4 / DK;
   constexpr int RB = RB0 < DV ? RB0 : DV;
   const long long grid = static_cast<long long>(a.L) * a.B * a.Hv * (DV / RB);
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.T <= 16)
-    hipLaunchKernelGGL((k_tape_rollback<DK, DV, 16>), dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_tape_rollback<DK, DV, 64>), dim3(grid), dim3(256), 0, s, a);
+  if (grid > 0x7fffffffLL || a.T > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_tape_rollback<DK, DV>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -62,8 +62,10 @@ template <int DK, int DV, int TMAX, int ROWS, int KM, typename TIn>
 struct VerifyLayout {
   static constexpr int KQ_ROWS = 2 * TMAX;  // k rows [0,TMAX), q rows [TMAX,2TMAX)
   static constexpr int KQ_LD = DK + 4;      // +4 floats: conflict-free float4 column reads
-  static constexpr int RHS_LD = ROWS + 4;
-  static constexpr int CO_LD = TMAX + 1;
+  // RHS stored transposed, [ROWS][RT_LD]: odd stride (conflict-free scalar
+  // access) for short chunks, multiple of 4 (float4 access) for long ones.
+  static constexpr int RT_LD = TMAX <= 16 ? TMAX + 1 : TMAX + 4;
+  static constexpr int CO_LD = TMAX + 4;  // multiple of 4: float4 row reads
   static constexpr int NCH = 2 * DK + ROWS;  // q, k of the k-head; v rows of the block
   static constexpr int XR = TMAX + KM - 1;
   // Raw conv inputs [old window rows; node rows] x [q | k | v-rows], staged
@@ -72,7 +74,7 @@ struct VerifyLayout {
   static constexpr int STAGE_BYTES = XR * CPR * 16;
   static constexpr int COEF_BYTES = 3 * TMAX * CO_LD * 4;  // [A;Oc] then [M2;Oc], and Ti
   static constexpr int U1_BYTES = STAGE_BYTES > COEF_BYTES ? STAGE_BYTES : COEF_BYTES;
-  static constexpr int TOTAL = 2 * TMAX * KQ_LD * 4 + TMAX * RHS_LD * 4 + U1_BYTES + TMAX * 56 + 16;
+  static constexpr int TOTAL = 2 * TMAX * KQ_LD * 4 + ROWS * RT_LD * 4 + U1_BYTES + TMAX * 56 + 16;
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one workgroup exceeded");
 };
 
@@ -80,7 +82,7 @@ template <int DK, int DV, int TMAX, int ROWS, int KC, typename TIn>
 __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   constexpr int KM = KC > 0 ? KC : kMaxK;  // unroll bound of the conv taps
   using LY = VerifyLayout<DK, DV, TMAX, ROWS, KM, TIn>;
-  constexpr int KQ_LD = LY::KQ_LD, RHS_LD = LY::RHS_LD, CO_LD = LY::CO_LD;
+  constexpr int KQ_LD = LY::KQ_LD, RT_LD = LY::RT_LD, CO_LD = LY::CO_LD;
   constexpr int NCH = LY::NCH;
   constexpr int NRB = LY::KQ_ROWS / 16;
   constexpr int NTILE = ROWS / 16;
@@ -90,12 +92,12 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   static_assert(ROWS % 16 == 0 && DV % ROWS == 0 && TMAX % 8 == 0 && TMAX <= 64, "tiling");
 
   __shared__ __align__(16) float s_kq[LY::KQ_ROWS * KQ_LD];
-  __shared__ __align__(16) float s_rhs[TMAX * RHS_LD];        // v, then RHS
+  __shared__ __align__(16) float s_rhs[ROWS * RT_LD];         // v, then RHS, [row of S][node]
   __shared__ __align__(16) unsigned char s_u1[LY::U1_BYTES];  // staging, then coefficients
   __shared__ float s_gam[TMAX], s_ga[TMAX], s_gb[TMAX];
   __shared__ unsigned long long s_anc[TMAX];
   __shared__ int s_par[TMAX];
-  __shared__ int s_widx[TMAX * kMaxK];
+  __shared__ __align__(16) int s_widx[TMAX * kMaxK];
   __shared__ int s_bad;
   float* s_G = reinterpret_cast<float*>(s_u1);  // [2TMAX][CO_LD]: KK then A (-> M2); QK then Oc
   float* s_Ti = s_G + 2 * TMAX * CO_LD;         // [TMAX][CO_LD]
@@ -227,11 +229,14 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
       }
     }
   }
-  if (tid == 0) {
-    for (int v = 0; v < T; ++v) {
-      const int pv = s_par[v];
-      s_anc[v] = pv < 0 ? 0ull : (s_anc[pv] | (1ull << pv));
+  if (tid < T) {  // proper-ancestor bitmask of node tid
+    unsigned long long m = 0ull;
+    if (tree) {
+      for (int c = s_par[tid]; c >= 0; c = s_par[c]) m |= 1ull << c;
+    } else {
+      m = tid == 0 ? 0ull : (~0ull >> (64 - tid));
     }
+    s_anc[tid] = m;
   }
   __syncthreads();
   if (p.conv_win && l == 0 && hk == 0 && g == 0 && rblk == 0) {
@@ -261,8 +266,8 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
         dst = s_kq + (c - DK);
         ld = KQ_LD;
       } else {
-        dst = s_rhs + (c - 2 * DK);
-        ld = RHS_LD;
+        dst = s_rhs + (c - 2 * DK) * RT_LD;
+        ld = 1;
       }
       if (!tree) {
         // chain: the window of token t is raw rows t .. t+K-1
@@ -278,14 +283,16 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
           dst[t * ld] = y;
         }
       } else {
-#pragma unroll 4
+#pragma unroll 8
         for (int t = 0; t < TMAX; ++t) {
           float y = 0.f;
           if (t < T) {
+            const int4 wa = *reinterpret_cast<const int4*>(s_widx + t * kMaxK);
+            const int4 wb = *reinterpret_cast<const int4*>(s_widx + t * kMaxK + 4);
+            const int wi[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
             for (int j = 0; j < KM; ++j)
-              if (KC > 0 || j < K)
-                y = fmaf(w[sl][j], ld_in(s_rawe, (s_widx[t * kMaxK + j] + K - 1) * NCH + c), y);
+              if (KC > 0 || j < K) y = fmaf(w[sl][j], ld_in(s_rawe, (wi[j] + K - 1) * NCH + c), y);
             if (p.silu) y = silu(y);
           }
           dst[t * ld] = y;
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
     }
   }
 
-  // (5) Gram [K;Q] K^T on MFMA: G[r][i] = (k or q)_r . k_i, r < 2TMAX, i < TMAX.
+  // (5) Gram [K;Q] K^T on bf16x3 MFMA: G[r][i] = (k or q)_r . k_i.
   {
     constexpr int NCT = (TMAX + 15) / 16;
     for (int job = wave; job < NRB * NCT; job += kNWave) {
@@ -336,11 +343,13 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
       const float* arow = s_kq + (rb * 16 + c16) * KQ_LD + 4 * kk;
       const float* brow = s_kq + (ct * 16 + c16) * KQ_LD + 4 * kk;
 #pragma unroll
-      for (int m = 0; m < MSTEPS; ++m) {
-        const floatx4 av = *reinterpret_cast<const floatx4*>(arow + 16 * m);
-        const floatx4 bv = *reinterpret_cast<const floatx4*>(brow + 16 * m);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) gacc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[h], bv[h], gacc, 0, 0, 0);
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        bf16x8 ahi, alo, bhi, blo;
+        split_bf16x8(*reinterpret_cast<const floatx4*>(arow + 32 * ks),
+                     *reinterpret_cast<const floatx4*>(arow + 32 * ks + 16), ahi, alo);
+        split_bf16x8(*reinterpret_cast<const floatx4*>(brow + 32 * ks),
+                     *reinterpret_cast<const floatx4*>(brow + 32 * ks + 16), bhi, blo);
+        gacc = mfma_bf16x3(ahi, alo, bhi, blo, gacc);
       }
       const int col = ct * 16 + c16;
       if (col < TMAX) {
@@ -351,34 +360,34 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   }
   __syncthreads();
 
-  // (6) A and Oc in place of the Gram rows, gamma: one thread per node walks
-  //     its ancestor path accumulating Gamma.
-  if (tid < TMAX) {
-    const int t = tid;
-    float* arow = s_G + t * CO_LD;
-    float* orow = s_G + (TMAX + t) * CO_LD;
-    const unsigned long long anc = t < T ? s_anc[t] : 0ull;
-    for (int i = 0; i < TMAX; ++i) {
-      const bool is_anc = (anc >> i) & 1ull;
-      if (!is_anc) arow[i] = 0.f;
-      if (!is_anc && (i != t || t >= T)) orow[i] = 0.f;
-    }
-    if (t < T) {
-      const float bt = s_gb[t];
-      float gm = 1.f;
-      int cur = t;
-      for (;;) {
-        gm *= s_ga[cur];
-        const int nxt = s_par[cur];
-        if (nxt < 0) break;
-        arow[nxt] = bt * gm * arow[nxt];
-        orow[nxt] = gm * orow[nxt];
-        cur = nxt;
-      }
-      s_gam[t] = gm;
-    }
+  // (6) gamma per node (walk to the root), then A and Oc in place of the
+  //     Gram rows, one thread per (t, i): Gamma[t,i] = gamma_t / gamma_i, or
+  //     the product of a along the path when gamma_i has underflowed.
+  if (tid < T) {
+    float gm = 1.f;
+    for (int c = tid; c >= 0; c = s_par[c]) gm *= s_ga[c];
+    s_gam[tid] = gm;
   }
-
+  __syncthreads();
+  for (int e = tid; e < TMAX * TMAX; e += kNT) {
+    const int t = e / TMAX, i = e % TMAX;
+    const bool on = t < T && (i == t || ((s_anc[t] >> i) & 1ull));
+    float av = 0.f, ov = 0.f;
+    if (on) {
+      float gm;
+      const float gi = s_gam[i];
+      if (gi > 1e-30f) {
+        gm = s_gam[t] / gi;
+      } else {
+        gm = 1.f;
+        for (int c = t; c != i; c = s_par[c]) gm *= s_ga[c];
+      }
+      if (i != t) av = s_gb[t] * gm * s_G[t * CO_LD + i];
+      ov = gm * s_G[(TMAX + t) * CO_LD + i];
+    }
+    s_G[t * CO_LD + i] = av;
+    s_G[(TMAX + t) * CO_LD + i] = ov;
+  }
   __syncthreads();  // A, Oc, gamma complete
 
   // (7) Ti = (I + A)^-1 by columns (forward substitution, thread j = column).
@@ -394,42 +403,79 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
         xc[t] = (t < T && j < T) ? v : 0.f;
         s_Ti[t * CO_LD + j] = xc[t];
       }
-    } else {
-      for (int t = 0; t < TMAX; ++t) {
+    }
+  }
+  if constexpr (TMAX > 16) {
+    // Level by level over node depth: row t of Ti needs only rows of its
+    // ancestors, which sit at smaller depths.  One thread per (t, s) pair.
+    int md = 0;
+    for (int t = 0; t < T; ++t) {
+      const int d = __popcll(s_anc[t]);
+      md = d > md ? d : md;
+    }
+    for (int d = 0; d <= md; ++d) {
+      for (int e = tid; e < TMAX * TMAX; e += kNT) {
+        const int t = e / TMAX, sc = e % TMAX;
+        const unsigned long long anc = t < T ? s_anc[t] : 0ull;
+        const int dt = t < T ? __popcll(anc) : -1;
+        if (d == 0 && t >= T) s_Ti[t * CO_LD + sc] = 0.f;  // padding rows
+        if (dt != d) continue;
         float v = 0.f;
-        if (t < T && j < T) {
-          if (t == j) {
+        if (sc < T) {
+          if (sc == t) {
             v = 1.f;
-          } else if (t > j) {
-            for (unsigned long long mm = s_anc[t] & ~((1ull << j) - 1ull); mm; mm &= mm - 1) {
+          } else if (sc < t) {
+            for (unsigned long long mm = anc & ~((1ull << sc) - 1ull); mm; mm &= mm - 1) {
               const int a = __builtin_ctzll(mm);
-              v = fmaf(-s_G[t * CO_LD + a], s_Ti[a * CO_LD + j], v);
+              v = fmaf(-s_G[t * CO_LD + a], s_Ti[a * CO_LD + sc], v);
             }
           }
         }
-        s_Ti[t * CO_LD + j] = v;
+        s_Ti[t * CO_LD + sc] = v;
       }
+      __syncthreads();
     }
   }
   __syncthreads();  // Ti complete
 
   // (8) M2 = Oc Ti (support: ancestors-or-self), written over A.
-  for (int e = tid; e < TMAX * TMAX; e += kNT) {
-    const int t = e / TMAX, s = e % TMAX;
-    float mv = 0.f;
-    if (t < T && s <= t) {
-      const float* orow = s_G + (TMAX + t) * CO_LD;
-      mv = orow[t] * s_Ti[t * CO_LD + s];
-      if (TMAX <= 16) {
-        for (int a = s; a < t; ++a) mv = fmaf(orow[a], s_Ti[a * CO_LD + s], mv);
-      } else {
-        for (unsigned long long mm = s_anc[t] & ~((1ull << s) - 1ull); mm; mm &= mm - 1) {
-          const int a = __builtin_ctzll(mm);
-          mv = fmaf(orow[a], s_Ti[a * CO_LD + s], mv);
-        }
+  if constexpr (TMAX <= 16) {
+    for (int e = tid; e < TMAX * TMAX; e += kNT) {
+      const int t = e / TMAX, sc = e % TMAX;
+      float mv = 0.f;
+      if (t < T && sc <= t) {
+        const float* orow = s_G + (TMAX + t) * CO_LD;
+        mv = orow[t] * s_Ti[t * CO_LD + sc];
+        for (int a = sc; a < t; ++a) mv = fmaf(orow[a], s_Ti[a * CO_LD + sc], mv);
       }
+      s_G[t * CO_LD + sc] = mv;
     }
-    s_G[t * CO_LD + s] = mv;
+  } else {
+    // bf16x3 MFMA: A = Oc rows (float4 reads), B = Ti columns.
+    constexpr int NB = TMAX / 16;
+    for (int job = wave; job < NB * NB; job += kNWave) {
+      const int rb = job / NB, ct = job % NB;
+      floatx4 macc = {0.f, 0.f, 0.f, 0.f};
+      const float* orow = s_G + (TMAX + rb * 16 + c16) * CO_LD + 8 * kk;
+#pragma unroll
+      for (int st = 0; st < TMAX / 32; ++st) {
+        bf16x8 ahi, alo, bhi, blo;
+        split_bf16x8(*reinterpret_cast<const floatx4*>(orow + 32 * st),
+                     *reinterpret_cast<const floatx4*>(orow + 32 * st + 4), ahi, alo);
+        floatx4 b0, b1;
+        const float* tcol = s_Ti + (32 * st + 8 * kk) * CO_LD + ct * 16 + c16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          b0[e] = tcol[e * CO_LD];
+          b1[e] = tcol[(e + 4) * CO_LD];
+        }
+        split_bf16x8(b0, b1, bhi, blo);
+        macc = mfma_bf16x3(ahi, alo, bhi, blo, macc);
+      }
+      // the A rows are no longer read (Ti is complete): store the tile there
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_G[(rb * 16 + 4 * kk + r) * CO_LD + ct * 16 + c16] = macc[r];
+    }
   }
   __syncthreads();
 
@@ -470,14 +516,25 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   for (int tt = 0; tt < TPW; ++tt) {
     const int tile = wave + tt * kNWave;
     if (tile < NTILE) {
+      float* col = s_rhs + (tile * 16 + c16) * RT_LD;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
+        const int row0 = rb * 16 + 4 * kk;
+        if (row0 < TMAX) {
+          if constexpr (TMAX <= 16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rb * 16 + 4 * kk + r;
-          if (row < TMAX) {
-            float* d = s_rhs + row * RHS_LD + tile * 16 + c16;
-            *d = row < T ? s_gb[row] * (*d - s_gam[row] * acc1[tt][rb][r]) : 0.f;
+            for (int r = 0; r < 4; ++r) {
+              const int t = row0 + r;
+              col[t] = t < T ? s_gb[t] * (col[t] - s_gam[t] * acc1[tt][rb][r]) : 0.f;
+            }
+          } else {
+            floatx4 v = *reinterpret_cast<floatx4*>(col + row0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = row0 + r;
+              v[r] = t < T ? s_gb[t] * (v[r] - s_gam[t] * acc1[tt][rb][r]) : 0.f;
+            }
+            *reinterpret_cast<floatx4*>(col + row0) = v;
           }
         }
       }
@@ -492,21 +549,49 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) acc2[tt][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // B operand of the long-chunk path: this lane's RHS columns, split once.
+  constexpr int RST = TMAX >= 32 ? TMAX / 32 : 1;
+  bf16x8 rhi[TPW][RST], rlo[TPW][RST];
+  if constexpr (TMAX >= 32) {
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int tile = wave + tt * kNWave;
+      const float* brow = s_rhs + ((tile < NTILE ? tile : 0) * 16 + c16) * RT_LD + 8 * kk;
+#pragma unroll
+      for (int st = 0; st < RST; ++st)
+        split_bf16x8(*reinterpret_cast<const floatx4*>(brow + 32 * st),
+                     *reinterpret_cast<const floatx4*>(brow + 32 * st + 4), rhi[tt][st], rlo[tt][st]);
+    }
+  }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     if (TMAX >= 16 && (rb * 16) % TMAX >= T) continue;
     const int arow = rb * 16 + c16;
     const float* amat = arow < TMAX ? s_Ti + arow * CO_LD : s_G + (arow - TMAX) * CO_LD;
+    if constexpr (TMAX >= 32) {
 #pragma unroll
-    for (int st = 0; st < TMAX / 4; ++st) {
-      if (st * 4 >= T) break;
-      const float a_op = amat[4 * st + kk];
+      for (int st = 0; st < TMAX / 32; ++st) {
+        if (st * 32 >= T) break;
+        bf16x8 ahi, alo;
+        split_bf16x8(*reinterpret_cast<const floatx4*>(amat + 32 * st + 8 * kk),
+                     *reinterpret_cast<const floatx4*>(amat + 32 * st + 8 * kk + 4), ahi, alo);
 #pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        const int tile = wave + tt * kNWave;
-        if (tile < NTILE) {
-          const float b_op = s_rhs[(4 * st + kk) * RHS_LD + tile * 16 + c16];
-          acc2[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_op, b_op, acc2[tt][rb], 0, 0, 0);
+        for (int tt = 0; tt < TPW; ++tt)
+          if (wave + tt * kNWave < NTILE)
+            acc2[tt][rb] = mfma_bf16x3(ahi, alo, rhi[tt][st], rlo[tt][st], acc2[tt][rb]);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < TMAX / 4; ++st) {
+        if (st * 4 >= T) break;
+        const float a_op = amat[4 * st + kk];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+          const int tile = wave + tt * kNWave;
+          if (tile < NTILE) {
+            const float b_op = s_rhs[(tile * 16 + c16) * RT_LD + 4 * st + kk];
+            acc2[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_op, b_op, acc2[tt][rb], 0, 0, 0);
+          }
         }
       }
     }
