@@ -35,8 +35,13 @@ namespace gdn {
 namespace {
 
 constexpr int kMaxK = 8;
-constexpr int kNT = 256;
-constexpr int kNWave = kNT / kWave;
+
+// Threads per workgroup: eight waves for 64-node chunks (one workgroup per CU
+// by LDS, so its latency-bound phases get more lanes), four waves otherwise.
+template <int TMAX>
+constexpr int threads_for() {
+  return TMAX >= 64 ? 512 : 256;
+}
 
 // Sum over aligned groups of 8 lanes (DPP; every lane gets its group's sum).
 __device__ __forceinline__ float sum8(float v) {
@@ -46,7 +51,9 @@ __device__ __forceinline__ float sum8(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu(float y) { return y / (1.f + __expf(-y)); }
+__device__ __forceinline__ float silu(float y) {
+  return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
+}
 
 // Back to the input dtype; exact for values that were widened from it.
 template <typename TIn>
@@ -79,7 +86,9 @@ struct VerifyLayout {
 };
 
 template <int DK, int DV, int TMAX, int ROWS, int KC, typename TIn>
-__global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
+__global__ __launch_bounds__(threads_for<TMAX>()) void k_verify_wy(VerifyArgs p) {
+  constexpr int kNT = threads_for<TMAX>();
+  constexpr int kNWave = kNT / kWave;
   constexpr int KM = KC > 0 ? KC : kMaxK;  // unroll bound of the conv taps
   using LY = VerifyLayout<DK, DV, TMAX, ROWS, KM, TIn>;
   constexpr int KQ_LD = LY::KQ_LD, RT_LD = LY::RT_LD, CO_LD = LY::CO_LD;
@@ -216,6 +225,10 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
     if (tid == 0 && p.dev_err) atomicOr(p.dev_err, GDN_DEV_ERR_PARENT);
     return;
   }
+  if (tid >= T && tid < TMAX) {  // padding nodes read a valid (discarded) window
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) s_widx[tid * kMaxK + j] = 0;
+  }
   if (tid < T) {
     if (rblk == 0) p.tg[(lb * T + tid) * p.Hv + hv] = s_ga[tid];
     // conv window of node tid: the node, its ancestors upward, then old rows
@@ -269,33 +282,30 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
         dst = s_rhs + (c - 2 * DK) * RT_LD;
         ld = 1;
       }
+      // Branch-free over nodes: padding nodes read valid rows and are zeroed.
       if (!tree) {
         // chain: the window of token t is raw rows t .. t+K-1
-#pragma unroll 4
+#pragma unroll 8
         for (int t = 0; t < TMAX; ++t) {
           float y = 0.f;
-          if (t < T) {
 #pragma unroll
-            for (int j = 0; j < KM; ++j)
-              if (KC > 0 || j < K) y = fmaf(w[sl][j], ld_in(s_rawe, (t + j) * NCH + c), y);
-            if (p.silu) y = silu(y);
-          }
-          dst[t * ld] = y;
+          for (int j = 0; j < KM; ++j)
+            if (KC > 0 || j < K) y = fmaf(w[sl][j], ld_in(s_rawe, (t + j) * NCH + c), y);
+          if (p.silu) y = silu(y);
+          dst[t * ld] = t < T ? y : 0.f;
         }
       } else {
 #pragma unroll 8
         for (int t = 0; t < TMAX; ++t) {
+          const int4 wa = *reinterpret_cast<const int4*>(s_widx + t * kMaxK);
+          const int4 wb = *reinterpret_cast<const int4*>(s_widx + t * kMaxK + 4);
+          const int wi[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
           float y = 0.f;
-          if (t < T) {
-            const int4 wa = *reinterpret_cast<const int4*>(s_widx + t * kMaxK);
-            const int4 wb = *reinterpret_cast<const int4*>(s_widx + t * kMaxK + 4);
-            const int wi[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
-            for (int j = 0; j < KM; ++j)
-              if (KC > 0 || j < K) y = fmaf(w[sl][j], ld_in(s_rawe, (wi[j] + K - 1) * NCH + c), y);
-            if (p.silu) y = silu(y);
-          }
-          dst[t * ld] = y;
+          for (int j = 0; j < KM; ++j)
+            if (KC > 0 || j < K) y = fmaf(w[sl][j], ld_in(s_rawe, (wi[j] + K - 1) * NCH + c), y);
+          if (p.silu) y = silu(y);
+          dst[t * ld] = t < T ? y : 0.f;
         }
       }
     }
@@ -369,7 +379,11 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
     s_gam[tid] = gm;
   }
   __syncthreads();
-  for (int e = tid; e < TMAX * TMAX; e += kNT) {
+  constexpr int NPQ = (TMAX * TMAX + kNT - 1) / kNT;  // pairs per thread
+#pragma unroll
+  for (int q = 0; q < NPQ; ++q) {
+    const int e = tid + q * kNT;
+    if (e >= TMAX * TMAX) break;
     const int t = e / TMAX, i = e % TMAX;
     const bool on = t < T && (i == t || ((s_anc[t] >> i) & 1ull));
     float av = 0.f, ov = 0.f;
@@ -407,25 +421,38 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
   }
   if constexpr (TMAX > 16) {
     // Level by level over node depth: row t of Ti needs only rows of its
-    // ancestors, which sit at smaller depths.  One thread per (t, s) pair.
+    // ancestors, which sit at smaller depths.  Thread pairs (t, s) fixed:
+    // e = tid + q * kNT, with each pair's depth and ancestors in registers.
+    constexpr int NQ = TMAX * TMAX / kNT;
+    static_assert(TMAX * TMAX % kNT == 0, "pairs per thread");
+    const int sc = tid % TMAX;
+    int dq[NQ];
+    unsigned long long aq[NQ];
     int md = 0;
-    for (int t = 0; t < T; ++t) {
-      const int d = __popcll(s_anc[t]);
-      md = d > md ? d : md;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int t = (tid + q * kNT) / TMAX;
+      aq[q] = t < T ? s_anc[t] : 0ull;
+      dq[q] = t < T ? __popcll(aq[q]) : -1;
+      md = dq[q] > md ? dq[q] : md;
+      if (t >= T) s_Ti[t * CO_LD + sc] = 0.f;  // padding rows
     }
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    atomicMax(&s_bad, md);  // LDS max of depths (s_bad is free again)
+    __syncthreads();
+    md = s_bad;
     for (int d = 0; d <= md; ++d) {
-      for (int e = tid; e < TMAX * TMAX; e += kNT) {
-        const int t = e / TMAX, sc = e % TMAX;
-        const unsigned long long anc = t < T ? s_anc[t] : 0ull;
-        const int dt = t < T ? __popcll(anc) : -1;
-        if (d == 0 && t >= T) s_Ti[t * CO_LD + sc] = 0.f;  // padding rows
-        if (dt != d) continue;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (dq[q] != d) continue;
+        const int t = (tid + q * kNT) / TMAX;
         float v = 0.f;
         if (sc < T) {
           if (sc == t) {
             v = 1.f;
           } else if (sc < t) {
-            for (unsigned long long mm = anc & ~((1ull << sc) - 1ull); mm; mm &= mm - 1) {
+            for (unsigned long long mm = aq[q] & ~((1ull << sc) - 1ull); mm; mm &= mm - 1) {
               const int a = __builtin_ctzll(mm);
               v = fmaf(-s_G[t * CO_LD + a], s_Ti[a * CO_LD + sc], v);
             }
@@ -625,9 +652,11 @@ __global__ __launch_bounds__(kNT) void k_verify_wy(VerifyArgs p) {
 template <int DK, int DV, int TMAX, int ROWS, typename TIn>
 hipError_t launch_k(const VerifyArgs& a, int grid, hipStream_t s) {
   if (a.K == 4)
-    hipLaunchKernelGGL((k_verify_wy<DK, DV, TMAX, ROWS, 4, TIn>), dim3(grid), dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((k_verify_wy<DK, DV, TMAX, ROWS, 4, TIn>), dim3(grid),
+                       dim3(threads_for<TMAX>()), 0, s, a);
   else
-    hipLaunchKernelGGL((k_verify_wy<DK, DV, TMAX, ROWS, 0, TIn>), dim3(grid), dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((k_verify_wy<DK, DV, TMAX, ROWS, 0, TIn>), dim3(grid),
+                       dim3(threads_for<TMAX>()), 0, s, a);
   return hipGetLastError();
 }
 
