@@ -33,6 +33,60 @@ import numpy as np
 import torch
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per verify launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (calibrated on a plain copy), or None when the verify
+    kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "verify_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec.get("sources", []):
+        with open(os.path.join(ROOT, src), "rb") as g:
+            h.update(g.read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else w["traffic_bytes"]
+
+
+def rollback_sweep(cfg, rb, stream, reps=10):
+    """Rollback time (tape replay + conv window) with every sequence forced
+    to the same accepted length n = 0..T; least-squares fit of
+    t(n) = c0 [n >= 1] + c1 n over n >= 1."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    from speculative_decode_verify_gdn_amd import spec_round as sr
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        sr.rollback(rb, stream)
+    us = []
+    for n in range(cfg.T + 1):
+        rb.n_keep.fill_(n)
+        for _ in range(2):
+            g.replay()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) / reps * 1e3)
+    ns = np.arange(1, cfg.T + 1)
+    A = np.stack([np.ones_like(ns), ns], 1).astype(np.float64)
+    y = np.array(us[1:])
+    coef, *_ = np.linalg.lstsq(A, y, rcond=None)
+    pred = A @ coef
+    r2 = 1.0 - float(np.sum((y - pred) ** 2) / max(np.sum((y - y.mean()) ** 2), 1e-30))
+    tape_tok = cfg.Hv * cfg.Dv * 4 + cfg.Hk * cfg.Dk * 4 + cfg.Hv * 4
+    return {"n": list(range(cfg.T + 1)), "us": us, "c0_us": float(coef[0]),
+            "c1_us_per_token": float(coef[1]), "r2": r2,
+            "tape_bytes_per_token_per_stack": cfg.L * cfg.B * tape_tok}
 
 
 def parse():
@@ -119,14 +173,16 @@ def oracle_baseline(cfg, seconds: float) -> dict:
     import oracle
     from speculative_decode_verify_gdn_amd import workload as W
 
-    def one(L_s, B_s):
+    def prepare(L_s, B_s):
         c = cfg.with_(L=L_s, B=B_s)
         inp = {k: W.to_f64(v) for k, v in W.layer_inputs(c, 0, "cpu").items()}
         acc = W.tree_accept_inputs(c, 0, "cpu") if c.is_tree else W.chain_accept_inputs(c, 0, "cpu")
         sh = oracle.Shape(L_s, B_s, c.Hk, c.Hv, c.Dk, c.Dv, c.K, c.silu, c.eps)
-        draft = acc["draft"].numpy()
-        logits = W.to_f64(acc["logits"])
-        parent = acc["parent"].numpy() if c.is_tree else None
+        return (sh, inp, acc["draft"].numpy(), W.to_f64(acc["logits"]),
+                acc["parent"].numpy() if c.is_tree else None)
+
+    def run(sample):
+        sh, inp, draft, logits, parent = sample
         keys = ("x", "conv_state", "conv_w", "a", "b", "S0")
         t0 = time.perf_counter()
         if parent is None:
@@ -147,17 +203,24 @@ def oracle_baseline(cfg, seconds: float) -> dict:
                          + cfg.T * cfg.C) + 8 * (cfg.T + 1) * cfg.V
     b_cap = int(max(1, min(cfg.B, 3e9 // per_seq)))
     B_s = min(2, b_cap)
-    t = one(L_s, B_s)
+    t = run(prepare(L_s, B_s))
     want = int(B_s * seconds / max(t, 1e-3))
     if want > B_s:
         B_s = int(min(b_cap, want))
-        t = one(L_s, B_s)
+    # the sample is memory-bounded; repeat it until about `seconds` of CPU work
+    sample = prepare(L_s, B_s)
+    times = [run(sample)]
+    while sum(times) < seconds:
+        times.append(run(sample))
+    del sample
+    t = float(np.mean(times))
     t_round = t * (cfg.L * cfg.B) / (L_s * B_s)
     return {"value": cfg.B * cfg.T / t_round, "unit": "tokens/s", "cores": nthr,
             "kind": "oracle",
             "sample": "fp64 oracle round (verify, accept, tape and conv rollback) on %d layers x "
-                      "%d sequences of the %d x %d workload in %.1f s, scaled by unit count to "
-                      "%.1f s per round" % (L_s, B_s, cfg.L, cfg.B, t, t_round)}
+                      "%d sequences of the %d x %d workload, %d repetitions in %.1f s (mean "
+                      "%.2f s), scaled by unit count to %.1f s per round"
+                      % (L_s, B_s, cfg.L, cfg.B, len(times), sum(times), t, t_round)}
 
 
 # ------------------------------------------------------------------- main --
@@ -235,34 +298,48 @@ def main():
         torch.cuda.synchronize()
         total_ms = e0.elapsed_time(e1)
 
-        # Kernel pass: same rounds, eager, HIP events around each launch group
-        # on the launch stream (per-kernel durations; not the headline).
+        # Kernel pass: the same rounds as three captured phases (verify of all
+        # layers, accept, rollback), each replayed between HIP events on the
+        # launch stream, so per-kernel times carry no host launch gaps.
         ev = lambda: torch.cuda.Event(enable_timing=True)
+        phase_graphs = []
+        for rb in rbs:
+            gv, ga, gr = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gv, stream=stream):
+                for l in range(cfg.L):
+                    sr.verify_layer(rb, l)
+            with torch.cuda.graph(ga, stream=stream):
+                sr.accept(rb)
+            with torch.cuda.graph(gr, stream=stream):
+                sr.rollback(rb)
+            phase_graphs.append((gv, ga, gr))
+        torch.cuda.synchronize()
         v_ms, a_ms, r_ms = [], [], []
         for i in range(args.steps):
             rb = rbs[i % len(rbs)]
-            for l in range(cfg.L):
+            gv, ga, gr = phase_graphs[i % len(rbs)]
+            for g, acc in ((gv, v_ms), (ga, a_ms)):
                 s0, s1 = ev(), ev()
                 s0.record(stream)
-                sr.verify_layer(rb, l)
+                g.replay()
                 s1.record(stream)
-                v_ms.append((s0, s1))
-            s0, s1 = ev(), ev()
-            s0.record(stream)
-            sr.accept(rb)
-            s1.record(stream)
-            a_ms.append((s0, s1))
+                acc.append((s0, s1))
             n_hist[i].copy_(rb.n_keep)
             s0, s1 = ev(), ev()
             s0.record(stream)
-            sr.rollback(rb)
+            gr.replay()
             s1.record(stream)
             r_ms.append((s0, s1))
         torch.cuda.synchronize()
-    verify_ms = float(np.mean([a.elapsed_time(b) for a, b in v_ms]))
+    verify_ms = float(np.mean([a.elapsed_time(b) for a, b in v_ms])) / cfg.L
     accept_ms = float(np.mean([a.elapsed_time(b) for a, b in a_ms]))
     rollback_ms = float(np.mean([a.elapsed_time(b) for a, b in r_ms]))
     assert int(shared.dev_err.item()) == 0, "device-side error bits set"
+
+    sweep = None
+    if args.sweep_n and not cfg.is_tree:
+        with torch.cuda.stream(stream):
+            sweep = rollback_sweep(cfg, rbs[0], stream)
 
     ms = total_ms / args.steps
     n_keep = n_hist.cpu().numpy()
@@ -302,9 +379,11 @@ def main():
                       "rollback_state_and_conv": rollback_ms},
         "roofline": {"kernel": "k_verify_wy (gdn_verify_chunk / gdn_tree_verify, one layer)",
                      "bound": "hbm", "achieved": verify_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": verify_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_launch": vb},
+                     "unit": "GB/s", "frac": verify_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(cfg.name), "bytes_per_launch": vb},
     }
+    if sweep is not None:
+        out["rollback_sweep"] = sweep
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = oracle_baseline(cfg, args.cpu_seconds)
     print(json.dumps(out), flush=True)
