@@ -11,18 +11,19 @@
 //   o_t = gamma_t S0 q_t + sum_{i in anc(t)+t} Oc[t,i] u_i,  Oc[t,i] = Gamma[t,i] q_t.k_i
 // With Ti = (I + A)^-1 and M2 = Oc Ti (both T x T, supported on ancestors):
 //   U = Ti RHS,   O = diag(gamma) Q S0^T + M2 RHS.
-// The state enters only through [K;Q] S0^T, one dense (2T x Dk) x (Dk x Dv)
-// contraction per head on fp32 MFMA with S0 read once from HBM into the
-// B-operand registers; [Ti;M2] RHS is a second, small MFMA whose output lands
-// in the same lanes as Q S0^T, so o and u leave straight from registers.  A
-// tree is the same algebra with the ancestor set from the parent array
-// (tree-aware verify, GDN page s8).  S0 and the conv window are never
-// written: they stay the pre-verify snapshot that rollback replays onto.
+// The state enters only through S0 [K;Q]^T, one dense (Dv x Dk) x (Dk x 2T)
+// contraction per head on bf16 MFMA with hi/lo operand splits (fp32-level
+// accuracy), S0 read once from HBM straight into the A-operand registers;
+// RHS^T [Ti;M2]^T is a second, small MFMA whose output lands in the same
+// lanes as S0 Q^T, so o and u leave straight from registers.  A tree is the
+// same algebra with the ancestor set from the parent array (tree-aware
+// verify, GDN page s8).  S0 and the conv window are never written: they stay
+// the pre-verify snapshot that rollback replays onto.
 //
-// Work decomposition: one 256-thread workgroup per (layer, seq, v-head,
-// ROWS-row block of S); the rows of S are independent recurrences sharing
-// q, k and the gates.  Each wave owns 16-row tiles of S; lane (c16 = lane%16,
-// kk = lane/16) holds S0[row c16][16m + 4kk .. +3] for every 16-column step m.
+// Work decomposition: one workgroup per (layer, seq, v-head, ROWS-row block
+// of S); the rows of S are independent recurrences sharing q, k and the
+// gates.  Each wave owns 16-row tiles of S; lane (c16 = lane%16, kk =
+// lane/16) holds S0[row c16][16m + 4kk .. +3] for every 16-column step m.
 // The per-head prologue (conv, L2 norm, Gram on MFMA, the T x T algebra)
 // runs while the state loads are in flight.
 
@@ -41,6 +42,14 @@ constexpr int kMaxK = 8;
 template <int TMAX>
 constexpr int threads_for() {
   return TMAX >= 64 ? 512 : 256;
+}
+
+// Waves per SIMD to keep resident: chunks of up to 16 nodes fit four
+// workgroups per CU in LDS, so registers must not be what limits them
+// (at most 128 per lane); longer chunks are held to two or one by LDS.
+template <int TMAX>
+constexpr int waves_per_eu() {
+  return TMAX <= 16 ? 4 : 1;
 }
 
 // Sum over aligned groups of 8 lanes (DPP; every lane gets its group's sum).
@@ -86,7 +95,8 @@ struct VerifyLayout {
 };
 
 template <int DK, int DV, int TMAX, int ROWS, int KC, typename TIn>
-__global__ __launch_bounds__(threads_for<TMAX>()) void k_verify_wy(VerifyArgs p) {
+__global__ __launch_bounds__(threads_for<TMAX>())
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(VerifyArgs p) {
   constexpr int kNT = threads_for<TMAX>();
   constexpr int kNWave = kNT / kWave;
   constexpr int KM = KC > 0 ? KC : kMaxK;  // unroll bound of the conv taps
@@ -195,16 +205,18 @@ __global__ __launch_bounds__(threads_for<TMAX>()) void k_verify_wy(VerifyArgs p)
       }
     }
   }
+  // The state loads too are unconditional (a wave without a tile re-reads the
+  // last one): with loads under a branch the compiler can only count the
+  // loads issued on every path, and the first use of a small input would
+  // then wait for the whole state to arrive.
   floatx4 sreg[TPW][MSTEPS];
   const float* S_head = p.S + (lb * p.Hv + hv) * static_cast<size_t>(DV * DK);
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    const int tile = wave + tt * kNWave;
-    if (tile < NTILE) {
-      const float* rp = S_head + static_cast<size_t>(r0 + tile * 16 + c16) * DK + 4 * kk;
+    const int tile = wave + tt * kNWave < NTILE ? wave + tt * kNWave : NTILE - 1;
+    const float* rp = S_head + static_cast<size_t>(r0 + tile * 16 + c16) * DK + 4 * kk;
 #pragma unroll
-      for (int m = 0; m < MSTEPS; ++m) sreg[tt][m] = *reinterpret_cast<const floatx4*>(rp + 16 * m);
-    }
+    for (int m = 0; m < MSTEPS; ++m) sreg[tt][m] = *reinterpret_cast<const floatx4*>(rp + 16 * m);
   }
 
   // (2) Parents (validated) and gates.
@@ -231,6 +243,9 @@ __global__ __launch_bounds__(threads_for<TMAX>()) void k_verify_wy(VerifyArgs p)
   }
   if (tid < T) {
     if (rblk == 0) p.tg[(lb * T + tid) * p.Hv + hv] = s_ga[tid];
+    // slots beyond the kernel width stay valid row indices (the conv reads
+    // every slot; their weights are zero)
+    for (int j = K; j < kMaxK; ++j) s_widx[tid * kMaxK + j] = 0;
     // conv window of node tid: the node, its ancestors upward, then old rows
     int cur = tid, old = 0;
     for (int j = K - 1; j >= 0; --j) {
@@ -283,29 +298,61 @@ __global__ __launch_bounds__(threads_for<TMAX>()) void k_verify_wy(VerifyArgs p)
         ld = 1;
       }
       // Branch-free over nodes: padding nodes read valid rows and are zeroed.
+      // Each batch reads all of its inputs before its first store, so the
+      // LDS reads of a batch are in flight together instead of one round
+      // trip per node behind the previous node's store.
       if (!tree) {
         // chain: the window of token t is raw rows t .. t+K-1
-#pragma unroll 8
-        for (int t = 0; t < TMAX; ++t) {
-          float y = 0.f;
+        constexpr int CH = 8;
 #pragma unroll
-          for (int j = 0; j < KM; ++j)
-            if (KC > 0 || j < K) y = fmaf(w[sl][j], ld_in(s_rawe, (t + j) * NCH + c), y);
-          if (p.silu) y = silu(y);
-          dst[t * ld] = t < T ? y : 0.f;
+        for (int t0 = 0; t0 < TMAX; t0 += CH) {
+          float xr[CH + KM - 1];
+#pragma unroll
+          for (int j = 0; j < CH + KM - 1; ++j) xr[j] = ld_in(s_rawe, (t0 + j) * NCH + c);
+#pragma unroll
+          for (int tt = 0; tt < CH; ++tt) {
+            float y = 0.f;
+#pragma unroll
+            for (int j = 0; j < KM; ++j)
+              if (KC > 0 || j < K) y = fmaf(w[sl][j], xr[tt + j], y);
+            if (p.silu) y = silu(y);
+            dst[(t0 + tt) * ld] = t0 + tt < T ? y : 0.f;
+          }
         }
       } else {
-#pragma unroll 8
-        for (int t = 0; t < TMAX; ++t) {
-          const int4 wa = *reinterpret_cast<const int4*>(s_widx + t * kMaxK);
-          const int4 wb = *reinterpret_cast<const int4*>(s_widx + t * kMaxK + 4);
-          const int wi[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-          float y = 0.f;
+        constexpr int NB = TMAX <= 16 ? 2 : 4;  // nodes per batch (registers: the state is live)
 #pragma unroll
-          for (int j = 0; j < KM; ++j)
-            if (KC > 0 || j < K) y = fmaf(w[sl][j], ld_in(s_rawe, (wi[j] + K - 1) * NCH + c), y);
-          if (p.silu) y = silu(y);
-          dst[t * ld] = t < T ? y : 0.f;
+        for (int t0 = 0; t0 < TMAX; t0 += NB) {
+          int wi[NB][KM];
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            const int4 wa = *reinterpret_cast<const int4*>(s_widx + (t0 + n) * kMaxK);
+            wi[n][0] = wa.x;
+            if (KM > 1) wi[n][1 % KM] = wa.y;
+            if (KM > 2) wi[n][2 % KM] = wa.z;
+            if (KM > 3) wi[n][3 % KM] = wa.w;
+            if constexpr (KM > 4) {
+              const int4 wb = *reinterpret_cast<const int4*>(s_widx + (t0 + n) * kMaxK + 4);
+              wi[n][4 % KM] = wb.x;
+              wi[n][5 % KM] = wb.y;
+              wi[n][6 % KM] = wb.z;
+              wi[n][7 % KM] = wb.w;
+            }
+          }
+          float xv[NB][KM];
+#pragma unroll
+          for (int n = 0; n < NB; ++n)
+#pragma unroll
+            for (int j = 0; j < KM; ++j) xv[n][j] = ld_in(s_rawe, (wi[n][j] + K - 1) * NCH + c);
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            float y = 0.f;
+#pragma unroll
+            for (int j = 0; j < KM; ++j)
+              if (KC > 0 || j < K) y = fmaf(w[sl][j], xv[n][j], y);
+            if (p.silu) y = silu(y);
+            dst[(t0 + n) * ld] = t0 + n < T ? y : 0.f;
+          }
         }
       }
     }
@@ -375,32 +422,43 @@ __global__ __launch_bounds__(threads_for<TMAX>()) void k_verify_wy(VerifyArgs p)
   //     the product of a along the path when gamma_i has underflowed.
   if (tid < T) {
     float gm = 1.f;
-    for (int c = tid; c >= 0; c = s_par[c]) gm *= s_ga[c];
+    if (!tree) {  // chain: independent reads, same product order as the walk
+#pragma unroll
+      for (int c = TMAX - 1; c >= 0; --c) gm *= c <= tid ? s_ga[c] : 1.f;
+    } else {
+      for (int c = tid; c >= 0; c = s_par[c]) gm *= s_ga[c];
+    }
     s_gam[tid] = gm;
   }
   __syncthreads();
+  // All reads of a thread's pairs come before its first store.
   constexpr int NPQ = (TMAX * TMAX + kNT - 1) / kNT;  // pairs per thread
+  {
+    float av[NPQ], ov[NPQ];
 #pragma unroll
-  for (int q = 0; q < NPQ; ++q) {
-    const int e = tid + q * kNT;
-    if (e >= TMAX * TMAX) break;
-    const int t = e / TMAX, i = e % TMAX;
-    const bool on = t < T && (i == t || ((s_anc[t] >> i) & 1ull));
-    float av = 0.f, ov = 0.f;
-    if (on) {
-      float gm;
-      const float gi = s_gam[i];
-      if (gi > 1e-30f) {
-        gm = s_gam[t] / gi;
-      } else {
+    for (int q = 0; q < NPQ; ++q) {
+      const int e = tid + q * kNT;
+      const int t = (e / TMAX) % TMAX, i = e % TMAX;
+      const bool on = e < TMAX * TMAX && t < T && (i == t || ((s_anc[t] >> i) & 1ull));
+      const float gi = s_gam[i], gt = s_gam[t], bt = s_gb[t];
+      const float gk = s_G[t * CO_LD + i], gq = s_G[(TMAX + t) * CO_LD + i];
+      float gm = gt / gi;
+      if (on && !(gi > 1e-30f)) {  // gamma_i underflowed: product along the path
         gm = 1.f;
         for (int c = t; c != i; c = s_par[c]) gm *= s_ga[c];
       }
-      if (i != t) av = s_gb[t] * gm * s_G[t * CO_LD + i];
-      ov = gm * s_G[(TMAX + t) * CO_LD + i];
+      av[q] = on && i != t ? bt * gm * gk : 0.f;
+      ov[q] = on ? gm * gq : 0.f;
     }
-    s_G[t * CO_LD + i] = av;
-    s_G[(TMAX + t) * CO_LD + i] = ov;
+#pragma unroll
+    for (int q = 0; q < NPQ; ++q) {
+      const int e = tid + q * kNT;
+      if (e < TMAX * TMAX) {
+        const int t = e / TMAX, i = e % TMAX;
+        s_G[t * CO_LD + i] = av[q];
+        s_G[(TMAX + t) * CO_LD + i] = ov[q];
+      }
+    }
   }
   __syncthreads();  // A, Oc, gamma complete
 
@@ -408,6 +466,8 @@ __global__ __launch_bounds__(threads_for<TMAX>()) void k_verify_wy(VerifyArgs p)
   if (tid < TMAX) {
     const int j = tid;
     if (TMAX <= 16) {
+      // column j by forward substitution; the column is stored only after
+      // the solve, so every read of A can be in flight at once
       float xc[TMAX];
 #pragma unroll
       for (int t = 0; t < TMAX; ++t) {
@@ -415,8 +475,9 @@ __global__ __launch_bounds__(threads_for<TMAX>()) void k_verify_wy(VerifyArgs p)
 #pragma unroll
         for (int a = 0; a < t; ++a) v = fmaf(-s_G[t * CO_LD + a], xc[a], v);
         xc[t] = (t < T && j < T) ? v : 0.f;
-        s_Ti[t * CO_LD + j] = xc[t];
       }
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) s_Ti[t * CO_LD + j] = xc[t];
     }
   }
   if constexpr (TMAX > 16) {
@@ -506,143 +567,151 @@ __global__ __launch_bounds__(threads_for<TMAX>()) void k_verify_wy(VerifyArgs p)
   }
   __syncthreads();
 
-  // (9) [K;Q] S0^T on bf16 MFMA (16x16x32) with every operand split into a
+  // (9) S0 [K;Q]^T on bf16 MFMA (16x16x32) with every operand split into a
   //     bf16 high part and a bf16 residual (three products, fp32 accumulate).
+  //     A = this wave's 16-row tile of S0 (from registers), B = a 16-column
+  //     block of [K;Q] rows, so lane (n, kk) ends with rows i = 4kk..4kk+3 of
+  //     the tile for one k or q row n: one node per lane, four consecutive
+  //     state rows, which keeps the RHS in registers and the outputs float4.
   //     Step s contracts the 32 columns {32s + 16h + 4kk + e}: the two float4
   //     this lane holds for m = 2s, 2s+1, and the matching k/q columns.
   constexpr int KSTEPS = DK / 32;
+  constexpr int NCB = NRB;  // 16-column blocks of [K;Q]: k rows, then q rows
   bf16x8 shi[TPW][KSTEPS], slo[TPW][KSTEPS];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
       split_bf16x8(sreg[tt][2 * ks], sreg[tt][2 * ks + 1], shi[tt][ks], slo[tt][ks]);
-  floatx4 acc1[TPW][NRB];
+  // this lane's node in each column block, its gates and its role
+  float gam_c[NCB], gb_c[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int kq = cb * 16 + c16;
+    const int t = kq < TMAX ? kq : kq - TMAX;
+    gam_c[cb] = s_gam[t];
+    gb_c[cb] = s_gb[t];
+  }
+  floatx4 acc1[TPW][NCB];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) acc1[tt][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) acc1[tt][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    if (TMAX >= 16 && (rb * 16) % TMAX >= T) continue;  // all-padding block
-    const float* arow = s_kq + (rb * 16 + c16) * KQ_LD + 4 * kk;
+  for (int cb = 0; cb < NCB; ++cb) {
+    if (TMAX >= 16 && (cb * 16) % TMAX >= T) continue;  // all-padding block
+    const float* brow = s_kq + (cb * 16 + c16) * KQ_LD + 4 * kk;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      bf16x8 ahi, alo;
-      split_bf16x8(*reinterpret_cast<const floatx4*>(arow + 32 * ks),
-                   *reinterpret_cast<const floatx4*>(arow + 32 * ks + 16), ahi, alo);
+      bf16x8 bhi, blo;
+      split_bf16x8(*reinterpret_cast<const floatx4*>(brow + 32 * ks),
+                   *reinterpret_cast<const floatx4*>(brow + 32 * ks + 16), bhi, blo);
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt)
         if (wave + tt * kNWave < NTILE)
-          acc1[tt][rb] = mfma_bf16x3(ahi, alo, shi[tt][ks], slo[tt][ks], acc1[tt][rb]);
+          acc1[tt][cb] = mfma_bf16x3(shi[tt][ks], slo[tt][ks], bhi, blo, acc1[tt][cb]);
     }
   }
-  // RHS_t[i] = b_t (v_t[i] - gamma_t W[t][i]) from the W rows of acc1, in place
-  // of v; padding rows become 0.
+  // RHS_t[i] = b_t (v_t[i] - gamma_t W[i][t]) on the k-row lanes, in place of
+  // v (stored [row of S][node]); padding nodes become 0.  Only this wave
+  // reads its tiles' RHS back, and a wave's LDS accesses execute in order, so
+  // no workgroup barrier separates this from the product below.
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int tile = wave + tt * kNWave;
     if (tile < NTILE) {
-      float* col = s_rhs + (tile * 16 + c16) * RT_LD;
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const int row0 = rb * 16 + 4 * kk;
-        if (row0 < TMAX) {
-          if constexpr (TMAX <= 16) {
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int kq = cb * 16 + c16;
+        if (kq < TMAX) {
+          float* col = s_rhs + (tile * 16 + 4 * kk) * RT_LD + kq;
+          float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = row0 + r;
-              col[t] = t < T ? s_gb[t] * (col[t] - s_gam[t] * acc1[tt][rb][r]) : 0.f;
-            }
-          } else {
-            floatx4 v = *reinterpret_cast<floatx4*>(col + row0);
+          for (int r = 0; r < 4; ++r) v[r] = col[r * RT_LD];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = row0 + r;
-              v[r] = t < T ? s_gb[t] * (v[r] - s_gam[t] * acc1[tt][rb][r]) : 0.f;
-            }
-            *reinterpret_cast<floatx4*>(col + row0) = v;
-          }
+          for (int r = 0; r < 4; ++r)
+            col[r * RT_LD] = kq < T ? gb_c[cb] * (v[r] - gam_c[cb] * acc1[tt][cb][r]) : 0.f;
         }
       }
     }
   }
-  __syncthreads();  // RHS complete
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // (10) [Ti; M2] RHS on MFMA: rows [0,TMAX) give U, rows [TMAX,2TMAX) give
-  //      M2 RHS, in the same lanes as the Q S0^T rows of acc1.
-  floatx4 acc2[TPW][NRB];
+  // (10) RHS^T [Ti; M2]^T on MFMA: A = this wave's RHS tile (rows of S x
+  //      nodes), B = a 16-row block of [Ti; M2]; block cb's columns are the
+  //      same nodes as block cb of the first product, so U (k-row lanes) and
+  //      M2 RHS (q-row lanes) land where W and Q S0^T are.
+  floatx4 acc2[TPW][NCB];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) acc2[tt][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // B operand of the long-chunk path: this lane's RHS columns, split once.
+    for (int cb = 0; cb < NCB; ++cb) acc2[tt][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // A operand of the long-chunk path: this lane's RHS row, split once.
   constexpr int RST = TMAX >= 32 ? TMAX / 32 : 1;
   bf16x8 rhi[TPW][RST], rlo[TPW][RST];
   if constexpr (TMAX >= 32) {
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
       const int tile = wave + tt * kNWave;
-      const float* brow = s_rhs + ((tile < NTILE ? tile : 0) * 16 + c16) * RT_LD + 8 * kk;
+      const float* arow = s_rhs + ((tile < NTILE ? tile : 0) * 16 + c16) * RT_LD + 8 * kk;
 #pragma unroll
       for (int st = 0; st < RST; ++st)
-        split_bf16x8(*reinterpret_cast<const floatx4*>(brow + 32 * st),
-                     *reinterpret_cast<const floatx4*>(brow + 32 * st + 4), rhi[tt][st], rlo[tt][st]);
+        split_bf16x8(*reinterpret_cast<const floatx4*>(arow + 32 * st),
+                     *reinterpret_cast<const floatx4*>(arow + 32 * st + 4), rhi[tt][st], rlo[tt][st]);
     }
   }
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    if (TMAX >= 16 && (rb * 16) % TMAX >= T) continue;
-    const int arow = rb * 16 + c16;
-    const float* amat = arow < TMAX ? s_Ti + arow * CO_LD : s_G + (arow - TMAX) * CO_LD;
+  for (int cb = 0; cb < NCB; ++cb) {
+    if (TMAX >= 16 && (cb * 16) % TMAX >= T) continue;
+    const int brow = cb * 16 + c16;
+    const float* bmat = brow < TMAX ? s_Ti + brow * CO_LD : s_G + (brow - TMAX) * CO_LD;
     if constexpr (TMAX >= 32) {
 #pragma unroll
       for (int st = 0; st < TMAX / 32; ++st) {
         if (st * 32 >= T) break;
-        bf16x8 ahi, alo;
-        split_bf16x8(*reinterpret_cast<const floatx4*>(amat + 32 * st + 8 * kk),
-                     *reinterpret_cast<const floatx4*>(amat + 32 * st + 8 * kk + 4), ahi, alo);
+        bf16x8 bhi, blo;
+        split_bf16x8(*reinterpret_cast<const floatx4*>(bmat + 32 * st + 8 * kk),
+                     *reinterpret_cast<const floatx4*>(bmat + 32 * st + 8 * kk + 4), bhi, blo);
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
           if (wave + tt * kNWave < NTILE)
-            acc2[tt][rb] = mfma_bf16x3(ahi, alo, rhi[tt][st], rlo[tt][st], acc2[tt][rb]);
+            acc2[tt][cb] = mfma_bf16x3(rhi[tt][st], rlo[tt][st], bhi, blo, acc2[tt][cb]);
       }
     } else {
 #pragma unroll
       for (int st = 0; st < TMAX / 4; ++st) {
         if (st * 4 >= T) break;
-        const float a_op = amat[4 * st + kk];
+        const float b_op = bmat[4 * st + kk];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const int tile = wave + tt * kNWave;
           if (tile < NTILE) {
-            const float b_op = s_rhs[(tile * 16 + c16) * RT_LD + 4 * st + kk];
-            acc2[tt][rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_op, b_op, acc2[tt][rb], 0, 0, 0);
+            const float a_op = s_rhs[(tile * 16 + c16) * RT_LD + 4 * st + kk];
+            acc2[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_op, b_op, acc2[tt][cb], 0, 0, 0);
           }
         }
       }
     }
   }
 
-  // (11) Outputs straight from registers: u rows and o = gamma Z + M2 RHS.
+  // (11) Outputs straight from registers, four consecutive state rows per
+  //      lane: u on the k-row lanes, o = gamma Z + M2 RHS on the q-row lanes.
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int tile = wave + tt * kNWave;
     if (tile < NTILE) {
-      const int i = r0 + tile * 16 + c16;
+      const int i0 = r0 + tile * 16 + 4 * kk;
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rb * 16 + 4 * kk + r;
-          const int t = row < TMAX ? row : row - TMAX;
-          if (t < T) {
-            const size_t oi = ((lb * T + t) * p.Hv + hv) * DV + i;
-            if (row < TMAX)
-              p.tu[oi] = acc2[tt][rb][r];
-            else
-              p.o[oi] = fmaf(s_gam[t], acc1[tt][rb][r], acc2[tt][rb][r]);
-          }
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int kq = cb * 16 + c16;
+        const bool isk = kq < TMAX;
+        const int t = isk ? kq : kq - TMAX;
+        if (t < T) {
+          const size_t oi = ((lb * T + t) * p.Hv + hv) * DV + i0;
+          floatx4 val = acc2[tt][cb];
+          if (!isk) val += gam_c[cb] * acc1[tt][cb];
+          *reinterpret_cast<floatx4*>((isk ? p.tu : p.o) + oi) = val;
         }
       }
     }
