@@ -90,7 +90,7 @@ struct VerifyLayout {
   static constexpr int STAGE_BYTES = XR * CPR * 16;
   static constexpr int COEF_BYTES = 3 * TMAX * CO_LD * 4;  // [A;Oc] then [M2;Oc], and Ti
   static constexpr int U1_BYTES = STAGE_BYTES > COEF_BYTES ? STAGE_BYTES : COEF_BYTES;
-  static constexpr int TOTAL = 2 * TMAX * KQ_LD * 4 + ROWS * RT_LD * 4 + U1_BYTES + TMAX * 56 + 16;
+  static constexpr int TOTAL = 2 * TMAX * KQ_LD * 4 + ROWS * RT_LD * 4 + U1_BYTES + TMAX * (24 + 4 * KM) + 16;
   static_assert(TOTAL <= 160 * 1024, "LDS budget of one workgroup exceeded");
 };
 
@@ -100,6 +100,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
   constexpr int kNT = threads_for<TMAX>();
   constexpr int kNWave = kNT / kWave;
   constexpr int KM = KC > 0 ? KC : kMaxK;  // unroll bound of the conv taps
+  static_assert(KM == 4 || KM == 8, "window rows are read as int4");
   using LY = VerifyLayout<DK, DV, TMAX, ROWS, KM, TIn>;
   constexpr int KQ_LD = LY::KQ_LD, RT_LD = LY::RT_LD, CO_LD = LY::CO_LD;
   constexpr int NCH = LY::NCH;
@@ -116,7 +117,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
   __shared__ float s_gam[TMAX], s_ga[TMAX], s_gb[TMAX];
   __shared__ unsigned long long s_anc[TMAX];
   __shared__ int s_par[TMAX];
-  __shared__ __align__(16) int s_widx[TMAX * kMaxK];
+  __shared__ __align__(16) int s_widx[TMAX * KM];  // conv window rows per node
   __shared__ int s_bad;
   float* s_G = reinterpret_cast<float*>(s_u1);  // [2TMAX][CO_LD]: KK then A (-> M2); QK then Oc
   float* s_Ti = s_G + 2 * TMAX * CO_LD;         // [TMAX][CO_LD]
@@ -143,9 +144,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
   const int K = KC > 0 ? KC : p.K;
   const bool tree = p.parent != nullptr;
 
-  // (1) Issue every load up front, small inputs first and the state last.
+  // (1) Issue the small loads, then the first group of state loads.
   //     Vector-memory loads return in order, so the prologue below waits only
-  //     for the small loads while the 64 KiB of state stay in flight.
+  //     for the small loads while the state stays in flight.
   const TIn* x = static_cast<const TIn*>(p.x);
   const TIn* cs = static_cast<const TIn*>(p.conv_state);
   const float* cw = p.conv_w + static_cast<size_t>(l) * p.C * K;
@@ -205,19 +206,27 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
       }
     }
   }
-  // The state loads too are unconditional (a wave without a tile re-reads the
-  // last one): with loads under a branch the compiler can only count the
+  // The state loads are unconditional too (a wave without a tile re-reads
+  // the last one): with loads under a branch the compiler can only count the
   // loads issued on every path, and the first use of a small input would
-  // then wait for the whole state to arrive.
+  // then wait for the whole state to arrive.  They go out in four groups
+  // between the prologue phases: a wave cannot issue past a load the memory
+  // pipeline has no room for, so issuing all 16 KiB at once would hold the
+  // prologue until most of the CU's state had arrived; in groups the queue
+  // stays full while the phases run in between.
   floatx4 sreg[TPW][MSTEPS];
   const float* S_head = p.S + (lb * p.Hv + hv) * static_cast<size_t>(DV * DK);
+  auto load_state = [&](int grp) {
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int tile = wave + tt * kNWave < NTILE ? wave + tt * kNWave : NTILE - 1;
-    const float* rp = S_head + static_cast<size_t>(r0 + tile * 16 + c16) * DK + 4 * kk;
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int tile = wave + tt * kNWave < NTILE ? wave + tt * kNWave : NTILE - 1;
+      const float* rp = S_head + static_cast<size_t>(r0 + tile * 16 + c16) * DK + 4 * kk;
 #pragma unroll
-    for (int m = 0; m < MSTEPS; ++m) sreg[tt][m] = *reinterpret_cast<const floatx4*>(rp + 16 * m);
-  }
+      for (int m = 0; m < MSTEPS; ++m)
+        if (m * 4 / MSTEPS == grp) sreg[tt][m] = *reinterpret_cast<const floatx4*>(rp + 16 * m);
+    }
+  };
+  load_state(0);
 
   // (2) Parents (validated) and gates.
   if (tid == 0) s_bad = 0;
@@ -239,21 +248,21 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
   }
   if (tid >= T && tid < TMAX) {  // padding nodes read a valid (discarded) window
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) s_widx[tid * kMaxK + j] = 0;
+    for (int j = 0; j < KM; ++j) s_widx[tid * KM + j] = 0;
   }
   if (tid < T) {
     if (rblk == 0) p.tg[(lb * T + tid) * p.Hv + hv] = s_ga[tid];
     // slots beyond the kernel width stay valid row indices (the conv reads
     // every slot; their weights are zero)
-    for (int j = K; j < kMaxK; ++j) s_widx[tid * kMaxK + j] = 0;
+    for (int j = K; j < KM; ++j) s_widx[tid * KM + j] = 0;
     // conv window of node tid: the node, its ancestors upward, then old rows
     int cur = tid, old = 0;
     for (int j = K - 1; j >= 0; --j) {
       if (cur >= 0) {
-        s_widx[tid * kMaxK + j] = cur;
+        s_widx[tid * KM + j] = cur;
         cur = s_par[cur];
       } else {
-        s_widx[tid * kMaxK + j] = --old;
+        s_widx[tid * KM + j] = --old;
       }
     }
   }
@@ -269,7 +278,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
   __syncthreads();
   if (p.conv_win && l == 0 && hk == 0 && g == 0 && rblk == 0) {
     for (int e = tid; e < T * K; e += kNT)
-      p.conv_win[static_cast<size_t>(bb) * T * K + e] = s_widx[(e / K) * kMaxK + (e % K)];
+      p.conv_win[static_cast<size_t>(bb) * T * K + e] = s_widx[(e / K) * KM + (e % K)];
   }
 
   // (3) Conv + SiLU out of the staged raw block, one thread per channel.
@@ -326,13 +335,13 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
           int wi[NB][KM];
 #pragma unroll
           for (int n = 0; n < NB; ++n) {
-            const int4 wa = *reinterpret_cast<const int4*>(s_widx + (t0 + n) * kMaxK);
+            const int4 wa = *reinterpret_cast<const int4*>(s_widx + (t0 + n) * KM);
             wi[n][0] = wa.x;
             if (KM > 1) wi[n][1 % KM] = wa.y;
             if (KM > 2) wi[n][2 % KM] = wa.z;
             if (KM > 3) wi[n][3 % KM] = wa.w;
             if constexpr (KM > 4) {
-              const int4 wb = *reinterpret_cast<const int4*>(s_widx + (t0 + n) * kMaxK + 4);
+              const int4 wb = *reinterpret_cast<const int4*>(s_widx + (t0 + n) * KM + 4);
               wi[n][4 % KM] = wb.x;
               wi[n][5 % KM] = wb.y;
               wi[n][6 % KM] = wb.z;
@@ -358,6 +367,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
     }
   }
   __syncthreads();
+
+  load_state(1);
 
   // (4) L2-normalise the 2T vectors (k rows, q rows): 8 lanes per vector.
   for (int v0 = 0; v0 < 2 * T; v0 += kNT / 8) {
@@ -416,6 +427,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
     }
   }
   __syncthreads();
+
+  load_state(2);
 
   // (6) gamma per node (walk to the root), then A and Oc in place of the
   //     Gram rows, one thread per (t, i): Gamma[t,i] = gamma_t / gamma_i, or
@@ -525,6 +538,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
     }
   }
   __syncthreads();  // Ti complete
+
+  load_state(3);
 
   // (8) M2 = Oc Ti (support: ancestors-or-self), written over A.
   if constexpr (TMAX <= 16) {
