@@ -125,6 +125,13 @@ def verify_bytes_per_launch(cfg, B) -> int:
     return B * per_seq + C * cfg.K * 4                  # + conv weights
 
 
+def verify_kernel_name(cfg) -> str:
+    """The verify kernel the library dispatches for this workload (one layer)."""
+    if not cfg.is_tree and cfg.T <= 8:
+        return "k_verify_chain (gdn_verify_chunk, chains of <= 8 tokens, one layer)"
+    return "k_verify_wy (%s, one layer)" % ("gdn_tree_verify" if cfg.is_tree else "gdn_verify_chunk")
+
+
 def rollback_bytes(cfg, n_keep: np.ndarray) -> int:
     """Tape replay: for n >= 1 read + write the state, read n tape entries."""
     P = cfg.Hv * cfg.Dv * cfg.Dk * 4
@@ -377,7 +384,7 @@ def main():
         "round_algorithmic_bytes": mean_round_bytes,
         "kernel_ms": {"verify_per_layer": verify_ms, "accept": accept_ms,
                       "rollback_state_and_conv": rollback_ms},
-        "roofline": {"kernel": "k_verify_wy (gdn_verify_chunk / gdn_tree_verify, one layer)",
+        "roofline": {"kernel": verify_kernel_name(cfg),
                      "bound": "hbm", "achieved": verify_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": verify_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(cfg.name), "bytes_per_launch": vb},

@@ -70,6 +70,8 @@ struct AcceptArgs {
 // Each returns hipErrorInvalidValue for an uninstantiated combination, else
 // the launch status.  dtype: 0 fp32, 1 bf16.
 hipError_t launch_verify_wy(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
+// Chains of at most 8 tokens (wave-specialised kernel).
+hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
 hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream_t s);
 hipError_t launch_conv_rollback(const ConvRollbackArgs& a, int dtype, hipStream_t s);
 hipError_t launch_accept(const AcceptArgs& a, int dtype, hipStream_t s);

@@ -1,0 +1,483 @@
+// k_verify_chain.hip -- verify of a short drafted chain (T <= 8 tokens)
+// through one GDN layer, for gfx950, with one wave specialised for the
+// per-head prologue and the others for the state.
+//
+// Same algebra as the chunked form in k_verify_wy.hip (GDN page s2.1, the
+// delta rule unrolled over the chunk; replay form in s4), for a chain:
+//   gamma_t = a_0 ... a_t,  Gamma[t,i] = a_{i+1} ... a_t
+//   A[t,i]  = b_t Gamma[t,i] k_t.k_i (i < t),  Oc[t,i] = Gamma[t,i] q_t.k_i (i <= t)
+//   Ti = (I + A)^-1,  M2 = Oc Ti,  RHS_t = b_t (v_t - gamma_t S0 k_t)
+//   U = Ti RHS,  O = diag(gamma) Q S0^T + M2 RHS.
+// q and k are L2-normalised after the conv.  Here the normalisation is a
+// scale: the Gram of the raw (post-conv) rows gives the norms on its
+// diagonal, and the state products use the raw rows with the per-node
+// scales r_t = 1/sqrt(|x_t|^2 + eps) applied to their fp32 results.
+//
+// Why wave 0 works alone first.  A wave that has queued 16 KiB of state
+// loads cannot issue further instructions until the memory pipeline has
+// accepted them, which under full load takes most of the time the state
+// takes to arrive.  So:
+//   wave 0 issues only the small loads (raw conv rows, weights, gates), then
+//     -- with no workgroup barrier -- does conv + SiLU, the Gram of [K;Q] on
+//     bf16x3 MFMA, the norms and the T x T algebra, and leaves the pre-split
+//     K/Q operands, V, [Ti;M2] and per-node scales in LDS;
+//   waves 1.. wait only until wave 0 has issued its loads, then queue their
+//     whole share of S0 at once;
+//   after one barrier every wave runs S0 [K;Q]^T (bf16x3 MFMA), the RHS,
+//     RHS [Ti;M2]^T (fp32 MFMA) and stores u and o from registers; wave 0
+//     queues its own share of S0 only then, so it arrives last.
+// Workgroups of four waves pack four to a CU: a fifth, state-less prologue
+// wave would put two waves of one workgroup on a SIMD and leave a quarter of
+// the workgroups waiting for a free slot.  (Measured alternatives -- a
+// prologue-only wave with the state on three waves, raised issue priority
+// for the prologue, delaying the state loads -- were no faster.)
+// S0 and the conv window are never written (they stay the snapshot).
+//
+// Work item: one workgroup per (layer, seq, v-head), all Dv rows of S.
+
+#include "gdn_common.hpp"
+#include "gdn_kernels.hpp"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+template <int DV>
+constexpr int chain_waves() {
+  return DV / 16 < 4 ? DV / 16 : 4;
+}
+template <int DV>
+constexpr int chain_threads() {
+  return 64 * chain_waves<DV>();
+}
+
+// Split two fp32 values into packed bf16 high parts and residuals.
+__device__ __forceinline__ void split_pair(float y0, float y1, uint32_t& hi, uint32_t& lo) {
+  const __bf16 h0 = static_cast<__bf16>(y0);
+  const __bf16 h1 = static_cast<__bf16>(y1);
+  bf16x2 h = {h0, h1};
+  bf16x2 l = {static_cast<__bf16>(y0 - static_cast<float>(h0)),
+              static_cast<__bf16>(y1 - static_cast<float>(h1))};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+__device__ __forceinline__ float silu_f(float y) {
+  return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
+}
+
+// Two adjacent input elements widened to fp32.
+template <typename TIn>
+struct Pair;
+template <>
+struct Pair<uint16_t> {
+  typedef uint32_t raw;
+  static __device__ __forceinline__ raw load(const uint16_t* p) {
+    return *reinterpret_cast<const uint32_t*>(p);
+  }
+  static __device__ __forceinline__ float lo(raw r) { return __uint_as_float(r << 16); }
+  static __device__ __forceinline__ float hi(raw r) { return __uint_as_float(r & 0xffff0000u); }
+};
+template <>
+struct Pair<float> {
+  typedef floatx2 raw;
+  static __device__ __forceinline__ raw load(const float* p) {
+    return *reinterpret_cast<const floatx2*>(p);
+  }
+  static __device__ __forceinline__ float lo(raw r) { return r[0]; }
+  static __device__ __forceinline__ float hi(raw r) { return r[1]; }
+};
+
+template <int DK, int DV, int TMAX, int KM, typename TIn>
+struct ChainLayout {
+  static constexpr int NW = chain_waves<DV>();
+  static constexpr int NT = chain_threads<DV>();
+  static constexpr int NTILE = DV / 16;
+  static constexpr int TPW = NTILE / NW;  // 16-row tiles per wave
+  static_assert(NTILE % NW == 0, "tiles per wave");
+  static constexpr int NKQ = 2 * TMAX;          // k rows [0,TMAX), q rows [TMAX,2TMAX)
+  static constexpr int KQS = 4 * DK + 16;       // bytes per pre-split row (+16: conflict-free b128)
+  static constexpr int RT_LD = TMAX + 1;        // V / RHS, [row of S][node]
+  static constexpr int GLD = NKQ + 1;           // Gram
+  static constexpr int ALD = TMAX + 1;          // A, Oc
+  static constexpr int BLD = TMAX + 1;          // [Ti; M2]
+  static constexpr int NPAIR = (2 * DK + DV) / 2;
+  static constexpr int PPL = (NPAIR + 63) / 64;  // channel pairs per prologue lane
+  static constexpr int XR = TMAX + KM - 1;       // raw rows: old window + tokens
+  static constexpr int RAW_WORDS = PPL * XR * (int)sizeof(TIn) / 2;
+  static constexpr bool LOAD_ALL = RAW_WORDS + PPL * 2 * KM <= 64;
+  static_assert(DK % 32 == 0 && DV % 16 == 0 && TMAX == 8, "tiling");
+};
+
+template <int DK, int DV, int TMAX, int KC, typename TIn>
+__global__ __launch_bounds__(chain_threads<DV>())
+__attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
+  constexpr int KM = KC > 0 ? KC : 8;
+  using LY = ChainLayout<DK, DV, TMAX, KM, TIn>;
+  using PR = Pair<TIn>;
+  constexpr int NW = LY::NW, TPW = LY::TPW, NKQ = LY::NKQ, KQS = LY::KQS;
+  constexpr int RT_LD = LY::RT_LD, GLD = LY::GLD, ALD = LY::ALD, BLD = LY::BLD;
+  constexpr int NPAIR = LY::NPAIR, PPL = LY::PPL, XR = LY::XR;
+  constexpr int KSTEPS = DK / 32;
+  constexpr int NCB = NKQ / 16;  // 16-column blocks of [K;Q]
+
+  __shared__ __align__(16) unsigned char s_kq[NKQ * KQS];  // pre-split raw k, q rows
+  __shared__ __align__(16) float s_kf[TMAX * DK];          // raw k rows (fp32), for the tape
+  __shared__ __align__(16) float s_rhs[DV * RT_LD];        // v, then RHS
+  __shared__ float s_G[NKQ * GLD];
+  __shared__ float s_A[TMAX * ALD], s_Oc[TMAX * ALD];
+  __shared__ float s_B[NKQ * BLD];                         // rows: Ti, then M2
+  __shared__ float s_rn[NKQ], s_ga[TMAX], s_gb[TMAX];
+  __shared__ float s_ck[TMAX], s_cq[TMAX], s_cb[TMAX];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c16 = lane & 15;
+  const int kk = lane >> 4;
+
+  const int G = p.Hv / p.Hk;
+  const int n_units = p.L * p.B * p.Hk;
+  const UnitSub us = xcd_unit_sub(blockIdx.x, G);
+  if (us.unit >= n_units) return;
+  const int hk = us.unit % p.Hk;
+  const size_t lb = us.unit / p.Hk;  // l * B + b
+  const int l = static_cast<int>(lb / p.B);
+  const int g = us.sub;
+  const int hv = hk * G + g;
+  const int T = p.T;
+  const int K = KC > 0 ? KC : p.K;
+
+  // This wave's tiles of S0 (tile wave + tt * NW): lane (c16, kk) holds row
+  // c16 of a tile, columns 16m + 4kk .. +3, as MFMA A operands.
+  floatx4 sreg[TPW][DK / 16];
+  const float* S_head = p.S + (lb * p.Hv + hv) * static_cast<size_t>(DV * DK);
+  auto load_state = [&]() {
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const float* rp = S_head + static_cast<size_t>((wave + tt * NW) * 16 + c16) * DK + 4 * kk;
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m) sreg[tt][m] = *reinterpret_cast<const floatx4*>(rp + 16 * m);
+    }
+  };
+
+  if (wave == 0) {
+    // ---------------------------------------------------------- prologue --
+    const TIn* x = static_cast<const TIn*>(p.x);
+    const TIn* cs = static_cast<const TIn*>(p.conv_state);
+    const float* cw = p.conv_w + static_cast<size_t>(l) * p.C * K;
+    const TIn* xcol = x + lb * T * p.C;
+    const TIn* ccol = cs + lb * (K - 1) * p.C;
+    const int nrows = K - 1 + T;
+    // local channel c in [q | k | v-rows] -> qkv channel
+    auto chan = [&](int c) {
+      return c < DK ? hk * DK + c
+                    : (c < 2 * DK ? p.Hk * DK + hk * DK + (c - DK)
+                                  : 2 * p.Hk * DK + hv * DV + (c - 2 * DK));
+    };
+    // Gates (clamped, unconditional loads).
+    const int tq = lane < T ? lane : 0;
+    const size_t gi = (lb * T + tq) * p.Hv + hv;
+    const float ga_ld = ld_in(static_cast<const TIn*>(p.a), gi);
+    const float gb_ld = ld_in(static_cast<const TIn*>(p.b), gi);
+
+    auto load_pair = [&](int j, typename PR::raw* xr, float* w0, float* w1) {
+      const int pr = lane + 64 * j;
+      const int c0 = 2 * (pr < NPAIR ? pr : NPAIR - 1);
+      const int ch = chan(c0);
+#pragma unroll
+      for (int r = 0; r < XR; ++r) {
+        const int rr = r < nrows ? r : nrows - 1;
+        const TIn* base = rr < K - 1 ? ccol + static_cast<size_t>(rr) * p.C
+                                     : xcol + static_cast<size_t>(rr - (K - 1)) * p.C;
+        xr[r] = PR::load(base + ch);
+      }
+      if (KC == 4) {
+        const floatx4 a0 = *reinterpret_cast<const floatx4*>(cw + static_cast<size_t>(ch) * 4);
+        const floatx4 a1 = *reinterpret_cast<const floatx4*>(cw + static_cast<size_t>(ch) * 4 + 4);
+#pragma unroll
+        for (int jj = 0; jj < KM; ++jj) {
+          w0[jj] = a0[jj % 4];
+          w1[jj] = a1[jj % 4];
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < KM; ++jj) {
+          const int q = jj < K ? jj : 0;
+          const float v0 = cw[static_cast<size_t>(ch) * K + q];
+          const float v1 = cw[static_cast<size_t>(ch + 1) * K + q];
+          w0[jj] = jj < K ? v0 : 0.f;
+          w1[jj] = jj < K ? v1 : 0.f;
+        }
+      }
+    };
+    // conv + SiLU of one channel pair over the chunk; results to LDS.
+    auto conv_pair = [&](int j, const typename PR::raw* xr, const float* w0, const float* w1) {
+      const int pr = lane + 64 * j;
+      if (pr >= NPAIR) return;
+      const int c0 = 2 * pr;
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < KM; ++jj) {
+          if (t + jj < XR) {
+            y0 = fmaf(w0[jj], PR::lo(xr[t + jj]), y0);
+            y1 = fmaf(w1[jj], PR::hi(xr[t + jj]), y1);
+          }
+        }
+        if (p.silu) {
+          y0 = silu_f(y0);
+          y1 = silu_f(y1);
+        }
+        if (t >= T) y0 = y1 = 0.f;
+        if (c0 < 2 * DK) {
+          const int isq = c0 < DK;
+          const int c = isq ? c0 : c0 - DK;
+          const int n = isq ? TMAX + t : t;
+          // element c -> 32-column step s, half h, lane group kg, slot e
+          const int s = c / 32, h = (c % 32) / 16, kg = (c % 16) / 4, e = c % 4;
+          unsigned char* row = s_kq + n * KQS + s * 128 + kg * 32 + (h * 4 + e) * 2;
+          uint32_t hi, lo;
+          split_pair(y0, y1, hi, lo);
+          *reinterpret_cast<uint32_t*>(row) = hi;
+          *reinterpret_cast<uint32_t*>(row + 16) = lo;
+          if (!isq) *reinterpret_cast<floatx2*>(s_kf + t * DK + c) = floatx2{y0, y1};
+        } else {
+          const int i = c0 - 2 * DK;
+          s_rhs[i * RT_LD + t] = y0;
+          s_rhs[(i + 1) * RT_LD + t] = y1;
+        }
+      }
+    };
+
+    if constexpr (LY::LOAD_ALL) {
+      typename PR::raw xr[PPL][XR];
+      float w0[PPL][KM], w1[PPL][KM];
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) load_pair(j, xr[j], w0[j], w1[j]);
+      __syncthreads();  // (B0) every small load is queued ahead of the state
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) conv_pair(j, xr[j], w0[j], w1[j]);
+    } else {
+      __syncthreads();  // (B0)
+#pragma unroll 1
+      for (int j = 0; j < PPL; ++j) {
+        typename PR::raw xr[XR];
+        float w0[KM], w1[KM];
+        load_pair(j, xr, w0, w1);
+        conv_pair(j, xr, w0, w1);
+      }
+    }
+    if (lane < TMAX) {
+      s_ga[lane] = lane < T ? ga_ld : 1.f;
+      s_gb[lane] = lane < T ? gb_ld : 0.f;
+      if (lane < T) p.tg[(lb * T + lane) * p.Hv + hv] = ga_ld;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // Gram G' = [K;Q][K;Q]^T of the raw rows on bf16x3 MFMA (lower tiles).
+#pragma unroll
+    for (int rb = 0; rb < NCB; ++rb) {
+#pragma unroll
+      for (int cb = 0; cb <= rb; ++cb) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        const unsigned char* ar = s_kq + (rb * 16 + c16) * KQS + kk * 32;
+        const unsigned char* br = s_kq + (cb * 16 + c16) * KQS + kk * 32;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(ar + s * 128);
+          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(ar + s * 128 + 16);
+          const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(br + s * 128);
+          const bf16x8 blo = *reinterpret_cast<const bf16x8*>(br + s * 128 + 16);
+          acc = mfma_bf16x3(ahi, alo, bhi, blo, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_G[(rb * 16 + 4 * kk + r) * GLD + cb * 16 + c16] = acc[r];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < NKQ) {
+      const float d = s_G[lane * GLD + lane];
+      s_rn[lane] = (lane % TMAX) < T ? 1.f / sqrtf(d + p.eps) : 0.f;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // T x T coefficients, one (t, i) pair per lane (TMAX^2 = 64).
+    float ga[TMAX];
+#pragma unroll
+    for (int s = 0; s < TMAX; ++s) ga[s] = s_ga[s];
+    {
+      const int t = lane / TMAX, i = lane % TMAX;
+      float gm = 1.f;  // Gamma[t,i] = a_{i+1} ... a_t
+#pragma unroll
+      for (int s = 0; s < TMAX; ++s) gm *= (s > i && s <= t) ? ga[s] : 1.f;
+      const float rki = s_rn[i];
+      const float av = s_gb[t] * gm * s_G[t * GLD + i] * s_rn[t] * rki;
+      const float ov = gm * s_G[(TMAX + t) * GLD + i] * s_rn[TMAX + t] * rki;
+      s_A[t * ALD + i] = (t < T && i < t) ? av : 0.f;
+      s_Oc[t * ALD + i] = (t < T && i <= t) ? ov : 0.f;
+    }
+    if (lane < TMAX) {
+      float gm = 1.f;  // gamma_t = a_0 ... a_t
+#pragma unroll
+      for (int s = 0; s < TMAX; ++s) gm *= s <= lane ? ga[s] : 1.f;
+      const bool live = lane < T;
+      s_ck[lane] = live ? s_gb[lane] * gm * s_rn[lane] : 0.f;
+      s_cq[lane] = live ? gm * s_rn[TMAX + lane] : 0.f;
+      s_cb[lane] = live ? s_gb[lane] : 0.f;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // Ti = (I + A)^-1 and M2 = Oc Ti, column j per lane, in registers.
+    if (lane < TMAX) {
+      const int j = lane;
+      float xc[TMAX];
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        float v = (t == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int a = 0; a < t; ++a) v = fmaf(-s_A[t * ALD + a], xc[a], v);
+        xc[t] = (t < T && j < T) ? v : 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        float m = 0.f;
+#pragma unroll
+        for (int a = 0; a <= t; ++a) m = fmaf(s_Oc[t * ALD + a], xc[a], m);
+        s_B[t * BLD + j] = xc[t];
+        s_B[(TMAX + t) * BLD + j] = m;
+      }
+    }
+  } else {
+    __syncthreads();  // (B0)
+    load_state();
+  }
+  __syncthreads();  // (B1) prologue results in LDS
+  if (wave == 0) {
+    load_state();
+    // Tape k: the normalised k rows, once per k-head.
+    if (g == 0) {
+      constexpr int C4 = DK / 4;
+      for (int e = lane; e < T * C4; e += 64) {
+        const int t = e / C4, c4 = e % C4;
+        const floatx4 v = *reinterpret_cast<const floatx4*>(s_kf + t * DK + 4 * c4) * s_rn[t];
+        __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(p.tk + ((lb * T + t) * p.Hk + hk) * DK) + c4);
+      }
+    }
+  }
+
+  // this lane's node in each column block: k rows then q rows
+  float cnode[NCB], cbv[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int n = cb * 16 + c16;
+    const int t = n < TMAX ? n : n - TMAX;
+    cnode[cb] = n < TMAX ? s_ck[t] : s_cq[t];
+    cbv[cb] = s_cb[t];
+  }
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tile = wave + tt * NW;
+    // S0 [K;Q]^T: A = this 16-row tile (registers), B = raw k/q rows.
+    floatx4 acc1[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc1[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      bf16x8 ahi, alo;
+      split_bf16x8(sreg[tt][2 * s], sreg[tt][2 * s + 1], ahi, alo);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const unsigned char* br = s_kq + (cb * 16 + c16) * KQS + kk * 32 + s * 128;
+        const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(br);
+        const bf16x8 blo = *reinterpret_cast<const bf16x8*>(br + 16);
+        acc1[cb] = mfma_bf16x3(ahi, alo, bhi, blo, acc1[cb]);
+      }
+    }
+    // RHS_t[i] = b_t v_t[i] - (b_t gamma_t r_t) (S0 k_t)[i], in place of v.
+    // Only this wave touches its tile's rows, and a wave's LDS accesses
+    // execute in order, so no workgroup barrier is needed around it.
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int n = cb * 16 + c16;
+      if (n < TMAX) {
+        float* col = s_rhs + (tile * 16 + 4 * kk) * RT_LD + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          col[r * RT_LD] = cbv[cb] * col[r * RT_LD] - cnode[cb] * acc1[cb][r];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // RHS^T [Ti; M2]^T on fp32 MFMA: k columns get u, q columns M2 RHS.
+    floatx4 acc2[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc2[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < TMAX / 4; ++st) {
+      const float a_op = s_rhs[(tile * 16 + c16) * RT_LD + 4 * st + kk];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const float b_op = s_B[(cb * 16 + c16) * BLD + 4 * st + kk];
+        acc2[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_op, b_op, acc2[cb], 0, 0, 0);
+      }
+    }
+    const int i0 = tile * 16 + 4 * kk;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int n = cb * 16 + c16;
+      const bool isk = n < TMAX;
+      const int t = isk ? n : n - TMAX;
+      if (t < T) {
+        const size_t oi = ((lb * T + t) * p.Hv + hv) * DV + i0;
+        floatx4 val = acc2[cb];
+        if (!isk) val += cnode[cb] * acc1[cb];
+        __builtin_nontemporal_store(val, reinterpret_cast<floatx4*>((isk ? p.tu : p.o) + oi));
+      }
+    }
+  }
+}
+
+template <int DK, int DV, typename TIn>
+hipError_t launch_c(const VerifyArgs& a, hipStream_t s) {
+  const int G = a.Hv / a.Hk;
+  const int n_units = a.L * a.B * a.Hk;
+  const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
+  if (grid > 0x7fffffffLL || a.T > 8) return hipErrorInvalidValue;
+  if (a.K == 4) {
+    constexpr int NT = ChainLayout<DK, DV, 8, 4, TIn>::NT;
+    hipLaunchKernelGGL((k_verify_chain<DK, DV, 8, 4, TIn>), dim3(static_cast<int>(grid)),
+                       dim3(NT), 0, s, a);
+  } else {
+    constexpr int NT = ChainLayout<DK, DV, 8, 8, TIn>::NT;
+    hipLaunchKernelGGL((k_verify_chain<DK, DV, 8, 0, TIn>), dim3(static_cast<int>(grid)),
+                       dim3(NT), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_cd(const VerifyArgs& a, int dk, int dv, hipStream_t s) {
+  if (dk != dv) return hipErrorInvalidValue;
+  switch (dk) {
+    case 32: return launch_c<32, 32, TIn>(a, s);
+    case 64: return launch_c<64, 64, TIn>(a, s);
+    case 128: return launch_c<128, 128, TIn>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s) {
+  return dtype == 1 ? launch_cd<uint16_t>(a, dk, dv, s) : launch_cd<float>(a, dk, dv, s);
+}
+
+}  // namespace gdn

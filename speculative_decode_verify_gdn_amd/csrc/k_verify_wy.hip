@@ -27,8 +27,6 @@
 // The per-head prologue (conv, L2 norm, Gram on MFMA, the T x T algebra)
 // runs while the state loads are in flight.
 
-#include <stdlib.h>
-
 #include "gdn_common.hpp"
 #include "gdn_kernels.hpp"
 
@@ -395,8 +393,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
   if (g == 0 && rblk == 0) {
     for (int e = tid; e < T * (DK / 4); e += kNT) {
       const int t = e / (DK / 4), c4 = e % (DK / 4);
-      reinterpret_cast<floatx4*>(p.tk + ((lb * T + t) * p.Hk + hk) * DK)[c4] =
-          reinterpret_cast<const floatx4*>(s_kq + t * KQ_LD)[c4];
+      __builtin_nontemporal_store(reinterpret_cast<const floatx4*>(s_kq + t * KQ_LD)[c4],
+                                  reinterpret_cast<floatx4*>(p.tk + ((lb * T + t) * p.Hk + hk) * DK) + c4);
     }
   }
 
@@ -726,7 +724,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<TMAX>()))) void k_verify_wy(Veri
           const size_t oi = ((lb * T + t) * p.Hv + hv) * DV + i0;
           floatx4 val = acc2[tt][cb];
           if (!isk) val += gam_c[cb] * acc1[tt][cb];
-          *reinterpret_cast<floatx4*>((isk ? p.tu : p.o) + oi) = val;
+          __builtin_nontemporal_store(val, reinterpret_cast<floatx4*>((isk ? p.tu : p.o) + oi));
         }
       }
     }
@@ -779,13 +777,7 @@ hipError_t launch_d(const VerifyArgs& a, int dk, int dv, hipStream_t s) {
   switch (dk) {
     case 32: return launch_t<32, 32, 32, TIn>(a, s);
     case 64: return launch_t<64, 64, 64, TIn>(a, s);
-    case 128: {
-      static const int rows = [] {
-        const char* e = getenv("GDN_VERIFY_ROWS");
-        return e ? atoi(e) : 128;
-      }();
-      return rows == 64 ? launch_t<128, 128, 64, TIn>(a, s) : launch_t<128, 128, 128, TIn>(a, s);
-    }
+    case 128: return launch_t<128, 128, 128, TIn>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
