@@ -30,7 +30,8 @@ COMMON = [
     "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
 ]
 
-SOURCES = ["gdn_api.cpp", "k_verify_wy.hip", "k_verify_chain.hip", "k_rollback.hip",
+SOURCES = ["gdn_api.cpp", "k_verify_wy.hip", "k_verify_chain.hip", "k_verify_tree.hip",
+           "k_rollback.hip",
            "k_accept.hip"]
 
 

@@ -113,8 +113,10 @@ gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* par
   v.parent = parent;
   v.conv_win = conv_win;
   v.dev_err = dev_err;
-  return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype,
-                                             static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128)
+    return launch_status(gdn::launch_verify_tree(v, s));
+  return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype, s));
 }
 
 size_t spec_accept_workspace_bytes(int32_t B, int32_t T, int32_t V) {

@@ -72,6 +72,8 @@ struct AcceptArgs {
 hipError_t launch_verify_wy(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
 // Chains of at most 8 tokens (wave-specialised kernel).
 hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
+// Trees of 33..64 nodes, 128-dim heads, bf16 inputs (per-node path solve).
+hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream_t s);
 hipError_t launch_conv_rollback(const ConvRollbackArgs& a, int dtype, hipStream_t s);
 hipError_t launch_accept(const AcceptArgs& a, int dtype, hipStream_t s);

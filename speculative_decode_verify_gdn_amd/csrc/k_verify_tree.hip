@@ -1,0 +1,604 @@
+// k_verify_tree.hip -- verify of a draft tree of 33..64 nodes through one GDN
+// layer (128-dim heads, bf16 inputs), for gfx950.
+//
+// Per node v with parent p (p = -1: the committed state S0), the gated delta
+// rule of the GDN page (s2.1) steps from the parent's state:
+//   S_v = a_v S_p + u_v k_v^T,  u_v = b_v (v_v - a_v S_p k_v),  o_v = S_v q_v,
+// which is how a draft tree is verified through the recurrent state in one
+// pass (GDN page s8, tree-aware verify).  Unrolled along the root path of each
+// node (path(t) = its ancestors and itself, in depth order p_0 .. p_{d-1} = t),
+// with Gamma[t,i] the product of a over the path strictly below i up to t:
+//   (I + A) U = RHS,  A[t,i] = b_t Gamma[t,i] k_t.k_i   (i a proper ancestor)
+//   RHS_t = b_t (v_t - gamma_t S0 k_t),  gamma_t = prod of a over path(t)
+//   o_t = gamma_t S0 q_t + sum_{i in path(t)} Oc[t,i] u_i,  Oc[t,i] = Gamma[t,i] q_t.k_i
+// With Ti = (I + A)^-1 and M2 = Oc Ti:  U = Ti RHS,  O = diag(gamma) Q S0^T + M2 RHS.
+// Ti and M2 are supported on ancestor-or-self pairs, and row t of Ti depends
+// only on the entries of A among the nodes of path(t): each node solves its
+// own row (backward substitution along its path), with no level-by-level
+// barriers.  A, Oc, Ti and M2 live in packed rows (row t holds one value per
+// node of path(t), slot = depth - 1), at most T(T+1)/2 values each.
+//
+// One workgroup of eight waves per (layer, seq, v-head); wave w owns rows
+// 16w .. 16w+15 of S0 (registers, MFMA A operand).  Phases:
+//   loads: parents, gates, the raw conv rows (staged in LDS), conv weights;
+//   wave 0: node depths, ancestor masks, conv windows, path products, packed
+//     row offsets (one lane per node, wave-level scan);
+//   conv + SiLU: one 16-lane group per (node, q/k/v segment), 8 channels per
+//     lane; q and k rows are L2-normalised with a 16-lane reduction, written
+//     as pre-split bf16 hi/lo MFMA operands, and k goes to the tape;
+//   Gram [K;Q] K^T on bf16x3 MFMA, keeping only ancestor-or-self entries;
+//   wave 0 solves the packed Ti and M2 rows while the other waves run
+//   S0 [K;Q]^T (bf16x3 MFMA) and form RHS in LDS;
+//   [Ti; M2] is expanded to a dense pre-split operand in the space of K/Q;
+//   RHS [Ti; M2]^T (bf16x3 MFMA); u and o are stored from registers.
+// S0 and the conv window are never written (they stay the snapshot).
+
+#include "gdn_common.hpp"
+#include "gdn_kernels.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int TR_D = 128;       // head dimension (Dk = Dv)
+constexpr int TR_T = 64;        // nodes per tree (padded)
+constexpr int TR_NT = 512;      // eight waves
+constexpr int TR_KQS = 528;     // bytes per pre-split [K;Q] row: 128 x (hi, lo) + 16 pad
+constexpr int TR_B2S = 272;     // bytes per pre-split [Ti;M2] row: 64 x (hi, lo) + 16 pad
+constexpr int TR_VLD = 68;      // floats per V / RHS row ([row of S][node])
+
+// Position of node t in V / RHS row i: 8-node groups are permuted by the row's
+// 8-row block, so the transposing writes of the conv spread over the banks
+// while each group of 8 nodes stays contiguous for float4 reads.
+__device__ __forceinline__ int vsw(int i) { return ((i >> 3) & 7) << 3; }
+constexpr int TR_PK = TR_T * (TR_T + 1) / 2;  // packed triangle capacity
+constexpr int TR_ROWB = 3 * TR_D * 2;         // raw staging bytes per row (q | k | v rows, bf16)
+
+__device__ __forceinline__ float silu_t(float y) {
+  return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
+}
+
+// Sum over aligned groups of 16 lanes (DPP; every lane gets its group's sum).
+__device__ __forceinline__ float sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// Pack four fp32 values as bf16 high parts and bf16 residuals (8 bytes each).
+__device__ __forceinline__ void split4(const float* y, uint2& hi, uint2& lo) {
+  uint32_t h[4], r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 bh = static_cast<__bf16>(y[e]);
+    const __bf16 bl = static_cast<__bf16>(y[e] - static_cast<float>(bh));
+    h[e] = __builtin_bit_cast(uint16_t, bh);
+    r[e] = __builtin_bit_cast(uint16_t, bl);
+  }
+  hi = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  lo = make_uint2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
+}
+
+template <int KM>
+struct TreeLds {
+  static constexpr int XR = TR_T + KM - 1;  // raw rows: old window, then nodes
+  static constexpr int STAGE = XR * TR_ROWB;
+  static constexpr int VBYTES = TR_D * TR_VLD * 4;
+  static constexpr int PKBYTES = 4 * TR_PK * 4;  // KK, QK, Ti, M2
+  static constexpr int R2 = STAGE > VBYTES + PKBYTES ? STAGE : VBYTES + PKBYTES;
+  static constexpr int R1 = 2 * TR_T * TR_KQS;
+};
+
+template <int KC>
+__global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
+  constexpr int KM = KC > 0 ? KC : 8;
+  using LY = TreeLds<KM>;
+  constexpr int XR = LY::XR;
+  static_assert(2 * TR_T * TR_B2S <= LY::R1, "[Ti;M2] operand fits in the K/Q space");
+  static_assert(LY::R1 + LY::R2 + 3 * TR_D * KM * 4 + TR_T * (48 + 4 * KM) <= 160 * 1024,
+                "LDS budget");
+
+  __shared__ __align__(16) unsigned char s_r1[LY::R1];  // pre-split [K;Q], later [Ti;M2]
+  __shared__ __align__(16) unsigned char s_r2[LY::R2];  // raw staging, later V/RHS + packed
+  __shared__ __align__(16) float s_w[3 * TR_D * KM];    // conv weights [channel][tap]
+  __shared__ unsigned long long s_anc[TR_T];            // proper-ancestor masks
+  __shared__ int s_par[TR_T], s_dep[TR_T], s_off[TR_T];
+  __shared__ __align__(16) int s_widx[TR_T * KM];       // conv window: staging byte offsets
+  __shared__ float s_ga[TR_T], s_gb[TR_T], s_gam[TR_T];
+  __shared__ int s_bad, s_maxd;
+
+  float* s_v = reinterpret_cast<float*>(s_r2);            // [row of S][node]
+  float* s_KK = s_v + TR_D * TR_VLD;                      // packed rows
+  float* s_QK = s_KK + TR_PK;
+  float* s_TI = s_QK + TR_PK;
+  float* s_M2 = s_TI + TR_PK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c16 = lane & 15;
+  const int kk = lane >> 4;
+
+  const int G = p.Hv / p.Hk;
+  const int n_units = p.L * p.B * p.Hk;
+  const UnitSub us = xcd_unit_sub(blockIdx.x, G);
+  if (us.unit >= n_units) return;
+  const int hk = us.unit % p.Hk;
+  const size_t lb = us.unit / p.Hk;  // l * B + b
+  const int bb = static_cast<int>(lb % p.B);
+  const int l = static_cast<int>(lb / p.B);
+  const int g = us.sub;
+  const int hv = hk * G + g;
+  const int T = p.T;
+  const int K = KC > 0 ? KC : p.K;
+  const uint16_t* x = static_cast<const uint16_t*>(p.x);
+  const uint16_t* cs = static_cast<const uint16_t*>(p.conv_state);
+
+  // ------------------------------------------------------------------ loads --
+  // Every load is unconditional from a clamped, valid address.
+  const int tq = lane < T ? lane : 0;
+  const int par_raw = p.parent[static_cast<size_t>(bb) * T + tq];
+  const size_t gi = (lb * T + tq) * p.Hv + hv;
+  const float ga_ld = ld_in(static_cast<const uint16_t*>(p.a), gi);
+  const float gb_ld = ld_in(static_cast<const uint16_t*>(p.b), gi);
+  // local channel c in [q | k | v-rows] -> qkv channel
+  auto chan = [&](int c) {
+    return c < TR_D ? hk * TR_D + c
+                    : (c < 2 * TR_D ? p.Hk * TR_D + hk * TR_D + (c - TR_D)
+                                    : 2 * p.Hk * TR_D + hv * TR_D + (c - 2 * TR_D));
+  };
+  constexpr int CPR = TR_ROWB / 16;                     // 16-byte chunks per raw row (48)
+  constexpr int NRAW = (XR * CPR + TR_NT - 1) / TR_NT;  // per thread
+  const int nrows = K - 1 + T;
+  const uint16_t* xcol = x + lb * T * p.C;
+  const uint16_t* ccol = cs + lb * (K - 1) * p.C;
+  u32x4 raw[NRAW];
+#pragma unroll
+  for (int q = 0; q < NRAW; ++q) {
+    const int e = tid + q * TR_NT;
+    const int row = e / CPR, chunk = e % CPR;
+    const int rr = row < nrows ? row : nrows - 1;
+    const uint16_t* base = rr < K - 1 ? ccol + static_cast<size_t>(rr) * p.C
+                                      : xcol + static_cast<size_t>(rr - (K - 1)) * p.C;
+    raw[q] = *reinterpret_cast<const u32x4*>(base + chan(chunk * 8));
+  }
+  // conv weights of the 384 channels, zero beyond the kernel width
+  const float* cw = p.conv_w + static_cast<size_t>(l) * p.C * K;
+  constexpr int NWL = (3 * TR_D * KM + TR_NT - 1) / TR_NT;
+  float wv[NWL];
+#pragma unroll
+  for (int q = 0; q < NWL; ++q) {
+    const int e = tid + q * TR_NT;
+    const int c = e / KM, j = e % KM;
+    const bool ok = e < 3 * TR_D * KM && j < K;
+    const float v = cw[static_cast<size_t>(chan(ok ? c : 0)) * K + (ok ? j : 0)];
+    wv[q] = ok ? v : 0.f;
+  }
+
+  // --------------------------------------------- node structure (wave 0) --
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (wave == 0) {
+    const int t = lane;
+    int pv = -1;
+    if (t < T) {
+      pv = par_raw;
+      if (pv < -1 || pv >= t) {
+        s_bad = 1;
+        pv = -1;
+      }
+      s_ga[t] = ga_ld;
+      s_gb[t] = gb_ld;
+      p.tg[(lb * T + t) * p.Hv + hv] = ga_ld;
+    } else {
+      s_ga[t] = 1.f;
+      s_gb[t] = 0.f;
+    }
+    s_par[t] = pv;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ancestors, depth, path product of a, conv window (node, then upward)
+    unsigned long long m = 0ull;
+    int d = 0;
+    float gm = 1.f;
+    if (t < T) {
+      gm = s_ga[t];
+      d = 1;
+      for (int c = s_par[t]; c >= 0; c = s_par[c]) {
+        m |= 1ull << c;
+        gm *= s_ga[c];
+        ++d;
+      }
+    }
+    s_anc[t] = m;
+    s_dep[t] = d;
+    s_gam[t] = gm;
+    {
+      int cur = t < T ? t : -1, old = 0;
+#pragma unroll
+      for (int j = KM - 1; j >= 0; --j) {
+        int w = 0;
+        if (j < K) {
+          if (cur >= 0) {
+            w = cur;
+            cur = s_par[cur];
+          } else {
+            w = --old;
+          }
+        }
+        s_widx[t * KM + j] = (w + K - 1) * TR_ROWB;
+      }
+    }
+    // packed row offsets: exclusive prefix sum of depths over nodes
+    int incl = d;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    s_off[t] = incl - d;
+    int md = d;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) md = max(md, __shfl_xor(md, o, 64));
+    if (lane == 0) s_maxd = md;
+  }
+  // raw rows and weights into LDS
+  u32x4* s_stage = reinterpret_cast<u32x4*>(s_r2);
+#pragma unroll
+  for (int q = 0; q < NRAW; ++q) {
+    const int e = tid + q * TR_NT;
+    if (e < XR * CPR) s_stage[e] = raw[q];
+  }
+#pragma unroll
+  for (int q = 0; q < NWL; ++q) {
+    const int e = tid + q * TR_NT;
+    if (e < 3 * TR_D * KM) s_w[e] = wv[q];
+  }
+  __syncthreads();  // (B_a) staging, weights, node structure
+  if (s_bad) {
+    if (tid == 0 && p.dev_err) atomicOr(p.dev_err, GDN_DEV_ERR_PARENT);
+    return;
+  }
+  if (p.conv_win && l == 0 && hk == 0 && g == 0) {
+    for (int e = tid; e < T * K; e += TR_NT)
+      p.conv_win[static_cast<size_t>(bb) * T * K + e] = s_widx[(e / K) * KM + (e % K)] / TR_ROWB - (K - 1);
+  }
+
+  // The state tile of this wave: lane (c16, kk) holds row 16w + c16, columns
+  // 16m + 4kk .. +3.  Issued after the raw rows are in LDS (queued earlier
+  // it holds up the staging), used after the conv and the Gram.
+  floatx4 sreg[TR_D / 16];
+  {
+    const float* rp = p.S + (lb * p.Hv + hv) * static_cast<size_t>(TR_D * TR_D) +
+                      static_cast<size_t>(wave * 16 + c16) * TR_D + 4 * kk;
+#pragma unroll
+    for (int m = 0; m < TR_D / 16; ++m) sreg[m] = *reinterpret_cast<const floatx4*>(rp + 16 * m);
+  }
+
+  // ---------------------------------------------------------- conv + SiLU --
+  // 16-lane group gr handles (segment, node) items gr + 32 r; lane li holds
+  // channels 8 li .. 8 li + 7 of the segment.
+  const int gr = tid >> 4, li = tid & 15;
+  float vout[2][8];
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int item = gr + 32 * r;
+    const int sg = item / TR_T;  // 0 q, 1 k, 2 v (uniform per round)
+    const int t = item % TR_T;
+    const int4 wa = *reinterpret_cast<const int4*>(s_widx + t * KM);
+    int wi[KM];
+    wi[0] = wa.x;
+    if (KM > 1) wi[1 % KM] = wa.y;
+    if (KM > 2) wi[2 % KM] = wa.z;
+    if (KM > 3) wi[3 % KM] = wa.w;
+    if constexpr (KM > 4) {
+      const int4 wb = *reinterpret_cast<const int4*>(s_widx + t * KM + 4);
+      wi[4 % KM] = wb.x;
+      wi[5 % KM] = wb.y;
+      wi[6 % KM] = wb.z;
+      wi[7 % KM] = wb.w;
+    }
+    u32x4 xv[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      xv[j] = *reinterpret_cast<const u32x4*>(s_r2 + wi[j] + sg * 256 + li * 16);
+    float y[8];
+    const float* wrow = s_w + (sg * TR_D + 8 * li) * KM;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const uint32_t wd = xv[j][e / 2];
+        const float xe = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+        acc = fmaf(wrow[e * KM + j], xe, acc);
+      }
+      if (p.silu) acc = silu_t(acc);
+      y[e] = t < T ? acc : 0.f;
+    }
+    if (sg < 2) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+      ss = sum16(ss);
+      const float rn = t < T ? __builtin_amdgcn_rsqf(ss + p.eps) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= rn;
+      if (sg == 1 && g == 0 && t < T) {
+        floatx4* dst = reinterpret_cast<floatx4*>(p.tk + ((lb * T + t) * p.Hk + hk) * TR_D + 8 * li);
+        __builtin_nontemporal_store(floatx4{y[0], y[1], y[2], y[3]}, dst);
+        __builtin_nontemporal_store(floatx4{y[4], y[5], y[6], y[7]}, dst + 1);
+      }
+      // pre-split operand row n: element c = 8 li + e sits at 32-column step
+      // c / 32, half (c % 32) / 16, lane group (c % 16) / 4, slot c % 4.
+      const int n = sg == 0 ? TR_T + t : t;
+      const int s = li / 4, h = (li % 4) / 2, kg = 2 * (li % 2);
+      unsigned char* row = s_r1 + n * TR_KQS + s * 128 + h * 8;
+      uint2 hi, lo;
+      split4(y, hi, lo);
+      *reinterpret_cast<uint2*>(row + kg * 32) = hi;
+      *reinterpret_cast<uint2*>(row + kg * 32 + 16) = lo;
+      split4(y + 4, hi, lo);
+      *reinterpret_cast<uint2*>(row + (kg + 1) * 32) = hi;
+      *reinterpret_cast<uint2*>(row + (kg + 1) * 32 + 16) = lo;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vout[r - 4][e] = y[e];
+    }
+  }
+  __syncthreads();  // (B_b) staging consumed
+  // V rows into [row of S][node] (over the staging space)
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int t = (gr + 32 * (4 + r)) % TR_T;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_v[(8 * li + e) * TR_VLD + (t ^ vsw(8 * li))] = vout[r][e];
+  }
+
+  // -------------------------- Gram [K;Q] K^T, ancestor-or-self entries only --
+  {
+    const int rb = wave;           // 16-row block of [K;Q]
+    const bool isq = rb >= 4;
+    const int nb = rb % 4;         // node block of the rows
+    const unsigned char* ar = s_r1 + (rb * 16 + c16) * TR_KQS + kk * 32;
+    bf16x8 ahi[4], alo[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      ahi[s] = *reinterpret_cast<const bf16x8*>(ar + s * 128);
+      alo[s] = *reinterpret_cast<const bf16x8*>(ar + s * 128 + 16);
+    }
+    unsigned long long rm[4];
+    int ro[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = nb * 16 + 4 * kk + r;
+      // padding rows (depth 0) take no entries
+      rm[r] = tr < T ? (s_anc[tr] | (isq ? (1ull << tr) : 0ull)) : 0ull;
+      ro[r] = s_off[tr];
+    }
+    float* dst = isq ? s_QK : s_KK;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      if (cb > nb) break;  // columns are ancestors: never above the row block
+      const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_KQS + kk * 32;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(br + s * 128);
+        const bf16x8 blo = *reinterpret_cast<const bf16x8*>(br + s * 128 + 16);
+        acc = mfma_bf16x3(ahi[s], alo[s], bhi, blo, acc);
+      }
+      const int tc = cb * 16 + c16;
+      const int slot = s_dep[tc] - 1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if ((rm[r] >> tc) & 1ull) dst[ro[r] + slot] = acc[r];
+    }
+  }
+  __syncthreads();  // (B_c) packed Gram rows, V rows
+
+  // --------------- wave 0: packed Ti and M2 rows; waves 1..7: S0 [K;Q]^T --
+  auto solve_rows = [&]() {
+    const int t = lane;
+    if (t >= T) return;
+    const int d = s_dep[t];
+    const int off = s_off[t];
+    const unsigned long long mask = s_anc[t] | (1ull << t);
+    if (s_maxd <= 8) {
+      // Registers: path nodes, gates and the strictly-lower path entries of A.
+      int pn[8], po[8];
+      float pa[8], pb[8];
+      unsigned long long mm = mask;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int v = mm ? __builtin_ctzll(mm) : 0;
+        mm &= mm - 1ull;
+        pn[m] = v;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        pa[m] = s_ga[pn[m]];
+        pb[m] = s_gb[pn[m]];
+        po[m] = s_off[pn[m]];
+      }
+      float kv[8][8];
+#pragma unroll
+      for (int j = 1; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < j; ++i) kv[j][i] = (j < d) ? s_KK[po[j] + i] : 0.f;
+      // Row t of Ti: x_{d-1} = 1, x_i = -sum_{j>i} x_j b_j Gamma(j,i) kk(j,i)
+      float xs[8];
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        float acc = 0.f, gmm = 1.f;
+#pragma unroll
+        for (int j = i + 1; j < 8; ++j) {
+          gmm *= pa[j];
+          acc = fmaf(xs[j] * pb[j] * gmm, kv[j][i], acc);
+        }
+        xs[i] = (i == d - 1) ? 1.f : (i < d - 1 ? -acc : 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < d) s_TI[off + i] = xs[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Row t of M2: sum_{j>=i} Gamma(d-1,j) qk(t,p_j) Ti[p_j][p_i]
+      float oc[8];
+      {
+        float gmm = 1.f;
+#pragma unroll
+        for (int j = 7; j >= 0; --j) {
+          oc[j] = (j < d) ? gmm * s_QK[off + j] : 0.f;
+          if (j < d) gmm *= pa[j];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = i; j < 8; ++j) {
+          const float tv = (j < d) ? s_TI[po[j] + i] : 0.f;
+          acc = fmaf(oc[j], tv, acc);
+        }
+        if (i < d) s_M2[off + i] = acc;
+      }
+    } else {
+      // Any depth: the same recurrences with the path walked from the mask.
+      s_TI[off + d - 1] = 1.f;
+      for (int i = d - 2; i >= 0; --i) {
+        unsigned long long mm = mask;
+        for (int c = 0; c <= i; ++c) mm &= mm - 1ull;  // drop p_0 .. p_i
+        float acc = 0.f, gmm = 1.f;
+        for (int j = i + 1; j < d; ++j) {
+          const int v = __builtin_ctzll(mm);
+          mm &= mm - 1ull;
+          gmm *= s_ga[v];
+          acc = fmaf(s_TI[off + j] * s_gb[v] * gmm, s_KK[s_off[v] + i], acc);
+        }
+        s_TI[off + i] = -acc;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int i = 0; i < d; ++i) {
+        unsigned long long mm = mask;
+        float acc = 0.f, gmm = 1.f;
+        for (int j = d - 1; j >= i; --j) {
+          const int v = 63 - __builtin_clzll(mm);
+          mm ^= 1ull << v;
+          acc = fmaf(gmm * s_QK[off + j], s_TI[s_off[v] + i], acc);
+          gmm *= s_ga[v];
+        }
+        s_M2[off + i] = acc;
+      }
+    }
+  };
+  if (wave == 0) {
+    solve_rows();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // S0 [K;Q]^T: A = this wave's tile, B = pre-split k rows then q rows.
+  floatx4 acc1[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) acc1[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bf16x8 ahi, alo;
+    split_bf16x8(sreg[2 * s], sreg[2 * s + 1], ahi, alo);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_KQS + kk * 32 + s * 128;
+      const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(br);
+      const bf16x8 blo = *reinterpret_cast<const bf16x8*>(br + 16);
+      acc1[cb] = mfma_bf16x3(ahi, alo, bhi, blo, acc1[cb]);
+    }
+  }
+  // RHS_t[i] = b_t (v_t[i] - gamma_t (S0 k_t)[i]) in place of v (own rows).
+  float gam_c[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) gam_c[cb] = s_gam[(cb * 16 + c16) % TR_T];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int t = cb * 16 + c16;
+    const float bt = s_gb[t];
+    float* col = s_v + (wave * 16 + 4 * kk) * TR_VLD + (t ^ vsw(wave * 16 + 4 * kk));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) col[r * TR_VLD] = bt * (col[r * TR_VLD] - gam_c[cb] * acc1[cb][r]);
+  }
+  __syncthreads();  // (B_d) packed Ti, M2; RHS; K/Q space free
+
+  // ----------------------- dense pre-split [Ti; M2] in the K/Q space --
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = tid + q * TR_NT;  // (row n, step st, lane group kg)
+    const int n = e / 8, st = (e / 4) % 2, kg = e % 4;
+    const int nn = n % TR_T;
+    const bool m2 = n >= TR_T;
+    const unsigned long long mask = nn < T ? (s_anc[nn] | (1ull << nn)) : 0ull;
+    const int off = s_off[nn];
+    const float* src = m2 ? s_M2 : s_TI;
+    float vv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int sidx = 32 * st + 8 * kg + i;
+      const bool on = (mask >> sidx) & 1ull;
+      const float val = src[on ? off + s_dep[sidx] - 1 : 0];
+      vv[i] = on ? val : 0.f;
+    }
+    uint2 h0, l0, h1, l1;
+    split4(vv, h0, l0);
+    split4(vv + 4, h1, l1);
+    unsigned char* dst = s_r1 + n * TR_B2S + (st * 4 + kg) * 32;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(l0.x, l0.y, l1.x, l1.y);
+  }
+  __syncthreads();  // (B_e)
+
+  // ------------------------------- RHS^T [Ti; M2]^T, outputs from registers --
+  floatx4 acc2[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) acc2[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const float* ar = s_v + (wave * 16 + c16) * TR_VLD + ((32 * st + 8 * kk) ^ vsw(wave * 16 + c16));
+    bf16x8 ahi, alo;
+    split_bf16x8(*reinterpret_cast<const floatx4*>(ar), *reinterpret_cast<const floatx4*>(ar + 4), ahi, alo);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_B2S + (st * 4 + kk) * 32;
+      const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(br);
+      const bf16x8 blo = *reinterpret_cast<const bf16x8*>(br + 16);
+      acc2[cb] = mfma_bf16x3(ahi, alo, bhi, blo, acc2[cb]);
+    }
+  }
+  const int i0 = wave * 16 + 4 * kk;
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const int t = (cb * 16 + c16) % TR_T;
+    if (t < T) {
+      const size_t oi = ((lb * T + t) * p.Hv + hv) * TR_D + i0;
+      floatx4 val = acc2[cb];
+      if (cb >= 4) val += gam_c[cb] * acc1[cb];
+      __builtin_nontemporal_store(val, reinterpret_cast<floatx4*>((cb < 4 ? p.tu : p.o) + oi));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s) {
+  const int G = a.Hv / a.Hk;
+  const int n_units = a.L * a.B * a.Hk;
+  const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
+  if (grid > 0x7fffffffLL || a.T > TR_T || a.T <= 32) return hipErrorInvalidValue;
+  if (a.K == 4)
+    hipLaunchKernelGGL((k_verify_tree<4>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_verify_tree<0>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdn
