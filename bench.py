@@ -38,22 +38,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 def measured_traffic(workload: str):
     """HBM bytes per verify launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs (calibrated on a plain copy), or None when the verify
-    kernel's sources changed since the counters were taken."""
+    WRITE_SIZE runs (calibrated on a plain copy), or None when the sources of
+    the kernel that serves this workload changed since the counters were
+    taken (each workload records the files it hashed)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "verify_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    w = rec.get("workloads", {}).get(workload)
+    if w is None:
+        return None
     h = hashlib.sha256()
-    for src in rec.get("sources", []):
+    for src in w.get("sources", []):
         with open(os.path.join(ROOT, src), "rb") as g:
             h.update(g.read())
-    if h.hexdigest() != rec.get("source_sha256"):
+    if not w.get("sources") or h.hexdigest() != w.get("source_sha256"):
         return None
-    w = rec.get("workloads", {}).get(workload)
-    return None if w is None else w["traffic_bytes"]
+    return w["traffic_bytes"]
 
 
 def rollback_sweep(cfg, rb, stream, reps=10):
@@ -129,6 +132,8 @@ def verify_kernel_name(cfg) -> str:
     """The verify kernel the library dispatches for this workload (one layer)."""
     if not cfg.is_tree and cfg.T <= 8:
         return "k_verify_chain (gdn_verify_chunk, chains of <= 8 tokens, one layer)"
+    if cfg.is_tree and cfg.T > 32 and cfg.dtype == torch.bfloat16 and cfg.Dk == cfg.Dv == 128:
+        return "k_verify_tree (gdn_tree_verify, trees of 33..64 nodes, one layer)"
     return "k_verify_wy (%s, one layer)" % ("gdn_tree_verify" if cfg.is_tree else "gdn_verify_chunk")
 
 

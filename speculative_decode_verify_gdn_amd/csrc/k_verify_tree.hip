@@ -266,15 +266,12 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   }
 
   // The state tile of this wave: lane (c16, kk) holds row 16w + c16, columns
-  // 16m + 4kk .. +3.  Issued after the raw rows are in LDS (queued earlier
-  // it holds up the staging), used after the conv and the Gram.
+  // 16m + 4kk .. +3, used after the conv and the Gram.  Its loads go out two
+  // per conv round: issued as one burst they would stall the wave until the
+  // memory pipeline had accepted them all.
   floatx4 sreg[TR_D / 16];
-  {
-    const float* rp = p.S + (lb * p.Hv + hv) * static_cast<size_t>(TR_D * TR_D) +
+  const float* srow = p.S + (lb * p.Hv + hv) * static_cast<size_t>(TR_D * TR_D) +
                       static_cast<size_t>(wave * 16 + c16) * TR_D + 4 * kk;
-#pragma unroll
-    for (int m = 0; m < TR_D / 16; ++m) sreg[m] = *reinterpret_cast<const floatx4*>(rp + 16 * m);
-  }
 
   // ---------------------------------------------------------- conv + SiLU --
   // 16-lane group gr handles (segment, node) items gr + 32 r; lane li holds
@@ -283,6 +280,10 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   float vout[2][8];
 #pragma unroll
   for (int r = 0; r < 6; ++r) {
+    if (r < TR_D / 32) {
+      sreg[2 * r] = *reinterpret_cast<const floatx4*>(srow + 32 * r);
+      sreg[2 * r + 1] = *reinterpret_cast<const floatx4*>(srow + 32 * r + 16);
+    }
     const int item = gr + 32 * r;
     const int sg = item / TR_T;  // 0 q, 1 k, 2 v (uniform per round)
     const int t = item % TR_T;
@@ -582,7 +583,9 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
       const size_t oi = ((lb * T + t) * p.Hv + hv) * TR_D + i0;
       floatx4 val = acc2[cb];
       if (cb >= 4) val += gam_c[cb] * acc1[cb];
-      __builtin_nontemporal_store(val, reinterpret_cast<floatx4*>((cb < 4 ? p.tu : p.o) + oi));
+      // regular stores: the other 64 bytes of each 128-byte line come from
+      // the neighbouring wave and are merged in L2 before the line is written
+      *reinterpret_cast<floatx4*>((cb < 4 ? p.tu : p.o) + oi) = val;
     }
   }
 }
