@@ -130,8 +130,8 @@ def verify_bytes_per_launch(cfg, B) -> int:
 
 def verify_kernel_name(cfg) -> str:
     """The verify kernel the library dispatches for this workload (one layer)."""
-    if not cfg.is_tree and cfg.T <= 8:
-        return "k_verify_chain (gdn_verify_chunk, chains of <= 8 tokens, one layer)"
+    if not cfg.is_tree and cfg.T <= 16:
+        return "k_verify_chain (gdn_verify_chunk, chains of <= 16 tokens, one layer)"
     if cfg.is_tree and cfg.T > 32 and cfg.dtype == torch.bfloat16 and cfg.Dk == cfg.Dv == 128:
         return "k_verify_tree (gdn_tree_verify, trees of 33..64 nodes, one layer)"
     return "k_verify_wy (%s, one layer)" % ("gdn_tree_verify" if cfg.is_tree else "gdn_verify_chunk")

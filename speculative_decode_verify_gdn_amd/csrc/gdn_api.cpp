@@ -96,7 +96,7 @@ gdn_status gdn_verify_chunk(const gdn_shape* shape, int32_t T, const void* x,
   if (!verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape)) return GDN_ERR_INVALID_ARG;
   VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (T <= 8) return launch_status(gdn::launch_verify_chain(v, shape->d_k, shape->d_v, shape->in_dtype, s));
+  if (T <= 16) return launch_status(gdn::launch_verify_chain(v, shape->d_k, shape->d_v, shape->in_dtype, s));
   return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype, s));
 }
 

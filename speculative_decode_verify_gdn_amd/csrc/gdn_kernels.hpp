@@ -70,7 +70,7 @@ struct AcceptArgs {
 // Each returns hipErrorInvalidValue for an uninstantiated combination, else
 // the launch status.  dtype: 0 fp32, 1 bf16.
 hipError_t launch_verify_wy(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
-// Chains of at most 8 tokens (wave-specialised kernel).
+// Chains of at most 16 tokens (wave-specialised kernel).
 hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
 // Trees of 33..64 nodes, 128-dim heads, bf16 inputs (per-node path solve).
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s);

@@ -1,4 +1,4 @@
-// k_verify_chain.hip -- verify of a short drafted chain (T <= 8 tokens)
+// k_verify_chain.hip -- verify of a short drafted chain (T <= 16 tokens)
 // through one GDN layer, for gfx950, with one wave specialised for the
 // per-head prologue and the others for the state.
 //
@@ -101,14 +101,16 @@ struct ChainLayout {
   static constexpr int KQS = 4 * DK + 16;       // bytes per pre-split row (+16: conflict-free b128)
   static constexpr int RT_LD = TMAX + 1;        // V / RHS, [row of S][node]
   static constexpr int GLD = NKQ + 1;           // Gram
-  static constexpr int ALD = TMAX + 1;          // A, Oc
+  static constexpr int ALD = NKQ + 1;           // A, Oc (in place of the Gram rows)
   static constexpr int BLD = TMAX + 1;          // [Ti; M2]
   static constexpr int NPAIR = (2 * DK + DV) / 2;
   static constexpr int PPL = (NPAIR + 63) / 64;  // channel pairs per prologue lane
   static constexpr int XR = TMAX + KM - 1;       // raw rows: old window + tokens
   static constexpr int RAW_WORDS = PPL * XR * (int)sizeof(TIn) / 2;
-  static constexpr bool LOAD_ALL = RAW_WORDS + PPL * 2 * KM <= 64;
-  static_assert(DK % 32 == 0 && DV % 16 == 0 && TMAX == 8, "tiling");
+  static constexpr bool LOAD_ALL = RAW_WORDS + PPL * 2 * KM <= 96;
+  static_assert(DK % 32 == 0 && DV % 16 == 0 && (TMAX == 8 || TMAX == 16), "tiling");
+  static constexpr int KF = TMAX * DK > NKQ * BLD ? TMAX * DK : NKQ * BLD;  // raw k rows, then [Ti; M2]
+  static_assert(ALD == GLD, "A and Oc overwrite the Gram rows in place");
 };
 
 template <int DK, int DV, int TMAX, int KC, typename TIn>
@@ -124,11 +126,12 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
   constexpr int NCB = NKQ / 16;  // 16-column blocks of [K;Q]
 
   __shared__ __align__(16) unsigned char s_kq[NKQ * KQS];  // pre-split raw k, q rows
-  __shared__ __align__(16) float s_kf[TMAX * DK];          // raw k rows (fp32), for the tape
+  __shared__ __align__(16) float s_kf[LY::KF];             // raw k rows (fp32) for the tape, then [Ti; M2]
   __shared__ __align__(16) float s_rhs[DV * RT_LD];        // v, then RHS
-  __shared__ float s_G[NKQ * GLD];
-  __shared__ float s_A[TMAX * ALD], s_Oc[TMAX * ALD];
-  __shared__ float s_B[NKQ * BLD];                         // rows: Ti, then M2
+  __shared__ float s_G[NKQ * GLD];                         // Gram, then A (k rows) and Oc (q rows) in place
+  float* const s_A = s_G;
+  float* const s_Oc = s_G + TMAX * GLD;
+  float* const s_B = s_kf;                                 // rows: Ti, then M2
   __shared__ float s_rn[NKQ], s_ga[TMAX], s_gb[TMAX];
   __shared__ float s_ck[TMAX], s_cq[TMAX], s_cb[TMAX];
 
@@ -308,12 +311,26 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // T x T coefficients, one (t, i) pair per lane (TMAX^2 = 64).
+    // Tape k: the normalised k rows, once per k-head (before [Ti; M2] takes
+    // their space).
+    if (g == 0) {
+      constexpr int C4 = DK / 4;
+      for (int e = lane; e < T * C4; e += 64) {
+        const int t = e / C4, c4 = e % C4;
+        const floatx4 v = *reinterpret_cast<const floatx4*>(s_kf + t * DK + 4 * c4) * s_rn[t];
+        __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(p.tk + ((lb * T + t) * p.Hk + hk) * DK) + c4);
+      }
+    }
+
+    // T x T coefficients, (t, i) pairs over the lanes, each written in place
+    // of the Gram entries it reads.
     float ga[TMAX];
 #pragma unroll
     for (int s = 0; s < TMAX; ++s) ga[s] = s_ga[s];
-    {
-      const int t = lane / TMAX, i = lane % TMAX;
+#pragma unroll
+    for (int q = 0; q < TMAX * TMAX / 64; ++q) {
+      const int e = lane + 64 * q;
+      const int t = e / TMAX, i = e % TMAX;
       float gm = 1.f;  // Gamma[t,i] = a_{i+1} ... a_t
 #pragma unroll
       for (int s = 0; s < TMAX; ++s) gm *= (s > i && s <= t) ? ga[s] : 1.f;
@@ -360,18 +377,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
     load_state();
   }
   __syncthreads();  // (B1) prologue results in LDS
-  if (wave == 0) {
-    load_state();
-    // Tape k: the normalised k rows, once per k-head.
-    if (g == 0) {
-      constexpr int C4 = DK / 4;
-      for (int e = lane; e < T * C4; e += 64) {
-        const int t = e / C4, c4 = e % C4;
-        const floatx4 v = *reinterpret_cast<const floatx4*>(s_kf + t * DK + 4 * c4) * s_rn[t];
-        __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(p.tk + ((lb * T + t) * p.Hk + hk) * DK) + c4);
-      }
-    }
-  }
+  if (wave == 0) load_state();
 
   // this lane's node in each column block: k rows then q rows
   float cnode[NCB], cbv[NCB];
@@ -450,15 +456,15 @@ hipError_t launch_c(const VerifyArgs& a, hipStream_t s) {
   const int G = a.Hv / a.Hk;
   const int n_units = a.L * a.B * a.Hk;
   const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
-  if (grid > 0x7fffffffLL || a.T > 8) return hipErrorInvalidValue;
-  if (a.K == 4) {
-    constexpr int NT = ChainLayout<DK, DV, 8, 4, TIn>::NT;
-    hipLaunchKernelGGL((k_verify_chain<DK, DV, 8, 4, TIn>), dim3(static_cast<int>(grid)),
-                       dim3(NT), 0, s, a);
+  if (grid > 0x7fffffffLL || a.T > 16) return hipErrorInvalidValue;
+  constexpr int NT = chain_threads<DV>();
+  const dim3 gd(static_cast<int>(grid));
+  if (a.T <= 8) {
+    if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<DK, DV, 8, 4, TIn>), gd, dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((k_verify_chain<DK, DV, 8, 0, TIn>), gd, dim3(NT), 0, s, a);
   } else {
-    constexpr int NT = ChainLayout<DK, DV, 8, 8, TIn>::NT;
-    hipLaunchKernelGGL((k_verify_chain<DK, DV, 8, 0, TIn>), dim3(static_cast<int>(grid)),
-                       dim3(NT), 0, s, a);
+    if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<DK, DV, 16, 4, TIn>), gd, dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((k_verify_chain<DK, DV, 16, 0, TIn>), gd, dim3(NT), 0, s, a);
   }
   return hipGetLastError();
 }

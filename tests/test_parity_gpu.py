@@ -188,6 +188,10 @@ def test_tree_shapes(T, branching, depth):
 
 
 def test_tree_with_chain_parents_equals_chunk():
+    """A chain is the tree with parent t-1 (GDN page s8: tree-aware verify
+    generalises the chunk).  The two calls run different kernels, so the
+    results agree up to rounding: within the parity bar, with the gate tape
+    (a copy of the input) bit-exact."""
     _need_gpu()
     cfg = W.CONFIGS[3].with_(L=1, B=2, Hk=2, Hv=4, T=9, V=100)
     inp, acc = host_round_inputs(cfg, 1)
@@ -206,8 +210,11 @@ def test_tree_with_chain_parents_equals_chunk():
                                 d["S0"], o, tape)
         outs.append((o, tape))
     torch.cuda.synchronize()
-    assert torch.equal(outs[0][0], outs[1][0])
-    assert torch.equal(outs[0][1].u, outs[1][1].u)
+    c = lambda t: t.cpu().double().numpy()
+    assert rel_fro(c(outs[1][0]), c(outs[0][0])) <= 1e-4
+    assert rel_fro(c(outs[1][1].u), c(outs[0][1].u)) <= 1e-4
+    assert rel_fro(c(outs[1][1].k), c(outs[0][1].k)) <= 1e-4
+    assert torch.equal(outs[0][1].g, outs[1][1].g)
 
 
 # -------------------------------------------------------------- accept only -
