@@ -163,6 +163,34 @@ def test_shapes_and_dtypes(D, Hk, Hv, K, silu, dtype):
     compare(got, ref, tree=False)
 
 
+@pytest.mark.parametrize("D,K,silu,dtype", [
+    (128, 8, True, torch.float32),    # 16-token chunk, prologue loads one channel pair at a time
+    (128, 3, False, torch.bfloat16),
+    (64, 6, True, torch.float32),
+    (32, 4, True, torch.bfloat16),
+])
+def test_sixteen_token_chunks(D, K, silu, dtype):
+    """Chains of 16 tokens (the block-draft length) across head sizes, conv
+    widths and input types."""
+    _need_gpu()
+    cfg = W.CONFIGS[4].with_(L=2, B=3, Hk=2, Hv=4, Dk=D, Dv=D, K=K, silu=silu, dtype=dtype,
+                             V=257)
+    inp, acc = host_round_inputs(cfg, 4)
+    got, ref = run_pair(cfg, inp, acc)
+    compare(got, ref, tree=False)
+
+
+@pytest.mark.parametrize("T,K,silu,depth", [(48, 3, False, 8), (64, 8, True, 8), (33, 2, True, 12)])
+def test_tree_conv_widths(T, K, silu, depth):
+    """Trees of 33..64 nodes with conv widths other than 4 (windows that reach
+    past the old rows), SiLU off, and depths past the unrolled path solve."""
+    _need_gpu()
+    cfg = W.CONFIGS[5].with_(L=1, B=3, Hk=2, Hv=4, T=T, K=K, silu=silu, V=300, max_depth=depth)
+    inp, acc = host_round_inputs(cfg, 6)
+    got, ref = run_pair(cfg, inp, acc)
+    compare(got, ref, tree=True)
+
+
 @pytest.mark.parametrize("n", [0, "T"])
 def test_all_rejected_and_all_accepted(n):
     _need_gpu()
