@@ -62,23 +62,32 @@ __global__ __launch_bounds__(256) void k_argmax_part(AcceptArgs p) {
     const uint4* vp = reinterpret_cast<const uint4*>(base);
     const int vbeg = beg / EPV;
     const int vend = end / EPV;  // full vectors
-    for (int q = vbeg + tid; q < vend; q += NT) {
-      const uint4 w = vp[q];
-      const int i0 = q * EPV;
-      if (ESZ == 2) {
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    // A thread sees its elements in increasing index order, so a strict
+    // greater-than keeps the lowest index among equal values.
+    auto scan = [&](const uint4& w, int i0) {
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          best = better(best, Best{bf16_lo(ws[h]), i0 + 2 * h});
-          best = better(best, Best{bf16_hi(ws[h]), i0 + 2 * h + 1});
+      for (int h = 0; h < 4; ++h) {
+        if (ESZ == 2) {
+          const float lo = bf16_lo(ws[h]), hi = bf16_hi(ws[h]);
+          if (lo > best.v) best = Best{lo, i0 + 2 * h};
+          if (hi > best.v) best = Best{hi, i0 + 2 * h + 1};
+        } else {
+          const float v = __uint_as_float(ws[h]);
+          if (v > best.v) best = Best{v, i0 + h};
         }
-      } else {
-        best = better(best, Best{__uint_as_float(w.x), i0});
-        best = better(best, Best{__uint_as_float(w.y), i0 + 1});
-        best = better(best, Best{__uint_as_float(w.z), i0 + 2});
-        best = better(best, Best{__uint_as_float(w.w), i0 + 3});
       }
+    };
+    constexpr int U = 4;  // vectors in flight per thread
+    int q = vbeg + tid;
+    for (; q + (U - 1) * NT < vend; q += U * NT) {
+      uint4 w[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) w[j] = vp[q + j * NT];
+#pragma unroll
+      for (int j = 0; j < U; ++j) scan(w[j], (q + j * NT) * EPV);
     }
+    for (; q < vend; q += NT) scan(vp[q], q * EPV);
     for (int i = vend * EPV + tid; i < end; i += NT) {  // ragged tail
       const float v = ESZ == 2 ? ld_in(reinterpret_cast<const uint16_t*>(base), i)
                                : ld_in(reinterpret_cast<const float*>(base), i);
