@@ -1,16 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark: speculative rounds through a 30-layer GDN stack on one MI355X.
 
-One step = one speculative round over the whole stack, all on one stream:
-  30 x gdn_verify_chunk (or gdn_tree_verify)  ->  spec_accept_prefix
-  ->  gdn_tape_rollback (all layers)  ->  gdn_conv_state_rollback (all layers)
-with every input already resident in HBM.  The round is captured once per
-input set into a HIP graph and replayed (eager with --eager).
+One step = one speculative round over the whole stack, all on one stream,
+with every input already resident in HBM, in one of two forms:
+  plain   30 x gdn_verify_chunk (or gdn_tree_verify)  ->  spec_accept_prefix
+          ->  gdn_tape_rollback (all layers)  ->  gdn_conv_state_rollback
+  fused   30 x gdn_verify_chunk_replay, each first replaying the previous
+          round's accepted prefix of its layer  ->  spec_accept_prefix
+          ->  gdn_conv_state_rollback        (chains of at most 16 drafts)
+Both do the same work per round in steady state: K timed fused rounds replay
+K accepted prefixes.  `value` is the form spec_round.fused_pays picks for
+the shape (--round forces one); chains report both under "rounds".  Each
+round is captured once per input set into a HIP graph and replayed (eager
+with --eager).
 
 Prints ONE JSON line.  `value` is verified draft tokens per second for the
 30-layer stack (B * T drafted tokens per round / round time).  Extra fields
-give accepted and committed tokens/s, rollback time per round, whole-round
-HBM fraction from the algorithmic byte model, the dominant kernel's roofline
+give accepted and committed tokens/s, per-kernel times, whole-round HBM
+fraction from the algorithmic byte model, the dominant kernel's roofline
 (measured with HIP events around its launches on the launch stream), and the
 fp64 oracle's throughput on a bounded sample on the host cores.
 
@@ -37,10 +44,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per verify launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs (calibrated on a plain copy), or None when the sources of
-    the kernel that serves this workload changed since the counters were
-    taken (each workload records the files it hashed)."""
+    """(HBM bytes, algorithmic bytes) per verify launch of the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (calibrated on a plain copy), or
+    None when the sources of the kernel that serves this workload changed
+    since the counters were taken (each workload records the files it
+    hashed)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "verify_traffic.json")
     if not os.path.exists(path):
@@ -56,7 +64,7 @@ def measured_traffic(workload: str):
             h.update(g.read())
     if not w.get("sources") or h.hexdigest() != w.get("source_sha256"):
         return None
-    return w["traffic_bytes"]
+    return w["traffic_bytes"], w["algorithmic_bytes"]
 
 
 def rollback_sweep(cfg, rb, stream, reps=10):
@@ -92,6 +100,83 @@ def rollback_sweep(cfg, rb, stream, reps=10):
             "tape_bytes_per_token_per_stack": cfg.L * cfg.B * tape_tok}
 
 
+def fused_pass(cfg, rbs, shared, stream, steps, warmup, eager):
+    """The same rounds with each layer's state rollback folded into the next
+    round's verify (gdn_verify_chunk_replay): per round, 30 fused verifies,
+    accept, conv rollback.  Returns round time, per-phase kernel times and the
+    accepted lengths of the timed rounds."""
+    from speculative_decode_verify_gdn_amd import binding as gb
+    from speculative_decode_verify_gdn_amd import spec_round as sr
+    dev = shared.S.device
+    tapes = [shared.tape, gb.Tape.empty(shared.sh, cfg.T, dev)]
+    nks = [torch.zeros((cfg.B,), dtype=torch.int32, device=dev) for _ in range(2)]
+    frs = [sr.FusedRound(rb, tapes=tapes, n_keeps=nks) for rb in rbs]
+    n = len(frs)
+    # round i runs input set i % n with tape parity i % 2; capture one graph
+    # per (set, parity) pair that occurs
+    keys = sorted({(i % n, i % 2) for i in range(2 * n)})
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        frs[0].round(0, first=True)
+        for i in range(1, 2 * n):  # eager warm-up of every (set, parity)
+            frs[i % n].round(i)
+        torch.cuda.synchronize()
+        graphs, phases = {}, {}
+        for j, par in keys:
+            if not eager:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    frs[j].round(par)
+                graphs[(j, par)] = g
+            gv, ga = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gv, stream=stream):
+                frs[j].verify_layers(par)
+            with torch.cuda.graph(ga, stream=stream):
+                frs[j].accept_and_conv(par)
+            phases[(j, par)] = (gv, ga)
+        torch.cuda.synchronize()
+        base = 2 * n  # rounds so far (keeps the parity chain unbroken)
+
+        def step(i):
+            key = (i % n, i % 2)
+            if graphs:
+                graphs[key].replay()
+            else:
+                frs[key[0]].round(key[1])
+
+        for i in range(base, base + warmup):
+            step(i)
+        base += warmup
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for i in range(base, base + steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = e0.elapsed_time(e1)
+        base += steps
+        n_hist = torch.zeros((steps, cfg.B), dtype=torch.int32, device=dev)
+        p_hist = torch.zeros((steps, cfg.B), dtype=torch.int32, device=dev)
+        v_ev, a_ev = [], []
+        for s_i, i in enumerate(range(base, base + steps)):
+            gv, ga = phases[(i % n, i % 2)]
+            p_hist[s_i].copy_(nks[(i + 1) % 2])  # what this round's verify replays
+            for g, acc in ((gv, v_ev), (ga, a_ev)):
+                s0, s1 = ev(), ev()
+                s0.record(stream)
+                g.replay()
+                s1.record(stream)
+                acc.append((s0, s1))
+            n_hist[s_i].copy_(nks[i % 2])
+        torch.cuda.synchronize()
+    assert int(shared.dev_err.item()) == 0, "device-side error bits set"
+    return {"ms": total_ms / steps,
+            "verify_replay_ms": float(np.mean([a.elapsed_time(b) for a, b in v_ev])) / cfg.L,
+            "accept_conv_ms": float(np.mean([a.elapsed_time(b) for a, b in a_ev])),
+            "n_keep": n_hist.cpu().numpy(), "n_prev": p_hist.cpu().numpy()}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +191,10 @@ def parse():
                     help="target host time of the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--round", choices=("auto", "plain", "fused"), default="auto",
+                    help="round whose time is `value`: plain (verify, accept, rollback) or fused "
+                         "(the state rollback folded into the next round's verify); auto picks "
+                         "by the rule in spec_round.fused_pays; chains also report the other")
     ap.add_argument("--sweep-n", action="store_true",
                     help="also time rollback with every sequence forced to n = 0..T")
     return ap.parse_args()
@@ -128,8 +217,33 @@ def verify_bytes_per_launch(cfg, B) -> int:
     return B * per_seq + C * cfg.K * 4                  # + conv weights
 
 
-def verify_kernel_name(cfg) -> str:
+def fused_verify_bytes(cfg, B, n_prev: np.ndarray) -> float:
+    """Algorithmic bytes of one fused verify launch (gdn_verify_chunk_replay):
+    the verify's bytes, plus for every sequence whose previous round kept
+    n >= 1 the replayed state's write and its n previous tape entries (the
+    state read is the verify's own)."""
+    P = cfg.Hv * cfg.Dv * cfg.Dk * 4
+    tape_tok = cfg.Hv * cfg.Dv * 4 + cfg.Hk * cfg.Dk * 4 + cfg.Hv * 4
+    n = n_prev.astype(np.int64)
+    return verify_bytes_per_launch(cfg, B) + float(np.sum((n >= 1) * P + n * tape_tok))
+
+
+def roofline(kernel: str, bytes_per_launch: float, ms_per_launch: float, traffic) -> dict:
+    gbs = bytes_per_launch / (ms_per_launch * 1e-3) / 1e9
+    # traffic: calibrated FETCH_SIZE + WRITE_SIZE bytes per launch of the
+    # committed counter runs, with the algorithmic bytes of those launches
+    # (equal to bytes_per_launch except where they depend on accepted lengths)
+    return {"kernel": kernel, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": None if traffic is None else traffic[0],
+            "traffic_algorithmic_bytes": None if traffic is None else traffic[1],
+            "bytes_per_launch": bytes_per_launch}
+
+
+def verify_kernel_name(cfg, fused: bool = False) -> str:
     """The verify kernel the library dispatches for this workload (one layer)."""
+    if fused:
+        return "k_verify_chain, replay variant (gdn_verify_chunk_replay, one layer)"
     if not cfg.is_tree and cfg.T <= 16:
         return "k_verify_chain (gdn_verify_chunk, chains of <= 16 tokens, one layer)"
     if cfg.is_tree and cfg.T > 32 and cfg.dtype == torch.bfloat16 and cfg.Dk == cfg.Dv == 128:
@@ -348,23 +462,55 @@ def main():
     rollback_ms = float(np.mean([a.elapsed_time(b) for a, b in r_ms]))
     assert int(shared.dev_err.item()) == 0, "device-side error bits set"
 
+    pays = sr.fused_pays(shared.sh, cfg.T, cfg.is_tree)
+    mode = args.round if args.round != "auto" else ("fused" if pays else "plain")
+    if mode == "fused" and (cfg.is_tree or cfg.T > 16):
+        sys.stderr.write("the fused round takes chains of at most 16 drafts\n")
+        sys.exit(2)
+    fused = None
+    if not cfg.is_tree and cfg.T <= 16:
+        fused = fused_pass(cfg, rbs, shared, stream, args.steps, args.warmup, args.eager)
+
     sweep = None
     if args.sweep_n and not cfg.is_tree:
         with torch.cuda.stream(stream):
             sweep = rollback_sweep(cfg, rbs[0], stream)
 
-    ms = total_ms / args.steps
-    n_keep = n_hist.cpu().numpy()
     B, T = cfg.B, cfg.T
     vb = verify_bytes_per_launch(cfg, B)
-    round_bytes = [cfg.L * vb + accept_bytes(cfg, B) + rollback_bytes(cfg, n_keep[i])
-                   + conv_rollback_bytes(cfg, n_keep[i]) for i in range(args.steps)]
-    mean_round_bytes = float(np.mean(round_bytes))
-    verify_gbs = vb / (verify_ms * 1e-3) / 1e9
-    acc_tok = float(n_keep.sum()) / args.steps
+    # plain round: L verifies, accept, state + conv rollback
+    ms = total_ms / args.steps
+    n_keep = n_hist.cpu().numpy()
+    plain_bytes = float(np.mean([cfg.L * vb + accept_bytes(cfg, B) + rollback_bytes(cfg, n_keep[i])
+                                 + conv_rollback_bytes(cfg, n_keep[i]) for i in range(args.steps)]))
+    rounds = {"plain": {
+        "value": B * T / (ms * 1e-3), "ms_per_step": ms, "n_keep": n_keep,
+        "round_bytes": plain_bytes,
+        "kernel_ms": {"verify_per_layer": verify_ms, "accept": accept_ms,
+                      "rollback_state_and_conv": rollback_ms},
+        "roofline": roofline(verify_kernel_name(cfg), vb, verify_ms,
+                             measured_traffic(cfg.name))}}
+    if fused is not None:
+        # fused round: L verifies that each replay the previous round's prefix,
+        # accept, conv rollback
+        fms = fused["ms"]
+        nk, npv = fused["n_keep"], fused["n_prev"]
+        fvb = float(np.mean([fused_verify_bytes(cfg, B, npv[i]) for i in range(args.steps)]))
+        fused_bytes = float(np.mean([cfg.L * fused_verify_bytes(cfg, B, npv[i]) + accept_bytes(cfg, B)
+                                     + conv_rollback_bytes(cfg, nk[i]) for i in range(args.steps)]))
+        rounds["fused"] = {
+            "value": B * T / (fms * 1e-3), "ms_per_step": fms, "n_keep": nk,
+            "round_bytes": fused_bytes,
+            "kernel_ms": {"verify_with_replay_per_layer": fused["verify_replay_ms"],
+                          "accept_and_conv_rollback": fused["accept_conv_ms"]},
+            "roofline": roofline(verify_kernel_name(cfg, fused=True), fvb, fused["verify_replay_ms"],
+                                 measured_traffic(cfg.name + "_fused"))}
+    r = rounds[mode]
+    ms = r["ms_per_step"]
+    acc_tok = float(r["n_keep"].sum()) / args.steps
     out = {
         "metric": "verified draft tokens/s per 30-layer GDN stack",
-        "value": B * T / (ms * 1e-3),
+        "value": r["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -381,18 +527,17 @@ def main():
                    "k_heads": cfg.Hk, "v_heads": cfg.Hv, "d_k": cfg.Dk, "d_v": cfg.Dv,
                    "conv_kernel": cfg.K, "inputs": "bf16" if cfg.dtype == torch.bfloat16 else "f32",
                    "state": "f32", "vocab": cfg.V, "hip_graph": not args.eager,
-                   "input_sets": len(rbs)},
+                   "input_sets": len(rbs), "round": mode},
         "accepted_tokens_per_s": acc_tok / (ms * 1e-3),
         "committed_tokens_per_s": (acc_tok + B) / (ms * 1e-3),
-        "rollback_us": rollback_ms * 1e3,
-        "round_hbm_frac": mean_round_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "round_algorithmic_bytes": mean_round_bytes,
-        "kernel_ms": {"verify_per_layer": verify_ms, "accept": accept_ms,
-                      "rollback_state_and_conv": rollback_ms},
-        "roofline": {"kernel": verify_kernel_name(cfg),
-                     "bound": "hbm", "achieved": verify_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": verify_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(cfg.name), "bytes_per_launch": vb},
+        "round_hbm_frac": r["round_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "round_algorithmic_bytes": r["round_bytes"],
+        "kernel_ms": r["kernel_ms"],
+        "roofline": r["roofline"],
+        "rounds": {k: {"value": v["value"], "ms_per_step": v["ms_per_step"],
+                       "kernel_ms": v["kernel_ms"],
+                       "verify_bytes_per_launch": v["roofline"]["bytes_per_launch"],
+                       "verify_roofline_frac": v["roofline"]["frac"]} for k, v in rounds.items()},
     }
     if sweep is not None:
         out["rollback_sweep"] = sweep

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
   GDN_OK = 0,
@@ -112,6 +112,33 @@ gdn_status gdn_verify_chunk(const gdn_shape* shape, int32_t T, const void* x,
                             const void* conv_state, const float* conv_w, const void* a,
                             const void* b, const float* S, float* o, const gdn_tape* tape,
                             void* stream);
+
+/*
+ * gdn_verify_chunk with the previous round's state rollback folded in.
+ * On entry S holds the previous round's pre-verify snapshot (as
+ * gdn_verify_chunk left it), and prev_tape / prev_n_keep describe that
+ * round's accepted prefix of a chain of prev_T tokens.  The call replays the
+ * accepted steps onto S exactly as gdn_tape_rollback(prev_T, S, prev_tape,
+ * NULL, prev_n_keep) would, writes the rolled state back to S (sequences with
+ * n = 0 keep S), then verifies the T drafted tokens from it exactly as
+ * gdn_verify_chunk.  S is read once for both steps instead of twice.
+ *   S           [L,B,Hv,Dv,Dk] in/out (fp32)
+ *   prev_tape   the previous round's tape (prev_T entries); must not share
+ *               buffers with tape
+ *   prev_n_keep [B] int32, the previous round's accepted lengths
+ *   other arguments as gdn_verify_chunk; conv_state must already be the
+ *   window after the previous round (gdn_conv_state_rollback).
+ * n_keep outside [0, prev_T] sets GDN_DEV_ERR_N_KEEP and that sequence is
+ * verified from S unchanged.  Chains only.  Both steps run in one kernel when
+ * T <= 16 and prev_T <= 16, otherwise as the two calls in sequence.
+ * Source: GDN page s4 (restore the snapshot and replay the accepted steps),
+ * applied at the start of the next verify of the same layer; s2.1 (verify).
+ */
+gdn_status gdn_verify_chunk_replay(const gdn_shape* shape, int32_t T, const void* x,
+                                   const void* conv_state, const float* conv_w, const void* a,
+                                   const void* b, float* S, float* o, const gdn_tape* tape,
+                                   int32_t prev_T, const gdn_tape* prev_tape,
+                                   const int32_t* prev_n_keep, int32_t* dev_err, void* stream);
 
 /*
  * Verify a draft tree of T nodes (T <= 64) per sequence: node v with parent

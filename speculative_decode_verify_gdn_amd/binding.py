@@ -22,7 +22,7 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH, GDN_ERR_WORKSP
 GDN_F32, GDN_BF16 = 0, 1
 DEV_ERR_N_KEEP, DEV_ERR_PARENT, DEV_ERR_PATH = 1, 2, 4
 
-EXPORTS = ("gdn_verify_chunk", "gdn_tree_verify", "spec_accept_prefix",
+EXPORTS = ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify", "spec_accept_prefix",
            "spec_accept_workspace_bytes", "gdn_tape_rollback", "gdn_conv_state_rollback",
            "gdn_status_string", "gdn_abi_version")
 
@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
         P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         SP, TP = ctypes.POINTER(_CShape), ctypes.POINTER(_CTape)
         L.gdn_verify_chunk.argtypes = [SP, I32, P, P, P, P, P, P, P, TP, P]
+        L.gdn_verify_chunk_replay.argtypes = [SP, I32, P, P, P, P, P, P, P, TP, I32, TP, P, P, P]
         L.gdn_tree_verify.argtypes = [SP, I32, P, P, P, P, P, P, P, P, TP, P, P, P]
         L.spec_accept_prefix.argtypes = [I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P, P]
         L.spec_accept_workspace_bytes.argtypes = [I32, I32, I32]
@@ -94,7 +95,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_status_string.argtypes = [I32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
-        for name in ("gdn_verify_chunk", "gdn_tree_verify", "spec_accept_prefix",
+        for name in ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
+                     "spec_accept_prefix",
                      "gdn_tape_rollback", "gdn_conv_state_rollback", "gdn_abi_version"):
             getattr(L, name).restype = I32
         _lib = L
@@ -187,6 +189,24 @@ def gdn_verify_chunk(sh: GdnShape, x, conv_state, conv_w, a, b, S, o, tape: Tape
     ct = tape.c(sh, T)
     _check(lib().gdn_verify_chunk(ctypes.byref(sh.c()), T, *ptrs, ctypes.byref(ct),
                                   _stream(stream)), "gdn_verify_chunk")
+
+
+def gdn_verify_chunk_replay(sh: GdnShape, x, conv_state, conv_w, a, b, S, o, tape: Tape,
+                            prev_tape: Tape, prev_n_keep, dev_err=None, stream=None):
+    """Replay the previous round's accepted prefix (prev_tape, prev_n_keep)
+    onto S in place, then verify the chain of T = x.shape[2] tokens from it."""
+    T = int(x.shape[2])
+    pT = int(prev_tape.g.shape[2])
+    ptrs = _verify_ptrs(sh, T, x, conv_state, conv_w, a, b, S, o)
+    _dev(x.device, conv_state, conv_w, a, b, S, o, tape.u, tape.k, tape.g, prev_tape.u,
+         prev_tape.k, prev_tape.g, prev_n_keep, dev_err)
+    ct = tape.c(sh, T)
+    pt = prev_tape.c(sh, pT)
+    pn = _need(prev_n_keep, "prev_n_keep", torch.int32, (sh.B,), 4)
+    de = _opt(dev_err, "dev_err", torch.int32, (1,))
+    _check(lib().gdn_verify_chunk_replay(ctypes.byref(sh.c()), T, *ptrs, ctypes.byref(ct), pT,
+                                         ctypes.byref(pt), pn, de, _stream(stream)),
+           "gdn_verify_chunk_replay")
 
 
 def gdn_tree_verify(sh: GdnShape, parent, x, conv_state, conv_w, a, b, S, o, tape: Tape,

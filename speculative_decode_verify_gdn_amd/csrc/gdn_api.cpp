@@ -100,6 +100,37 @@ gdn_status gdn_verify_chunk(const gdn_shape* shape, int32_t T, const void* x,
   return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype, s));
 }
 
+gdn_status gdn_verify_chunk_replay(const gdn_shape* shape, int32_t T, const void* x,
+                                   const void* conv_state, const float* conv_w, const void* a,
+                                   const void* b, float* S, float* o, const gdn_tape* tape,
+                                   int32_t prev_T, const gdn_tape* prev_tape,
+                                   const int32_t* prev_n_keep, int32_t* dev_err, void* stream) {
+  gdn_status st = check_shape(shape, T);
+  if (st != GDN_OK) return st;
+  if (!verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape)) return GDN_ERR_INVALID_ARG;
+  if (!prev_tape || !prev_tape->u || !prev_tape->k || !prev_tape->g || !prev_n_keep)
+    return GDN_ERR_INVALID_ARG;
+  if (prev_T < 1) return GDN_ERR_INVALID_ARG;
+  if (prev_T > kMaxT) return GDN_ERR_UNSUPPORTED;
+  if (prev_tape->u == tape->u || prev_tape->k == tape->k || prev_tape->g == tape->g)
+    return GDN_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
+  v.dev_err = dev_err;
+  if (T <= 16 && prev_T <= 16) {
+    v.S_out = S;
+    v.ptu = prev_tape->u;
+    v.ptk = prev_tape->k;
+    v.ptg = prev_tape->g;
+    v.prev_n_keep = prev_n_keep;
+    v.pT = prev_T;
+    return launch_status(gdn::launch_verify_chain(v, shape->d_k, shape->d_v, shape->in_dtype, s));
+  }
+  st = gdn_tape_rollback(shape, prev_T, S, prev_tape, nullptr, prev_n_keep, dev_err, stream);
+  if (st != GDN_OK) return st;
+  return gdn_verify_chunk(shape, T, x, conv_state, conv_w, a, b, S, o, tape, stream);
+}
+
 gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* parent,
                            const void* x, const void* conv_state, const float* conv_w,
                            const void* a, const void* b, const float* S, float* o,

@@ -28,6 +28,14 @@ struct VerifyArgs {
   int L, B, Hk, Hv, K, T, silu;
   float eps;
   int C;
+  // Replay of the previous round's accepted prefix onto S before this verify
+  // (chain kernel; prev_n_keep == nullptr: none).  S_out = S, written in place.
+  float* S_out;
+  const float* ptu;
+  const float* ptk;
+  const float* ptg;
+  const int32_t* prev_n_keep;
+  int pT;
 };
 
 // Tape-replay rollback.

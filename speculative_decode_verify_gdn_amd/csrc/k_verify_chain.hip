@@ -113,7 +113,7 @@ struct ChainLayout {
   static_assert(ALD == GLD, "A and Oc overwrite the Gram rows in place");
 };
 
-template <int DK, int DV, int TMAX, int KC, typename TIn>
+template <int DK, int DV, int TMAX, int KC, typename TIn, bool RP>
 __global__ __launch_bounds__(chain_threads<DV>())
 __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
   constexpr int KM = KC > 0 ? KC : 8;
@@ -134,6 +134,11 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
   float* const s_B = s_kf;                                 // rows: Ti, then M2
   __shared__ float s_rn[NKQ], s_ga[TMAX], s_gb[TMAX];
   __shared__ float s_ck[TMAX], s_cq[TMAX], s_cb[TMAX];
+  // previous round's accepted prefix: w_i = prod_{i<j<pn} g_j (zero for
+  // i >= pn) and gamma = prod_{j<pn} g_j
+  constexpr int PM = 16;
+  __shared__ float s_pw[RP ? PM : 1];
+  __shared__ float s_pgam;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,11 +157,44 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
   const int hv = hk * G + g;
   const int T = p.T;
   const int K = KC > 0 ? KC : p.K;
+  // accepted length of the previous round (replay variant)
+  int pn = 0;
+  if constexpr (RP) {
+    const int bb = static_cast<int>(lb % p.B);
+    const int v = p.prev_n_keep[bb];
+    pn = (v >= 0 && v <= p.pT && v <= PM) ? v : 0;
+    if (pn != v && tid == 0 && p.dev_err && l == 0 && hk == 0 && g == 0)
+      atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
+  }
 
   // This wave's tiles of S0 (tile wave + tt * NW): lane (c16, kk) holds row
   // c16 of a tile, columns 16m + 4kk .. +3, as MFMA A operands.
   floatx4 sreg[TPW][DK / 16];
   const float* S_head = p.S + (lb * p.Hv + hv) * static_cast<size_t>(DV * DK);
+  float* const S_live = RP ? p.S_out + (lb * p.Hv + hv) * static_cast<size_t>(DV * DK) : nullptr;
+  // Replay operands, straight from the previous tape into registers: lane
+  // (c16, kk) takes k_i[16m + c16] (A) and u_i[16 tile + c16] (B) for
+  // i = 4 st + kk.  Steps with 4 st >= pn are skipped (pn is uniform).
+  float kt[RP ? PM / 4 : 1][RP ? DK / 16 : 1];
+  float ut[RP ? TPW : 1][RP ? PM / 4 : 1];
+  auto load_tape = [&]() {
+    if constexpr (RP) {
+      const size_t base = lb * p.pT;
+#pragma unroll
+      for (int st = 0; st < PM / 4; ++st) {
+        if (4 * st < pn) {
+          const int i = 4 * st + kk;
+          const size_t ii = base + (i < pn ? i : 0);
+          const float* kr = p.ptk + (ii * p.Hk + hk) * DK + c16;
+#pragma unroll
+          for (int m = 0; m < DK / 16; ++m) kt[st][m] = kr[16 * m];
+          const float* ur = p.ptu + (ii * p.Hv + hv) * DV + c16;
+#pragma unroll
+          for (int tt = 0; tt < TPW; ++tt) ut[tt][st] = ur[(wave + tt * NW) * 16];
+        }
+      }
+    }
+  };
   auto load_state = [&]() {
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
@@ -185,6 +223,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
     const size_t gi = (lb * T + tq) * p.Hv + hv;
     const float ga_ld = ld_in(static_cast<const TIn*>(p.a), gi);
     const float gb_ld = ld_in(static_cast<const TIn*>(p.b), gi);
+    const float pg_ld = RP && lane < pn ? p.ptg[(lb * p.pT + lane) * p.Hv + hv] : 1.f;
 
     auto load_pair = [&](int j, typename PR::raw* xr, float* w0, float* w1) {
       const int pr = lane + 64 * j;
@@ -273,6 +312,17 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
         load_pair(j, xr, w0, w1);
         conv_pair(j, xr, w0, w1);
       }
+    }
+    if constexpr (RP) {
+      float w = 1.f, gm = 1.f;
+#pragma unroll
+      for (int j = 0; j < PM; ++j) {
+        const float gj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg_ld), j));
+        gm *= gj;
+        if (j > lane) w *= gj;
+      }
+      if (lane < PM) s_pw[lane] = lane < pn ? w : 0.f;
+      if (lane == 0) s_pgam = gm;
     }
     if (lane < TMAX) {
       s_ga[lane] = lane < T ? ga_ld : 1.f;
@@ -375,9 +425,42 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
   } else {
     __syncthreads();  // (B0)
     load_state();
+    load_tape();
   }
   __syncthreads();  // (B1) prologue results in LDS
-  if (wave == 0) load_state();
+  if (wave == 0) {
+    load_state();
+    load_tape();
+  }
+  if constexpr (RP) {
+    // S <- gamma S + sum_i w_i u_i k_i^T on this wave's tiles, as transposed
+    // 16x16 tiles on fp32 MFMA: D[j][r] = sum_i k_i[16m + j] (w_i u_i)[r],
+    // whose lane (c16, kk) holds exactly the sreg[.][m] element of row c16,
+    // columns 16m + 4kk .. +3.  The rolled state is written back in place.
+    if (pn > 0) {
+      const float gam = s_pgam;
+      float wv[PM / 4];
+#pragma unroll
+      for (int st = 0; st < PM / 4; ++st) wv[st] = s_pw[4 * st + kk];
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) {
+        const int tile = wave + tt * NW;
+        float* const wp = S_live + (tile * 16 + c16) * DK + 4 * kk;
+        float bu[PM / 4];
+#pragma unroll
+        for (int st = 0; st < PM / 4; ++st) bu[st] = 4 * st + kk < pn ? ut[tt][st] * wv[st] : 0.f;
+#pragma unroll
+        for (int m = 0; m < DK / 16; ++m) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < PM / 4; ++st)
+            if (4 * st < pn) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[st][m], bu[st], acc, 0, 0, 0);
+          sreg[tt][m] = sreg[tt][m] * gam + acc;
+          *reinterpret_cast<floatx4*>(wp + 16 * m) = sreg[tt][m];
+        }
+      }
+    }
+  }
 
   // this lane's node in each column block: k rows then q rows
   float cnode[NCB], cbv[NCB];
@@ -451,22 +534,31 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
   }
 }
 
+template <int DK, int DV, typename TIn, bool RP>
+hipError_t launch_cr(const VerifyArgs& a, const dim3& gd, hipStream_t s) {
+  constexpr int NT = chain_threads<DV>();
+  if (a.T <= 8) {
+    if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<DK, DV, 8, 4, TIn, RP>), gd, dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((k_verify_chain<DK, DV, 8, 0, TIn, RP>), gd, dim3(NT), 0, s, a);
+  } else {
+    if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<DK, DV, 16, 4, TIn, RP>), gd, dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((k_verify_chain<DK, DV, 16, 0, TIn, RP>), gd, dim3(NT), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <int DK, int DV, typename TIn>
 hipError_t launch_c(const VerifyArgs& a, hipStream_t s) {
   const int G = a.Hv / a.Hk;
   const int n_units = a.L * a.B * a.Hk;
   const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
   if (grid > 0x7fffffffLL || a.T > 16) return hipErrorInvalidValue;
-  constexpr int NT = chain_threads<DV>();
   const dim3 gd(static_cast<int>(grid));
-  if (a.T <= 8) {
-    if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<DK, DV, 8, 4, TIn>), gd, dim3(NT), 0, s, a);
-    else hipLaunchKernelGGL((k_verify_chain<DK, DV, 8, 0, TIn>), gd, dim3(NT), 0, s, a);
-  } else {
-    if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<DK, DV, 16, 4, TIn>), gd, dim3(NT), 0, s, a);
-    else hipLaunchKernelGGL((k_verify_chain<DK, DV, 16, 0, TIn>), gd, dim3(NT), 0, s, a);
+  if (a.prev_n_keep) {
+    if (a.pT > 16 || !a.S_out || !a.ptu || !a.ptk || !a.ptg) return hipErrorInvalidValue;
+    return launch_cr<DK, DV, TIn, true>(a, gd, s);
   }
-  return hipGetLastError();
+  return launch_cr<DK, DV, TIn, false>(a, gd, s);
 }
 
 template <typename TIn>

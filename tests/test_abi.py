@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gb.abi_version() == 1
+    assert gb.abi_version() == 2
     assert gb.status_string(0) == "GDN_OK"
     assert gb.status_string(1) == "GDN_ERR_INVALID_ARG"
     assert gb.status_string(4) == "GDN_ERR_WORKSPACE"
@@ -73,6 +73,17 @@ def test_host_validation_before_launch(lib):
     assert _verify(_shape(Dk=64, Dv=128)) == gb.GDN_ERR_UNSUPPORTED
     assert _verify(_shape(K=9)) == gb.GDN_ERR_UNSUPPORTED
     assert _verify(_shape(B=0)) == gb.GDN_ERR_INVALID_ARG
+    # fused replay: previous tape missing, aliasing the current one, bad prev_T
+    cur = gb._CTape(0x1000, 0x2000, 0x3000)
+    prev = gb._CTape(0x4000, 0x5000, 0x6000)
+    rv = lambda pT, pt, pn: lib.gdn_verify_chunk_replay(
+        ctypes.byref(_shape()), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(cur),
+        pT, pt, pn, None, None)
+    assert rv(4, None, FAKE) == gb.GDN_ERR_INVALID_ARG
+    assert rv(4, ctypes.byref(prev), None) == gb.GDN_ERR_INVALID_ARG
+    assert rv(4, ctypes.byref(cur), FAKE) == gb.GDN_ERR_INVALID_ARG
+    assert rv(0, ctypes.byref(prev), FAKE) == gb.GDN_ERR_INVALID_ARG
+    assert rv(65, ctypes.byref(prev), FAKE) == gb.GDN_ERR_UNSUPPORTED
     tape = gb._CTape(FAKE.value, FAKE.value, None)
     assert lib.gdn_tape_rollback(ctypes.byref(_shape()), 4, FAKE, ctypes.byref(tape), None, FAKE,
                                  None, None) == gb.GDN_ERR_INVALID_ARG

@@ -16,7 +16,7 @@ from speculative_decode_verify_gdn_amd import binding as gb
 from speculative_decode_verify_gdn_amd import spec_round
 from speculative_decode_verify_gdn_amd import workload as W
 
-from round_ref import compare, gpu_outputs, make_buffers, oracle_round, rel_fro
+from round_ref import compare, gpu_outputs, gshape, make_buffers, oracle_round, rel_fro
 
 pytestmark = pytest.mark.gpu
 
@@ -243,6 +243,76 @@ def test_tree_with_chain_parents_equals_chunk():
     assert rel_fro(c(outs[1][1].u), c(outs[0][1].u)) <= 1e-4
     assert rel_fro(c(outs[1][1].k), c(outs[0][1].k)) <= 1e-4
     assert torch.equal(outs[0][1].g, outs[1][1].g)
+
+
+@pytest.mark.parametrize("cfg_id,L,B,rounds,forced", [
+    (2, 1, 1, 6, None), (3, 2, 5, 5, None), (4, 2, 3, 4, None), (3, 2, 4, 3, "T"),
+    (3, 2, 4, 3, 0), (4, 1, 2, 3, "T")])
+def test_fused_replay_rounds(cfg_id, L, B, rounds, forced):
+    """Rounds whose state rollback is folded into the next round's verify of
+    each layer (gdn_verify_chunk_replay, GDN page s4 replay applied one verify
+    later) give the oracle's plain rounds: outputs, tape, accepted lengths,
+    conv windows every round, and the state after the last accepted prefix."""
+    _need_gpu()
+    cfg = W.CONFIGS[cfg_id].with_(L=L, B=B, V=601)
+    inp0 = W.layer_inputs(cfg, 0, "cpu")
+    oS, ocs = W.to_f64(inp0["S0"]), W.to_f64(inp0["conv_state"])
+    fr = None
+    for r in range(rounds):
+        inp = W.layer_inputs(cfg, r, "cpu")
+        forced_n = None if forced is None else (cfg.T if forced == "T" else 0)
+        acc = W.chain_accept_inputs(cfg, r, "cpu", forced_n=forced_n)
+        d = {k: v.to(DEV) for k, v in inp.items()}
+        da = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in acc.items()}
+        if fr is None:
+            d["S0"], d["conv_state"] = inp0["S0"].to(DEV), inp0["conv_state"].to(DEV)
+            fr = spec_round.FusedRound(make_buffers(cfg, d, da))
+        else:
+            rb = fr.rb
+            rb.x, rb.a, rb.b, rb.conv_w = d["x"], d["a"], d["b"], d["conv_w"]
+            rb.logits, rb.draft = da["logits"], da["draft"]
+        fr.round(r, first=(r == 0))
+        torch.cuda.synchronize()
+        f = {k: W.to_f64(v) for k, v in inp.items()}
+        f["S0"], f["conv_state"] = oS, ocs
+        ref = oracle_round(cfg, f, acc["draft"].numpy(), W.to_f64(acc["logits"]))
+        tape = fr.tapes[r % 2]
+        np.testing.assert_array_equal(fr.n_keeps[r % 2].cpu().numpy(), ref["n_keep"])
+        np.testing.assert_array_equal(fr.rb.bonus.cpu().numpy(), ref["bonus"])
+        np.testing.assert_array_equal(fr.rb.conv_state.cpu().double().numpy(), ref["cs_new"])
+        for name, got, want in (("o", fr.rb.o, ref["o"]), ("u", tape.u, ref["u"]),
+                                ("k", tape.k, ref["k"])):
+            err = rel_fro(got.cpu().double().numpy(), want)
+            assert err <= 1e-4, (r, name, err)
+        np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
+        oS, ocs = ref["S_new"], ref["cs_new"]
+    fr.finish(rounds - 1)
+    torch.cuda.synchronize()
+    assert rel_fro(fr.rb.S.cpu().double().numpy(), oS) <= 1e-4
+    assert int(fr.rb.dev_err.item()) == 0
+
+
+def test_fused_replay_bad_prev_n_keep_flags():
+    """An accepted length outside [0, prev_T] sets GDN_DEV_ERR_N_KEEP and
+    that sequence is verified from its state unchanged."""
+    _need_gpu()
+    cfg = W.CONFIGS[3].with_(L=1, B=2, V=97)
+    inp = W.layer_inputs(cfg, 0, "cpu")
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    sh = gshape(cfg)
+    prev = gb.Tape.empty(sh, cfg.T, DEV)
+    for t in (prev.u, prev.k, prev.g):
+        t.fill_(1.0)
+    cur = gb.Tape.empty(sh, cfg.T, DEV)
+    o = torch.empty((1, 2, cfg.T, cfg.Hv, cfg.Dv), device=DEV)
+    pn = torch.tensor([cfg.T + 1, 0], dtype=torch.int32, device=DEV)
+    err = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    S = d["S0"].clone()
+    gb.gdn_verify_chunk_replay(sh, d["x"], d["conv_state"], d["conv_w"], d["a"], d["b"], S, o,
+                               cur, prev, pn, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & gb.DEV_ERR_N_KEEP
+    assert torch.equal(S, d["S0"])
 
 
 # -------------------------------------------------------------- accept only -
