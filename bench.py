@@ -7,10 +7,11 @@ with every input already resident in HBM, in one of two forms:
           ->  gdn_tape_rollback (all layers)  ->  gdn_conv_state_rollback
   fused   30 x gdn_verify_chunk_replay, each first replaying the previous
           round's accepted prefix of its layer  ->  spec_accept_prefix
-          ->  gdn_conv_state_rollback        (chains of at most 16 drafts)
+          ->  gdn_conv_state_rollback
+          (gdn_tree_verify_replay for trees; where the library fuses both)
 Both do the same work per round in steady state: K timed fused rounds replay
 K accepted prefixes.  `value` is the form spec_round.fused_pays picks for
-the shape (--round forces one); chains report both under "rounds".  Each
+the shape (--round forces one); both are reported under "rounds".  Each
 round is captured once per input set into a HIP graph and replayed (eager
 with --eager).
 
@@ -102,15 +103,16 @@ def rollback_sweep(cfg, rb, stream, reps=10):
 
 def fused_pass(cfg, rbs, shared, stream, steps, warmup, eager):
     """The same rounds with each layer's state rollback folded into the next
-    round's verify (gdn_verify_chunk_replay): per round, 30 fused verifies,
-    accept, conv rollback.  Returns round time, per-phase kernel times and the
+    round's verify (gdn_verify_chunk_replay / gdn_tree_verify_replay): per
+    round, 30 fused verifies, accept, conv rollback.  Returns round time, per-phase kernel times and the
     accepted lengths of the timed rounds."""
     from speculative_decode_verify_gdn_amd import binding as gb
     from speculative_decode_verify_gdn_amd import spec_round as sr
     dev = shared.S.device
     tapes = [shared.tape, gb.Tape.empty(shared.sh, cfg.T, dev)]
     nks = [torch.zeros((cfg.B,), dtype=torch.int32, device=dev) for _ in range(2)]
-    frs = [sr.FusedRound(rb, tapes=tapes, n_keeps=nks) for rb in rbs]
+    paths = [torch.full((cfg.B, cfg.T), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+    frs = [sr.FusedRound(rb, tapes=tapes, n_keeps=nks, paths=paths) for rb in rbs]
     n = len(frs)
     # round i runs input set i % n with tape parity i % 2; capture one graph
     # per (set, parity) pair that occurs
@@ -218,12 +220,13 @@ def verify_bytes_per_launch(cfg, B) -> int:
 
 
 def fused_verify_bytes(cfg, B, n_prev: np.ndarray) -> float:
-    """Algorithmic bytes of one fused verify launch (gdn_verify_chunk_replay):
-    the verify's bytes, plus for every sequence whose previous round kept
-    n >= 1 the replayed state's write and its n previous tape entries (the
-    state read is the verify's own)."""
+    """Algorithmic bytes of one fused verify launch (gdn_verify_chunk_replay,
+    gdn_tree_verify_replay): the verify's bytes, plus for every sequence
+    whose previous round kept n >= 1 the replayed state's write and its n
+    previous tape entries (and, for trees, path entries); the state read is
+    the verify's own."""
     P = cfg.Hv * cfg.Dv * cfg.Dk * 4
-    tape_tok = cfg.Hv * cfg.Dv * 4 + cfg.Hk * cfg.Dk * 4 + cfg.Hv * 4
+    tape_tok = cfg.Hv * cfg.Dv * 4 + cfg.Hk * cfg.Dk * 4 + cfg.Hv * 4 + (4 if cfg.is_tree else 0)
     n = n_prev.astype(np.int64)
     return verify_bytes_per_launch(cfg, B) + float(np.sum((n >= 1) * P + n * tape_tok))
 
@@ -240,8 +243,17 @@ def roofline(kernel: str, bytes_per_launch: float, ms_per_launch: float, traffic
             "bytes_per_launch": bytes_per_launch}
 
 
+def fused_kernel(cfg) -> bool:
+    """Whether the library runs the replay and the verify as one kernel."""
+    if not cfg.is_tree:
+        return cfg.T <= 16
+    return 32 < cfg.T <= 64 and cfg.dtype == torch.bfloat16 and cfg.Dk == cfg.Dv == 128
+
+
 def verify_kernel_name(cfg, fused: bool = False) -> str:
     """The verify kernel the library dispatches for this workload (one layer)."""
+    if fused and cfg.is_tree:
+        return "k_verify_tree, replay variant (gdn_tree_verify_replay, one layer)"
     if fused:
         return "k_verify_chain, replay variant (gdn_verify_chunk_replay, one layer)"
     if not cfg.is_tree and cfg.T <= 16:
@@ -464,11 +476,13 @@ def main():
 
     pays = sr.fused_pays(shared.sh, cfg.T, cfg.is_tree)
     mode = args.round if args.round != "auto" else ("fused" if pays else "plain")
-    if mode == "fused" and (cfg.is_tree or cfg.T > 16):
-        sys.stderr.write("the fused round takes chains of at most 16 drafts\n")
+    fusable = fused_kernel(cfg)
+    if mode == "fused" and not fusable:
+        sys.stderr.write("the library fuses chains of at most 16 drafts and trees of 33..64 "
+                         "nodes (bf16, 128-dim heads) only\n")
         sys.exit(2)
     fused = None
-    if not cfg.is_tree and cfg.T <= 16:
+    if fusable:
         fused = fused_pass(cfg, rbs, shared, stream, args.steps, args.warmup, args.eager)
 
     sweep = None

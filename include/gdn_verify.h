@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
   GDN_OK = 0,
@@ -159,6 +159,40 @@ gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* par
                            const void* a, const void* b, const float* S, float* o,
                            const gdn_tape* tape, int32_t* conv_win, int32_t* dev_err,
                            void* stream);
+
+/*
+ * gdn_tree_verify with the previous round's state rollback folded in, as
+ * gdn_verify_chunk_replay is for chains.  On entry S holds the previous
+ * round's pre-verify snapshot; prev_tape / prev_path / prev_n_keep describe
+ * that round's accepted root path (as spec_accept_prefix wrote them) over a
+ * tape of prev_T entries.  The call replays the accepted steps onto S exactly
+ * as gdn_tape_rollback(prev_T, S, prev_tape, prev_path, prev_n_keep) would,
+ * writes the rolled state back to S (n = 0 keeps S), then verifies the tree
+ * from it exactly as gdn_tree_verify.
+ *   S           [L,B,Hv,Dv,Dk] in/out (fp32)
+ *   prev_tape   the previous round's tape (prev_T entries); must not share
+ *               buffers with tape
+ *   prev_path   [B,prev_T] int32 tape entries of the accepted steps, or NULL
+ *               for entries 0 .. n-1 (a chain)
+ *   prev_n_keep [B] int32, the previous round's accepted lengths
+ *   other arguments as gdn_tree_verify; conv_state must already be the
+ *   window after the previous round.
+ * n_keep outside [0, prev_T] sets GDN_DEV_ERR_N_KEEP and a path entry outside
+ * [0, prev_T) sets GDN_DEV_ERR_PATH; that sequence is verified from S
+ * unchanged.  A malformed parent array sets GDN_DEV_ERR_PARENT and leaves the
+ * sequence's outputs unwritten, but the replay is still applied to S.  Both
+ * steps run in one kernel for trees of 33..64 nodes with bf16 inputs and
+ * 128-dim heads; otherwise as the two calls in sequence.
+ * Source: GDN page s4 (restore the snapshot and replay the accepted steps),
+ * applied at the start of the next verify of the same layer; s2.2 and s8
+ * (tree-aware verify).
+ */
+gdn_status gdn_tree_verify_replay(const gdn_shape* shape, int32_t T, const int32_t* parent,
+                                  const void* x, const void* conv_state, const float* conv_w,
+                                  const void* a, const void* b, float* S, float* o,
+                                  const gdn_tape* tape, int32_t* conv_win, int32_t prev_T,
+                                  const gdn_tape* prev_tape, const int32_t* prev_path,
+                                  const int32_t* prev_n_keep, int32_t* dev_err, void* stream);
 
 /*
  * Greedy acceptance.  logits [B,T+1,V] (F32 or BF16): row 0 is the target's

@@ -22,7 +22,8 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH, GDN_ERR_WORKSP
 GDN_F32, GDN_BF16 = 0, 1
 DEV_ERR_N_KEEP, DEV_ERR_PARENT, DEV_ERR_PATH = 1, 2, 4
 
-EXPORTS = ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify", "spec_accept_prefix",
+EXPORTS = ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
+           "gdn_tree_verify_replay", "spec_accept_prefix",
            "spec_accept_workspace_bytes", "gdn_tape_rollback", "gdn_conv_state_rollback",
            "gdn_status_string", "gdn_abi_version")
 
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_verify_chunk.argtypes = [SP, I32, P, P, P, P, P, P, P, TP, P]
         L.gdn_verify_chunk_replay.argtypes = [SP, I32, P, P, P, P, P, P, P, TP, I32, TP, P, P, P]
         L.gdn_tree_verify.argtypes = [SP, I32, P, P, P, P, P, P, P, P, TP, P, P, P]
+        L.gdn_tree_verify_replay.argtypes = [SP, I32, P, P, P, P, P, P, P, P, TP, P, I32, TP, P,
+                                             P, P, P]
         L.spec_accept_prefix.argtypes = [I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P, P]
         L.spec_accept_workspace_bytes.argtypes = [I32, I32, I32]
         L.spec_accept_workspace_bytes.restype = SZ
@@ -96,7 +99,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
         for name in ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
-                     "spec_accept_prefix",
+                     "gdn_tree_verify_replay", "spec_accept_prefix",
                      "gdn_tape_rollback", "gdn_conv_state_rollback", "gdn_abi_version"):
             getattr(L, name).restype = I32
         _lib = L
@@ -222,6 +225,28 @@ def gdn_tree_verify(sh: GdnShape, parent, x, conv_state, conv_w, a, b, S, o, tap
     ct = tape.c(sh, T)
     _check(lib().gdn_tree_verify(ctypes.byref(sh.c()), T, pp, *ptrs, ctypes.byref(ct), cw, de,
                                  _stream(stream)), "gdn_tree_verify")
+
+
+def gdn_tree_verify_replay(sh: GdnShape, parent, x, conv_state, conv_w, a, b, S, o, tape: Tape,
+                           prev_tape: Tape, prev_n_keep, prev_path=None, conv_win=None,
+                           dev_err=None, stream=None):
+    """Replay the previous round's accepted path (prev_tape, prev_path,
+    prev_n_keep) onto S in place, then verify the T-node tree from it."""
+    T = int(x.shape[2])
+    pT = int(prev_tape.g.shape[2])
+    pp = _need(parent, "parent", torch.int32, (sh.B, T), 4)
+    ptrs = _verify_ptrs(sh, T, x, conv_state, conv_w, a, b, S, o)
+    cw = _opt(conv_win, "conv_win", torch.int32, (sh.B, T, sh.K))
+    de = _opt(dev_err, "dev_err", torch.int32, (1,))
+    pn = _need(prev_n_keep, "prev_n_keep", torch.int32, (sh.B,), 4)
+    ppath = _opt(prev_path, "prev_path", torch.int32, (sh.B, pT))
+    _dev(x.device, parent, conv_state, conv_w, a, b, S, o, tape.u, tape.k, tape.g, prev_tape.u,
+         prev_tape.k, prev_tape.g, prev_n_keep, prev_path, conv_win, dev_err)
+    ct = tape.c(sh, T)
+    pt = prev_tape.c(sh, pT)
+    _check(lib().gdn_tree_verify_replay(ctypes.byref(sh.c()), T, pp, *ptrs, ctypes.byref(ct), cw,
+                                        pT, ctypes.byref(pt), ppath, pn, de, _stream(stream)),
+           "gdn_tree_verify_replay")
 
 
 def spec_accept_workspace_bytes(B: int, T: int, V: int) -> int:

@@ -150,6 +150,43 @@ gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* par
   return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype, s));
 }
 
+gdn_status gdn_tree_verify_replay(const gdn_shape* shape, int32_t T, const int32_t* parent,
+                                  const void* x, const void* conv_state, const float* conv_w,
+                                  const void* a, const void* b, float* S, float* o,
+                                  const gdn_tape* tape, int32_t* conv_win, int32_t prev_T,
+                                  const gdn_tape* prev_tape, const int32_t* prev_path,
+                                  const int32_t* prev_n_keep, int32_t* dev_err, void* stream) {
+  gdn_status st = check_shape(shape, T);
+  if (st != GDN_OK) return st;
+  if (!parent || !verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape))
+    return GDN_ERR_INVALID_ARG;
+  if (!prev_tape || !prev_tape->u || !prev_tape->k || !prev_tape->g || !prev_n_keep)
+    return GDN_ERR_INVALID_ARG;
+  if (prev_T < 1) return GDN_ERR_INVALID_ARG;
+  if (prev_T > kMaxT) return GDN_ERR_UNSUPPORTED;
+  if (prev_tape->u == tape->u || prev_tape->k == tape->k || prev_tape->g == tape->g)
+    return GDN_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128) {
+    VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
+    v.parent = parent;
+    v.conv_win = conv_win;
+    v.dev_err = dev_err;
+    v.S_out = S;
+    v.ptu = prev_tape->u;
+    v.ptk = prev_tape->k;
+    v.ptg = prev_tape->g;
+    v.prev_n_keep = prev_n_keep;
+    v.prev_path = prev_path;
+    v.pT = prev_T;
+    return launch_status(gdn::launch_verify_tree(v, s));
+  }
+  st = gdn_tape_rollback(shape, prev_T, S, prev_tape, prev_path, prev_n_keep, dev_err, stream);
+  if (st != GDN_OK) return st;
+  return gdn_tree_verify(shape, T, parent, x, conv_state, conv_w, a, b, S, o, tape, conv_win,
+                         dev_err, stream);
+}
+
 size_t spec_accept_workspace_bytes(int32_t B, int32_t T, int32_t V) {
   if (B < 1 || T < 1 || V < 1 || T > kMaxT) return 0;
   int split = 1, chunk = 1;

@@ -29,12 +29,15 @@ struct VerifyArgs {
   float eps;
   int C;
   // Replay of the previous round's accepted prefix onto S before this verify
-  // (chain kernel; prev_n_keep == nullptr: none).  S_out = S, written in place.
+  // (chain and tree kernels; prev_n_keep == nullptr: none).  S_out = S,
+  // written in place.  prev_path: [B,pT] tape entries of the accepted steps
+  // (tree kernel; nullptr: entries 0 .. n-1).
   float* S_out;
   const float* ptu;
   const float* ptk;
   const float* ptg;
   const int32_t* prev_n_keep;
+  const int32_t* prev_path;
   int pT;
 };
 

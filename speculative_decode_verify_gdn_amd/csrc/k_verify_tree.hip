@@ -90,7 +90,7 @@ struct TreeLds {
   static constexpr int R1 = 2 * TR_T * TR_KQS;
 };
 
-template <int KC>
+template <int KC, bool RP>
 __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   constexpr int KM = KC > 0 ? KC : 8;
   using LY = TreeLds<KM>;
@@ -107,6 +107,12 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   __shared__ __align__(16) int s_widx[TR_T * KM];       // conv window: staging byte offsets
   __shared__ float s_ga[TR_T], s_gb[TR_T], s_gam[TR_T];
   __shared__ int s_bad, s_maxd;
+  // previous round's accepted path (replay variant): tape entry of step i,
+  // w_i = prod_{i<j<pn} g_j (zero for i >= pn), gamma = prod_{j<pn} g_j
+  __shared__ int s_ppath[RP ? TR_T : 1];
+  __shared__ float s_pw[RP ? TR_T : 1];
+  __shared__ float s_pgam;
+  __shared__ int s_pbad;
 
   float* s_v = reinterpret_cast<float*>(s_r2);            // [row of S][node]
   float* s_KK = s_v + TR_D * TR_VLD;                      // packed rows
@@ -134,6 +140,14 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   const int K = KC > 0 ? KC : p.K;
   const uint16_t* x = static_cast<const uint16_t*>(p.x);
   const uint16_t* cs = static_cast<const uint16_t*>(p.conv_state);
+  // accepted length of the previous round (replay variant)
+  int pn = 0;
+  if constexpr (RP) {
+    const int v = p.prev_n_keep[bb];
+    pn = (v >= 0 && v <= p.pT) ? v : 0;
+    if (pn != v && tid == 0 && p.dev_err && l == 0 && hk == 0 && g == 0)
+      atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
+  }
 
   // ------------------------------------------------------------------ loads --
   // Every load is unconditional from a clamped, valid address.
@@ -243,6 +257,34 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
     for (int o = 32; o >= 1; o >>= 1) md = max(md, __shfl_xor(md, o, 64));
     if (lane == 0) s_maxd = md;
   }
+  if constexpr (RP) {
+    // wave 1: the previous accepted path, validated, and its gate products
+    if (wave == 1) {
+      int pp = lane;
+      bool bad = false;
+      if (lane < pn) {
+        if (p.prev_path) pp = p.prev_path[static_cast<size_t>(bb) * p.pT + lane];
+        bad = pp < 0 || pp >= p.pT;
+      }
+      pp = lane < pn && !bad ? pp : 0;
+      const float gv = lane < pn ? p.ptg[(lb * p.pT + pp) * p.Hv + hv] : 1.f;
+      float x_s = gv;  // inclusive suffix product prod_{j >= lane} g_j
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_down(x_s, o, 64);
+        if (lane + o < 64) x_s *= y;
+      }
+      float w = __shfl_down(x_s, 1, 64);
+      if (lane == 63) w = 1.f;
+      s_ppath[lane] = pp;
+      s_pw[lane] = lane < pn ? w : 0.f;
+      const unsigned long long anybad = __ballot(bad);
+      if (lane == 0) {
+        s_pgam = x_s;
+        s_pbad = anybad != 0ull;
+      }
+    }
+  }
   // raw rows and weights into LDS
   u32x4* s_stage = reinterpret_cast<u32x4*>(s_r2);
 #pragma unroll
@@ -256,8 +298,84 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
     if (e < 3 * TR_D * KM) s_w[e] = wv[q];
   }
   __syncthreads();  // (B_a) staging, weights, node structure
+  if constexpr (RP) {
+    if (s_pbad) {
+      if (tid == 0 && p.dev_err && l == 0 && hk == 0 && g == 0) atomicOr(p.dev_err, GDN_DEV_ERR_PATH);
+      pn = 0;
+    }
+  }
+
+  // Replay operands of the first PRE steps, straight from the previous tape
+  // into registers: lane (c16, kk) takes k_{p_i}[16m + c16] (A) and
+  // u_{p_i}[16 wave + c16] (B) for i = 4 st + kk; longer paths load the
+  // remaining steps as they go.  Steps with 4 st >= pn are skipped (pn is
+  // uniform).
+  constexpr int PRE = 4;
+  float kt[RP ? PRE : 1][RP ? TR_D / 16 : 1];
+  float ut[RP ? PRE : 1];
+  auto load_step = [&](int st, float* ka, float& ua) {
+    const int i = 4 * st + kk;
+    const size_t e = lb * p.pT + s_ppath[i < pn ? i : 0];
+    const float* kr = p.ptk + (e * p.Hk + hk) * TR_D + c16;
+#pragma unroll
+    for (int m = 0; m < TR_D / 16; ++m) ka[m] = kr[16 * m];
+    ua = p.ptu[(e * p.Hv + hv) * TR_D + wave * 16 + c16];
+  };
+  if constexpr (RP) {
+#pragma unroll
+    for (int st = 0; st < PRE; ++st)
+      if (4 * st < pn) load_step(st, kt[st], ut[st]);
+  }
+  floatx4 sreg[TR_D / 16];
+  const float* srow = p.S + (lb * p.Hv + hv) * static_cast<size_t>(TR_D * TR_D) +
+                      static_cast<size_t>(wave * 16 + c16) * TR_D + 4 * kk;
+  // S <- gamma S + sum_i w_i u_{p_i} k_{p_i}^T on this wave's tile, as
+  // transposed 16x16 fp32 MFMA tiles D[j][r] = sum_i k_i[16m + j] (w_i u_i)[r]
+  // (lane (c16, kk) of D holds exactly sreg[m]); the rolled tile is written
+  // back in place.
+  auto replay = [&]() {
+    if constexpr (RP) {
+      floatx4 acc[TR_D / 16];
+#pragma unroll
+      for (int m = 0; m < TR_D / 16; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < PRE; ++st) {
+        if (4 * st < pn) {
+          const int i = 4 * st + kk;
+          const float bu = i < pn ? ut[st] * s_pw[i] : 0.f;
+#pragma unroll
+          for (int m = 0; m < TR_D / 16; ++m)
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[st][m], bu, acc[m], 0, 0, 0);
+        }
+      }
+      for (int st = PRE; 4 * st < pn; ++st) {
+        float ka[TR_D / 16], ua;
+        load_step(st, ka, ua);
+        const int i = 4 * st + kk;
+        const float bu = i < pn ? ua * s_pw[i] : 0.f;
+#pragma unroll
+        for (int m = 0; m < TR_D / 16; ++m)
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m], bu, acc[m], 0, 0, 0);
+      }
+      const float gam = s_pgam;
+      float* wrow = p.S_out + (lb * p.Hv + hv) * static_cast<size_t>(TR_D * TR_D) +
+                    static_cast<size_t>(wave * 16 + c16) * TR_D + 4 * kk;
+#pragma unroll
+      for (int m = 0; m < TR_D / 16; ++m) {
+        sreg[m] = sreg[m] * gam + acc[m];
+        *reinterpret_cast<floatx4*>(wrow + 16 * m) = sreg[m];
+      }
+    }
+  };
+
   if (s_bad) {
     if (tid == 0 && p.dev_err) atomicOr(p.dev_err, GDN_DEV_ERR_PARENT);
+    // the previous round's replay is still owed to the state
+    if (RP && pn > 0) {
+#pragma unroll
+      for (int m = 0; m < TR_D / 16; ++m) sreg[m] = *reinterpret_cast<const floatx4*>(srow + 16 * m);
+      replay();
+    }
     return;
   }
   if (p.conv_win && l == 0 && hk == 0 && g == 0) {
@@ -269,9 +387,6 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   // 16m + 4kk .. +3, used after the conv and the Gram.  Its loads go out two
   // per conv round: issued as one burst they would stall the wave until the
   // memory pipeline had accepted them all.
-  floatx4 sreg[TR_D / 16];
-  const float* srow = p.S + (lb * p.Hv + hv) * static_cast<size_t>(TR_D * TR_D) +
-                      static_cast<size_t>(wave * 16 + c16) * TR_D + 4 * kk;
 
   // ---------------------------------------------------------- conv + SiLU --
   // 16-lane group gr handles (segment, node) items gr + 32 r; lane li holds
@@ -397,6 +512,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
         if ((rm[r] >> tc) & 1ull) dst[ro[r] + slot] = acc[r];
     }
   }
+  if (RP && pn > 0) replay();
   __syncthreads();  // (B_c) packed Gram rows, V rows
 
   // --------------- wave 0: packed Ti and M2 rows; waves 1..7: S0 [K;Q]^T --
@@ -597,10 +713,16 @@ hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s) {
   const int n_units = a.L * a.B * a.Hk;
   const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
   if (grid > 0x7fffffffLL || a.T > TR_T || a.T <= 32) return hipErrorInvalidValue;
-  if (a.K == 4)
-    hipLaunchKernelGGL((k_verify_tree<4>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_verify_tree<0>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
+  const bool rp = a.prev_n_keep != nullptr;
+  if (rp && (a.pT < 1 || a.pT > TR_T || !a.ptu || !a.ptk || !a.ptg || !a.S_out))
+    return hipErrorInvalidValue;
+  if (a.K == 4) {
+    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
+    else hipLaunchKernelGGL((k_verify_tree<4, false>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
+  } else {
+    if (rp) hipLaunchKernelGGL((k_verify_tree<0, true>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
+    else hipLaunchKernelGGL((k_verify_tree<0, false>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
+  }
   return hipGetLastError();
 }
 

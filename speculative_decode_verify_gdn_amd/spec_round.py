@@ -113,42 +113,46 @@ def fused_pays(sh: gb.GdnShape, T: int, tree: bool, device=None) -> bool:
     """Whether rounds should fold the state rollback into the next verify.
 
     The fused verify writes the replayed state back from inside the verify.
-    When the verify grid (B * Hv four-wave workgroups per layer) fits the chip
-    in about one pass, every workgroup streams its state at once and the
-    kernel is latency bound: the extra writes land on that critical path and
-    cost more than the separate rollback, a single launch over all layers
-    that streams at a much higher fraction of HBM bandwidth.  From two passes
-    of workgroups on (4 per CU) the writes overlap other workgroups' loads and
-    the fused round saves the rollback's state read.  Chains of at most 16
-    drafts only (longer ones are not fused by the library)."""
-    if tree or T > 16:
-        return False
+    When the verify grid fits the chip in about one pass, every workgroup
+    streams its state at once and the kernel is latency bound: the extra
+    writes land on that critical path and cost more than the separate
+    rollback, a single launch over all layers that streams at a much higher
+    fraction of HBM bandwidth.  From two passes of workgroups on, the writes
+    overlap other workgroups' loads and the fused round saves the rollback's
+    state read.  A pass is 4 workgroups per CU for the chain kernel (chains of
+    at most 16 drafts) and 1 for the tree kernel (trees of 33..64 nodes, bf16
+    inputs, 128-dim heads); other shapes are not fused by the library."""
     cus = torch.cuda.get_device_properties(device or torch.cuda.current_device()).multi_processor_count
-    return sh.B * sh.Hv >= 2 * 4 * cus
+    if not tree:
+        return T <= 16 and sh.B * sh.Hv >= 2 * 4 * cus
+    tree_kernel = 32 < T <= 64 and sh.dtype == torch.bfloat16 and sh.Dk == sh.Dv == 128
+    return tree_kernel and sh.B * sh.Hv >= 2 * cus
 
 
 @dataclass
 class FusedRound:
     """Rounds with each layer's state rollback folded into the next round's
-    verify of that layer (gdn_verify_chunk_replay).  Two tapes and two sets of
-    accepted lengths alternate: round r writes tape[r % 2] and n_keep[r % 2]
-    and replays tape[(r - 1) % 2] with n_keep[(r - 1) % 2].  Between rounds the
-    live state lags one accepted prefix behind; finish() applies the last one
-    with gdn_tape_rollback.  The conv window is rolled back every round (the
-    next verify reads it as its snapshot).  Several FusedRound objects over
-    different input buffers may share `tapes` and `n_keeps`.  Chains only."""
+    verify of that layer (gdn_verify_chunk_replay, gdn_tree_verify_replay).
+    Two tapes and two sets of accepted lengths (and, for trees, paths)
+    alternate: round r writes tape[r % 2] and n_keep[r % 2] and replays
+    tape[(r - 1) % 2] with n_keep[(r - 1) % 2].  Between rounds the live state
+    lags one accepted prefix behind; finish() applies the last one with
+    gdn_tape_rollback.  The conv window is rolled back every round (the next
+    verify reads it as its snapshot).  Several FusedRound objects over
+    different input buffers may share `tapes`, `n_keeps` and `paths`."""
     rb: RoundBuffers
     tapes: list = None
     n_keeps: list = None
+    paths: list = None
 
     def __post_init__(self):
         rb = self.rb
-        if rb.tree:
-            raise ValueError("the fused round takes chains")
         if self.tapes is None:
             self.tapes = [rb.tape, gb.Tape.empty(rb.sh, rb.T, rb.S.device)]
         if self.n_keeps is None:
             self.n_keeps = [rb.n_keep, torch.zeros_like(rb.n_keep)]
+        if self.paths is None:
+            self.paths = [rb.path, torch.full_like(rb.path, -1)]
 
     def verify_layers(self, r: int, stream=None, first: bool = False):
         """Every layer's verify of round r, replaying round r-1's prefix first
@@ -158,22 +162,35 @@ class FusedRound:
         for l in range(rb.sh.L):
             sl = slice(l, l + 1)
             lt = gb.Tape(tape.u[sl], tape.k[sl], tape.g[sl])
-            if first:
+            pt = gb.Tape(ptape.u[sl], ptape.k[sl], ptape.g[sl])
+            if rb.tree:
+                cw = rb.conv_win if l == 0 else None
+                args = (rb.layer_shape, rb.parent, rb.x[sl], rb.conv_state[sl], rb.conv_w[sl],
+                        rb.a[sl], rb.b[sl], rb.S[sl], rb.o[sl], lt)
+                if first:
+                    gb.gdn_tree_verify(*args, conv_win=cw, dev_err=rb.dev_err, stream=stream)
+                else:
+                    gb.gdn_tree_verify_replay(*args, pt, self.n_keeps[prev],
+                                              prev_path=self.paths[prev], conv_win=cw,
+                                              dev_err=rb.dev_err, stream=stream)
+            elif first:
                 gb.gdn_verify_chunk(rb.layer_shape, rb.x[sl], rb.conv_state[sl], rb.conv_w[sl],
                                     rb.a[sl], rb.b[sl], rb.S[sl], rb.o[sl], lt, stream=stream)
             else:
-                pt = gb.Tape(ptape.u[sl], ptape.k[sl], ptape.g[sl])
                 gb.gdn_verify_chunk_replay(rb.layer_shape, rb.x[sl], rb.conv_state[sl],
                                            rb.conv_w[sl], rb.a[sl], rb.b[sl], rb.S[sl],
                                            rb.o[sl], lt, pt, self.n_keeps[prev],
                                            dev_err=rb.dev_err, stream=stream)
 
     def accept_and_conv(self, r: int, stream=None):
-        """Greedy accept into n_keep[r % 2], then the conv-window rollback."""
-        rb, nk = self.rb, self.n_keeps[r % 2]
-        gb.spec_accept_prefix(rb.draft, rb.logits, nk, rb.path, rb.bonus, rb.workspace,
-                              dev_err=rb.dev_err, stream=stream)
-        gb.gdn_conv_state_rollback(rb.sh, rb.conv_state, rb.x, nk, win_idx=rb.win_idx,
+        """Greedy accept into n_keep[r % 2] (and path[r % 2]), then the
+        conv-window rollback."""
+        rb, nk, path = self.rb, self.n_keeps[r % 2], self.paths[r % 2]
+        gb.spec_accept_prefix(rb.draft, rb.logits, nk, path, rb.bonus, rb.workspace,
+                              parent=rb.parent if rb.tree else None, dev_err=rb.dev_err,
+                              stream=stream)
+        gb.gdn_conv_state_rollback(rb.sh, rb.conv_state, rb.x, nk,
+                                   path=path if rb.tree else None, win_idx=rb.win_idx,
                                    dev_err=rb.dev_err, stream=stream)
 
     def round(self, r: int, stream=None, first: bool = False):
@@ -185,4 +202,5 @@ class FusedRound:
         """Apply round r's accepted prefix to the state (after the last round)."""
         cur = r % 2
         gb.gdn_tape_rollback(self.rb.sh, self.rb.S, self.tapes[cur], self.n_keeps[cur],
+                             path=self.paths[cur] if self.rb.tree else None,
                              dev_err=self.rb.dev_err, stream=stream)

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gb.abi_version() == 2
+    assert gb.abi_version() == 3
     assert gb.status_string(0) == "GDN_OK"
     assert gb.status_string(1) == "GDN_ERR_INVALID_ARG"
     assert gb.status_string(4) == "GDN_ERR_WORKSPACE"
@@ -84,6 +84,16 @@ def test_host_validation_before_launch(lib):
     assert rv(4, ctypes.byref(cur), FAKE) == gb.GDN_ERR_INVALID_ARG
     assert rv(0, ctypes.byref(prev), FAKE) == gb.GDN_ERR_INVALID_ARG
     assert rv(65, ctypes.byref(prev), FAKE) == gb.GDN_ERR_UNSUPPORTED
+    # tree replay: no parent, previous tape missing or aliased, bad prev_T
+    tv = lambda par, pT, pt, pn: lib.gdn_tree_verify_replay(
+        ctypes.byref(_shape()), 40, par, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        ctypes.byref(cur), None, pT, pt, None, pn, None, None)
+    assert tv(None, 40, ctypes.byref(prev), FAKE) == gb.GDN_ERR_INVALID_ARG
+    assert tv(FAKE, 40, None, FAKE) == gb.GDN_ERR_INVALID_ARG
+    assert tv(FAKE, 40, ctypes.byref(prev), None) == gb.GDN_ERR_INVALID_ARG
+    assert tv(FAKE, 40, ctypes.byref(cur), FAKE) == gb.GDN_ERR_INVALID_ARG
+    assert tv(FAKE, 0, ctypes.byref(prev), FAKE) == gb.GDN_ERR_INVALID_ARG
+    assert tv(FAKE, 65, ctypes.byref(prev), FAKE) == gb.GDN_ERR_UNSUPPORTED
     tape = gb._CTape(FAKE.value, FAKE.value, None)
     assert lib.gdn_tape_rollback(ctypes.byref(_shape()), 4, FAKE, ctypes.byref(tape), None, FAKE,
                                  None, None) == gb.GDN_ERR_INVALID_ARG

@@ -292,6 +292,92 @@ def test_fused_replay_rounds(cfg_id, L, B, rounds, forced):
     assert int(fr.rb.dev_err.item()) == 0
 
 
+@pytest.mark.parametrize("L,B,rounds,T", [(2, 3, 4, 64), (1, 2, 3, 40), (1, 2, 3, 24)])
+def test_fused_replay_tree_rounds(L, B, rounds, T):
+    """Tree rounds with the rollback folded into the next verify
+    (gdn_tree_verify_replay) give the oracle's plain tree rounds every round
+    and after finish(); T = 24 runs the library's two-call form."""
+    _need_gpu()
+    cfg = W.CONFIGS[5].with_(L=L, B=B, T=T, V=311)
+    inp0 = W.layer_inputs(cfg, 0, "cpu")
+    oS, ocs = W.to_f64(inp0["S0"]), W.to_f64(inp0["conv_state"])
+    fr = None
+    for r in range(rounds):
+        inp = W.layer_inputs(cfg, r, "cpu")
+        acc = W.tree_accept_inputs(cfg, r, "cpu")
+        d = {k: v.to(DEV) for k, v in inp.items()}
+        da = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in acc.items()}
+        if fr is None:
+            d["S0"], d["conv_state"] = inp0["S0"].to(DEV), inp0["conv_state"].to(DEV)
+            fr = spec_round.FusedRound(make_buffers(cfg, d, da))
+        else:
+            rb = fr.rb
+            rb.x, rb.a, rb.b, rb.conv_w = d["x"], d["a"], d["b"], d["conv_w"]
+            rb.logits, rb.draft, rb.parent = da["logits"], da["draft"], da["parent"]
+        fr.round(r, first=(r == 0))
+        torch.cuda.synchronize()
+        f = {k: W.to_f64(v) for k, v in inp.items()}
+        f["S0"], f["conv_state"] = oS, ocs
+        ref = oracle_round(cfg, f, acc["draft"].numpy(), W.to_f64(acc["logits"]),
+                           parent=acc["parent"].numpy())
+        tape = fr.tapes[r % 2]
+        np.testing.assert_array_equal(fr.n_keeps[r % 2].cpu().numpy(), ref["n_keep"])
+        np.testing.assert_array_equal(fr.paths[r % 2].cpu().numpy(), ref["path"])
+        np.testing.assert_array_equal(fr.rb.bonus.cpu().numpy(), ref["bonus"])
+        np.testing.assert_array_equal(fr.rb.conv_win.cpu().numpy(), ref["conv_win"])
+        np.testing.assert_array_equal(fr.rb.conv_state.cpu().double().numpy(), ref["cs_new"])
+        for name, got, want in (("o", fr.rb.o, ref["o"]), ("u", tape.u, ref["u"]),
+                                ("k", tape.k, ref["k"])):
+            err = rel_fro(got.cpu().double().numpy(), want)
+            assert err <= 1e-4, (r, name, err)
+        np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
+        oS, ocs = ref["S_new"], ref["cs_new"]
+    fr.finish(rounds - 1)
+    torch.cuda.synchronize()
+    assert rel_fro(fr.rb.S.cpu().double().numpy(), oS) <= 1e-4
+    assert int(fr.rb.dev_err.item()) == 0
+
+
+def test_fused_tree_replay_bad_inputs_flag():
+    """A previous path entry outside [0, prev_T) sets GDN_DEV_ERR_PATH and the
+    sequence is verified from its state unchanged; a malformed parent array
+    sets GDN_DEV_ERR_PARENT and the replay is still applied."""
+    _need_gpu()
+    cfg = W.CONFIGS[5].with_(L=1, B=2, T=40, V=97)
+    inp = W.layer_inputs(cfg, 0, "cpu")
+    acc = W.tree_accept_inputs(cfg, 0, "cpu")
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    sh = gshape(cfg)
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    prev = gb.Tape.empty(sh, cfg.T, DEV)
+    for t in (prev.u, prev.k):
+        t.copy_(torch.randn(t.shape, generator=gen).to(DEV) * 0.1)
+    prev.g.fill_(0.9)
+    pn = torch.tensor([3, 2], dtype=torch.int32, device=DEV)
+    ppath = torch.full((2, cfg.T), -1, dtype=torch.int32, device=DEV)
+    ppath[0, :3] = torch.tensor([0, 5, 9], dtype=torch.int32)
+    ppath[1, :2] = torch.tensor([1, cfg.T], dtype=torch.int32)  # out of range
+    parent = acc["parent"].clone()
+    parent[0, 7] = 7  # not an earlier node: malformed
+    o = torch.empty((1, 2, cfg.T, cfg.Hv, cfg.Dv), device=DEV)
+    cur = gb.Tape.empty(sh, cfg.T, DEV)
+    err = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    S = d["S0"].clone()
+    gb.gdn_tree_verify_replay(sh, parent.to(DEV), d["x"], d["conv_state"], d["conv_w"], d["a"],
+                              d["b"], S, o, cur, prev, pn, prev_path=ppath, dev_err=err)
+    torch.cuda.synchronize()
+    e = int(err.item())
+    assert e & gb.DEV_ERR_PATH and e & gb.DEV_ERR_PARENT
+    # sequence 1: bad path, state unchanged
+    assert torch.equal(S[:, 1], d["S0"][:, 1])
+    # sequence 0: replayed exactly as the standalone rollback does it
+    S_ref = d["S0"].clone()
+    gb.gdn_tape_rollback(sh, S_ref, prev, torch.tensor([3, 0], dtype=torch.int32, device=DEV),
+                         path=ppath.clamp(0, cfg.T - 1))
+    torch.cuda.synchronize()
+    assert rel_fro(S[:, 0].cpu().double().numpy(), S_ref[:, 0].cpu().double().numpy()) <= 1e-5
+
+
 def test_fused_replay_bad_prev_n_keep_flags():
     """An accepted length outside [0, prev_T] sets GDN_DEV_ERR_N_KEEP and
     that sequence is verified from its state unchanged."""
