@@ -18,6 +18,10 @@ Parity status of each function (the pins live in ``tests/test_oracle_*.py``):
   tree_verify             pinned: chain parents == verify_chunk; every node ==
                           verify_chunk along its root path.
   accept                  pinned: brute-force enumeration of prefixes / paths.
+  accept_sample           pinned: the first output token's distribution equals
+                          p exactly (quadrature over the uniforms), the
+                          low-temperature limit equals the greedy accept,
+                          hand-computed cases, uniform extremes.
   tape_rollback           pinned: replay(n) == fresh recompute over n tokens,
                           closed-form rank-n sum, n=0 identity.
   conv_rollback           pinned: numpy concatenation of the accepted rows;
@@ -278,3 +282,72 @@ def conv_rollback(sh: Shape, conv_state, x, n_keep, path=None):
     _check(_load().oracle_conv_rollback(ctypes.byref(c), T, _p(cs), _p(x), _p(path),
                                         _p(n_keep), _p(win)), "conv_rollback")
     return cs, win
+
+
+def _softmax64(z: np.ndarray) -> np.ndarray:
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def sample_cdf(logits_row, temperature: float, ban: int = -1) -> np.ndarray:
+    """Cumulative mass, in index order, of softmax(logits_row / temperature)
+    with token `ban` (if >= 0) set to zero; not renormalised."""
+    q = _softmax64(_f64(logits_row) / float(temperature))
+    if ban >= 0:
+        q[ban] = 0.0
+    return np.cumsum(q)
+
+
+def accept_sample(draft, logits, temperature: float, uniforms, detail: bool = False):
+    """Rejection-sampling acceptance of a deterministic draft chain.
+
+    colibri "MTP speculative decoding and prefetch" s5: the draft is a point
+    mass, so draft token d at position j is kept with probability p_j(d),
+    where p_j = softmax(logits[j] / temperature); at the first rejection the
+    output token is drawn from p_j with d removed and the rest renormalised
+    (which keeps the output distribution exactly p); if every draft is kept,
+    the output token is drawn from p_T.
+
+    draft (B, T) int, logits (B, T+1, V), temperature > 0, uniforms (B, T+1)
+    in [0, 1): uniforms[b, j] decides draft j (kept iff u < p_j(d)),
+    uniforms[b, T] draws the output token as the smallest index i whose
+    cumulative mass (index order, removed token counting zero) exceeds u
+    times the total remaining mass.  A draft token outside [0, V) is never
+    kept and removes nothing.  All arithmetic in float64.
+
+    Returns (n_keep (B,), path (B, T) -1 padded, token (B,)); with
+    detail=True also p_draft (B, T), the probability of each draft token
+    (NaN past the first rejection)."""
+    draft = _i32(draft)
+    B, T = draft.shape
+    logits = _f64(logits)
+    V = logits.shape[2]
+    u = _f64(uniforms, (B, T + 1))
+    tau = float(temperature)
+    if not tau > 0.0:
+        raise ValueError("temperature must be > 0")
+    n_keep = np.zeros(B, dtype=np.int32)
+    path = np.full((B, T), -1, dtype=np.int32)
+    token = np.zeros(B, dtype=np.int32)
+    p_draft = np.full((B, T), np.nan)
+    for b in range(B):
+        n = T
+        for j in range(T):
+            d = int(draft[b, j])
+            pd = _softmax64(logits[b, j] / tau)[d] if 0 <= d < V else 0.0
+            p_draft[b, j] = pd
+            if not u[b, j] < pd:
+                n = j
+                break
+        ban = int(draft[b, n]) if n < T and 0 <= draft[b, n] < V else -1
+        c = sample_cdf(logits[b, n], tau, ban)
+        i = int(np.searchsorted(c, u[b, T] * c[-1], side="right"))
+        if i >= V:  # no index passes the threshold: the last one with mass
+            q = np.diff(np.concatenate([[0.0], c]))
+            i = int(np.flatnonzero(q > 0)[-1])
+        n_keep[b] = n
+        path[b, :n] = np.arange(n)
+        token[b] = i
+    if detail:
+        return n_keep, path, token, p_draft
+    return n_keep, path, token
