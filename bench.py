@@ -179,6 +179,55 @@ def fused_pass(cfg, rbs, shared, stream, steps, warmup, eager):
             "n_keep": n_hist.cpu().numpy(), "n_prev": p_hist.cpu().numpy()}
 
 
+def sample_accept_pass(cfg, rb, stream, reps, oracle_seqs=2):
+    """Rejection-sampling acceptance (spec_accept_sample, temperature 1) on
+    the round's logits and drafts with seeded uniforms: mean time per call of
+    a replayed graph, its algorithmic bytes (every logits row read once, the
+    drawn chunk re-read, partials written and read), and the fp64 oracle's
+    time on `oracle_seqs` sequences scaled to the batch."""
+    from speculative_decode_verify_gdn_amd import binding as gb
+    B, T, V = cfg.B, cfg.T, cfg.V
+    dev = rb.S.device
+    gen = torch.Generator(device=dev).manual_seed(cfg.seed ^ 0x5A)
+    uni = torch.rand((B, T + 1), device=dev, generator=gen)
+    i32 = dict(device=dev, dtype=torch.int32)
+    n, path, tok = torch.empty((B,), **i32), torch.empty((B, T), **i32), torch.empty((B,), **i32)
+    ws = torch.empty((gb.spec_sample_workspace_bytes(B, T, V),), device=dev, dtype=torch.uint8)
+    call = lambda: gb.spec_accept_sample(rb.draft, rb.logits, 1.0, uni, n, path, tok, ws,
+                                         dev_err=rb.dev_err)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        call()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            call()
+        g.replay()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    esz = 2 if rb.logits.dtype == torch.bfloat16 else 4
+    split = (V + 4095) // 4096
+    byts = B * (T + 1) * V * esz + B * 4096 * esz + 2 * B * (T + 1) * split * 8 \
+        + B * T * (4 + esz) + B * (T + 1) * 4 + B * (T + 2) * 4
+    import oracle
+    k = min(oracle_seqs, B)
+    lg = rb.logits[:k].double().cpu().numpy()
+    dr = rb.draft[:k].cpu().numpy()
+    un = uni[:k].double().cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.accept_sample(dr, lg, 1.0, un)
+    o_us = (time.perf_counter() - t0) * 1e6 * B / k
+    gbs = byts / (us * 1e-6) / 1e9
+    return {"us_per_round": us, "algorithmic_bytes": byts, "achieved_GBps": gbs,
+            "frac": gbs / HBM_PEAK_GBS, "mean_kept": float(n.float().mean().item()),
+            "oracle_us_per_round": o_us, "oracle_sample_sequences": k, "temperature": 1.0}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -485,6 +534,10 @@ def main():
     if fusable:
         fused = fused_pass(cfg, rbs, shared, stream, args.steps, args.warmup, args.eager)
 
+    sampled = None
+    if not cfg.is_tree:
+        sampled = sample_accept_pass(cfg, rbs[0], stream, args.steps)
+
     sweep = None
     if args.sweep_n and not cfg.is_tree:
         with torch.cuda.stream(stream):
@@ -553,6 +606,8 @@ def main():
                        "verify_bytes_per_launch": v["roofline"]["bytes_per_launch"],
                        "verify_roofline_frac": v["roofline"]["frac"]} for k, v in rounds.items()},
     }
+    if sampled is not None:
+        out["sample_accept"] = sampled
     if sweep is not None:
         out["rollback_sweep"] = sweep
     if not args.no_cpu_baseline:

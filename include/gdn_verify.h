@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
   GDN_OK = 0,
@@ -71,6 +71,7 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 #define GDN_DEV_ERR_N_KEEP 1 /* n_keep[b] outside [0, T] */
 #define GDN_DEV_ERR_PARENT 2 /* parent[b][v] outside [-1, v-1] */
 #define GDN_DEV_ERR_PATH 4   /* path entry outside [0, T) or not a child of the previous */
+#define GDN_DEV_ERR_TOKEN 8  /* draft token outside [0, V) (sampling acceptance) */
 
 typedef struct {
   int32_t n_layers;    /* L: leading dimension of every per-layer tensor */
@@ -215,6 +216,37 @@ gdn_status spec_accept_prefix(int32_t B, int32_t T, int32_t V, const int32_t* pa
 
 /* Bytes of device workspace spec_accept_prefix needs for (B, T, V). */
 size_t spec_accept_workspace_bytes(int32_t B, int32_t T, int32_t V);
+
+/*
+ * Rejection-sampling acceptance of a draft chain (sampling at temperature
+ * > 0; the greedy rule is spec_accept_prefix).  The draft is a point mass, so
+ * with p_j = softmax(logits[b][j] / temperature):
+ *   draft j is kept while uniforms[b][j] < p_j(draft[b][j]) (in order);
+ *   n_keep[b] = n, the first rejected position (T if none);
+ *   token[b] is drawn from p_n with draft[b][n] removed and renormalised
+ *   (n < T), or from p_T (n = T): the smallest index i whose cumulative mass
+ *   in index order (the removed token counting zero) exceeds
+ *   uniforms[b][T] times the total remaining mass.
+ * The output tokens are then distributed exactly as the target's p.
+ *   draft    [B,T] int32;  logits [B,T+1,V] (logits_dtype, finite values)
+ *   uniforms [B,T+1] fp32 in [0, 1), caller-drawn
+ *   n_keep [B], path [B,T] (0..n-1, then -1), token [B] int32 outputs
+ *   workspace: device scratch of at least spec_sample_workspace_bytes(B,T,V)
+ * temperature must be finite and > 0.  A draft token outside [0, V) is never
+ * kept, removes nothing and sets GDN_DEV_ERR_TOKEN.  Decisions and draws are
+ * taken in fp32 (softmax statistics from per-chunk partials), so a uniform
+ * within rounding distance of a threshold may fall either way.
+ * Source: colibri "MTP speculative decoding and prefetch" s5 (rejection
+ * sampling keeps speculation lossless under sampling).
+ */
+gdn_status spec_accept_sample(int32_t B, int32_t T, int32_t V, const int32_t* draft,
+                              const void* logits, int32_t logits_dtype, float temperature,
+                              const float* uniforms, int32_t* n_keep, int32_t* path,
+                              int32_t* token, void* workspace, size_t workspace_bytes,
+                              int32_t* dev_err, void* stream);
+
+/* Bytes of device workspace spec_accept_sample needs for (B, T, V). */
+size_t spec_sample_workspace_bytes(int32_t B, int32_t T, int32_t V);
 
 /*
  * Tape-replay rollback of L layers at once: S holds the pre-verify snapshot

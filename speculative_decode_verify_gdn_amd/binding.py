@@ -20,10 +20,11 @@ LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH, GDN_ERR_WORKSPACE = range(5)
 GDN_F32, GDN_BF16 = 0, 1
-DEV_ERR_N_KEEP, DEV_ERR_PARENT, DEV_ERR_PATH = 1, 2, 4
+DEV_ERR_N_KEEP, DEV_ERR_PARENT, DEV_ERR_PATH, DEV_ERR_TOKEN = 1, 2, 4, 8
 
 EXPORTS = ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
-           "gdn_tree_verify_replay", "spec_accept_prefix",
+           "gdn_tree_verify_replay", "spec_accept_prefix", "spec_accept_sample",
+           "spec_sample_workspace_bytes",
            "spec_accept_workspace_bytes", "gdn_tape_rollback", "gdn_conv_state_rollback",
            "gdn_status_string", "gdn_abi_version")
 
@@ -93,13 +94,17 @@ def lib() -> ctypes.CDLL:
         L.spec_accept_prefix.argtypes = [I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P, P]
         L.spec_accept_workspace_bytes.argtypes = [I32, I32, I32]
         L.spec_accept_workspace_bytes.restype = SZ
+        L.spec_accept_sample.argtypes = [I32, I32, I32, P, P, I32, ctypes.c_float, P, P, P, P, P,
+                                         SZ, P, P]
+        L.spec_sample_workspace_bytes.argtypes = [I32, I32, I32]
+        L.spec_sample_workspace_bytes.restype = SZ
         L.gdn_tape_rollback.argtypes = [SP, I32, P, TP, P, P, P, P]
         L.gdn_conv_state_rollback.argtypes = [SP, I32, P, P, P, P, P, P, P]
         L.gdn_status_string.argtypes = [I32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
         for name in ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
-                     "gdn_tree_verify_replay", "spec_accept_prefix",
+                     "gdn_tree_verify_replay", "spec_accept_prefix", "spec_accept_sample",
                      "gdn_tape_rollback", "gdn_conv_state_rollback", "gdn_abi_version"):
             getattr(L, name).restype = I32
         _lib = L
@@ -277,6 +282,38 @@ def spec_accept_prefix(draft, logits, n_keep, path, bonus, workspace, parent=Non
                                     GDN_BF16 if logits.dtype == torch.bfloat16 else GDN_F32,
                                     *args, workspace.data_ptr(), workspace.numel(), de,
                                     _stream(stream)), "spec_accept_prefix")
+
+
+def spec_sample_workspace_bytes(B: int, T: int, V: int) -> int:
+    return int(lib().spec_sample_workspace_bytes(B, T, V))
+
+
+def spec_accept_sample(draft, logits, temperature: float, uniforms, n_keep, path, token,
+                       workspace, dev_err=None, stream=None):
+    """Rejection-sampling acceptance of a draft chain at temperature > 0
+    (uniforms [B, T+1] fp32 in [0, 1)); outputs stay on the device."""
+    B, T = int(draft.shape[0]), int(draft.shape[1])
+    V = int(logits.shape[-1])
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("logits must be float32 or bfloat16")
+    lp = _need(logits, "logits", logits.dtype, (B, T + 1, V))
+    dp = _need(draft, "draft", torch.int32, (B, T), 4)
+    up = _need(uniforms, "uniforms", torch.float32, (B, T + 1), 4)
+    need = spec_sample_workspace_bytes(B, T, V)
+    if (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8
+            or workspace.numel() < need or not workspace.is_cuda
+            or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a device uint8 tensor of >= %d bytes" % need)
+    args = [_need(n_keep, "n_keep", torch.int32, (B,), 4),
+            _need(path, "path", torch.int32, (B, T), 4),
+            _need(token, "token", torch.int32, (B,), 4)]
+    de = _opt(dev_err, "dev_err", torch.int32, (1,))
+    _dev(draft.device, logits, uniforms, n_keep, path, token, workspace, dev_err)
+    _check(lib().spec_accept_sample(B, T, V, dp, lp,
+                                    GDN_BF16 if logits.dtype == torch.bfloat16 else GDN_F32,
+                                    float(temperature), up, *args, workspace.data_ptr(),
+                                    workspace.numel(), de, _stream(stream)),
+           "spec_accept_sample")
 
 
 def gdn_tape_rollback(sh: GdnShape, S, tape: Tape, n_keep, path=None, dev_err=None, stream=None):

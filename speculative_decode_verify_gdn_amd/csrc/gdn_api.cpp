@@ -5,6 +5,7 @@
 // before anything is launched; device-detected data errors go to *dev_err.
 // Nothing here allocates, synchronises or keeps state between calls.
 
+#include <cmath>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -185,6 +186,43 @@ gdn_status gdn_tree_verify_replay(const gdn_shape* shape, int32_t T, const int32
   if (st != GDN_OK) return st;
   return gdn_tree_verify(shape, T, parent, x, conv_state, conv_w, a, b, S, o, tape, conv_win,
                          dev_err, stream);
+}
+
+size_t spec_sample_workspace_bytes(int32_t B, int32_t T, int32_t V) {
+  if (B < 1 || T < 1 || V < 1 || T > kMaxT) return 0;
+  const size_t parts = static_cast<size_t>(B) * (T + 1) * gdn::sample_split(V);
+  return (parts * sizeof(float) + 255) / 256 * 256 * 2;
+}
+
+gdn_status spec_accept_sample(int32_t B, int32_t T, int32_t V, const int32_t* draft,
+                              const void* logits, int32_t logits_dtype, float temperature,
+                              const float* uniforms, int32_t* n_keep, int32_t* path,
+                              int32_t* token, void* workspace, size_t workspace_bytes,
+                              int32_t* dev_err, void* stream) {
+  if (B < 1 || T < 1 || V < 1) return GDN_ERR_INVALID_ARG;
+  if (logits_dtype != GDN_F32 && logits_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (!draft || !logits || !uniforms || !n_keep || !path || !token) return GDN_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !std::isfinite(temperature) || !std::isfinite(1.f / temperature))
+    return GDN_ERR_INVALID_ARG;
+  if (T > kMaxT) return GDN_ERR_UNSUPPORTED;
+  const size_t need = spec_sample_workspace_bytes(B, T, V);
+  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  gdn::SampleArgs a{};
+  a.logits = logits;
+  a.draft = draft;
+  a.uniforms = uniforms;
+  a.n_keep = n_keep;
+  a.path = path;
+  a.token = token;
+  a.dev_err = dev_err;
+  a.B = B;
+  a.T = T;
+  a.V = V;
+  a.split = gdn::sample_split(V);
+  a.inv_tau = 1.f / temperature;
+  a.part_m = static_cast<float*>(workspace);
+  a.part_s = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
+  return launch_status(gdn::launch_sample(a, logits_dtype, static_cast<hipStream_t>(stream)));
 }
 
 size_t spec_accept_workspace_bytes(int32_t B, int32_t T, int32_t V) {

@@ -78,6 +78,24 @@ struct AcceptArgs {
   int B, T, V, split, chunk;
 };
 
+// Rejection-sampling acceptance of a point-mass draft chain.
+constexpr int kSampleChunk = 4096;  // logits elements per partial (256 threads x 16)
+struct SampleArgs {
+  const void* logits;      // [B, T+1, V]
+  const int32_t* draft;    // [B, T]
+  const float* uniforms;   // [B, T+1]
+  int32_t* n_keep;
+  int32_t* path;
+  int32_t* token;
+  int32_t* dev_err;
+  float* part_m;  // [rows, split] chunk max of logit / temperature
+  float* part_s;  // [rows, split] chunk sum of exp(z - max)
+  int B, T, V, split;
+  float inv_tau;
+};
+int sample_split(int V);
+hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t s);
+
 // Each returns hipErrorInvalidValue for an uninstantiated combination, else
 // the launch status.  dtype: 0 fp32, 1 bf16.
 hipError_t launch_verify_wy(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gb.abi_version() == 3
+    assert gb.abi_version() == 4
     assert gb.status_string(0) == "GDN_OK"
     assert gb.status_string(1) == "GDN_ERR_INVALID_ARG"
     assert gb.status_string(4) == "GDN_ERR_WORKSPACE"
@@ -102,6 +102,21 @@ def test_host_validation_before_launch(lib):
     assert lib.gdn_tree_verify(ctypes.byref(_shape()), 4, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                FAKE, FAKE, ctypes.byref(gb._CTape(1, 1, 1)), None, None,
                                None) == gb.GDN_ERR_INVALID_ARG
+    # sampling accept: bad temperature, missing uniforms, short workspace
+    sa = lambda T, tau, uni, ws, wsb: lib.spec_accept_sample(
+        2, T, 100, FAKE, FAKE, gb.GDN_BF16, tau, uni, FAKE, FAKE, FAKE, ws, wsb, None, None)
+    big = 1 << 24
+    assert sa(4, 0.0, FAKE, FAKE, big) == gb.GDN_ERR_INVALID_ARG
+    assert sa(4, -1.0, FAKE, FAKE, big) == gb.GDN_ERR_INVALID_ARG
+    assert sa(4, float("inf"), FAKE, FAKE, big) == gb.GDN_ERR_INVALID_ARG
+    assert sa(4, float("nan"), FAKE, FAKE, big) == gb.GDN_ERR_INVALID_ARG
+    assert sa(4, 1e-40, FAKE, FAKE, big) == gb.GDN_ERR_INVALID_ARG  # 1/temperature overflows
+    assert sa(4, 1.0, None, FAKE, big) == gb.GDN_ERR_INVALID_ARG
+    assert sa(65, 1.0, FAKE, FAKE, big) == gb.GDN_ERR_UNSUPPORTED
+    assert sa(4, 1.0, FAKE, FAKE, 8) == gb.GDN_ERR_WORKSPACE
+    assert sa(4, 1.0, FAKE, None, big) == gb.GDN_ERR_WORKSPACE
+    assert gb.spec_sample_workspace_bytes(32, 8, 151936) >= 32 * 9 * 38 * 8
+    assert gb.spec_sample_workspace_bytes(1, 65, 100) == 0
     # accept: missing / short workspace, bad dtype
     assert lib.spec_accept_prefix(2, 4, 100, None, FAKE, FAKE, gb.GDN_BF16, FAKE, FAKE, FAKE,
                                   FAKE, 8, None, None) == gb.GDN_ERR_WORKSPACE

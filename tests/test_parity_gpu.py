@@ -522,3 +522,104 @@ def test_full_size_sampled(cfg_id):
     compare(got, ref, tree=cfg.is_tree)
     del rb, inp, acc
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------- sampling accept --
+
+def _sample_inputs(B, T, V, tau, dtype, seed, p_lo=0.05, p_hi=0.95):
+    """Logits N(0, 1) with each draft token's logit set so that its
+    probability lands near a uniform draw in [p_lo, p_hi] (bf16 rounding
+    moves it slightly); seeded uniforms in [0, 1)."""
+    rng = np.random.default_rng(seed)
+    logits = rng.normal(size=(B, T + 1, V))
+    draft = rng.integers(0, V, size=(B, T))
+    for b in range(B):
+        for j in range(T):
+            z = logits[b, j] / tau
+            z_others = np.delete(z, draft[b, j])
+            lse = z_others.max() + np.log(np.exp(z_others - z_others.max()).sum())
+            p = rng.uniform(p_lo, p_hi)
+            logits[b, j, draft[b, j]] = (lse + np.log(p / (1 - p))) * tau
+    lt = torch.from_numpy(logits).to(dtype)
+    uni = torch.from_numpy(rng.uniform(size=(B, T + 1))).float()
+    return draft.astype(np.int32), lt, uni
+
+
+def _run_sample(draft, lt, uni, tau):
+    B, T = draft.shape
+    V = lt.shape[-1]
+    dev = dict(device=DEV, dtype=torch.int32)
+    n = torch.empty((B,), **dev)
+    path = torch.empty((B, T), **dev)
+    tok = torch.empty((B,), **dev)
+    err = torch.zeros((1,), **dev)
+    ws = torch.empty((gb.spec_sample_workspace_bytes(B, T, V),), device=DEV, dtype=torch.uint8)
+    gb.spec_accept_sample(torch.from_numpy(draft).to(DEV), lt.to(DEV), tau, uni.to(DEV), n, path,
+                          tok, ws, dev_err=err)
+    torch.cuda.synchronize()
+    return n.cpu().numpy(), path.cpu().numpy(), tok.cpu().numpy(), int(err.item())
+
+
+def _check_sample(draft, lt, uni, tau, n_g, path_g, tok_g, margin=1e-5):
+    """Exact agreement with the fp64 oracle, except where a uniform lies within
+    `margin` of the threshold it is compared with (fp32 vs fp64 statistics):
+    there the GPU's choice must still be a valid one.  Returns the number of
+    such near-threshold sequences."""
+    lg = lt.double().numpy()
+    u = uni.double().numpy()
+    B, T = draft.shape
+    n_o, path_o, tok_o, pd = oracle.accept_sample(draft, lg, tau, u, detail=True)
+    near = 0
+    for b in range(B):
+        if n_g[b] != n_o[b]:
+            j = min(n_g[b], n_o[b])
+            assert abs(u[b, j] - pd[b, j]) < margin, (b, j, u[b, j], pd[b, j], n_g[b], n_o[b])
+            near += 1
+            continue
+        np.testing.assert_array_equal(path_g[b], path_o[b])
+        if tok_g[b] != tok_o[b]:
+            n = n_g[b]
+            ban = int(draft[b, n]) if n < T and 0 <= draft[b, n] < lg.shape[-1] else -1
+            c = oracle.sample_cdf(lg[b, n], tau, ban)
+            target, tol, i = u[b, T] * c[-1], margin * c[-1], int(tok_g[b])
+            assert i != ban and c[i] > target - tol and (i == 0 or c[i - 1] <= target + tol), \
+                (b, i, int(tok_o[b]), target, c[max(i - 1, 0)], c[i])
+            near += 1
+    return near
+
+
+@pytest.mark.parametrize("B,T,V,tau,dtype", [
+    (3, 4, 7, 1.0, torch.float32), (32, 8, 151936, 1.0, torch.bfloat16),
+    (5, 16, 1001, 0.5, torch.bfloat16), (4, 1, 4100, 2.0, torch.float32),
+    (2, 64, 9000, 0.8, torch.bfloat16), (6, 5, 151936, 1.3, torch.float32),
+    (64, 3, 8192, 1.0, torch.bfloat16)])
+def test_sample_accept_matches_oracle(B, T, V, tau, dtype):
+    _need_gpu()
+    draft, lt, uni = _sample_inputs(B, T, V, tau, dtype, seed=B * 1000 + T * 10 + V % 97)
+    n_g, path_g, tok_g, err = _run_sample(draft, lt, uni, tau)
+    assert err == 0
+    near = _check_sample(draft, lt, uni, tau, n_g, path_g, tok_g)
+    assert near <= max(1, B // 50)
+
+
+def test_sample_accept_extremes_and_bad_tokens():
+    """Uniforms of zero keep every draft and draw from the last row; a token
+    outside [0, V) is never kept and flags GDN_DEV_ERR_TOKEN; uniforms near
+    one reject the first draft and draw high indices."""
+    _need_gpu()
+    B, T, V, tau = 8, 6, 5000, 1.0
+    draft, lt, uni = _sample_inputs(B, T, V, tau, torch.bfloat16, seed=77)
+    zero = torch.zeros_like(uni)
+    n_g, path_g, tok_g, err = _run_sample(draft, lt, zero, tau)
+    assert err == 0 and (n_g == T).all()
+    _check_sample(draft, lt, zero, tau, n_g, path_g, tok_g)
+    bad = draft.copy()
+    bad[:, 3] = V + 5
+    bad[1, 3] = -2
+    n_g, path_g, tok_g, err = _run_sample(bad, lt, zero, tau)
+    assert err & gb.DEV_ERR_TOKEN and (n_g == 3).all()
+    _check_sample(bad, lt, zero, tau, n_g, path_g, tok_g)
+    high = torch.full_like(uni, 0.999999)
+    n_g, path_g, tok_g, err = _run_sample(draft, lt, high, tau)
+    assert (n_g == 0).all()
+    _check_sample(draft, lt, high, tau, n_g, path_g, tok_g)
