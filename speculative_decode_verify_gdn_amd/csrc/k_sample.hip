@@ -10,9 +10,9 @@
 // remaining total mass.  Uniforms are inputs.
 //
 // Two launches.  (1) k_softmax_part: every logits row is cut into chunks of
-// kSampleChunk elements; a workgroup streams one chunk in 16-byte loads and
-// keeps an online (max, sum of exp(z - max)) per thread, z = logit /
-// temperature, then reduces them.  (2) k_sample_walk: one workgroup per
+// kSampleChunk elements; a wave streams one chunk in 16-byte loads and keeps
+// an online (max, sum of exp(z - max)) per lane, z = logit / temperature,
+// then reduces them.  (2) k_sample_walk: one workgroup per
 // sequence merges each row's partials into (m, Z), takes the acceptance
 // decisions, scans the chunk masses of the output row (the removed token
 // subtracted) to find the chunk where the cumulative mass crosses the
@@ -20,6 +20,8 @@
 // elements in order, a block scan finds the thread whose range holds the
 // crossing, and that thread walks its 16 elements in the same order, so the
 // two levels agree on every partial sum.  Logits must be finite.
+
+#include <algorithm>
 
 #include "gdn_common.hpp"
 #include "gdn_kernels.hpp"
@@ -52,61 +54,76 @@ __device__ __forceinline__ float logit(const SampleArgs& p, size_t row, int i) {
                   : ld_in(static_cast<const float*>(p.logits) + row * p.V, i);
 }
 
+// One wave per chunk: lane l takes 16-byte vectors l, l + 64, ... of its
+// chunk (all loads in flight at once), then the wave reduces.  Waves stride
+// over the (row, chunk) pairs of the whole batch, so the grid stays a few
+// thousand workgroups however many chunks there are.
 template <int ESZ>
 __global__ __launch_bounds__(kNT) void k_softmax_part(SampleArgs p) {
-  constexpr int EPV = 16 / ESZ;  // elements per 16-byte vector
-  __shared__ float s_m[kNT / kWave], s_s[kNT / kWave];
-  const int tid = threadIdx.x;
-  const int part = blockIdx.x % p.split;
-  const size_t row = blockIdx.x / p.split;
-  const int beg = part * kSampleChunk;
-  const int end = min(beg + kSampleChunk, p.V);
+  constexpr int EPV = 16 / ESZ;                           // elements per 16-byte vector
+  constexpr int VPL = kSampleChunk / EPV / kWave;         // vectors per lane per chunk
+  constexpr int NWV = kNT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
   const float it = p.inv_tau;
-  float m = -__builtin_inff(), s = 0.f;
+  const float c = it * 1.44269504088896341f;  // exp(z - m) = exp2(x c - mx c), z = x / tau
   const size_t V = p.V;
-  if (((V * ESZ) % 16) == 0) {
-    // chunk starts are multiples of 8 elements, so vectors stay aligned
-    const uint4* vp = reinterpret_cast<const uint4*>(static_cast<const char*>(p.logits) + row * V * ESZ);
-    const int vbeg = beg / EPV, vend = end / EPV;
-    for (int q = vbeg + tid; q < vend; q += kNT) {
-      const uint4 w = vp[q];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      float z[EPV];
+  const long long total = static_cast<long long>(p.B) * (p.T + 1) * p.split;
+  const bool vec = ((V * ESZ) % 16) == 0;
+  for (long long q = static_cast<long long>(blockIdx.x) * NWV + wave; q < total;
+       q += static_cast<long long>(gridDim.x) * NWV) {
+    const size_t row = q / p.split;
+    const int part = static_cast<int>(q % p.split);
+    const int beg = part * kSampleChunk;
+    const int end = min(beg + kSampleChunk, p.V);
+    float m = -__builtin_inff(), s = 0.f;
+    if (vec) {
+      // chunk starts are multiples of 8 elements, so vectors stay aligned;
+      // the running max mx is kept in logit units
+      const uint4* vp = reinterpret_cast<const uint4*>(static_cast<const char*>(p.logits) + row * V * ESZ);
+      const int vbeg = beg / EPV, vend = end / EPV;
+      uint4 w[VPL];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        if (ESZ == 2) {
-          z[2 * h] = __uint_as_float(ws[h] << 16) * it;
-          z[2 * h + 1] = __uint_as_float(ws[h] & 0xffff0000u) * it;
-        } else {
-          z[h] = __uint_as_float(ws[h]) * it;
+      for (int k = 0; k < VPL; ++k) {
+        const int v = vbeg + lane + k * kWave;
+        w[k] = vp[v < vend ? v : vbeg];
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) {
+        if (vbeg + lane + k * kWave >= vend) continue;
+        const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+        float x[EPV];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          if (ESZ == 2) {
+            x[2 * h] = __uint_as_float(ws[h] << 16);
+            x[2 * h + 1] = __uint_as_float(ws[h] & 0xffff0000u);
+          } else {
+            x[h] = __uint_as_float(ws[h]);
+          }
         }
-      }
-      float vm = z[0];
+        float vm = x[0];
 #pragma unroll
-      for (int e = 1; e < EPV; ++e) vm = fmaxf(vm, z[e]);
-      if (vm > m) {
-        s *= __expf(m - vm);
-        m = vm;
-      }
+        for (int e = 1; e < EPV; ++e) vm = fmaxf(vm, x[e]);
+        if (vm > mx) {
+          s *= __builtin_amdgcn_exp2f((mx - vm) * c);
+          mx = vm;
+        }
+        const float nmc = -mx * c;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) s += __expf(z[e] - m);
+        for (int e = 0; e < EPV; ++e) s += __builtin_amdgcn_exp2f(fmaf(x[e], c, nmc));
+      }
+      m = mx * it;  // back to z units (-inf stays -inf)
+      for (int i = vend * EPV + lane; i < end; i += kWave) lse_merge(m, s, logit<ESZ>(p, row, i) * it, 1.f);
+    } else {
+      for (int i = beg + lane; i < end; i += kWave) lse_merge(m, s, logit<ESZ>(p, row, i) * it, 1.f);
     }
-    for (int i = vend * EPV + tid; i < end; i += kNT) lse_merge(m, s, logit<ESZ>(p, row, i) * it, 1.f);
-  } else {
-    for (int i = beg + tid; i < end; i += kNT) lse_merge(m, s, logit<ESZ>(p, row, i) * it, 1.f);
-  }
-  wave_lse(m, s);
-  if ((tid & (kWave - 1)) == 0) {
-    s_m[tid / kWave] = m;
-    s_s[tid / kWave] = s;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float M = s_m[0], S = s_s[0];
-#pragma unroll
-    for (int w = 1; w < kNT / kWave; ++w) lse_merge(M, S, s_m[w], s_s[w]);
-    p.part_m[row * p.split + part] = M;
-    p.part_s[row * p.split + part] = S;
+    wave_lse(m, s);
+    if (lane == 0) {
+      p.part_m[q] = m;
+      p.part_s[q] = s;
+    }
   }
 }
 
@@ -277,8 +294,10 @@ __global__ __launch_bounds__(kNT) void k_sample_walk(SampleArgs p) {
 int sample_split(int V) { return (V + kSampleChunk - 1) / kSampleChunk; }
 
 hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t s) {
-  const long long grid = static_cast<long long>(a.B) * (a.T + 1) * a.split;
-  if (grid > 0x7fffffffLL || a.T + 1 > 65) return hipErrorInvalidValue;
+  const long long chunks = static_cast<long long>(a.B) * (a.T + 1) * a.split;
+  if (a.T + 1 > 65) return hipErrorInvalidValue;
+  const long long waves = kNT / kWave;
+  const long long grid = std::min<long long>((chunks + waves - 1) / waves, 4096);
   if (dtype == 1) {
     hipLaunchKernelGGL(k_softmax_part<2>, dim3(grid), dim3(kNT), 0, s, a);
   } else {
