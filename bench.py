@@ -228,6 +228,68 @@ def sample_accept_pass(cfg, rb, stream, reps, oracle_seqs=2):
             "oracle_us_per_round": o_us, "oracle_sample_sequences": k, "temperature": 1.0}
 
 
+def draft_sweep(cfg, stream, Ns=(1, 2, 4, 8, 16), reps=10):
+    """Round time of the 30-layer stack for each draft length N (same batch,
+    acceptance law and round form rule as the workload), the acceptance
+    estimated from the rounds' accepted lengths, and the draft length the
+    host policy (policy.choose_draft_length) picks from them."""
+    from speculative_decode_verify_gdn_amd import binding as gb
+    from speculative_decode_verify_gdn_amd import policy as pol
+    from speculative_decode_verify_gdn_amd import spec_round as sr
+    t_us, forms = {}, {}
+    stats = pol.AcceptanceStats()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for n in Ns:
+        c = cfg.with_(T=n)
+        base, sets = build_sets(c, 1, "cuda")
+        inp, acc = sets[0]
+        rb = sr.RoundBuffers(sh=gb.GdnShape(c.L, c.B, c.Hk, c.Hv, c.Dk, c.Dv, c.K, c.silu, c.eps,
+                                            c.dtype),
+                             T=n, V=c.V, tree=False, S=base["S0"], conv_state=base["conv_state"],
+                             conv_w=base["conv_w"], x=inp["x"], a=inp["a"], b=inp["b"],
+                             logits=acc["logits"], draft=acc["draft"], parent=None)
+        fused = sr.fused_pays(rb.sh, n, False)
+        forms[n] = "fused" if fused else "plain"
+        with torch.cuda.stream(stream):
+            if fused:
+                fr = sr.FusedRound(rb)
+                fr.round(0, first=True)
+                fr.round(1)
+                graphs = []
+                for par in (0, 1):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=stream):
+                        fr.round(par)
+                    graphs.append(g)
+                nk = fr.n_keeps[1]
+            else:
+                sr.run_round(rb)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    sr.run_round(rb)
+                graphs = [g]
+                nk = rb.n_keep
+            torch.cuda.synchronize()
+            for i in range(2):
+                graphs[i % len(graphs)].replay()
+            a, b = ev(), ev()
+            a.record(stream)
+            for i in range(reps):
+                graphs[i % len(graphs)].replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+        t_us[n] = a.elapsed_time(b) / reps * 1e3
+        stats.update(nk, n)
+        del rb, base, sets, inp, acc, graphs
+        torch.cuda.empty_cache()
+    alpha = stats.alpha()
+    chosen = pol.choose_draft_length(alpha, t_us)
+    return {"t_round_us": t_us, "round_form": forms, "alpha_estimate": alpha,
+            "committed_tokens_per_s": {n: cfg.B * pol.expected_committed(alpha, n) / (t * 1e-6)
+                                       for n, t in t_us.items()},
+            "chosen_draft_length": chosen}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +308,9 @@ def parse():
                     help="round whose time is `value`: plain (verify, accept, rollback) or fused "
                          "(the state rollback folded into the next round's verify); auto picks "
                          "by the rule in spec_round.fused_pays; chains also report the other")
+    ap.add_argument("--draft-sweep", action="store_true",
+                    help="also time rounds at N = 1, 2, 4, 8, 16 drafts and report the draft "
+                         "length the host policy picks (chain workloads)")
     ap.add_argument("--sweep-n", action="store_true",
                     help="also time rollback with every sequence forced to n = 0..T")
     return ap.parse_args()
@@ -538,6 +603,10 @@ def main():
     if not cfg.is_tree:
         sampled = sample_accept_pass(cfg, rbs[0], stream, args.steps)
 
+    dsweep = None
+    if args.draft_sweep and not cfg.is_tree:
+        dsweep = draft_sweep(cfg, stream)
+
     sweep = None
     if args.sweep_n and not cfg.is_tree:
         with torch.cuda.stream(stream):
@@ -608,6 +677,8 @@ def main():
     }
     if sampled is not None:
         out["sample_accept"] = sampled
+    if dsweep is not None:
+        out["draft_policy"] = dsweep
     if sweep is not None:
         out["rollback_sweep"] = sweep
     if not args.no_cpu_baseline:
