@@ -290,6 +290,51 @@ def draft_sweep(cfg, stream, Ns=(1, 2, 4, 8, 16), reps=10):
             "chosen_draft_length": chosen}
 
 
+def prefill_pass(cfg, n_tokens, stream, reps=3):
+    """gdn_prefill of n_tokens through the workload's L layers and B
+    sequences (graph replay): time per call, prefilled tokens/s (B x
+    n_tokens per call; each layer sees every token) and the HBM fraction of
+    the byte model: per 16-token chunk and (layer, seq) one state read and
+    write, plus per token x, gates, o, and the chunk tape written then read
+    back."""
+    from speculative_decode_verify_gdn_amd import binding as gb
+    from speculative_decode_verify_gdn_amd import workload as W
+    c = cfg.with_(T=n_tokens)
+    inp = W.layer_inputs(c, 0, "cuda")
+    sh = gb.GdnShape(c.L, c.B, c.Hk, c.Hv, c.Dk, c.Dv, c.K, c.silu, c.eps, c.dtype)
+    o = torch.empty((c.L, c.B, n_tokens, c.Hv, c.Dv), device="cuda")
+    ws = torch.empty((gb.gdn_prefill_workspace_bytes(sh),), device="cuda", dtype=torch.uint8)
+    S, cs = inp["S0"], inp["conv_state"]
+    call = lambda: gb.gdn_prefill(sh, inp["x"], cs, inp["conv_w"], inp["a"], inp["b"], S, o, ws)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        call()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            call()
+        g.replay()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    esz = 2 if c.dtype == torch.bfloat16 else 4
+    P = c.Hv * c.Dv * c.Dk * 4
+    chunks = (n_tokens + 15) // 16
+    tape_tok = c.Hv * c.Dv * 4 + c.Hk * c.Dk * 4 + c.Hv * 4
+    per_seq = chunks * 2 * P + n_tokens * (c.C * esz + 2 * c.Hv * esz + c.Hv * c.Dv * 4
+                                           + 2 * tape_tok) + chunks * 2 * (c.K - 1) * c.C * esz
+    byts = c.L * c.B * per_seq
+    del inp, o, ws
+    torch.cuda.empty_cache()
+    return {"tokens": n_tokens, "layers": c.L, "batch": c.B, "ms_per_call": ms,
+            "tokens_per_s": c.B * n_tokens / (ms * 1e-3), "algorithmic_bytes": byts,
+            "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,6 +353,8 @@ def parse():
                     help="round whose time is `value`: plain (verify, accept, rollback) or fused "
                          "(the state rollback folded into the next round's verify); auto picks "
                          "by the rule in spec_round.fused_pays; chains also report the other")
+    ap.add_argument("--prefill", type=int, default=0, metavar="N",
+                    help="also time gdn_prefill of N tokens through the workload's stack")
     ap.add_argument("--draft-sweep", action="store_true",
                     help="also time rounds at N = 1, 2, 4, 8, 16 drafts and report the draft "
                          "length the host policy picks (chain workloads)")
@@ -603,6 +650,8 @@ def main():
     if not cfg.is_tree:
         sampled = sample_accept_pass(cfg, rbs[0], stream, args.steps)
 
+    pre = prefill_pass(cfg, args.prefill, stream) if args.prefill > 0 else None
+
     dsweep = None
     if args.draft_sweep and not cfg.is_tree:
         dsweep = draft_sweep(cfg, stream)
@@ -677,6 +726,8 @@ def main():
     }
     if sampled is not None:
         out["sample_accept"] = sampled
+    if pre is not None:
+        out["prefill"] = pre
     if dsweep is not None:
         out["draft_policy"] = dsweep
     if sweep is not None:

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
   GDN_OK = 0,
@@ -247,6 +247,29 @@ gdn_status spec_accept_sample(int32_t B, int32_t T, int32_t V, const int32_t* dr
 
 /* Bytes of device workspace spec_accept_sample needs for (B, T, V). */
 size_t spec_sample_workspace_bytes(int32_t B, int32_t T, int32_t V);
+
+/*
+ * Prefill: run T tokens (any T >= 1) through L GDN layers and commit them,
+ * so that S and conv_state end as the state and window after the last token
+ * and o holds every token's output.  The tokens go through in chunks of 16:
+ * chunk c is verified while the replay of chunk c-1 (every token kept) is
+ * folded into the same kernel, the conv window follows each chunk, and the
+ * last chunk is committed by a tape replay.  The result is the sequential
+ * recurrence of GDN page s2.1 over all T tokens; the chunking is s4's
+ * tape replay with nothing rejected.
+ *   x [L,B,T,C], a / b [L,B,T,Hv] (in_dtype), conv_w [L,C,K] fp32
+ *   conv_state [L,B,K-1,C] in/out;  S [L,B,Hv,Dv,Dk] in/out (fp32)
+ *   o [L,B,T,Hv,Dv] fp32 output
+ *   workspace: device scratch of at least gdn_prefill_workspace_bytes(shape)
+ *     (two tapes of 16 tokens); its contents are not meaningful afterwards.
+ * Source: GDN page s2.1 (sequential GDN layer), s4 (tape replay).
+ */
+gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* conv_state,
+                       const float* conv_w, const void* a, const void* b, float* S, float* o,
+                       void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
+
+/* Bytes of device workspace gdn_prefill needs for this shape (any T). */
+size_t gdn_prefill_workspace_bytes(const gdn_shape* shape);
 
 /*
  * Tape-replay rollback of L layers at once: S holds the pre-verify snapshot

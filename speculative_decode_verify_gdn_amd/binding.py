@@ -24,7 +24,7 @@ DEV_ERR_N_KEEP, DEV_ERR_PARENT, DEV_ERR_PATH, DEV_ERR_TOKEN = 1, 2, 4, 8
 
 EXPORTS = ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
            "gdn_tree_verify_replay", "spec_accept_prefix", "spec_accept_sample",
-           "spec_sample_workspace_bytes",
+           "spec_sample_workspace_bytes", "gdn_prefill", "gdn_prefill_workspace_bytes",
            "spec_accept_workspace_bytes", "gdn_tape_rollback", "gdn_conv_state_rollback",
            "gdn_status_string", "gdn_abi_version")
 
@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
                                          SZ, P, P]
         L.spec_sample_workspace_bytes.argtypes = [I32, I32, I32]
         L.spec_sample_workspace_bytes.restype = SZ
+        L.gdn_prefill.argtypes = [SP, I32, P, P, P, P, P, P, P, P, SZ, P, P]
+        L.gdn_prefill_workspace_bytes.argtypes = [SP]
+        L.gdn_prefill_workspace_bytes.restype = SZ
         L.gdn_tape_rollback.argtypes = [SP, I32, P, TP, P, P, P, P]
         L.gdn_conv_state_rollback.argtypes = [SP, I32, P, P, P, P, P, P, P]
         L.gdn_status_string.argtypes = [I32]
@@ -105,6 +108,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_abi_version.argtypes = []
         for name in ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
                      "gdn_tree_verify_replay", "spec_accept_prefix", "spec_accept_sample",
+                     "gdn_prefill",
                      "gdn_tape_rollback", "gdn_conv_state_rollback", "gdn_abi_version"):
             getattr(L, name).restype = I32
         _lib = L
@@ -230,6 +234,29 @@ def gdn_tree_verify(sh: GdnShape, parent, x, conv_state, conv_w, a, b, S, o, tap
     ct = tape.c(sh, T)
     _check(lib().gdn_tree_verify(ctypes.byref(sh.c()), T, pp, *ptrs, ctypes.byref(ct), cw, de,
                                  _stream(stream)), "gdn_tree_verify")
+
+
+def gdn_prefill_workspace_bytes(sh: GdnShape) -> int:
+    return int(lib().gdn_prefill_workspace_bytes(ctypes.byref(sh.c())))
+
+
+def gdn_prefill(sh: GdnShape, x, conv_state, conv_w, a, b, S, o, workspace, dev_err=None,
+                stream=None):
+    """Run T = x.shape[2] tokens through the layers and commit them: S and
+    conv_state are updated in place, o receives every token's output."""
+    T = int(x.shape[2])
+    ptrs = _verify_ptrs(sh, T, x, conv_state, conv_w, a, b, S, o)
+    need = gdn_prefill_workspace_bytes(sh)
+    if (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8
+            or workspace.numel() < need or not workspace.is_cuda
+            or not workspace.is_contiguous() or workspace.data_ptr() % 256):
+        raise ValueError("workspace must be a 256-byte aligned device uint8 tensor of >= %d bytes"
+                         % need)
+    de = _opt(dev_err, "dev_err", torch.int32, (1,))
+    _dev(x.device, conv_state, conv_w, a, b, S, o, workspace, dev_err)
+    _check(lib().gdn_prefill(ctypes.byref(sh.c()), T, *ptrs, workspace.data_ptr(),
+                             workspace.numel(), de, _stream(stream)),
+           "gdn_prefill")
 
 
 def gdn_tree_verify_replay(sh: GdnShape, parent, x, conv_state, conv_w, a, b, S, o, tape: Tape,

@@ -76,6 +76,9 @@ VerifyArgs verify_args(const gdn_shape* s, int32_t T, const void* x, const void*
   v.silu = s->conv_silu ? 1 : 0;
   v.eps = s->l2_eps;
   v.C = channels(s);
+  v.x_ld = static_cast<size_t>(T) * v.C;
+  v.ab_ld = static_cast<size_t>(T) * v.Hv;
+  v.o_ld = static_cast<size_t>(T) * v.Hv * s->d_v;
   return v;
 }
 
@@ -304,8 +307,102 @@ gdn_status gdn_conv_state_rollback(const gdn_shape* shape, int32_t T, void* conv
   c.K = shape->conv_kernel;
   c.T = T;
   c.C = channels(shape);
+  c.x_ld = static_cast<size_t>(T) * c.C;
   return launch_status(gdn::launch_conv_rollback(c, shape->in_dtype,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+constexpr int kPrefillChunk = 16;  // tokens per chunk (the chain kernel's longest)
+
+size_t tape_floats(const gdn_shape* s, int T) {
+  const size_t lbt = static_cast<size_t>(s->n_layers) * s->batch * T;
+  return lbt * (static_cast<size_t>(s->n_v_heads) * s->d_v +
+                static_cast<size_t>(s->n_k_heads) * s->d_k + s->n_v_heads);
+}
+}  // namespace
+
+size_t gdn_prefill_workspace_bytes(const gdn_shape* shape) {
+  if (check_shape(shape, kPrefillChunk) != GDN_OK) return 0;
+  return 2 * ((tape_floats(shape, kPrefillChunk) * sizeof(float) + 255) / 256 * 256);
+}
+
+gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* conv_state,
+                       const float* conv_w, const void* a, const void* b, float* S, float* o,
+                       void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream) {
+  gdn_status st = check_shape(shape, 1);
+  if (st != GDN_OK) return st;
+  if (T < 1) return GDN_ERR_INVALID_ARG;
+  if (!x || !conv_state || !conv_w || !a || !b || !S || !o) return GDN_ERR_INVALID_ARG;
+  const size_t need = gdn_prefill_workspace_bytes(shape);
+  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int C = channels(shape);
+  const size_t esz = shape->in_dtype == GDN_BF16 ? 2 : 4;
+  const size_t Hv = shape->n_v_heads, Dv = shape->d_v;
+  // two tapes of one chunk each, alternating: chunk c writes tape c % 2 and
+  // replays chunk c - 1 (every token kept) from the other
+  gdn_tape tapes[2];
+  const size_t half = need / 2;
+  for (int i = 0; i < 2; ++i) {
+    float* base = reinterpret_cast<float*>(static_cast<char*>(workspace) + i * half);
+    const size_t lbt = static_cast<size_t>(shape->n_layers) * shape->batch * kPrefillChunk;
+    tapes[i].u = base;
+    tapes[i].k = base + lbt * Hv * Dv;
+    tapes[i].g = tapes[i].k + lbt * shape->n_k_heads * shape->d_k;
+  }
+  const int nch = (T + kPrefillChunk - 1) / kPrefillChunk;
+  int prev_tc = 0;
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = c * kPrefillChunk;
+    const int tc = T - t0 < kPrefillChunk ? T - t0 : kPrefillChunk;
+    const char* xc = static_cast<const char*>(x) + static_cast<size_t>(t0) * C * esz;
+    VerifyArgs v = verify_args(shape, tc, xc, conv_state, conv_w,
+                               static_cast<const char*>(a) + t0 * Hv * esz,
+                               static_cast<const char*>(b) + t0 * Hv * esz, S,
+                               o + t0 * Hv * Dv, &tapes[c % 2]);
+    v.x_ld = static_cast<size_t>(T) * C;
+    v.ab_ld = static_cast<size_t>(T) * Hv;
+    v.o_ld = static_cast<size_t>(T) * Hv * Dv;
+    v.dev_err = dev_err;
+    if (c > 0) {
+      v.S_out = S;
+      v.ptu = tapes[(c + 1) % 2].u;
+      v.ptk = tapes[(c + 1) % 2].k;
+      v.ptg = tapes[(c + 1) % 2].g;
+      v.prev_n_all = prev_tc;
+      v.pT = prev_tc;
+    }
+    st = launch_status(gdn::launch_verify_chain(v, shape->d_k, shape->d_v, shape->in_dtype, s));
+    if (st != GDN_OK) return st;
+    ConvRollbackArgs cr{};
+    cr.conv_state = conv_state;
+    cr.x = xc;
+    cr.n_all = tc;
+    cr.dev_err = dev_err;
+    cr.L = shape->n_layers;
+    cr.B = shape->batch;
+    cr.K = shape->conv_kernel;
+    cr.T = tc;
+    cr.C = C;
+    cr.x_ld = static_cast<size_t>(T) * C;
+    st = launch_status(gdn::launch_conv_rollback(cr, shape->in_dtype, s));
+    if (st != GDN_OK) return st;
+    prev_tc = tc;
+  }
+  RollbackArgs r{};
+  r.S = S;
+  r.tu = tapes[(nch - 1) % 2].u;
+  r.tk = tapes[(nch - 1) % 2].k;
+  r.tg = tapes[(nch - 1) % 2].g;
+  r.n_all = prev_tc;
+  r.dev_err = dev_err;
+  r.L = shape->n_layers;
+  r.B = shape->batch;
+  r.Hk = shape->n_k_heads;
+  r.Hv = shape->n_v_heads;
+  r.T = prev_tc;
+  return launch_status(gdn::launch_tape_rollback(r, shape->d_k, shape->d_v, s));
 }
 
 const char* gdn_status_string(int32_t status) {

@@ -39,6 +39,11 @@ struct VerifyArgs {
   const int32_t* prev_n_keep;
   const int32_t* prev_path;
   int pT;
+  int prev_n_all;  // every sequence replays this many steps (prev_n_keep == nullptr)
+  // Elements between consecutive (layer, seq) slabs of x, of a / b and of o
+  // (T*C, T*Hv, T*Hv*Dv for whole chunks; larger when a chunk is a slice of
+  // a longer sequence).  Chain kernel only.
+  size_t x_ld, ab_ld, o_ld;
 };
 
 // Tape-replay rollback.
@@ -48,9 +53,10 @@ struct RollbackArgs {
   const float* tk;
   const float* tg;
   const int32_t* path;  // [B,T] or nullptr
-  const int32_t* n_keep;
+  const int32_t* n_keep;  // or nullptr: every sequence keeps n_all
   int32_t* dev_err;
   int L, B, Hk, Hv, T;
+  int n_all;
 };
 
 // Conv-window rollback.
@@ -58,10 +64,12 @@ struct ConvRollbackArgs {
   void* conv_state;
   const void* x;
   const int32_t* path;
-  const int32_t* n_keep;
+  const int32_t* n_keep;  // or nullptr: every sequence keeps n_all
   int32_t* win_idx;
   int32_t* dev_err;
   int L, B, K, T, C;
+  int n_all;
+  size_t x_ld;  // elements between consecutive (layer, seq) slabs of x
 };
 
 // Greedy acceptance.

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void k_tape_rollback(RollbackArgs p) {
   const int bb = static_cast<int>(lb % p.B);
   const int l = static_cast<int>(lb / p.B);
   const int T = p.T;
-  const int n = p.n_keep[bb];
+  const int n = p.n_keep ? p.n_keep[bb] : p.n_all;
   if (n == 0) return;
   if (n < 0 || n > T) {
     if (tid == 0 && p.dev_err && l == 0 && hv == 0 && rblk == 0) atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void k_conv_rollback(ConvRollbackArgs p) {
   const size_t lb = blockIdx.x;
   const int bb = static_cast<int>(lb % p.B);
   const int l = static_cast<int>(lb / p.B);
-  const int n = p.n_keep[bb];
+  const int n = p.n_keep ? p.n_keep[bb] : p.n_all;
   const int T = p.T;
   const bool first_block = (l == 0 && blockIdx.y == 0);
   if (n < 0 || n > T) {
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void k_conv_rollback(ConvRollbackArgs p) {
   for (int j = 0; j < KM1; ++j) {
     const int id = idx[j];
     v[j] = id < 0 ? cs[(lb * KM1 + (KM1 + id)) * row_chunks + chunk]
-                  : xs[(lb * T + id) * row_chunks + chunk];
+                  : xs[lb * (p.x_ld / EPC) + id * row_chunks + chunk];
   }
 #pragma unroll
   for (int j = 0; j < KM1; ++j) cs[(lb * KM1 + j) * row_chunks + chunk] = v[j];

@@ -161,7 +161,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
   int pn = 0;
   if constexpr (RP) {
     const int bb = static_cast<int>(lb % p.B);
-    const int v = p.prev_n_keep[bb];
+    const int v = p.prev_n_keep ? p.prev_n_keep[bb] : p.prev_n_all;
     pn = (v >= 0 && v <= p.pT && v <= PM) ? v : 0;
     if (pn != v && tid == 0 && p.dev_err && l == 0 && hk == 0 && g == 0)
       atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
@@ -209,7 +209,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
     const TIn* x = static_cast<const TIn*>(p.x);
     const TIn* cs = static_cast<const TIn*>(p.conv_state);
     const float* cw = p.conv_w + static_cast<size_t>(l) * p.C * K;
-    const TIn* xcol = x + lb * T * p.C;
+    const TIn* xcol = x + lb * p.x_ld;
     const TIn* ccol = cs + lb * (K - 1) * p.C;
     const int nrows = K - 1 + T;
     // local channel c in [q | k | v-rows] -> qkv channel
@@ -220,7 +220,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
     };
     // Gates (clamped, unconditional loads).
     const int tq = lane < T ? lane : 0;
-    const size_t gi = (lb * T + tq) * p.Hv + hv;
+    const size_t gi = lb * p.ab_ld + static_cast<size_t>(tq) * p.Hv + hv;
     const float ga_ld = ld_in(static_cast<const TIn*>(p.a), gi);
     const float gb_ld = ld_in(static_cast<const TIn*>(p.b), gi);
     const float pg_ld = RP && lane < pn ? p.ptg[(lb * p.pT + lane) * p.Hv + hv] : 1.f;
@@ -525,7 +525,8 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
       const bool isk = n < TMAX;
       const int t = isk ? n : n - TMAX;
       if (t < T) {
-        const size_t oi = ((lb * T + t) * p.Hv + hv) * DV + i0;
+        const size_t oi = isk ? ((lb * T + t) * p.Hv + hv) * DV + i0
+                              : lb * p.o_ld + (static_cast<size_t>(t) * p.Hv + hv) * DV + i0;
         floatx4 val = acc2[cb];
         if (!isk) val += cnode[cb] * acc1[cb];
         __builtin_nontemporal_store(val, reinterpret_cast<floatx4*>((isk ? p.tu : p.o) + oi));
@@ -554,8 +555,9 @@ hipError_t launch_c(const VerifyArgs& a, hipStream_t s) {
   const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
   if (grid > 0x7fffffffLL || a.T > 16) return hipErrorInvalidValue;
   const dim3 gd(static_cast<int>(grid));
-  if (a.prev_n_keep) {
-    if (a.pT > 16 || !a.S_out || !a.ptu || !a.ptk || !a.ptg) return hipErrorInvalidValue;
+  if (a.prev_n_keep || a.prev_n_all > 0) {
+    if (a.pT > 16 || a.prev_n_all > a.pT || !a.S_out || !a.ptu || !a.ptk || !a.ptg)
+      return hipErrorInvalidValue;
     return launch_cr<DK, DV, TIn, true>(a, gd, s);
   }
   return launch_cr<DK, DV, TIn, false>(a, gd, s);

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gb.abi_version() == 4
+    assert gb.abi_version() == 5
     assert gb.status_string(0) == "GDN_OK"
     assert gb.status_string(1) == "GDN_ERR_INVALID_ARG"
     assert gb.status_string(4) == "GDN_ERR_WORKSPACE"
@@ -117,6 +117,17 @@ def test_host_validation_before_launch(lib):
     assert sa(4, 1.0, FAKE, None, big) == gb.GDN_ERR_WORKSPACE
     assert gb.spec_sample_workspace_bytes(32, 8, 151936) >= 32 * 9 * 38 * 8
     assert gb.spec_sample_workspace_bytes(1, 65, 100) == 0
+    # prefill: bad T, missing pointers, short workspace
+    pf = lambda T, xx, ws, wsb: lib.gdn_prefill(ctypes.byref(_shape()), T, xx, FAKE, FAKE, FAKE,
+                                                FAKE, FAKE, FAKE, ws, wsb, None, None)
+    wsb = gb.lib().gdn_prefill_workspace_bytes(ctypes.byref(_shape()))
+    assert wsb > 0
+    assert pf(0, FAKE, FAKE, wsb) == gb.GDN_ERR_INVALID_ARG
+    assert pf(100, None, FAKE, wsb) == gb.GDN_ERR_INVALID_ARG
+    assert pf(100, FAKE, FAKE, wsb - 1) == gb.GDN_ERR_WORKSPACE
+    assert pf(100, FAKE, None, wsb) == gb.GDN_ERR_WORKSPACE
+    assert lib.gdn_prefill(ctypes.byref(_shape(Dk=96, Dv=96)), 10, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           FAKE, FAKE, FAKE, wsb, None, None) == gb.GDN_ERR_UNSUPPORTED
     # accept: missing / short workspace, bad dtype
     assert lib.spec_accept_prefix(2, 4, 100, None, FAKE, FAKE, gb.GDN_BF16, FAKE, FAKE, FAKE,
                                   FAKE, 8, None, None) == gb.GDN_ERR_WORKSPACE

@@ -623,3 +623,36 @@ def test_sample_accept_extremes_and_bad_tokens():
     n_g, path_g, tok_g, err = _run_sample(draft, lt, high, tau)
     assert (n_g == 0).all()
     _check_sample(draft, lt, high, tau, n_g, path_g, tok_g)
+
+
+# ---------------------------------------------------------------- prefill --
+
+@pytest.mark.parametrize("T,L,B,Hk,Hv,D,K,dtype", [
+    (1, 1, 2, 2, 4, 128, 4, torch.bfloat16), (5, 1, 2, 2, 4, 128, 4, torch.bfloat16),
+    (16, 2, 2, 2, 4, 128, 4, torch.bfloat16), (17, 1, 3, 2, 4, 128, 4, torch.float32),
+    (40, 1, 2, 1, 3, 64, 3, torch.bfloat16), (100, 1, 2, 2, 4, 128, 4, torch.bfloat16),
+    (150, 1, 1, 1, 1, 32, 4, torch.float32)])
+def test_prefill_matches_sequential_oracle(T, L, B, Hk, Hv, D, K, dtype):
+    """gdn_prefill (16-token chunks, each chunk's replay folded into the next
+    verify) equals the oracle's sequential recurrence over all T tokens:
+    every output, the final state and the final conv window."""
+    _need_gpu()
+    cfg = W.CONFIGS[2].with_(L=L, B=B, Hk=Hk, Hv=Hv, Dk=D, Dv=D, K=K, T=T, dtype=dtype)
+    inp = W.layer_inputs(cfg, 0, "cpu")
+    sh = gshape(cfg)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    S, cs = d["S0"].clone(), d["conv_state"].clone()
+    o = torch.empty((L, B, T, Hv, D), device=DEV)
+    ws = torch.empty((gb.gdn_prefill_workspace_bytes(sh),), device=DEV, dtype=torch.uint8)
+    err = torch.zeros((1,), device=DEV, dtype=torch.int32)
+    gb.gdn_prefill(sh, d["x"], cs, d["conv_w"], d["a"], d["b"], S, o, ws, dev_err=err)
+    torch.cuda.synchronize()
+    f = {k: W.to_f64(v) for k, v in inp.items()}
+    osh = oracle.Shape(L=L, B=B, Hk=Hk, Hv=Hv, Dk=D, Dv=D, K=K, silu=cfg.silu, eps=cfg.eps)
+    ref = oracle.verify_chunk(osh, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"], f["S0"],
+                              want_final=True)
+    cs_ref, _ = oracle.conv_rollback(osh, f["conv_state"], f["x"], np.full(B, T, np.int32))
+    assert int(err.item()) == 0
+    assert rel_fro(o.cpu().double().numpy(), ref["o"]) <= 1e-4
+    assert rel_fro(S.cpu().double().numpy(), ref["S_final"]) <= 1e-4
+    np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
