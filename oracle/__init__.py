@@ -18,6 +18,12 @@ Parity status of each function (the pins live in ``tests/test_oracle_*.py``):
   tree_verify             pinned: chain parents == verify_chunk; every node ==
                           verify_chunk along its root path.
   accept                  pinned: brute-force enumeration of prefixes / paths.
+  verify_chunk_vg         pinned: equal per-channel gates give verify_chunk;
+                          the matrix form S diag(a)(I - b k k^T) + b v k^T;
+                          a zero gate erases its key column; replay of the
+                          whole tape gives S_final.
+  tape_rollback_vg        pinned: replay(n) == fresh recompute over n tokens,
+                          equal gates give tape_rollback.
   accept_sample           pinned: the first output token's distribution equals
                           p exactly (quadrature over the uniforms), the
                           low-temperature limit equals the greedy accept,
@@ -104,6 +110,10 @@ def _load():
         lib.oracle_accept.restype = I
         lib.oracle_tape_rollback.argtypes = [SP, I, P, P, P, P, P, P]
         lib.oracle_tape_rollback.restype = I
+        lib.oracle_verify_chunk_vg.argtypes = [SP, I] + [P] * 11
+        lib.oracle_verify_chunk_vg.restype = I
+        lib.oracle_tape_rollback_vg.argtypes = [SP, I, P, P, P, P, P, P]
+        lib.oracle_tape_rollback_vg.restype = I
         lib.oracle_conv_rollback.argtypes = [SP, I, P, P, P, P, P]
         lib.oracle_conv_rollback.restype = I
         lib.oracle_num_threads.argtypes = []
@@ -200,6 +210,47 @@ def verify_chunk(sh: Shape, x, conv_state, conv_w, a, b, S0, want_final=True,
     if want_qkv_post:
         out["qkv_post"] = qp
     return out
+
+
+def verify_chunk_vg(sh: Shape, x, conv_state, conv_w, a, b, S0) -> dict:
+    """verify_chunk with a per-key-channel decay gate a (L, B, T, Hv, Dk): per
+    token S <- S diag(a_t), u = b (v - S k), S <- S + u k^T, o = S q.
+    Returns o, u, k, g (= a, the decay tape) and S_final."""
+    L, B, C = sh.L, sh.B, sh.C
+    x = _f64(x)
+    T = x.shape[2]
+    x = _f64(x, (L, B, T, C))
+    conv_state = _f64(conv_state, (L, B, sh.K - 1, C))
+    conv_w = _f64(conv_w, (L, C, sh.K))
+    a = _f64(a, (L, B, T, sh.Hv, sh.Dk))
+    b = _f64(b, (L, B, T, sh.Hv))
+    S0 = _f64(S0, (L, B, sh.Hv, sh.Dv, sh.Dk))
+    o = np.empty((L, B, T, sh.Hv, sh.Dv))
+    u = np.empty((L, B, T, sh.Hv, sh.Dv))
+    k = np.empty((L, B, T, sh.Hk, sh.Dk))
+    g = np.empty((L, B, T, sh.Hv, sh.Dk))
+    Sf = np.empty_like(S0)
+    c = sh._c()
+    _check(_load().oracle_verify_chunk_vg(ctypes.byref(c), T, _p(x), _p(conv_state), _p(conv_w),
+                                          _p(a), _p(b), _p(S0), _p(o), _p(u), _p(k), _p(g),
+                                          _p(Sf)), "verify_chunk_vg")
+    return dict(o=o, u=u, k=k, g=g, S_final=Sf)
+
+
+def tape_rollback_vg(sh: Shape, S, u, k, g, n_keep, path=None) -> np.ndarray:
+    """tape_rollback with the per-key-channel decay tape g (L, B, T, Hv, Dk)."""
+    S = _f64(S, (sh.L, sh.B, sh.Hv, sh.Dv, sh.Dk)).copy()
+    u = _f64(u)
+    T = u.shape[2]
+    u = _f64(u, (sh.L, sh.B, T, sh.Hv, sh.Dv))
+    k = _f64(k, (sh.L, sh.B, T, sh.Hk, sh.Dk))
+    g = _f64(g, (sh.L, sh.B, T, sh.Hv, sh.Dk))
+    n_keep = _i32(n_keep, (sh.B,))
+    path = None if path is None else _i32(path, (sh.B, T))
+    c = sh._c()
+    _check(_load().oracle_tape_rollback_vg(ctypes.byref(c), T, _p(S), _p(u), _p(k), _p(g),
+                                           _p(path), _p(n_keep)), "tape_rollback_vg")
+    return S
 
 
 def tree_verify(sh: Shape, parent, x, conv_state, conv_w, a, b, S0,

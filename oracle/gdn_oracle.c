@@ -250,6 +250,93 @@ int oracle_verify_chunk(const oshape* sh, int T, const double* x,
   return bad;
 }
 
+/* One gated delta-rule step on one row of S whose decay acts per key channel
+ * (the [B,T,Hv,Dk] form of the decay tape, GDN page s4):
+ *   S_row <- S_row * a (elementwise over Dk);  u = b (v_i - S_row . k);
+ *   S_row <- S_row + u k;  returns u and writes S_row . q into *o_i.
+ * With every a[j] equal to one scalar this is delta_row_step.               */
+static double delta_row_step_vg(int Dk, double* Srow, const double* k, const double* q,
+                                const double* a, double b, double vi, double* o_i) {
+  for (int j = 0; j < Dk; ++j) Srow[j] *= a[j];
+  double s = 0.0;
+  for (int j = 0; j < Dk; ++j) s += Srow[j] * k[j];
+  double u = b * (vi - s);
+  for (int j = 0; j < Dk; ++j) Srow[j] += u * k[j];
+  double o = 0.0;
+  for (int j = 0; j < Dk; ++j) o += Srow[j] * q[j];
+  *o_i = o;
+  return u;
+}
+
+/* ---------------------------------------------------------------------------
+ * oracle_verify_chunk with a per-key-channel decay gate:
+ *   a        [L,B,T,Hv,Dk]  decay of each key channel
+ *   tape_g   [L,B,T,Hv,Dk]  the decay tape (= a)
+ * other arguments and outputs as oracle_verify_chunk.
+ */
+int oracle_verify_chunk_vg(const oshape* sh, int T, const double* x,
+                           const double* conv_state, const double* conv_w,
+                           const double* a, const double* b, const double* S0,
+                           double* o, double* tape_u, double* tape_k,
+                           double* tape_g, double* S_final) {
+  if (!shape_ok(sh) || T < 1) return ORACLE_BAD_ARG;
+  const int L = sh->L, B = sh->B, Hk = sh->Hk, Hv = sh->Hv, Dk = sh->Dk,
+            Dv = sh->Dv, K = sh->K;
+  const size_t C = n_channels(sh);
+  const size_t P = (size_t)Dv * Dk;
+  int bad = 0;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int l = 0; l < L; ++l) {
+    for (int bb = 0; bb < B; ++bb) {
+      const size_t lb = (size_t)l * B + bb;
+      double* y = malloc(sizeof(double) * T * C);
+      double* qn = malloc(sizeof(double) * (size_t)T * Hk * Dk);
+      double* kn = malloc(sizeof(double) * (size_t)T * Hk * Dk);
+      double* S = malloc(sizeof(double) * P);
+      if (!y || !qn || !kn || !S) {
+#pragma omp atomic write
+        bad = ORACLE_NOMEM;
+        free(y); free(qn); free(kn); free(S);
+        continue;
+      }
+      oracle_conv_chain(K, T, (int)C, sh->silu, conv_state + lb * (K - 1) * C,
+                        x + lb * T * C, conv_w + (size_t)l * C * K, y);
+      for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < Hk; ++h) {
+          const double* yq = y + (size_t)t * C + (size_t)h * Dk;
+          const double* yk = y + (size_t)t * C + (size_t)Hk * Dk + (size_t)h * Dk;
+          l2norm(Dk, sh->eps, yq, qn + ((size_t)t * Hk + h) * Dk);
+          l2norm(Dk, sh->eps, yk, kn + ((size_t)t * Hk + h) * Dk);
+        }
+      }
+      for (int t = 0; t < T; ++t)
+        memcpy(tape_k + (lb * T + t) * Hk * Dk, kn + (size_t)t * Hk * Dk,
+               sizeof(double) * Hk * Dk);
+      for (int hv = 0; hv < Hv; ++hv) {
+        const int hk = (int)(((long long)hv * Hk) / Hv);
+        memcpy(S, S0 + (lb * Hv + hv) * P, sizeof(double) * P);
+        for (int t = 0; t < T; ++t) {
+          const size_t gi = (lb * T + t) * Hv + hv;
+          const double* at = a + gi * Dk;
+          const double bt = b[gi];
+          const double* kt = kn + ((size_t)t * Hk + hk) * Dk;
+          const double* qt = qn + ((size_t)t * Hk + hk) * Dk;
+          const double* vt = y + (size_t)t * C + (size_t)2 * Hk * Dk + (size_t)hv * Dv;
+          double* ot = o + gi * Dv;
+          double* ut = tape_u + gi * Dv;
+          for (int i = 0; i < Dv; ++i)
+            ut[i] = delta_row_step_vg(Dk, S + (size_t)i * Dk, kt, qt, at, bt, vt[i], &ot[i]);
+          memcpy(tape_g + gi * Dk, at, sizeof(double) * Dk);
+        }
+        if (S_final) memcpy(S_final + (lb * Hv + hv) * P, S, sizeof(double) * P);
+      }
+      free(y); free(qn); free(kn); free(S);
+    }
+  }
+  return bad;
+}
+
 /* ---------------------------------------------------------------------------
  * Verify a draft tree of T nodes (T <= 64) per sequence.  Node v with parent
  * p runs one gated delta-rule step from the state after p (S0 when p = -1).
@@ -386,6 +473,43 @@ int oracle_accept(int B, int T, int V, const int* parent, const int* draft,
     n_keep[bb] = n;
     bonus[bb] = star;
   }
+  return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * oracle_tape_rollback with the per-key-channel decay tape
+ * tape_g [L,B,T,Hv,Dk]:  S <- S diag(g_t) + u_t k_t^T for the accepted steps.
+ */
+int oracle_tape_rollback_vg(const oshape* sh, int T, double* S,
+                            const double* tape_u, const double* tape_k,
+                            const double* tape_g, const int* path,
+                            const int* n_keep) {
+  if (!shape_ok(sh) || T < 1) return ORACLE_BAD_ARG;
+  const int L = sh->L, B = sh->B, Hk = sh->Hk, Hv = sh->Hv, Dk = sh->Dk, Dv = sh->Dv;
+  const size_t P = (size_t)Dv * Dk;
+  for (int bb = 0; bb < B; ++bb) {
+    if (n_keep[bb] < 0 || n_keep[bb] > T) return ORACLE_BAD_ARG;
+    if (path)
+      for (int i = 0; i < n_keep[bb]; ++i)
+        if (path[(size_t)bb * T + i] < 0 || path[(size_t)bb * T + i] >= T) return ORACLE_BAD_ARG;
+  }
+#pragma omp parallel for collapse(3) schedule(static)
+  for (int l = 0; l < L; ++l)
+    for (int bb = 0; bb < B; ++bb)
+      for (int hv = 0; hv < Hv; ++hv) {
+        const size_t lb = (size_t)l * B + bb;
+        const int hk = (int)(((long long)hv * Hk) / Hv);
+        double* St = S + (lb * Hv + hv) * P;
+        for (int i = 0; i < n_keep[bb]; ++i) {
+          const int t = path ? path[(size_t)bb * T + i] : i;
+          const double* g = tape_g + ((lb * T + t) * Hv + hv) * Dk;
+          const double* u = tape_u + ((lb * T + t) * Hv + hv) * Dv;
+          const double* k = tape_k + ((lb * T + t) * Hk + hk) * Dk;
+          for (int r = 0; r < Dv; ++r)
+            for (int j = 0; j < Dk; ++j)
+              St[(size_t)r * Dk + j] = g[j] * St[(size_t)r * Dk + j] + u[r] * k[j];
+        }
+      }
   return ORACLE_OK;
 }
 
