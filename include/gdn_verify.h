@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum {
   GDN_OK = 0,
@@ -84,6 +84,14 @@ typedef struct {
   int32_t conv_silu;   /* 1: SiLU after the conv, 0: identity */
   float l2_eps;        /* epsilon inside the q/k L2-norm square root */
   int32_t in_dtype;    /* gdn_dtype of x, conv_state, a, b */
+  int32_t gate_per_key; /* 0: decay a and tape g are [..,Hv] (one per v-head);
+                           1: they are [..,Hv,Dk], one per v-head and key
+                           channel (S decays column by column:
+                           S <- S diag(a_t) before each step).  Supported by
+                           gdn_verify_chunk, gdn_tape_rollback and the conv
+                           rollback; the other calls return
+                           GDN_ERR_UNSUPPORTED.  Source: GDN page s4 (the two
+                           forms of the decay tape). */
 } gdn_shape;
 
 /* The innovation tape written by verify and read by rollback (fp32):

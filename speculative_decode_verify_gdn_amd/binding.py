@@ -40,7 +40,8 @@ class _CShape(ctypes.Structure):
                 ("n_k_heads", ctypes.c_int32), ("n_v_heads", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("conv_kernel", ctypes.c_int32), ("conv_silu", ctypes.c_int32),
-                ("l2_eps", ctypes.c_float), ("in_dtype", ctypes.c_int32)]
+                ("l2_eps", ctypes.c_float), ("in_dtype", ctypes.c_int32),
+                ("gate_per_key", ctypes.c_int32)]
 
 
 class _CTape(ctypes.Structure):
@@ -60,6 +61,7 @@ class GdnShape:
     silu: bool = True
     eps: float = 1e-6
     dtype: torch.dtype = torch.bfloat16
+    gate_per_key: bool = False  # decay a / tape g per key channel: [..,Hv,Dk]
 
     @property
     def C(self) -> int:
@@ -70,7 +72,13 @@ class GdnShape:
             raise TypeError("input dtype must be float32 or bfloat16")
         return _CShape(self.L, self.B, self.Hk, self.Hv, self.Dk, self.Dv, self.K,
                        int(self.silu), float(self.eps),
-                       GDN_BF16 if self.dtype == torch.bfloat16 else GDN_F32)
+                       GDN_BF16 if self.dtype == torch.bfloat16 else GDN_F32,
+                       int(self.gate_per_key))
+
+    def gate_shape(self, T: int) -> tuple:
+        """Shape of the decay gate a and of the tape's g for T tokens."""
+        return ((self.L, self.B, T, self.Hv, self.Dk) if self.gate_per_key
+                else (self.L, self.B, T, self.Hv))
 
 
 _lib = None
@@ -164,7 +172,8 @@ def _opt(t, name, dtype, shape, align: int = 4):
 
 @dataclass
 class Tape:
-    """Innovation tape: u [L,B,T,Hv,Dv], k [L,B,T,Hk,Dk], g [L,B,T,Hv] (fp32)."""
+    """Innovation tape: u [L,B,T,Hv,Dv], k [L,B,T,Hk,Dk], g [L,B,T,Hv]
+    ([L,B,T,Hv,Dk] with a per-key-channel gate), all fp32."""
     u: torch.Tensor
     k: torch.Tensor
     g: torch.Tensor
@@ -174,12 +183,12 @@ class Tape:
         f = dict(device=device, dtype=torch.float32)
         return Tape(torch.empty((sh.L, sh.B, T, sh.Hv, sh.Dv), **f),
                     torch.empty((sh.L, sh.B, T, sh.Hk, sh.Dk), **f),
-                    torch.empty((sh.L, sh.B, T, sh.Hv), **f))
+                    torch.empty(sh.gate_shape(T), **f))
 
     def c(self, sh: GdnShape, T: int) -> _CTape:
         return _CTape(_need(self.u, "tape.u", torch.float32, (sh.L, sh.B, T, sh.Hv, sh.Dv)),
                       _need(self.k, "tape.k", torch.float32, (sh.L, sh.B, T, sh.Hk, sh.Dk)),
-                      _need(self.g, "tape.g", torch.float32, (sh.L, sh.B, T, sh.Hv), 4))
+                      _need(self.g, "tape.g", torch.float32, sh.gate_shape(T), 4))
 
 
 def _verify_ptrs(sh: GdnShape, T: int, x, conv_state, conv_w, a, b, S, o):
@@ -187,7 +196,7 @@ def _verify_ptrs(sh: GdnShape, T: int, x, conv_state, conv_w, a, b, S, o):
     return [_need(x, "x", dt, (sh.L, sh.B, T, sh.C)),
             _need(conv_state, "conv_state", dt, (sh.L, sh.B, sh.K - 1, sh.C)),
             _need(conv_w, "conv_w", torch.float32, (sh.L, sh.C, sh.K)),
-            _need(a, "a", dt, (sh.L, sh.B, T, sh.Hv), 2),
+            _need(a, "a", dt, sh.gate_shape(T), 2),
             _need(b, "b", dt, (sh.L, sh.B, T, sh.Hv), 2),
             _need(S, "S", torch.float32, (sh.L, sh.B, sh.Hv, sh.Dv, sh.Dk)),
             _need(o, "o", torch.float32, (sh.L, sh.B, T, sh.Hv, sh.Dv))]

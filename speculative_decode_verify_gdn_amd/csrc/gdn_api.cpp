@@ -33,6 +33,7 @@ gdn_status check_shape(const gdn_shape* s, int32_t T) {
   if (T < 1) return GDN_ERR_INVALID_ARG;
   if (s->in_dtype != GDN_F32 && s->in_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   if (!(s->l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  if (s->gate_per_key != 0 && s->gate_per_key != 1) return GDN_ERR_INVALID_ARG;
   if (T > kMaxT) return GDN_ERR_UNSUPPORTED;
   if (!dim_ok(s->d_k) || !dim_ok(s->d_v) || s->d_k != s->d_v) return GDN_ERR_UNSUPPORTED;
   if (s->conv_kernel < 2 || s->conv_kernel > 8) return GDN_ERR_UNSUPPORTED;
@@ -100,6 +101,8 @@ gdn_status gdn_verify_chunk(const gdn_shape* shape, int32_t T, const void* x,
   if (!verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape)) return GDN_ERR_INVALID_ARG;
   VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (shape->gate_per_key)
+    return launch_status(gdn::launch_verify_vg(v, shape->d_k, shape->d_v, shape->in_dtype, s));
   if (T <= 16) return launch_status(gdn::launch_verify_chain(v, shape->d_k, shape->d_v, shape->in_dtype, s));
   return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype, s));
 }
@@ -111,6 +114,7 @@ gdn_status gdn_verify_chunk_replay(const gdn_shape* shape, int32_t T, const void
                                    const int32_t* prev_n_keep, int32_t* dev_err, void* stream) {
   gdn_status st = check_shape(shape, T);
   if (st != GDN_OK) return st;
+  if (shape->gate_per_key) return GDN_ERR_UNSUPPORTED;
   if (!verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape)) return GDN_ERR_INVALID_ARG;
   if (!prev_tape || !prev_tape->u || !prev_tape->k || !prev_tape->g || !prev_n_keep)
     return GDN_ERR_INVALID_ARG;
@@ -142,6 +146,7 @@ gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* par
                            void* stream) {
   gdn_status st = check_shape(shape, T);
   if (st != GDN_OK) return st;
+  if (shape->gate_per_key) return GDN_ERR_UNSUPPORTED;
   if (!parent || !verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape))
     return GDN_ERR_INVALID_ARG;
   VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
@@ -162,6 +167,7 @@ gdn_status gdn_tree_verify_replay(const gdn_shape* shape, int32_t T, const int32
                                   const int32_t* prev_n_keep, int32_t* dev_err, void* stream) {
   gdn_status st = check_shape(shape, T);
   if (st != GDN_OK) return st;
+  if (shape->gate_per_key) return GDN_ERR_UNSUPPORTED;
   if (!parent || !verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape))
     return GDN_ERR_INVALID_ARG;
   if (!prev_tape || !prev_tape->u || !prev_tape->k || !prev_tape->g || !prev_n_keep)
@@ -285,6 +291,9 @@ gdn_status gdn_tape_rollback(const gdn_shape* shape, int32_t T, float* S, const 
   r.Hk = shape->n_k_heads;
   r.Hv = shape->n_v_heads;
   r.T = T;
+  if (shape->gate_per_key)
+    return launch_status(gdn::launch_tape_rollback_vg(r, shape->d_k, shape->d_v,
+                                                      static_cast<hipStream_t>(stream)));
   return launch_status(gdn::launch_tape_rollback(r, shape->d_k, shape->d_v,
                                                  static_cast<hipStream_t>(stream)));
 }
@@ -332,6 +341,7 @@ gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* c
                        void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream) {
   gdn_status st = check_shape(shape, 1);
   if (st != GDN_OK) return st;
+  if (shape->gate_per_key) return GDN_ERR_UNSUPPORTED;
   if (T < 1) return GDN_ERR_INVALID_ARG;
   if (!x || !conv_state || !conv_w || !a || !b || !S || !o) return GDN_ERR_INVALID_ARG;
   const size_t need = gdn_prefill_workspace_bytes(shape);

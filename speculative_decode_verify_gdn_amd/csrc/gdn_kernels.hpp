@@ -112,6 +112,10 @@ hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, h
 // Trees of 33..64 nodes, 128-dim heads, bf16 inputs (per-node path solve).
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream_t s);
+// Per-key-channel decay gate: sequential verify of chains of <= 64 tokens
+// (a [L,B,T,Hv,Dk], tape g [L,B,T,Hv,Dk]) and its tape rollback.
+hipError_t launch_verify_vg(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
+hipError_t launch_tape_rollback_vg(const RollbackArgs& a, int dk, int dv, hipStream_t s);
 hipError_t launch_conv_rollback(const ConvRollbackArgs& a, int dtype, hipStream_t s);
 hipError_t launch_accept(const AcceptArgs& a, int dtype, hipStream_t s);
 

@@ -136,6 +136,120 @@ hipError_t launch_rb(const RollbackArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Per-key-channel decay (the [B,T,Hv,Dk] decay tape): the closed form
+// becomes S_n = S0 diag(gamma) + sum_i u_{p_i} (k_{p_i} o w_i)^T with
+// w_i[c] = prod_{j>i} g_{p_j}[c] and gamma[c] = prod_j g_{p_j}[c].  One
+// thread per key channel forms the weights backwards along the path and
+// stages k o w for all n <= 64 steps at once; the state pass is as above.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_tape_rollback_vg(RollbackArgs p) {
+  constexpr int NT = 256;
+  constexpr int VPT = 4;
+  constexpr int RB0 = NT * VPT * 4 / DK;
+  constexpr int RB = RB0 < DV ? RB0 : DV;
+  constexpr int NRBLK = DV / RB;
+  constexpr int C4 = DK / 4;
+  constexpr int NV = RB * C4;
+  constexpr int TM = 64;
+  static_assert(DV % RB == 0 && NV <= NT * VPT && DK <= NT, "row blocks");
+
+  __shared__ __align__(16) float s_kw[TM * DK];
+  __shared__ float s_u[TM * RB];
+  __shared__ __align__(16) float s_gam[DK];
+  __shared__ int s_pi[TM];
+  __shared__ int s_bad;
+
+  const int tid = threadIdx.x;
+  const int rblk = blockIdx.x % NRBLK;
+  const int rest = blockIdx.x / NRBLK;
+  const int hv = rest % p.Hv;
+  const size_t lb = rest / p.Hv;
+  const int bb = static_cast<int>(lb % p.B);
+  const int l = static_cast<int>(lb / p.B);
+  const int T = p.T;
+  const int n = p.n_keep ? p.n_keep[bb] : p.n_all;
+  if (n == 0) return;
+  if (n < 0 || n > T) {
+    if (tid == 0 && p.dev_err && l == 0 && hv == 0 && rblk == 0) atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
+    return;
+  }
+  const int hk = hv / (p.Hv / p.Hk);
+  const int r0 = rblk * RB;
+  float* Sblk = p.S + ((lb * p.Hv + hv) * DV + r0) * static_cast<size_t>(DK);
+
+  floatx4 sv[VPT];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int e = tid + v * NT;
+    sv[v] = reinterpret_cast<const floatx4*>(Sblk)[e < NV ? e : 0];
+  }
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (tid < n) {
+    const int pi = p.path ? p.path[static_cast<size_t>(bb) * T + tid] : tid;
+    if (pi < 0 || pi >= T) s_bad = 1;
+    s_pi[tid] = pi < 0 ? 0 : (pi >= T ? T - 1 : pi);
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0 && p.dev_err && l == 0 && hv == 0 && rblk == 0) atomicOr(p.dev_err, GDN_DEV_ERR_PATH);
+    return;
+  }
+  if (tid < DK) {  // channel tid: weights backwards along the path
+    float w = 1.f;
+    for (int i1 = n; i1 > 0; i1 -= 16) {  // 16 steps' loads in flight at once
+      const int i0 = i1 - 16 > 0 ? i1 - 16 : 0;
+      float kv[16], gv[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = i1 - 1 - q;
+        const size_t t = lb * T + s_pi[i >= i0 ? i : i0];
+        kv[q] = p.tk[(t * p.Hk + hk) * DK + tid];
+        gv[q] = p.tg[(t * p.Hv + hv) * DK + tid];
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = i1 - 1 - q;
+        if (i >= i0) {
+          s_kw[i * DK + tid] = kv[q] * w;
+          w *= gv[q];
+        }
+      }
+    }
+    s_gam[tid] = w;
+  }
+  for (int e = tid; e < n * RB; e += NT) {
+    const int i = e / RB, rr = e % RB;
+    s_u[e] = p.tu[((lb * T + s_pi[i]) * p.Hv + hv) * DV + r0 + rr];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int e = tid + v * NT;
+    const int rr = (e % NV) / C4, c = (e % C4) * 4;
+    floatx4 acc = sv[v] * *reinterpret_cast<const floatx4*>(s_gam + c);
+    for (int i = 0; i < n; ++i) {
+      const float u = s_u[i * RB + rr];
+      const floatx4 k = *reinterpret_cast<const floatx4*>(s_kw + i * DK + c);
+      acc[0] = fmaf(u, k[0], acc[0]);
+      acc[1] = fmaf(u, k[1], acc[1]);
+      acc[2] = fmaf(u, k[2], acc[2]);
+      acc[3] = fmaf(u, k[3], acc[3]);
+    }
+    if (e < NV) reinterpret_cast<floatx4*>(Sblk)[e] = acc;
+  }
+}
+
+template <int DK, int DV>
+hipError_t launch_rb_vg(const RollbackArgs& a, hipStream_t s) {
+  constexpr int RB0 = 256 * 4 * 4 / DK;
+  constexpr int RB = RB0 < DV ? RB0 : DV;
+  const long long grid = static_cast<long long>(a.L) * a.B * a.Hv * (DV / RB);
+  if (grid > 0x7fffffffLL || a.T > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_tape_rollback_vg<DK, DV>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 // 16-byte chunks of channels per thread; KM1 = K-1 window rows.
 template <int ESZ, int KM1>
 __global__ __launch_bounds__(256) void k_conv_rollback(ConvRollbackArgs p) {
@@ -213,6 +327,16 @@ hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream
     case 32: return launch_rb<32, 32>(a, s);
     case 64: return launch_rb<64, 64>(a, s);
     case 128: return launch_rb<128, 128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_tape_rollback_vg(const RollbackArgs& a, int dk, int dv, hipStream_t s) {
+  if (dk != dv) return hipErrorInvalidValue;
+  switch (dk) {
+    case 32: return launch_rb_vg<32, 32>(a, s);
+    case 64: return launch_rb_vg<64, 64>(a, s);
+    case 128: return launch_rb_vg<128, 128>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

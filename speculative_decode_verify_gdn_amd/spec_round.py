@@ -13,6 +13,7 @@ arithmetic happens in libgdnverify.
 """
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -65,8 +66,7 @@ class RoundBuffers:
         if self.tree and self.conv_win is None:
             self.conv_win = torch.zeros((sh.B, T, sh.K), **i32)
         self.dev_err = torch.zeros((1,), **i32)
-        self.layer_shape = gb.GdnShape(1, sh.B, sh.Hk, sh.Hv, sh.Dk, sh.Dv, sh.K, sh.silu,
-                                       sh.eps, sh.dtype)
+        self.layer_shape = dataclasses.replace(sh, L=1)
 
     def layer_tape(self, l: int) -> gb.Tape:
         return gb.Tape(self.tape.u[l:l + 1], self.tape.k[l:l + 1], self.tape.g[l:l + 1])

@@ -656,3 +656,117 @@ def test_prefill_matches_sequential_oracle(T, L, B, Hk, Hv, D, K, dtype):
     assert rel_fro(o.cpu().double().numpy(), ref["o"]) <= 1e-4
     assert rel_fro(S.cpu().double().numpy(), ref["S_final"]) <= 1e-4
     np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
+
+
+# ------------------------------------------------ per-key-channel decay gate --
+
+def _vg_inputs(cfg, seed, gate_lo=0.05):
+    """Workload inputs with the decay gate drawn per key channel, U(gate_lo, 1),
+    rounded to the input dtype."""
+    inp = W.layer_inputs(cfg, seed, "cpu")
+    gen = torch.Generator().manual_seed(1000 + seed)
+    a = gate_lo + (1 - gate_lo) * torch.rand((cfg.L, cfg.B, cfg.T, cfg.Hv, cfg.Dk), generator=gen)
+    inp["a"] = a.to(cfg.dtype)
+    return inp
+
+
+def _vg_shapes(cfg):
+    g = gb.GdnShape(cfg.L, cfg.B, cfg.Hk, cfg.Hv, cfg.Dk, cfg.Dv, cfg.K, cfg.silu, cfg.eps,
+                    cfg.dtype, gate_per_key=True)
+    o = oracle.Shape(L=cfg.L, B=cfg.B, Hk=cfg.Hk, Hv=cfg.Hv, Dk=cfg.Dk, Dv=cfg.Dv, K=cfg.K,
+                     silu=cfg.silu, eps=cfg.eps)
+    return g, o
+
+
+@pytest.mark.parametrize("T,L,B,Hk,Hv,D,K,dtype", [
+    (1, 1, 2, 2, 4, 128, 4, torch.bfloat16), (8, 2, 2, 2, 4, 128, 4, torch.bfloat16),
+    (16, 1, 3, 1, 2, 64, 3, torch.float32), (17, 1, 2, 2, 4, 128, 4, torch.bfloat16),
+    (64, 1, 1, 1, 3, 32, 6, torch.float32), (40, 1, 2, 4, 4, 64, 4, torch.bfloat16)])
+def test_vgate_verify_matches_oracle(T, L, B, Hk, Hv, D, K, dtype):
+    """gdn_verify_chunk with a per-key-channel gate (sequential kernel) equals
+    the oracle's verify_chunk_vg: outputs and tape; S is left untouched."""
+    _need_gpu()
+    cfg = W.CONFIGS[2].with_(L=L, B=B, Hk=Hk, Hv=Hv, Dk=D, Dv=D, K=K, T=T, dtype=dtype)
+    inp = _vg_inputs(cfg, 3)
+    gsh, osh = _vg_shapes(cfg)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    S0 = d["S0"].clone()
+    o = torch.empty((L, B, T, Hv, D), device=DEV)
+    tape = gb.Tape.empty(gsh, T, DEV)
+    gb.gdn_verify_chunk(gsh, d["x"], d["conv_state"], d["conv_w"], d["a"], d["b"], d["S0"], o, tape)
+    torch.cuda.synchronize()
+    f = {k: W.to_f64(v) for k, v in inp.items()}
+    ref = oracle.verify_chunk_vg(osh, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"], f["S0"])
+    for name, got in (("o", o), ("u", tape.u), ("k", tape.k)):
+        err = rel_fro(got.cpu().double().numpy(), ref[name])
+        assert err <= 1e-4, (name, err)
+    np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
+    assert torch.equal(d["S0"], S0)
+
+
+@pytest.mark.parametrize("D,with_path", [(128, False), (64, True), (32, False)])
+def test_vgate_rollback_matches_oracle(D, with_path):
+    """gdn_tape_rollback with the per-key decay tape equals the oracle's
+    tape_rollback_vg for accepted lengths 0..T, chains or arbitrary paths."""
+    _need_gpu()
+    T, B = 12, 5
+    cfg = W.CONFIGS[2].with_(L=2, B=B, Hk=2, Hv=4, Dk=D, Dv=D, T=T, dtype=torch.bfloat16)
+    gsh, osh = _vg_shapes(cfg)
+    gen = torch.Generator().manual_seed(21)
+    S0 = torch.randn((cfg.L, B, cfg.Hv, D, D), generator=gen) * 0.1
+    u = torch.randn((cfg.L, B, T, cfg.Hv, D), generator=gen)
+    k = torch.nn.functional.normalize(torch.randn((cfg.L, B, T, cfg.Hk, D), generator=gen), dim=-1)
+    g = 0.05 + 0.95 * torch.rand((cfg.L, B, T, cfg.Hv, D), generator=gen)
+    nk = torch.tensor([0, 1, 5, T, 7], dtype=torch.int32)
+    path = None
+    if with_path:
+        path = torch.full((B, T), -1, dtype=torch.int32)
+        for bb in range(B):
+            perm = torch.randperm(T, generator=gen)[: int(nk[bb])]
+            path[bb, : int(nk[bb])] = perm.to(torch.int32)
+    S = S0.to(DEV).clone()
+    gb.gdn_tape_rollback(gsh, S, gb.Tape(u.to(DEV), k.to(DEV), g.to(DEV)), nk.to(DEV),
+                         path=None if path is None else path.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.tape_rollback_vg(osh, S0.double().numpy(), u.double().numpy(),
+                                  k.double().numpy(), g.double().numpy(), nk.numpy(),
+                                  None if path is None else path.numpy())
+    assert rel_fro(S.cpu().double().numpy(), ref) <= 1e-5
+    assert torch.equal(S[:, 0].cpu(), S0[:, 0])  # n = 0: untouched
+
+
+def test_vgate_chained_rounds():
+    """Plain rounds (verify, greedy accept, per-key rollback, conv rollback)
+    with a per-key-channel gate, four rounds chained, against the oracle."""
+    _need_gpu()
+    cfg = W.CONFIGS[3].with_(L=2, B=4, T=8, V=257)
+    gsh, osh = _vg_shapes(cfg)
+    inp0 = _vg_inputs(cfg, 0)
+    oS, ocs = W.to_f64(inp0["S0"]), W.to_f64(inp0["conv_state"])
+    rb = None
+    for r in range(4):
+        inp = _vg_inputs(cfg, r)
+        acc = W.chain_accept_inputs(cfg, r, "cpu")
+        d = {k: v.to(DEV) for k, v in inp.items()}
+        if rb is None:
+            rb = spec_round.RoundBuffers(sh=gsh, T=cfg.T, V=cfg.V, tree=False,
+                                         S=inp0["S0"].to(DEV), conv_state=inp0["conv_state"].to(DEV),
+                                         conv_w=d["conv_w"], x=d["x"], a=d["a"], b=d["b"],
+                                         logits=acc["logits"].to(DEV), draft=acc["draft"].to(DEV),
+                                         parent=None)
+        else:
+            rb.x, rb.a, rb.b, rb.conv_w = d["x"], d["a"], d["b"], d["conv_w"]
+            rb.logits, rb.draft = acc["logits"].to(DEV), acc["draft"].to(DEV)
+        spec_round.run_round(rb)
+        torch.cuda.synchronize()
+        f = {k: W.to_f64(v) for k, v in inp.items()}
+        ref = oracle.verify_chunk_vg(osh, f["x"], ocs, f["conv_w"], f["a"], f["b"], oS)
+        n, path, bonus = oracle.accept(acc["draft"].numpy(), W.to_f64(acc["logits"]))
+        np.testing.assert_array_equal(rb.n_keep.cpu().numpy(), n)
+        np.testing.assert_array_equal(rb.bonus.cpu().numpy(), bonus)
+        assert rel_fro(rb.o.cpu().double().numpy(), ref["o"]) <= 1e-4
+        oS = oracle.tape_rollback_vg(osh, oS, ref["u"], ref["k"], ref["g"], n)
+        ocs, _ = oracle.conv_rollback(osh, ocs, f["x"], n)
+        assert rel_fro(rb.S.cpu().double().numpy(), oS) <= 1e-4
+        np.testing.assert_array_equal(rb.conv_state.cpu().double().numpy(), ocs)
+    assert int(rb.dev_err.item()) == 0
