@@ -358,13 +358,17 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
           acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m], bu, acc[m], 0, 0, 0);
       }
       const float gam = s_pgam;
+#pragma unroll
+      for (int m = 0; m < TR_D / 16; ++m) sreg[m] = sreg[m] * gam + acc[m];
+    }
+  };
+  // the rolled tile back to the live state
+  auto store_replayed = [&]() {
+    if constexpr (RP) {
       float* wrow = p.S_out + (lb * p.Hv + hv) * static_cast<size_t>(TR_D * TR_D) +
                     static_cast<size_t>(wave * 16 + c16) * TR_D + 4 * kk;
 #pragma unroll
-      for (int m = 0; m < TR_D / 16; ++m) {
-        sreg[m] = sreg[m] * gam + acc[m];
-        *reinterpret_cast<floatx4*>(wrow + 16 * m) = sreg[m];
-      }
+      for (int m = 0; m < TR_D / 16; ++m) *reinterpret_cast<floatx4*>(wrow + 16 * m) = sreg[m];
     }
   };
 
@@ -375,6 +379,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
 #pragma unroll
       for (int m = 0; m < TR_D / 16; ++m) sreg[m] = *reinterpret_cast<const floatx4*>(srow + 16 * m);
       replay();
+      store_replayed();
     }
     return;
   }
@@ -645,7 +650,12 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) col[r * TR_VLD] = bt * (col[r * TR_VLD] - gam_c[cb] * acc1[cb][r]);
   }
+  // The rolled tiles go back to the live state where the stores cost least:
+  // waves 1..7 while they wait for wave 0's solve at the barrier below,
+  // wave 0 once past it (its stores then drain under the dense operand).
+  if (RP && pn > 0 && wave != 0) store_replayed();
   __syncthreads();  // (B_d) packed Ti, M2; RHS; K/Q space free
+  if (RP && pn > 0 && wave == 0) store_replayed();
 
   // ----------------------- dense pre-split [Ti; M2] in the K/Q space --
 #pragma unroll
