@@ -290,7 +290,7 @@ def draft_sweep(cfg, stream, Ns=(1, 2, 4, 8, 16), reps=10):
             "chosen_draft_length": chosen}
 
 
-def prefill_pass(cfg, n_tokens, stream, reps=3):
+def prefill_pass(cfg, n_tokens, stream, reps=3, gate_per_key=False):
     """gdn_prefill of n_tokens through the workload's L layers and B
     sequences (graph replay): time per call, prefilled tokens/s (B x
     n_tokens per call; each layer sees every token) and the HBM fraction of
@@ -301,9 +301,15 @@ def prefill_pass(cfg, n_tokens, stream, reps=3):
     from speculative_decode_verify_gdn_amd import workload as W
     c = cfg.with_(T=n_tokens)
     inp = W.layer_inputs(c, 0, "cuda")
-    sh = gb.GdnShape(c.L, c.B, c.Hk, c.Hv, c.Dk, c.Dv, c.K, c.silu, c.eps, c.dtype)
+    sh = gb.GdnShape(c.L, c.B, c.Hk, c.Hv, c.Dk, c.Dv, c.K, c.silu, c.eps, c.dtype,
+                     gate_per_key=gate_per_key)
+    if gate_per_key:
+        gen = torch.Generator(device="cuda").manual_seed(c.seed ^ 0x3C)
+        inp["a"] = (0.05 + 0.95 * torch.rand(sh.gate_shape(n_tokens), device="cuda",
+                                             generator=gen)).to(c.dtype)
     o = torch.empty((c.L, c.B, n_tokens, c.Hv, c.Dv), device="cuda")
-    ws = torch.empty((gb.gdn_prefill_workspace_bytes(sh),), device="cuda", dtype=torch.uint8)
+    need = gb.gdn_prefill_workspace_bytes(sh)
+    ws = torch.empty((need,), device="cuda", dtype=torch.uint8) if need else None
     S, cs = inp["S0"], inp["conv_state"]
     call = lambda: gb.gdn_prefill(sh, inp["x"], cs, inp["conv_w"], inp["a"], inp["b"], S, o, ws)
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -323,14 +329,18 @@ def prefill_pass(cfg, n_tokens, stream, reps=3):
     ms = a.elapsed_time(b) / reps
     esz = 2 if c.dtype == torch.bfloat16 else 4
     P = c.Hv * c.Dv * c.Dk * 4
-    chunks = (n_tokens + 15) // 16
+    # the per-key form runs the recurrence in one pass: one state read and write
+    chunks = 1 if gate_per_key else (n_tokens + 15) // 16
     tape_tok = c.Hv * c.Dv * 4 + c.Hk * c.Dk * 4 + c.Hv * 4
-    per_seq = chunks * 2 * P + n_tokens * (c.C * esz + 2 * c.Hv * esz + c.Hv * c.Dv * 4
-                                           + 2 * tape_tok) + chunks * 2 * (c.K - 1) * c.C * esz
+    gate = c.Hv * (c.Dk if gate_per_key else 1) * esz + c.Hv * esz
+    tape = 0 if gate_per_key else 2 * tape_tok
+    per_seq = chunks * 2 * P + n_tokens * (c.C * esz + gate + c.Hv * c.Dv * 4 + tape) \
+        + chunks * 2 * (c.K - 1) * c.C * esz
     byts = c.L * c.B * per_seq
     del inp, o, ws
     torch.cuda.empty_cache()
-    return {"tokens": n_tokens, "layers": c.L, "batch": c.B, "ms_per_call": ms,
+    return {"tokens": n_tokens, "layers": c.L, "batch": c.B, "gate_per_key": gate_per_key,
+            "ms_per_call": ms,
             "tokens_per_s": c.B * n_tokens / (ms * 1e-3), "algorithmic_bytes": byts,
             "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
@@ -704,6 +714,8 @@ def main():
         sampled = sample_accept_pass(cfg, rbs[0], stream, args.steps)
 
     pre = prefill_pass(cfg, args.prefill, stream) if args.prefill > 0 else None
+    pre_vg = (prefill_pass(cfg, args.prefill, stream, gate_per_key=True)
+              if args.prefill > 0 and args.gate_per_key and not cfg.is_tree else None)
     vgate = vgate_pass(cfg, stream, args.steps) if args.gate_per_key and not cfg.is_tree else None
 
     dsweep = None
@@ -782,6 +794,8 @@ def main():
         out["sample_accept"] = sampled
     if pre is not None:
         out["prefill"] = pre
+    if pre_vg is not None:
+        out["prefill_per_key_gate"] = pre_vg
     if vgate is not None:
         out["per_key_gate"] = vgate
     if dsweep is not None:

@@ -88,8 +88,8 @@ typedef struct {
                            1: they are [..,Hv,Dk], one per v-head and key
                            channel (S decays column by column:
                            S <- S diag(a_t) before each step).  Supported by
-                           gdn_verify_chunk, gdn_tape_rollback and the conv
-                           rollback; the other calls return
+                           gdn_verify_chunk, gdn_tape_rollback, the conv
+                           rollback and gdn_prefill; the other calls return
                            GDN_ERR_UNSUPPORTED.  Source: GDN page s4 (the two
                            forms of the decay tape). */
 } gdn_shape;
@@ -276,7 +276,9 @@ gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* c
                        const float* conv_w, const void* a, const void* b, float* S, float* o,
                        void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
 
-/* Bytes of device workspace gdn_prefill needs for this shape (any T). */
+/* Bytes of device workspace gdn_prefill needs for this shape (any T).  With
+ * gate_per_key the prefill runs the recurrence in one launch and needs no
+ * workspace (NULL is accepted). */
 size_t gdn_prefill_workspace_bytes(const gdn_shape* shape);
 
 /*

@@ -256,15 +256,18 @@ def gdn_prefill(sh: GdnShape, x, conv_state, conv_w, a, b, S, o, workspace, dev_
     T = int(x.shape[2])
     ptrs = _verify_ptrs(sh, T, x, conv_state, conv_w, a, b, S, o)
     need = gdn_prefill_workspace_bytes(sh)
-    if (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8
+    if need == 0 and workspace is None:
+        wp, wn = None, 0
+    elif (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8
             or workspace.numel() < need or not workspace.is_cuda
             or not workspace.is_contiguous() or workspace.data_ptr() % 256):
         raise ValueError("workspace must be a 256-byte aligned device uint8 tensor of >= %d bytes"
                          % need)
+    else:
+        wp, wn = workspace.data_ptr(), workspace.numel()
     de = _opt(dev_err, "dev_err", torch.int32, (1,))
     _dev(x.device, conv_state, conv_w, a, b, S, o, workspace, dev_err)
-    _check(lib().gdn_prefill(ctypes.byref(sh.c()), T, *ptrs, workspace.data_ptr(),
-                             workspace.numel(), de, _stream(stream)),
+    _check(lib().gdn_prefill(ctypes.byref(sh.c()), T, *ptrs, wp, wn, de, _stream(stream)),
            "gdn_prefill")
 
 

@@ -333,6 +333,7 @@ size_t tape_floats(const gdn_shape* s, int T) {
 
 size_t gdn_prefill_workspace_bytes(const gdn_shape* shape) {
   if (check_shape(shape, kPrefillChunk) != GDN_OK) return 0;
+  if (shape->gate_per_key) return 0;  // one launch, no tape
   return 2 * ((tape_floats(shape, kPrefillChunk) * sizeof(float) + 255) / 256 * 256);
 }
 
@@ -341,13 +342,34 @@ gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* c
                        void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream) {
   gdn_status st = check_shape(shape, 1);
   if (st != GDN_OK) return st;
-  if (shape->gate_per_key) return GDN_ERR_UNSUPPORTED;
   if (T < 1) return GDN_ERR_INVALID_ARG;
   if (!x || !conv_state || !conv_w || !a || !b || !S || !o) return GDN_ERR_INVALID_ARG;
-  const size_t need = gdn_prefill_workspace_bytes(shape);
-  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int C = channels(shape);
+  if (shape->gate_per_key) {
+    // one launch of the sequential kernel over all T tokens, committing the
+    // state, then the window; no tape, no workspace
+    gdn_tape none{nullptr, nullptr, nullptr};
+    VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, &none);
+    v.S_out = S;
+    v.dev_err = dev_err;
+    st = launch_status(gdn::launch_verify_vg(v, shape->d_k, shape->d_v, shape->in_dtype, s));
+    if (st != GDN_OK) return st;
+    ConvRollbackArgs cr{};
+    cr.conv_state = conv_state;
+    cr.x = x;
+    cr.n_all = T;
+    cr.dev_err = dev_err;
+    cr.L = shape->n_layers;
+    cr.B = shape->batch;
+    cr.K = shape->conv_kernel;
+    cr.T = T;
+    cr.C = C;
+    cr.x_ld = static_cast<size_t>(T) * C;
+    return launch_status(gdn::launch_conv_rollback(cr, shape->in_dtype, s));
+  }
+  const size_t need = gdn_prefill_workspace_bytes(shape);
+  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
   const size_t esz = shape->in_dtype == GDN_BF16 ? 2 : 4;
   const size_t Hv = shape->n_v_heads, Dv = shape->d_v;
   // two tapes of one chunk each, alternating: chunk c writes tape c % 2 and

@@ -17,7 +17,9 @@
 // in chunks of 16: all threads compute the chunk's conv + SiLU of the head's
 // q, k and v channels into LDS, one wave per token takes the q / k norms,
 // then every thread steps its row slice through the chunk.  S is read once
-// and not written (it stays the snapshot).
+// and not written (it stays the snapshot), except by the prefill, which sets
+// S_out, passes no tape, and gets the state after the last token written
+// back in place.
 
 #include "gdn_common.hpp"
 #include "gdn_kernels.hpp"
@@ -134,8 +136,8 @@ __global__ __launch_bounds__(vg_threads<D>()) void k_verify_vg(VerifyArgs p) {
         s_q[t][c] *= rq;
         const float kn = s_k[t][c] * rk;
         s_k[t][c] = kn;
-        if (g == 0) p.tk[((lb * T + t0 + t) * p.Hk + hk) * D + c] = kn;
-        p.tg[((lb * T + t0 + t) * p.Hv + hv) * D + c] = s_a[t][c];
+        if (p.tk && g == 0) p.tk[((lb * T + t0 + t) * p.Hk + hk) * D + c] = kn;
+        if (p.tg) p.tg[((lb * T + t0 + t) * p.Hv + hv) * D + c] = s_a[t][c];
       }
     }
     __syncthreads();
@@ -165,10 +167,16 @@ __global__ __launch_bounds__(vg_threads<D>()) void k_verify_vg(VerifyArgs p) {
       for (int off = TPR / 2; off >= 1; off >>= 1) od += __shfl_xor(od, off, kWave);
       if (h == 0) {
         const size_t oi = ((lb * T + t0 + t) * p.Hv + hv) * D + r;
-        p.tu[oi] = u;
+        if (p.tu) p.tu[oi] = u;
         p.o[oi] = od;
       }
     }
+  }
+  // committing (prefill): the state after the last token goes back in place
+  if (p.S_out) {
+    float* Sw = p.S_out + ((lb * p.Hv + hv) * D + r) * static_cast<size_t>(D) + c0;
+#pragma unroll
+    for (int j = 0; j < CPT / 4; ++j) reinterpret_cast<floatx4*>(Sw)[j] = S[j];
   }
 }
 
@@ -177,7 +185,9 @@ hipError_t launch_vg_t(const VerifyArgs& a, int d, hipStream_t s) {
   const int G = a.Hv / a.Hk;
   const int n_units = a.L * a.B * a.Hk;
   const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
-  if (grid > 0x7fffffffLL || a.T > 64 || a.K > 8) return hipErrorInvalidValue;
+  // verify writes a tape of T entries (T <= 64); committing (S_out set, no
+  // tape) takes any T
+  if (grid > 0x7fffffffLL || (a.T > 64 && !a.S_out) || a.K > 8) return hipErrorInvalidValue;
   switch (d) {
     case 32: hipLaunchKernelGGL((k_verify_vg<32, TIn>), dim3(grid), dim3(vg_threads<32>()), 0, s, a); break;
     case 64: hipLaunchKernelGGL((k_verify_vg<64, TIn>), dim3(grid), dim3(vg_threads<64>()), 0, s, a); break;

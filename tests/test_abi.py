@@ -126,8 +126,6 @@ def test_host_validation_before_launch(lib):
     assert lib.gdn_verify_chunk_replay(ctypes.byref(vg), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                        FAKE, ctypes.byref(cur), 4, ctypes.byref(prev), FAKE,
                                        None, None) == gb.GDN_ERR_UNSUPPORTED
-    assert lib.gdn_prefill(ctypes.byref(vg), 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                           1 << 30, None, None) == gb.GDN_ERR_UNSUPPORTED
     # prefill: bad T, missing pointers, short workspace
     pf = lambda T, xx, ws, wsb: lib.gdn_prefill(ctypes.byref(_shape()), T, xx, FAKE, FAKE, FAKE,
                                                 FAKE, FAKE, FAKE, ws, wsb, None, None)

@@ -770,3 +770,27 @@ def test_vgate_chained_rounds():
         assert rel_fro(rb.S.cpu().double().numpy(), oS) <= 1e-4
         np.testing.assert_array_equal(rb.conv_state.cpu().double().numpy(), ocs)
     assert int(rb.dev_err.item()) == 0
+
+
+@pytest.mark.parametrize("T,D,dtype", [(5, 128, torch.bfloat16), (70, 64, torch.float32),
+                                       (130, 128, torch.bfloat16)])
+def test_vgate_prefill_matches_oracle(T, D, dtype):
+    """gdn_prefill with a per-key-channel gate (one launch of the sequential
+    kernel, committing the state) equals the oracle's verify_chunk_vg over
+    all T tokens: outputs, final state, final conv window."""
+    _need_gpu()
+    cfg = W.CONFIGS[2].with_(L=1, B=2, Hk=2, Hv=4, Dk=D, Dv=D, K=4, T=T, dtype=dtype)
+    inp = _vg_inputs(cfg, 5)
+    gsh, osh = _vg_shapes(cfg)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    S, cs = d["S0"].clone(), d["conv_state"].clone()
+    o = torch.empty((1, 2, T, cfg.Hv, D), device=DEV)
+    assert gb.gdn_prefill_workspace_bytes(gsh) == 0
+    gb.gdn_prefill(gsh, d["x"], cs, d["conv_w"], d["a"], d["b"], S, o, None)
+    torch.cuda.synchronize()
+    f = {k: W.to_f64(v) for k, v in inp.items()}
+    ref = oracle.verify_chunk_vg(osh, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"], f["S0"])
+    cs_ref, _ = oracle.conv_rollback(osh, f["conv_state"], f["x"], np.full(2, T, np.int32))
+    assert rel_fro(o.cpu().double().numpy(), ref["o"]) <= 1e-4
+    assert rel_fro(S.cpu().double().numpy(), ref["S_final"]) <= 1e-4
+    np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
