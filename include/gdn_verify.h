@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum {
   GDN_OK = 0,
@@ -275,6 +275,20 @@ size_t spec_sample_workspace_bytes(int32_t B, int32_t T, int32_t V);
 gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* conv_state,
                        const float* conv_w, const void* a, const void* b, float* S, float* o,
                        void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
+
+/*
+ * gdn_tape_rollback followed by gdn_conv_state_rollback with the same T,
+ * path and n_keep, in one launch (the conv-window workgroups fill the tail
+ * of the state pass) when the conv width is 4 and the gate is per v-head;
+ * otherwise the two calls in sequence.  Arguments, results and errors are
+ * exactly those of the two calls.
+ * Source: GDN page s4 (restore and replay the state; rebuild the conv state
+ * from the qkv tape).
+ */
+gdn_status gdn_round_rollback(const gdn_shape* shape, int32_t T, float* S, const gdn_tape* tape,
+                              void* conv_state, const void* x, const int32_t* path,
+                              const int32_t* n_keep, int32_t* win_idx, int32_t* dev_err,
+                              void* stream);
 
 /* Bytes of device workspace gdn_prefill needs for this shape (any T).  With
  * gate_per_key the prefill runs the recurrence in one launch and needs no

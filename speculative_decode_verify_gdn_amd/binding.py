@@ -25,6 +25,7 @@ DEV_ERR_N_KEEP, DEV_ERR_PARENT, DEV_ERR_PATH, DEV_ERR_TOKEN = 1, 2, 4, 8
 EXPORTS = ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
            "gdn_tree_verify_replay", "spec_accept_prefix", "spec_accept_sample",
            "spec_sample_workspace_bytes", "gdn_prefill", "gdn_prefill_workspace_bytes",
+           "gdn_round_rollback",
            "spec_accept_workspace_bytes", "gdn_tape_rollback", "gdn_conv_state_rollback",
            "gdn_status_string", "gdn_abi_version")
 
@@ -110,13 +111,14 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill_workspace_bytes.argtypes = [SP]
         L.gdn_prefill_workspace_bytes.restype = SZ
         L.gdn_tape_rollback.argtypes = [SP, I32, P, TP, P, P, P, P]
+        L.gdn_round_rollback.argtypes = [SP, I32, P, TP, P, P, P, P, P, P, P]
         L.gdn_conv_state_rollback.argtypes = [SP, I32, P, P, P, P, P, P, P]
         L.gdn_status_string.argtypes = [I32]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
         for name in ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
                      "gdn_tree_verify_replay", "spec_accept_prefix", "spec_accept_sample",
-                     "gdn_prefill",
+                     "gdn_prefill", "gdn_round_rollback",
                      "gdn_tape_rollback", "gdn_conv_state_rollback", "gdn_abi_version"):
             getattr(L, name).restype = I32
         _lib = L
@@ -353,6 +355,25 @@ def spec_accept_sample(draft, logits, temperature: float, uniforms, n_keep, path
                                     float(temperature), up, *args, workspace.data_ptr(),
                                     workspace.numel(), de, _stream(stream)),
            "spec_accept_sample")
+
+
+def gdn_round_rollback(sh: GdnShape, S, tape: Tape, conv_state, x, n_keep, path=None,
+                       win_idx=None, dev_err=None, stream=None):
+    """gdn_tape_rollback + gdn_conv_state_rollback in one call (one launch
+    where the library can)."""
+    T = int(tape.g.shape[2])
+    dt = sh.dtype
+    sp = _need(S, "S", torch.float32, (sh.L, sh.B, sh.Hv, sh.Dv, sh.Dk))
+    ct = tape.c(sh, T)
+    cp = _need(conv_state, "conv_state", dt, (sh.L, sh.B, sh.K - 1, sh.C))
+    xp = _need(x, "x", dt, (sh.L, sh.B, T, sh.C))
+    np_ = _need(n_keep, "n_keep", torch.int32, (sh.B,), 4)
+    pp = _opt(path, "path", torch.int32, (sh.B, T))
+    wi = _opt(win_idx, "win_idx", torch.int32, (sh.B, sh.K - 1))
+    de = _opt(dev_err, "dev_err", torch.int32, (1,))
+    _dev(S.device, tape.u, tape.k, tape.g, conv_state, x, n_keep, path, win_idx, dev_err)
+    _check(lib().gdn_round_rollback(ctypes.byref(sh.c()), T, sp, ctypes.byref(ct), cp, xp, pp,
+                                    np_, wi, de, _stream(stream)), "gdn_round_rollback")
 
 
 def gdn_tape_rollback(sh: GdnShape, S, tape: Tape, n_keep, path=None, dev_err=None, stream=None):

@@ -437,6 +437,49 @@ gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* c
   return launch_status(gdn::launch_tape_rollback(r, shape->d_k, shape->d_v, s));
 }
 
+gdn_status gdn_round_rollback(const gdn_shape* shape, int32_t T, float* S, const gdn_tape* tape,
+                              void* conv_state, const void* x, const int32_t* path,
+                              const int32_t* n_keep, int32_t* win_idx, int32_t* dev_err,
+                              void* stream) {
+  gdn_status st = check_shape(shape, T);
+  if (st != GDN_OK) return st;
+  if (!S || !tape || !tape->u || !tape->k || !tape->g || !n_keep || !conv_state || !x)
+    return GDN_ERR_INVALID_ARG;
+  if (shape->gate_per_key || shape->conv_kernel != 4) {
+    st = gdn_tape_rollback(shape, T, S, tape, path, n_keep, dev_err, stream);
+    if (st != GDN_OK) return st;
+    return gdn_conv_state_rollback(shape, T, conv_state, x, path, n_keep, win_idx, dev_err, stream);
+  }
+  RollbackArgs r{};
+  r.S = S;
+  r.tu = tape->u;
+  r.tk = tape->k;
+  r.tg = tape->g;
+  r.path = path;
+  r.n_keep = n_keep;
+  r.dev_err = dev_err;
+  r.L = shape->n_layers;
+  r.B = shape->batch;
+  r.Hk = shape->n_k_heads;
+  r.Hv = shape->n_v_heads;
+  r.T = T;
+  ConvRollbackArgs c{};
+  c.conv_state = conv_state;
+  c.x = x;
+  c.path = path;
+  c.n_keep = n_keep;
+  c.win_idx = win_idx;
+  c.dev_err = dev_err;
+  c.L = shape->n_layers;
+  c.B = shape->batch;
+  c.K = shape->conv_kernel;
+  c.T = T;
+  c.C = channels(shape);
+  c.x_ld = static_cast<size_t>(T) * c.C;
+  return launch_status(gdn::launch_round_rollback(r, c, shape->d_k, shape->d_v, shape->in_dtype,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 const char* gdn_status_string(int32_t status) {
   switch (status) {
     case GDN_OK: return "GDN_OK";

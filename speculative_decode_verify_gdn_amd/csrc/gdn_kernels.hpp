@@ -112,6 +112,9 @@ hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, h
 // Trees of 33..64 nodes, 128-dim heads, bf16 inputs (per-node path solve).
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream_t s);
+// The state and conv-window rollbacks of a round in one launch.
+hipError_t launch_round_rollback(const RollbackArgs& r, const ConvRollbackArgs& c, int dk, int dv,
+                                 int dtype, hipStream_t s);
 // Per-key-channel decay gate: sequential verify of chains of <= 64 tokens
 // (a [L,B,T,Hv,Dk], tape g [L,B,T,Hv,Dk]) and its tape rollback.
 hipError_t launch_verify_vg(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);

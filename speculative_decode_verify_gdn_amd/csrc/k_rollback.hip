@@ -25,7 +25,7 @@ namespace gdn {
 namespace {
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_tape_rollback(RollbackArgs p) {
+__device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bid) {
   constexpr int NT = 256;
   constexpr int VPT = 4;                  // float4 per thread
   constexpr int RB0 = NT * VPT * 4 / DK;  // rows that fill the block
@@ -44,8 +44,8 @@ __global__ __launch_bounds__(256) void k_tape_rollback(RollbackArgs p) {
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
-  const int rblk = blockIdx.x % NRBLK;
-  const int rest = blockIdx.x / NRBLK;
+  const int rblk = bid % NRBLK;
+  const int rest = bid / NRBLK;
   const int hv = rest % p.Hv;
   const size_t lb = rest / p.Hv;
   const int bb = static_cast<int>(lb % p.B);
@@ -124,6 +124,11 @@ __global__ __launch_bounds__(256) void k_tape_rollback(RollbackArgs p) {
     const int e = tid + v * NT;
     if (e < NV) reinterpret_cast<floatx4*>(Sblk)[e] = acc[v];
   }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_tape_rollback(RollbackArgs p) {
+  tape_rollback_body<DK, DV>(p, blockIdx.x);
 }
 
 template <int DK, int DV>
@@ -252,15 +257,14 @@ hipError_t launch_rb_vg(const RollbackArgs& a, hipStream_t s) {
 
 // 16-byte chunks of channels per thread; KM1 = K-1 window rows.
 template <int ESZ, int KM1>
-__global__ __launch_bounds__(256) void k_conv_rollback(ConvRollbackArgs p) {
+__device__ __forceinline__ void conv_rollback_body(const ConvRollbackArgs& p, size_t lb, int by) {
   constexpr int EPC = 16 / ESZ;  // elements per chunk
   const int tid = threadIdx.x;
-  const size_t lb = blockIdx.x;
   const int bb = static_cast<int>(lb % p.B);
   const int l = static_cast<int>(lb / p.B);
   const int n = p.n_keep ? p.n_keep[bb] : p.n_all;
   const int T = p.T;
-  const bool first_block = (l == 0 && blockIdx.y == 0);
+  const bool first_block = (l == 0 && by == 0);
   if (n < 0 || n > T) {
     if (first_block && tid == 0 && p.dev_err) atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
     return;
@@ -288,20 +292,29 @@ __global__ __launch_bounds__(256) void k_conv_rollback(ConvRollbackArgs p) {
     for (int j = 0; j < KM1; ++j) p.win_idx[static_cast<size_t>(bb) * KM1 + j] = idx[j];
   }
   if (n == 0) return;  // window unchanged
-  const size_t chunk = static_cast<size_t>(blockIdx.y) * 256 + tid;
+  const size_t chunk = static_cast<size_t>(by) * 256 + tid;
   const size_t row_chunks = static_cast<size_t>(p.C) / EPC;
   if (chunk >= row_chunks) return;
   const uint4* xs = static_cast<const uint4*>(p.x);
   uint4* cs = static_cast<uint4*>(p.conv_state);
-  uint4 v[KM1];
+  // sources first (a select of addresses, so every load is unconditional)
+  const uint4* src[KM1];
 #pragma unroll
   for (int j = 0; j < KM1; ++j) {
     const int id = idx[j];
-    v[j] = id < 0 ? cs[(lb * KM1 + (KM1 + id)) * row_chunks + chunk]
-                  : xs[lb * (p.x_ld / EPC) + id * row_chunks + chunk];
+    src[j] = id < 0 ? cs + (lb * KM1 + (KM1 + id)) * row_chunks + chunk
+                    : xs + lb * (p.x_ld / EPC) + id * row_chunks + chunk;
   }
+  uint4 v[KM1];
+#pragma unroll
+  for (int j = 0; j < KM1; ++j) v[j] = *src[j];
 #pragma unroll
   for (int j = 0; j < KM1; ++j) cs[(lb * KM1 + j) * row_chunks + chunk] = v[j];
+}
+
+template <int ESZ, int KM1>
+__global__ __launch_bounds__(256) void k_conv_rollback(ConvRollbackArgs p) {
+  conv_rollback_body<ESZ, KM1>(p, blockIdx.x, blockIdx.y);
 }
 
 template <int ESZ>
@@ -331,12 +344,60 @@ hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream
   }
 }
 
+namespace {
+
+// Both rollbacks of a round in one launch: the state workgroups first, then
+// the conv-window ones, which fill the tail of the state pass.  Built for
+// the common conv width (K = 4); other widths take the two launches.
+template <int DK, int DV, int ESZ>
+__global__ __launch_bounds__(256) void k_round_rollback(RollbackArgs r, ConvRollbackArgs c,
+                                                        int n_state, int conv_y) {
+  const int bid = blockIdx.x;
+  if (bid < n_state) {
+    tape_rollback_body<DK, DV>(r, bid);
+  } else {
+    const int q = bid - n_state;
+    conv_rollback_body<ESZ, 3>(c, static_cast<size_t>(q / conv_y), q % conv_y);
+  }
+}
+
+template <int DK, int DV>
+hipError_t launch_rr(const RollbackArgs& r, const ConvRollbackArgs& c, int dtype, hipStream_t s) {
+  constexpr int RB0 = 256 * 4 * 4 / DK;
+  constexpr int RB = RB0 < DV ? RB0 : DV;
+  const long long n_state = static_cast<long long>(r.L) * r.B * r.Hv * (DV / RB);
+  const int esz = dtype == 1 ? 2 : 4;
+  const int conv_y = (c.C * esz / 16 + 255) / 256;
+  const long long grid = n_state + static_cast<long long>(c.L) * c.B * conv_y;
+  if (grid > 0x7fffffffLL || r.T > 64 || c.K != 4) return hipErrorInvalidValue;
+  if (dtype == 1)
+    hipLaunchKernelGGL((k_round_rollback<DK, DV, 2>), dim3(grid), dim3(256), 0, s, r, c,
+                       static_cast<int>(n_state), conv_y);
+  else
+    hipLaunchKernelGGL((k_round_rollback<DK, DV, 4>), dim3(grid), dim3(256), 0, s, r, c,
+                       static_cast<int>(n_state), conv_y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_tape_rollback_vg(const RollbackArgs& a, int dk, int dv, hipStream_t s) {
   if (dk != dv) return hipErrorInvalidValue;
   switch (dk) {
     case 32: return launch_rb_vg<32, 32>(a, s);
     case 64: return launch_rb_vg<64, 64>(a, s);
     case 128: return launch_rb_vg<128, 128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_round_rollback(const RollbackArgs& r, const ConvRollbackArgs& c, int dk, int dv,
+                                 int dtype, hipStream_t s) {
+  if (dk != dv) return hipErrorInvalidValue;
+  switch (dk) {
+    case 32: return launch_rr<32, 32>(r, c, dtype, s);
+    case 64: return launch_rr<64, 64>(r, c, dtype, s);
+    case 128: return launch_rr<128, 128>(r, c, dtype, s);
     default: return hipErrorInvalidValue;
   }
 }

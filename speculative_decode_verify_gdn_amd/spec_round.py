@@ -93,12 +93,11 @@ def accept(rb: RoundBuffers, stream=None):
 
 
 def rollback(rb: RoundBuffers, stream=None):
-    """Tape-replay the state and rebuild the conv window for all layers."""
+    """Tape-replay the state and rebuild the conv window for all layers (one
+    call; one launch where the library can)."""
     path = rb.path if rb.tree else None
-    gb.gdn_tape_rollback(rb.sh, rb.S, rb.tape, rb.n_keep, path=path, dev_err=rb.dev_err,
-                         stream=stream)
-    gb.gdn_conv_state_rollback(rb.sh, rb.conv_state, rb.x, rb.n_keep, path=path,
-                               win_idx=rb.win_idx, dev_err=rb.dev_err, stream=stream)
+    gb.gdn_round_rollback(rb.sh, rb.S, rb.tape, rb.conv_state, rb.x, rb.n_keep, path=path,
+                          win_idx=rb.win_idx, dev_err=rb.dev_err, stream=stream)
 
 
 def run_round(rb: RoundBuffers, stream=None):

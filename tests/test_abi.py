@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gb.abi_version() == 6
+    assert gb.abi_version() == 7
     assert gb.status_string(0) == "GDN_OK"
     assert gb.status_string(1) == "GDN_ERR_INVALID_ARG"
     assert gb.status_string(4) == "GDN_ERR_WORKSPACE"

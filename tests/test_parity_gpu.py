@@ -427,6 +427,62 @@ def test_accept_ties_and_ragged_vocab(dtype, V):
         np.testing.assert_array_equal(bonus.cpu().numpy(), b_ref)
 
 
+# ------------------------------------------------ one-launch round rollback -
+
+@pytest.mark.parametrize("K,dtype,tree", [(4, torch.bfloat16, False), (4, torch.float32, True),
+                                          (3, torch.bfloat16, True)])
+def test_round_rollback_equals_the_two_calls(K, dtype, tree):
+    """gdn_round_rollback (one launch at conv width 4, the two calls
+    otherwise) leaves S, the conv window and win_idx byte-identical to
+    gdn_tape_rollback followed by gdn_conv_state_rollback, for accepted
+    lengths 0..T on chains or arbitrary paths; both match the oracle."""
+    _need_gpu()
+    T, B, L, D = 11, 6, 2, 64
+    sh = gb.GdnShape(L, B, 2, 4, D, D, K, True, 1e-6, dtype)
+    gen = torch.Generator().manual_seed(31 + K)
+    S0 = torch.randn((L, B, 4, D, D), generator=gen) * 0.1
+    u = torch.randn((L, B, T, 4, D), generator=gen)
+    k = torch.nn.functional.normalize(torch.randn((L, B, T, 2, D), generator=gen), dim=-1)
+    g = 0.05 + 0.95 * torch.rand((L, B, T, 4), generator=gen)
+    C = sh.C
+    cs0 = torch.randn((L, B, K - 1, C), generator=gen).to(dtype)
+    x = torch.randn((L, B, T, C), generator=gen).to(dtype)
+    nk = torch.tensor([0, 1, 2, 5, T, 7], dtype=torch.int32)
+    path = None
+    if tree:
+        path = torch.full((B, T), -1, dtype=torch.int32)
+        for bb in range(B):
+            perm = torch.randperm(T, generator=gen)[: int(nk[bb])]
+            path[bb, : int(nk[bb])] = perm.to(torch.int32)
+    tape = gb.Tape(u.to(DEV), k.to(DEV), g.to(DEV))
+    pd = None if path is None else path.to(DEV)
+    outs = []
+    for combined in (True, False):
+        S, cs = S0.to(DEV).clone(), cs0.to(DEV).clone()
+        wi = torch.full((B, K - 1), -7, dtype=torch.int32, device=DEV)
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        if combined:
+            gb.gdn_round_rollback(sh, S, tape, cs, x.to(DEV), nk.to(DEV), path=pd, win_idx=wi,
+                                  dev_err=err)
+        else:
+            gb.gdn_tape_rollback(sh, S, tape, nk.to(DEV), path=pd, dev_err=err)
+            gb.gdn_conv_state_rollback(sh, cs, x.to(DEV), nk.to(DEV), path=pd, win_idx=wi,
+                                       dev_err=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        outs.append((S.cpu(), cs.cpu(), wi.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    osh = oracle.Shape(L=L, B=B, Hk=2, Hv=4, Dk=D, Dv=D, K=K, silu=True, eps=1e-6)
+    pnp = None if path is None else path.numpy()
+    ref = oracle.tape_rollback(osh, S0.double().numpy(), u.double().numpy(), k.double().numpy(),
+                               g.double().numpy(), nk.numpy(), pnp)
+    assert rel_fro(outs[0][0].double().numpy(), ref) <= 1e-5
+    cs_ref, wi_ref = oracle.conv_rollback(osh, W.to_f64(cs0), W.to_f64(x), nk.numpy(), pnp)
+    np.testing.assert_array_equal(outs[0][1].double().numpy(), cs_ref)
+    np.testing.assert_array_equal(outs[0][2].numpy(), wi_ref)
+
+
 # ------------------------------------------------------- device-side errors -
 
 def test_dev_err_bad_n_keep_leaves_state():
