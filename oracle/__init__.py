@@ -22,6 +22,10 @@ Parity status of each function (the pins live in ``tests/test_oracle_*.py``):
                           the matrix form S diag(a)(I - b k k^T) + b v k^T;
                           a zero gate erases its key column; replay of the
                           whole tape gives S_final.
+  tree_verify_vg          pinned: equal gates give tree_verify; chain parents
+                          give verify_chunk_vg; every node state and output
+                          against the matrix form along its root path; path
+                          replay of the tree's tape gives each node state.
   tape_rollback_vg        pinned: replay(n) == fresh recompute over n tokens,
                           equal gates give tape_rollback.
   accept_sample           pinned: the first output token's distribution equals
@@ -106,6 +110,8 @@ def _load():
         lib.oracle_verify_chunk.restype = I
         lib.oracle_tree_verify.argtypes = [SP, I] + [P] * 13
         lib.oracle_tree_verify.restype = I
+        lib.oracle_tree_verify_vg.argtypes = [SP, I] + [P] * 13
+        lib.oracle_tree_verify_vg.restype = I
         lib.oracle_accept.argtypes = [I, I, I, P, P, P, P, P, P]
         lib.oracle_accept.restype = I
         lib.oracle_tape_rollback.argtypes = [SP, I, P, P, P, P, P, P]
@@ -278,6 +284,38 @@ def tree_verify(sh: Shape, parent, x, conv_state, conv_w, a, b, S0,
     _check(_load().oracle_tree_verify(ctypes.byref(c), T, _p(parent), _p(x), _p(conv_state),
                                       _p(conv_w), _p(a), _p(b), _p(S0), _p(o), _p(u), _p(k),
                                       _p(g), _p(win), _p(Sn)), "tree_verify")
+    out = dict(o=o, u=u, k=k, g=g, conv_win=win)
+    if want_node_states:
+        out["S_nodes"] = Sn
+    return out
+
+
+def tree_verify_vg(sh: Shape, parent, x, conv_state, conv_w, a, b, S0,
+                   want_node_states=False) -> dict:
+    """tree_verify with a per-key-channel decay gate a (L, B, T, Hv, Dk):
+    node v steps from its parent's state as S <- S diag(a_v), u = b (v - S k),
+    S <- S + u k^T, o = S q.  Returns o, u, k, g (= a), conv_win and
+    optionally S_nodes."""
+    L, B, C = sh.L, sh.B, sh.C
+    x = _f64(x)
+    T = x.shape[2]
+    x = _f64(x, (L, B, T, C))
+    parent = _i32(parent, (B, T))
+    conv_state = _f64(conv_state, (L, B, sh.K - 1, C))
+    conv_w = _f64(conv_w, (L, C, sh.K))
+    a = _f64(a, (L, B, T, sh.Hv, sh.Dk))
+    b = _f64(b, (L, B, T, sh.Hv))
+    S0 = _f64(S0, (L, B, sh.Hv, sh.Dv, sh.Dk))
+    o = np.empty((L, B, T, sh.Hv, sh.Dv))
+    u = np.empty((L, B, T, sh.Hv, sh.Dv))
+    k = np.empty((L, B, T, sh.Hk, sh.Dk))
+    g = np.empty((L, B, T, sh.Hv, sh.Dk))
+    win = np.empty((B, T, sh.K), dtype=np.int32)
+    Sn = np.empty((L, B, T, sh.Hv, sh.Dv, sh.Dk)) if want_node_states else None
+    c = sh._c()
+    _check(_load().oracle_tree_verify_vg(ctypes.byref(c), T, _p(parent), _p(x), _p(conv_state),
+                                         _p(conv_w), _p(a), _p(b), _p(S0), _p(o), _p(u), _p(k),
+                                         _p(g), _p(win), _p(Sn)), "tree_verify_vg")
     out = dict(o=o, u=u, k=k, g=g, conv_win=win)
     if want_node_states:
         out["S_nodes"] = Sn

@@ -346,12 +346,12 @@ int oracle_verify_chunk_vg(const oshape* sh, int T, const double* x,
  *   NULL).  S_nodes [L,B,T,Hv,Dv,Dk] receives every node's state (may be
  *   NULL; large).
  */
-int oracle_tree_verify(const oshape* sh, int T, const int* parent,
-                       const double* x, const double* conv_state,
-                       const double* conv_w, const double* a, const double* b,
-                       const double* S0, double* o, double* tape_u,
-                       double* tape_k, double* tape_g, int* conv_win,
-                       double* S_nodes) {
+static int tree_verify_impl(const oshape* sh, int T, const int* parent,
+                            const double* x, const double* conv_state,
+                            const double* conv_w, const double* a, int per_key,
+                            const double* b, const double* S0, double* o,
+                            double* tape_u, double* tape_k, double* tape_g,
+                            int* conv_win, double* S_nodes) {
   if (!shape_ok(sh) || T < 1 || T > 64) return ORACLE_BAD_ARG;
   const int L = sh->L, B = sh->B, Hk = sh->Hk, Hv = sh->Hv, Dk = sh->Dk,
             Dv = sh->Dv, K = sh->K;
@@ -406,9 +406,16 @@ int oracle_tree_verify(const oshape* sh, int T, const int* parent,
           const double* vt = y + (size_t)v * C + (size_t)2 * Hk * Dk + (size_t)hv * Dv;
           double* ot = o + ((lb * T + v) * Hv + hv) * Dv;
           double* ut = tape_u + ((lb * T + v) * Hv + hv) * Dv;
-          for (int i = 0; i < Dv; ++i)
-            ut[i] = delta_row_step(Dk, S + (size_t)i * Dk, kt, qt, a[gi], b[gi], vt[i], &ot[i]);
-          tape_g[gi] = a[gi];
+          if (per_key) {
+            for (int i = 0; i < Dv; ++i)
+              ut[i] = delta_row_step_vg(Dk, S + (size_t)i * Dk, kt, qt, a + gi * Dk, b[gi],
+                                        vt[i], &ot[i]);
+            memcpy(tape_g + gi * Dk, a + gi * Dk, sizeof(double) * Dk);
+          } else {
+            for (int i = 0; i < Dv; ++i)
+              ut[i] = delta_row_step(Dk, S + (size_t)i * Dk, kt, qt, a[gi], b[gi], vt[i], &ot[i]);
+            tape_g[gi] = a[gi];
+          }
           if (S_nodes)
             memcpy(S_nodes + ((lb * T + v) * Hv + hv) * P, S, sizeof(double) * P);
         }
@@ -417,6 +424,31 @@ int oracle_tree_verify(const oshape* sh, int T, const int* parent,
     }
   }
   return bad;
+}
+
+int oracle_tree_verify(const oshape* sh, int T, const int* parent,
+                       const double* x, const double* conv_state,
+                       const double* conv_w, const double* a, const double* b,
+                       const double* S0, double* o, double* tape_u,
+                       double* tape_k, double* tape_g, int* conv_win,
+                       double* S_nodes) {
+  return tree_verify_impl(sh, T, parent, x, conv_state, conv_w, a, 0, b, S0, o, tape_u,
+                          tape_k, tape_g, conv_win, S_nodes);
+}
+
+/* ---------------------------------------------------------------------------
+ * oracle_tree_verify with a per-key-channel decay gate: a and tape_g are
+ * [L,B,T,Hv,Dk]; node v steps from its parent's state with
+ * delta_row_step_vg (S_v = S_p diag(a_v) + u_v k_v^T).
+ */
+int oracle_tree_verify_vg(const oshape* sh, int T, const int* parent,
+                          const double* x, const double* conv_state,
+                          const double* conv_w, const double* a, const double* b,
+                          const double* S0, double* o, double* tape_u,
+                          double* tape_k, double* tape_g, int* conv_win,
+                          double* S_nodes) {
+  return tree_verify_impl(sh, T, parent, x, conv_state, conv_w, a, 1, b, S0, o, tape_u,
+                          tape_k, tape_g, conv_win, S_nodes);
 }
 
 /* First index of the maximum of row[0..V-1]. */

@@ -101,3 +101,85 @@ def test_rollback_equal_gates_is_the_scalar_rollback():
     np.testing.assert_allclose(
         oracle.tape_rollback_vg(SH, S0, sc["u"], sc["k"], g_v, nk, path),
         oracle.tape_rollback(SH, S0, sc["u"], sc["k"], sc["g"], nk, path), rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------- per-key gate over a tree --
+
+def _tree_inputs(sh, T, seed, branching=3, depth=5):
+    from speculative_decode_verify_gdn_amd import workload as W
+    x, cs, w, a, b, S0 = _inputs(sh, T, seed)
+    rng = np.random.default_rng(seed + 100)
+    parent = np.stack([W.random_tree(rng, T, branching, depth) for _ in range(sh.B)])
+    return parent, x, cs, w, a, b, S0
+
+
+def test_tree_vg_equal_channel_gates_reduce_to_the_scalar_tree():
+    parent, x, cs, w, a, b, S0 = _tree_inputs(SH, 9, 6)
+    a_s = a[..., 0]
+    a_v = np.repeat(a_s[..., None], SH.Dk, axis=-1)
+    vg = oracle.tree_verify_vg(SH, parent, x, cs, w, a_v, b, S0, want_node_states=True)
+    sc = oracle.tree_verify(SH, parent, x, cs, w, a_s, b, S0, want_node_states=True)
+    for key in ("o", "u", "k", "S_nodes"):
+        np.testing.assert_allclose(vg[key], sc[key], rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(vg["conv_win"], sc["conv_win"])
+    np.testing.assert_array_equal(vg["g"], a_v)
+
+
+def test_tree_vg_with_chain_parents_is_the_chain():
+    T = 8
+    x, cs, w, a, b, S0 = _inputs(SH, T, 7)
+    parent = np.tile(np.arange(-1, T - 1, dtype=np.int32), (SH.B, 1))
+    tr = oracle.tree_verify_vg(SH, parent, x, cs, w, a, b, S0, want_node_states=True)
+    ch = oracle.verify_chunk_vg(SH, x, cs, w, a, b, S0)
+    for key in ("o", "u", "k", "g"):
+        np.testing.assert_array_equal(tr[key], ch[key])
+    np.testing.assert_array_equal(tr["S_nodes"][:, :, T - 1], ch["S_final"])
+
+
+def test_tree_vg_node_states_match_the_matrix_form_along_each_path():
+    """S_v = S_p diag(a_v) (I - b_v k_v k_v^T) + b_v v_v k_v^T from S0 along
+    v's root path, with q/k/v from the pinned tree conv and numpy norms."""
+    sh = oracle.Shape(L=1, B=2, Hk=1, Hv=2, Dk=5, Dv=4, K=3)
+    T = 10
+    parent, x, cs, w, a, b, S0 = _tree_inputs(sh, T, 8, branching=2, depth=6)
+    out = oracle.tree_verify_vg(sh, parent, x, cs, w, a, b, S0, want_node_states=True)
+    for bb in range(sh.B):
+        y, _ = oracle.conv_tree(parent[bb], cs[0, bb], x[0, bb], w[0], silu=True)
+        for hv in range(sh.Hv):
+            for v in range(T):
+                path = []
+                c = v
+                while c >= 0:
+                    path.append(c)
+                    c = parent[bb, c]
+                S = S0[0, bb, hv].copy()
+                for t in reversed(path):
+                    q = y[t, :sh.Dk] / np.sqrt((y[t, :sh.Dk] ** 2).sum() + sh.eps)
+                    k = y[t, sh.Dk:2 * sh.Dk] / np.sqrt((y[t, sh.Dk:2 * sh.Dk] ** 2).sum() + sh.eps)
+                    vv = y[t, 2 * sh.Dk + hv * sh.Dv:2 * sh.Dk + (hv + 1) * sh.Dv]
+                    bt = b[0, bb, t, hv]
+                    S = (S @ np.diag(a[0, bb, t, hv]) @ (np.eye(sh.Dk) - bt * np.outer(k, k))
+                         + bt * np.outer(vv, k))
+                np.testing.assert_allclose(out["S_nodes"][0, bb, v, hv], S, rtol=1e-10, atol=1e-12)
+                np.testing.assert_allclose(out["o"][0, bb, v, hv], S @ q, rtol=1e-10, atol=1e-12)
+
+
+def test_tree_vg_path_replay_gives_each_node_state():
+    """tape_rollback_vg along a node's root path, from the tree's own tape,
+    rebuilds that node's state (what rollback to an accepted tree path does)."""
+    T = 12
+    parent, x, cs, w, a, b, S0 = _tree_inputs(SH, T, 9)
+    out = oracle.tree_verify_vg(SH, parent, x, cs, w, a, b, S0, want_node_states=True)
+    for v in (0, 5, T - 1):
+        path = np.full((SH.B, T), -1, np.int32)
+        nk = np.zeros(SH.B, np.int32)
+        for bb in range(SH.B):
+            p, c = [], v
+            while c >= 0:
+                p.append(c)
+                c = parent[bb, c]
+            p = p[::-1]
+            path[bb, :len(p)] = p
+            nk[bb] = len(p)
+        S = oracle.tape_rollback_vg(SH, S0, out["u"], out["k"], out["g"], nk, path)
+        np.testing.assert_allclose(S, out["S_nodes"][:, :, v], rtol=1e-12, atol=1e-14)
