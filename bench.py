@@ -346,54 +346,75 @@ def prefill_pass(cfg, n_tokens, stream, reps=3, gate_per_key=False):
 
 
 def vgate_pass(cfg, stream, steps):
-    """The workload's plain round with the decay gate per key channel
-    (a [L,B,T,Hv,Dk], drawn U(0.05, 1)): round time, verify time per layer
-    (k_verify_vg, sequential recurrence) with its byte model and HBM
-    fraction, and the rollback time."""
+    """The workload's rounds with the decay gate per key channel
+    (a [L,B,T,Hv,Dk], drawn U(0.05, 1)), in both forms: the plain round
+    (verify, accept, rollback) with its verify time per layer, byte model and
+    HBM fraction and its rollback time, and the fused round (the rollback
+    folded into the next round's verify, k_verify_vgt replaying the previous
+    accepted prefix or path)."""
     from speculative_decode_verify_gdn_amd import binding as gb
     from speculative_decode_verify_gdn_amd import spec_round as sr
     base, sets = build_sets(cfg, 1, "cuda")
     inp, acc = sets[0]
+    tree = cfg.is_tree
     gen = torch.Generator(device="cuda").manual_seed(cfg.seed ^ 0x7A)
     a = (0.05 + 0.95 * torch.rand((cfg.L, cfg.B, cfg.T, cfg.Hv, cfg.Dk), device="cuda",
                                   generator=gen)).to(cfg.dtype)
     sh = gb.GdnShape(cfg.L, cfg.B, cfg.Hk, cfg.Hv, cfg.Dk, cfg.Dv, cfg.K, cfg.silu, cfg.eps,
                      cfg.dtype, gate_per_key=True)
-    rb = sr.RoundBuffers(sh=sh, T=cfg.T, V=cfg.V, tree=False, S=base["S0"],
+    rb = sr.RoundBuffers(sh=sh, T=cfg.T, V=cfg.V, tree=tree, S=base["S0"],
                          conv_state=base["conv_state"], conv_w=base["conv_w"], x=inp["x"], a=a,
-                         b=inp["b"], logits=acc["logits"], draft=acc["draft"], parent=None)
+                         b=inp["b"], logits=acc["logits"], draft=acc["draft"],
+                         parent=acc["parent"] if tree else None)
+    fr = sr.FusedRound(rb)
     ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        return g
+
+    def timed(gs):
+        """Mean time of one graph of `gs`, replayed in turn."""
+        for g in gs:
+            g.replay()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(steps):
+            for g in gs:
+                g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (steps * len(gs))
+
     with torch.cuda.stream(stream):
         sr.run_round(rb)
         torch.cuda.synchronize()
-        graphs = []
-        for fn in (lambda: sr.run_round(rb), lambda: [sr.verify_layer(rb, l) for l in range(cfg.L)],
-                   lambda: sr.rollback(rb)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                fn()
-            graphs.append(g)
-        times = []
-        for g in graphs:
-            g.replay()
-            e0, e1 = ev(), ev()
-            e0.record(stream)
-            for _ in range(steps):
-                g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) / steps)
+        plain = [capture(lambda: sr.run_round(rb)),
+                 capture(lambda: [sr.verify_layer(rb, l) for l in range(cfg.L)]),
+                 capture(lambda: sr.rollback(rb))]
+        t_plain = [timed([g]) for g in plain]
+        fr.round(0, first=True)
+        fr.round(1)
+        torch.cuda.synchronize()
+        f_round = [capture(lambda: fr.round(0)), capture(lambda: fr.round(1))]
+        f_verify = [capture(lambda: fr.verify_layers(0)), capture(lambda: fr.verify_layers(1))]
+        t_fround, t_fverify = timed(f_round), timed(f_verify)
     assert int(rb.dev_err.item()) == 0, "device-side error bits set"
     esz = 2 if cfg.dtype == torch.bfloat16 else 4
     extra = cfg.B * cfg.T * cfg.Hv * (cfg.Dk - 1) * (esz + 4)  # larger gate read and tape g
     vb = verify_bytes_per_launch(cfg, cfg.B) + extra
-    v_ms = times[1] / cfg.L
-    del rb, base, sets, inp, acc, a, graphs
+    v_ms = t_plain[1] / cfg.L
+    del rb, fr, base, sets, inp, acc, a, plain, f_round, f_verify
     torch.cuda.empty_cache()
-    return {"round_ms": times[0], "value": cfg.B * cfg.T / (times[0] * 1e-3),
+    return {"round_ms": t_plain[0], "value": cfg.B * cfg.T / (t_plain[0] * 1e-3),
             "verify_per_layer_ms": v_ms, "verify_bytes_per_launch": vb,
             "verify_hbm_frac": vb / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "rollback_state_and_conv_ms": times[2], "kernel": "k_verify_vg"}
+            "rollback_state_and_conv_ms": t_plain[2],
+            "kernel": "k_verify_vgt" if tree else "k_verify_vg",
+            "fused": {"round_ms": t_fround, "value": cfg.B * cfg.T / (t_fround * 1e-3),
+                      "verify_per_layer_ms": t_fverify / cfg.L, "kernel": "k_verify_vgt"}}
 
 
 def parse():
@@ -417,7 +438,7 @@ def parse():
     ap.add_argument("--prefill", type=int, default=0, metavar="N",
                     help="also time gdn_prefill of N tokens through the workload's stack")
     ap.add_argument("--gate-per-key", action="store_true",
-                    help="also time the round with the decay gate per key channel (chains)")
+                    help="also time the rounds with the decay gate per key channel")
     ap.add_argument("--draft-sweep", action="store_true",
                     help="also time rounds at N = 1, 2, 4, 8, 16 drafts and report the draft "
                          "length the host policy picks (chain workloads)")
@@ -716,7 +737,7 @@ def main():
     pre = prefill_pass(cfg, args.prefill, stream) if args.prefill > 0 else None
     pre_vg = (prefill_pass(cfg, args.prefill, stream, gate_per_key=True)
               if args.prefill > 0 and args.gate_per_key and not cfg.is_tree else None)
-    vgate = vgate_pass(cfg, stream, args.steps) if args.gate_per_key and not cfg.is_tree else None
+    vgate = vgate_pass(cfg, stream, args.steps) if args.gate_per_key else None
 
     dsweep = None
     if args.draft_sweep and not cfg.is_tree:

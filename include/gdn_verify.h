@@ -87,11 +87,12 @@ typedef struct {
   int32_t gate_per_key; /* 0: decay a and tape g are [..,Hv] (one per v-head);
                            1: they are [..,Hv,Dk], one per v-head and key
                            channel (S decays column by column:
-                           S <- S diag(a_t) before each step).  Supported by
-                           gdn_verify_chunk, gdn_tape_rollback, the conv
-                           rollback and gdn_prefill; the other calls return
-                           GDN_ERR_UNSUPPORTED.  Source: GDN page s4 (the two
-                           forms of the decay tape). */
+                           S <- S diag(a_t) before each step).  Every
+                           verify, rollback and prefill call takes either
+                           form; gdn_verify_chunk_replay and
+                           gdn_tree_verify_replay then run as one kernel for
+                           any T <= 64.  Source: GDN page s4 (the two forms
+                           of the decay tape). */
 } gdn_shape;
 
 /* The innovation tape written by verify and read by rollback (fp32):

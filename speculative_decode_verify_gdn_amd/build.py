@@ -32,7 +32,7 @@ COMMON = [
 
 SOURCES = ["gdn_api.cpp", "k_verify_wy.hip", "k_verify_chain.hip", "k_verify_tree.hip",
            "k_rollback.hip",
-           "k_accept.hip", "k_sample.hip", "k_verify_vg.hip"]
+           "k_accept.hip", "k_sample.hip", "k_verify_vg.hip", "k_verify_vgt.hip"]
 
 
 def _compile(src: str) -> str:

@@ -114,7 +114,6 @@ gdn_status gdn_verify_chunk_replay(const gdn_shape* shape, int32_t T, const void
                                    const int32_t* prev_n_keep, int32_t* dev_err, void* stream) {
   gdn_status st = check_shape(shape, T);
   if (st != GDN_OK) return st;
-  if (shape->gate_per_key) return GDN_ERR_UNSUPPORTED;
   if (!verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape)) return GDN_ERR_INVALID_ARG;
   if (!prev_tape || !prev_tape->u || !prev_tape->k || !prev_tape->g || !prev_n_keep)
     return GDN_ERR_INVALID_ARG;
@@ -125,6 +124,15 @@ gdn_status gdn_verify_chunk_replay(const gdn_shape* shape, int32_t T, const void
   const hipStream_t s = static_cast<hipStream_t>(stream);
   VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
   v.dev_err = dev_err;
+  if (shape->gate_per_key) {
+    v.S_out = S;
+    v.ptu = prev_tape->u;
+    v.ptk = prev_tape->k;
+    v.ptg = prev_tape->g;
+    v.prev_n_keep = prev_n_keep;
+    v.pT = prev_T;
+    return launch_status(gdn::launch_verify_vg_tree(v, shape->d_k, shape->d_v, shape->in_dtype, s));
+  }
   if (T <= 16 && prev_T <= 16) {
     v.S_out = S;
     v.ptu = prev_tape->u;
@@ -146,7 +154,6 @@ gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* par
                            void* stream) {
   gdn_status st = check_shape(shape, T);
   if (st != GDN_OK) return st;
-  if (shape->gate_per_key) return GDN_ERR_UNSUPPORTED;
   if (!parent || !verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape))
     return GDN_ERR_INVALID_ARG;
   VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
@@ -154,6 +161,8 @@ gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* par
   v.conv_win = conv_win;
   v.dev_err = dev_err;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (shape->gate_per_key)
+    return launch_status(gdn::launch_verify_vg_tree(v, shape->d_k, shape->d_v, shape->in_dtype, s));
   if (T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128)
     return launch_status(gdn::launch_verify_tree(v, s));
   return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype, s));
@@ -167,7 +176,6 @@ gdn_status gdn_tree_verify_replay(const gdn_shape* shape, int32_t T, const int32
                                   const int32_t* prev_n_keep, int32_t* dev_err, void* stream) {
   gdn_status st = check_shape(shape, T);
   if (st != GDN_OK) return st;
-  if (shape->gate_per_key) return GDN_ERR_UNSUPPORTED;
   if (!parent || !verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape))
     return GDN_ERR_INVALID_ARG;
   if (!prev_tape || !prev_tape->u || !prev_tape->k || !prev_tape->g || !prev_n_keep)
@@ -177,6 +185,20 @@ gdn_status gdn_tree_verify_replay(const gdn_shape* shape, int32_t T, const int32
   if (prev_tape->u == tape->u || prev_tape->k == tape->k || prev_tape->g == tape->g)
     return GDN_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (shape->gate_per_key) {
+    VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
+    v.parent = parent;
+    v.conv_win = conv_win;
+    v.dev_err = dev_err;
+    v.S_out = S;
+    v.ptu = prev_tape->u;
+    v.ptk = prev_tape->k;
+    v.ptg = prev_tape->g;
+    v.prev_n_keep = prev_n_keep;
+    v.prev_path = prev_path;
+    v.pT = prev_T;
+    return launch_status(gdn::launch_verify_vg_tree(v, shape->d_k, shape->d_v, shape->in_dtype, s));
+  }
   if (T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128) {
     VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
     v.parent = parent;

@@ -118,6 +118,9 @@ hipError_t launch_round_rollback(const RollbackArgs& r, const ConvRollbackArgs& 
 // Per-key-channel decay gate: sequential verify of chains of <= 64 tokens
 // (a [L,B,T,Hv,Dk], tape g [L,B,T,Hv,Dk]) and its tape rollback.
 hipError_t launch_verify_vg(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
+// Per-key-channel gate over a parent array (nullptr: a chain) of <= 64 nodes,
+// with the previous accepted path replayed first when prev_n_keep is set.
+hipError_t launch_verify_vg_tree(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
 hipError_t launch_tape_rollback_vg(const RollbackArgs& a, int dk, int dv, hipStream_t s);
 hipError_t launch_conv_rollback(const ConvRollbackArgs& a, int dtype, hipStream_t s);
 hipError_t launch_accept(const AcceptArgs& a, int dtype, hipStream_t s);

@@ -120,7 +120,15 @@ def fused_pays(sh: gb.GdnShape, T: int, tree: bool, device=None) -> bool:
     overlap other workgroups' loads and the fused round saves the rollback's
     state read.  A pass is 4 workgroups per CU for the chain kernel (chains of
     at most 16 drafts) and 1 for the tree kernel (trees of 33..64 nodes, bf16
-    inputs, 128-dim heads); other shapes are not fused by the library."""
+    inputs, 128-dim heads); other shapes are not fused by the library.
+
+    With the decay gate per key channel, both forms run the closed-form
+    per-key kernel for the fused verify.  For chains that kernel is slower
+    than the sequential one the plain round uses, so chains stay plain; for
+    trees the plain round runs the same kernel, and folding the rollback in
+    saves its state pass at any grid size."""
+    if sh.gate_per_key:
+        return tree and T <= 64
     cus = torch.cuda.get_device_properties(device or torch.cuda.current_device()).multi_processor_count
     if not tree:
         return T <= 16 and sh.B * sh.Hv >= 2 * 4 * cus

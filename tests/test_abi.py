@@ -117,15 +117,22 @@ def test_host_validation_before_launch(lib):
     assert sa(4, 1.0, FAKE, None, big) == gb.GDN_ERR_WORKSPACE
     assert gb.spec_sample_workspace_bytes(32, 8, 151936) >= 32 * 9 * 38 * 8
     assert gb.spec_sample_workspace_bytes(1, 65, 100) == 0
-    # per-key-channel gate: flag must be 0/1; calls without that form refuse it
+    # per-key-channel gate: flag must be 0/1; the tree and replay calls take
+    # it with the same host-side validation as the per-head form
     assert _verify(_shape(gate_per_key=2)) == gb.GDN_ERR_INVALID_ARG
     vg = _shape(gate_per_key=True)
-    assert lib.gdn_tree_verify(ctypes.byref(vg), 40, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+    assert lib.gdn_tree_verify(ctypes.byref(vg), 40, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, ctypes.byref(gb._CTape(1, 1, 1)), None, None,
+                               None) == gb.GDN_ERR_INVALID_ARG
+    assert lib.gdn_tree_verify(ctypes.byref(vg), 65, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                FAKE, ctypes.byref(gb._CTape(1, 1, 1)), None, None,
                                None) == gb.GDN_ERR_UNSUPPORTED
     assert lib.gdn_verify_chunk_replay(ctypes.byref(vg), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                       FAKE, ctypes.byref(cur), 4, ctypes.byref(prev), FAKE,
+                                       FAKE, ctypes.byref(cur), 65, ctypes.byref(prev), FAKE,
                                        None, None) == gb.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_verify_chunk_replay(ctypes.byref(vg), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, ctypes.byref(cur), 4, ctypes.byref(cur), FAKE,
+                                       None, None) == gb.GDN_ERR_INVALID_ARG
     # prefill: bad T, missing pointers, short workspace
     pf = lambda T, xx, ws, wsb: lib.gdn_prefill(ctypes.byref(_shape()), T, xx, FAKE, FAKE, FAKE,
                                                 FAKE, FAKE, FAKE, ws, wsb, None, None)

@@ -850,3 +850,227 @@ def test_vgate_prefill_matches_oracle(T, D, dtype):
     assert rel_fro(o.cpu().double().numpy(), ref["o"]) <= 1e-4
     assert rel_fro(S.cpu().double().numpy(), ref["S_final"]) <= 1e-4
     np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
+
+
+# ------------------------------- per-key gate over trees, and fused replay --
+
+def _vg_parents(rng, B, T, depth):
+    """Random draft trees, or chains given as parent arrays when depth >= T."""
+    if depth >= T:
+        return np.tile(np.arange(-1, T - 1, dtype=np.int32), (B, 1))
+    return np.stack([W.random_tree(rng, T, 4, depth) for _ in range(B)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,L,B,Hk,Hv,D,K,dtype,depth", [
+    (64, 1, 2, 2, 4, 128, 4, torch.bfloat16, 8), (40, 2, 2, 1, 2, 64, 3, torch.float32, 6),
+    (17, 1, 3, 2, 2, 32, 8, torch.bfloat16, 5), (1, 1, 2, 2, 4, 128, 4, torch.bfloat16, 1),
+    (64, 1, 1, 1, 2, 128, 4, torch.float32, 64), (33, 1, 2, 2, 4, 64, 2, torch.bfloat16, 33)])
+def test_vgate_tree_verify_matches_oracle(T, L, B, Hk, Hv, D, K, dtype, depth):
+    """gdn_tree_verify with a per-key-channel gate equals the oracle's
+    tree_verify_vg (outputs, tape, conv windows) and leaves S untouched; the
+    depth >= T cases are chains given as parent arrays (the deepest trees)."""
+    _need_gpu()
+    cfg = W.CONFIGS[2].with_(L=L, B=B, Hk=Hk, Hv=Hv, Dk=D, Dv=D, K=K, T=T, dtype=dtype)
+    inp = _vg_inputs(cfg, 5)
+    gsh, osh = _vg_shapes(cfg)
+    parent = _vg_parents(np.random.default_rng(T + D), B, T, depth)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    S0 = d["S0"].clone()
+    o = torch.empty((L, B, T, Hv, D), device=DEV)
+    tape = gb.Tape.empty(gsh, T, DEV)
+    win = torch.full((B, T, K), -99, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print("vgate tree", T, D, K, dtype, depth, flush=True)
+    gb.gdn_tree_verify(gsh, torch.from_numpy(parent).to(DEV), d["x"], d["conv_state"],
+                       d["conv_w"], d["a"], d["b"], d["S0"], o, tape, conv_win=win, dev_err=err)
+    torch.cuda.synchronize()
+    f = {k: W.to_f64(v) for k, v in inp.items()}
+    ref = oracle.tree_verify_vg(osh, parent, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"],
+                                f["S0"])
+    for name, got in (("o", o), ("u", tape.u), ("k", tape.k)):
+        e = rel_fro(got.cpu().double().numpy(), ref[name])
+        assert e <= 1e-4, (name, e)
+    np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
+    np.testing.assert_array_equal(win.cpu().numpy(), ref["conv_win"])
+    assert int(err.item()) == 0
+    assert torch.equal(d["S0"], S0)
+
+
+def _vg_prev_tape(cfg, pT, seed):
+    """A synthetic previous tape: u ~ N(0,1), unit k, per-key gates U(0.05, 1)."""
+    gen = torch.Generator().manual_seed(seed)
+    u = torch.randn((cfg.L, cfg.B, pT, cfg.Hv, cfg.Dv), generator=gen)
+    k = torch.nn.functional.normalize(torch.randn((cfg.L, cfg.B, pT, cfg.Hk, cfg.Dk),
+                                                  generator=gen), dim=-1)
+    g = 0.05 + 0.95 * torch.rand((cfg.L, cfg.B, pT, cfg.Hv, cfg.Dk), generator=gen)
+    return u, k, g
+
+
+@pytest.mark.parametrize("tree,T,pT,D,dtype", [
+    (False, 8, 8, 128, torch.bfloat16), (False, 16, 12, 64, torch.float32),
+    (False, 40, 64, 32, torch.bfloat16), (True, 64, 64, 128, torch.bfloat16),
+    (True, 24, 40, 32, torch.float32)])
+def test_vgate_replay_verify_equals_rollback_then_verify(tree, T, pT, D, dtype):
+    """gdn_verify_chunk_replay / gdn_tree_verify_replay with a per-key gate:
+    the state afterwards is the oracle's tape_rollback_vg of the previous tape
+    over the accepted prefix (or path), and the outputs are the oracle's
+    verify from that state.  Accepted lengths 0, 1, middle and all."""
+    _need_gpu()
+    L, B = 2, 4
+    cfg = W.CONFIGS[2].with_(L=L, B=B, Hk=2, Hv=4, Dk=D, Dv=D, K=4, T=T, dtype=dtype)
+    gsh, osh = _vg_shapes(cfg)
+    inp = _vg_inputs(cfg, 7)
+    pu, pk, pg = _vg_prev_tape(cfg, pT, 40 + T)
+    nk = torch.tensor([0, 1, pT // 2, pT], dtype=torch.int32)
+    gen = torch.Generator().manual_seed(9)
+    path = None
+    if tree:
+        path = torch.full((B, pT), -1, dtype=torch.int32)
+        for bb in range(B):
+            path[bb, :int(nk[bb])] = torch.randperm(pT, generator=gen)[:int(nk[bb])].to(torch.int32)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    S = d["S0"].clone()
+    o = torch.empty((L, B, T, cfg.Hv, D), device=DEV)
+    tape = gb.Tape.empty(gsh, T, DEV)
+    ptape = gb.Tape(pu.to(DEV), pk.to(DEV), pg.to(DEV))
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print("vgate replay", tree, T, pT, D, dtype, flush=True)
+    f = {k: W.to_f64(v) for k, v in inp.items()}
+    S_rep = oracle.tape_rollback_vg(osh, f["S0"], pu.double().numpy(), pk.double().numpy(),
+                                    pg.double().numpy(), nk.numpy(),
+                                    None if path is None else path.numpy())
+    if tree:
+        parent = _vg_parents(np.random.default_rng(T), B, T, 6)
+        win = torch.empty((B, T, cfg.K), dtype=torch.int32, device=DEV)
+        gb.gdn_tree_verify_replay(gsh, torch.from_numpy(parent).to(DEV), d["x"], d["conv_state"],
+                                  d["conv_w"], d["a"], d["b"], S, o, tape, ptape, nk.to(DEV),
+                                  prev_path=path.to(DEV), conv_win=win, dev_err=err)
+        ref = oracle.tree_verify_vg(osh, parent, f["x"], f["conv_state"], f["conv_w"], f["a"],
+                                    f["b"], S_rep)
+    else:
+        gb.gdn_verify_chunk_replay(gsh, d["x"], d["conv_state"], d["conv_w"], d["a"], d["b"], S,
+                                   o, tape, ptape, nk.to(DEV), dev_err=err)
+        ref = oracle.verify_chunk_vg(osh, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"],
+                                     S_rep)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert rel_fro(S.cpu().double().numpy(), S_rep) <= 1e-5
+    assert torch.equal(S[:, 0].cpu(), inp["S0"][:, 0])  # n = 0: untouched
+    for name, got in (("o", o), ("u", tape.u), ("k", tape.k)):
+        e = rel_fro(got.cpu().double().numpy(), ref[name])
+        assert e <= 1e-4, (name, e)
+    np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
+
+
+def test_vgate_tree_replay_bad_inputs_flag():
+    """Per-key tree replay: a malformed parent array flags GDN_DEV_ERR_PARENT,
+    skips that sequence's outputs and still applies its replay; an
+    out-of-range accepted length or path entry flags its bit and leaves that
+    sequence's state as it was."""
+    _need_gpu()
+    T, pT, D = 24, 8, 64
+    cfg = W.CONFIGS[2].with_(L=1, B=2, Hk=2, Hv=4, Dk=D, Dv=D, K=4, T=T, dtype=torch.bfloat16)
+    gsh, osh = _vg_shapes(cfg)
+    inp = _vg_inputs(cfg, 11)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    pu, pk, pg = _vg_prev_tape(cfg, pT, 77)
+    ptape = gb.Tape(pu.to(DEV), pk.to(DEV), pg.to(DEV))
+    parent = _vg_parents(np.random.default_rng(3), 2, T, 5)
+    good_path = torch.tensor([[2, 0, 5, -1, -1, -1, -1, -1], [1, 3, -1, -1, -1, -1, -1, -1]],
+                             dtype=torch.int32)
+    nk = torch.tensor([3, 2], dtype=torch.int32)
+    S_rep = oracle.tape_rollback_vg(osh, W.to_f64(inp["S0"]), pu.double().numpy(),
+                                    pk.double().numpy(), pg.double().numpy(), nk.numpy(),
+                                    good_path.numpy())
+
+    def run(par, n, path):
+        S = d["S0"].clone()
+        o = torch.full((1, 2, T, cfg.Hv, D), 7.0, device=DEV)
+        tape = gb.Tape.empty(gsh, T, DEV)
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        gb.gdn_tree_verify_replay(gsh, torch.from_numpy(par).to(DEV), d["x"], d["conv_state"],
+                                  d["conv_w"], d["a"], d["b"], S, o, tape, ptape, n.to(DEV),
+                                  prev_path=path.to(DEV), dev_err=err)
+        torch.cuda.synchronize()
+        return S.cpu(), o.cpu(), int(err.item())
+
+    print("vgate bad parent", flush=True)
+    bad_par = parent.copy()
+    bad_par[1, 5] = 6  # child before parent
+    S, o, err = run(bad_par, nk, good_path)
+    assert err & gb.DEV_ERR_PARENT
+    assert torch.all(o[:, 1] == 7.0)
+    assert rel_fro(S.double().numpy(), S_rep) <= 1e-5  # replay applied to both sequences
+    print("vgate bad n_keep", flush=True)
+    S, o, err = run(parent, torch.tensor([pT + 1, 2], dtype=torch.int32), good_path)
+    assert err & gb.DEV_ERR_N_KEEP
+    assert torch.equal(S[:, 0], inp["S0"][:, 0])
+    assert rel_fro(S[:, 1].double().numpy(), S_rep[:, 1]) <= 1e-5
+    print("vgate bad path", flush=True)
+    bad_path = good_path.clone()
+    bad_path[0, 1] = pT
+    S, o, err = run(parent, nk, bad_path)
+    assert err & gb.DEV_ERR_PATH
+    assert torch.equal(S[:, 0], inp["S0"][:, 0])
+    assert rel_fro(S[:, 1].double().numpy(), S_rep[:, 1]) <= 1e-5
+
+
+@pytest.mark.parametrize("tree,T", [(True, 64), (False, 8)])
+def test_vgate_fused_rounds(tree, T):
+    """Fused rounds (spec_round.FusedRound) with a per-key-channel gate: every
+    round's outputs, tape, accepted lengths and paths, conv window, and the
+    state after finish(), against the oracle's plain per-key rounds."""
+    _need_gpu()
+    cfg = (W.CONFIGS[5] if tree else W.CONFIGS[3]).with_(L=2, B=3, T=T, V=293)
+    gsh, osh = _vg_shapes(cfg)
+    inp0 = _vg_inputs(cfg, 0)
+    oS, ocs = W.to_f64(inp0["S0"]), W.to_f64(inp0["conv_state"])
+    fr = None
+    print("vgate fused rounds", tree, T, flush=True)
+    for r in range(4):
+        inp = _vg_inputs(cfg, r)
+        acc = (W.tree_accept_inputs(cfg, r, "cpu") if tree
+               else W.chain_accept_inputs(cfg, r, "cpu"))
+        d = {k: v.to(DEV) for k, v in inp.items()}
+        par = acc["parent"].to(DEV) if tree else None
+        if fr is None:
+            rb = spec_round.RoundBuffers(sh=gsh, T=T, V=cfg.V, tree=tree, S=inp0["S0"].to(DEV),
+                                         conv_state=inp0["conv_state"].to(DEV),
+                                         conv_w=d["conv_w"], x=d["x"], a=d["a"], b=d["b"],
+                                         logits=acc["logits"].to(DEV),
+                                         draft=acc["draft"].to(DEV), parent=par)
+            fr = spec_round.FusedRound(rb)
+        else:
+            rb = fr.rb
+            rb.x, rb.a, rb.b, rb.conv_w = d["x"], d["a"], d["b"], d["conv_w"]
+            rb.logits, rb.draft = acc["logits"].to(DEV), acc["draft"].to(DEV)
+            if tree:
+                rb.parent = par
+        fr.round(r, first=(r == 0))
+        torch.cuda.synchronize()
+        f = {k: W.to_f64(v) for k, v in inp.items()}
+        parent = acc["parent"].numpy() if tree else None
+        if tree:
+            ref = oracle.tree_verify_vg(osh, parent, f["x"], ocs, f["conv_w"], f["a"], f["b"], oS)
+        else:
+            ref = oracle.verify_chunk_vg(osh, f["x"], ocs, f["conv_w"], f["a"], f["b"], oS)
+        n, path, bonus = oracle.accept(acc["draft"].numpy(), W.to_f64(acc["logits"]), parent)
+        np.testing.assert_array_equal(fr.n_keeps[r % 2].cpu().numpy(), n)
+        np.testing.assert_array_equal(rb.bonus.cpu().numpy(), bonus)
+        if tree:
+            np.testing.assert_array_equal(fr.paths[r % 2].cpu().numpy(), path)
+            np.testing.assert_array_equal(rb.conv_win.cpu().numpy(), ref["conv_win"])
+        tape = fr.tapes[r % 2]
+        for name, got, want in (("o", rb.o, ref["o"]), ("u", tape.u, ref["u"]),
+                                ("k", tape.k, ref["k"])):
+            e = rel_fro(got.cpu().double().numpy(), want)
+            assert e <= 1e-4, (r, name, e)
+        np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
+        oS = oracle.tape_rollback_vg(osh, oS, ref["u"], ref["k"], ref["g"], n,
+                                     path if tree else None)
+        ocs, _ = oracle.conv_rollback(osh, ocs, f["x"], n, path if tree else None)
+        np.testing.assert_array_equal(rb.conv_state.cpu().double().numpy(), ocs)
+    fr.finish(3)
+    torch.cuda.synchronize()
+    assert rel_fro(fr.rb.S.cpu().double().numpy(), oS) <= 1e-4
+    assert int(fr.rb.dev_err.item()) == 0
