@@ -18,8 +18,12 @@
 // barriers.  A, Oc, Ti and M2 live in packed rows (row t holds one value per
 // node of path(t), slot = depth - 1), at most T(T+1)/2 values each.
 //
-// One workgroup of eight waves per (layer, seq, v-head); wave w owns rows
-// 16w .. 16w+15 of S0 (registers, MFMA A operand).  Phases:
+// One workgroup of eight waves per (layer, seq, v-head) -- or, with two
+// v-heads per k-head and conv width 4, per (layer, seq, k-head) running both
+// v-heads: their q/k conv, norms, pre-split operand and Gram are the same, so
+// they are done once and only the gate-dependent solve and the state
+// products repeat per head.  Wave w owns rows 16w .. 16w+15 of each head's
+// S0 (registers, MFMA A operand).  Phases:
 //   loads: parents, gates, the raw conv rows (staged in LDS), conv weights;
 //   wave 0: node depths, ancestor masks, conv windows, path products, packed
 //     row offsets (one lane per node, wave-level scan);
@@ -31,6 +35,10 @@
 //   S0 [K;Q]^T (bf16x3 MFMA) and form RHS in LDS;
 //   [Ti; M2] is expanded to a dense pre-split operand in the space of K/Q;
 //   RHS [Ti; M2]^T (bf16x3 MFMA); u and o are stored from registers.
+// With two heads the second head's S0 [K;Q]^T runs right after the first's
+// (K/Q are still in LDS), its v rows wait in registers until the first head
+// has finished with the V space, and wave 0 solves its packed rows while the
+// other waves run the first head's second product.
 // S0 and the conv window are never written (they stay the snapshot).
 
 #include "gdn_common.hpp"
@@ -51,7 +59,6 @@ constexpr int TR_VLD = 68;      // floats per V / RHS row ([row of S][node])
 // while each group of 8 nodes stays contiguous for float4 reads.
 __device__ __forceinline__ int vsw(int i) { return ((i >> 3) & 7) << 3; }
 constexpr int TR_PK = TR_T * (TR_T + 1) / 2;  // packed triangle capacity
-constexpr int TR_ROWB = 3 * TR_D * 2;         // raw staging bytes per row (q | k | v rows, bf16)
 
 __device__ __forceinline__ float silu_t(float y) {
   return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
@@ -80,38 +87,41 @@ __device__ __forceinline__ void split4(const float* y, uint2& hi, uint2& lo) {
   lo = make_uint2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
 }
 
-template <int KM>
+template <int KM, int NH>
 struct TreeLds {
+  static constexpr int ROWB = (2 + NH) * TR_D * 2;  // raw staging bytes per row (q | k | v rows)
   static constexpr int XR = TR_T + KM - 1;  // raw rows: old window, then nodes
-  static constexpr int STAGE = XR * TR_ROWB;
+  static constexpr int STAGE = XR * ROWB;
   static constexpr int VBYTES = TR_D * TR_VLD * 4;
   static constexpr int PKBYTES = 4 * TR_PK * 4;  // KK, QK, Ti, M2
   static constexpr int R2 = STAGE > VBYTES + PKBYTES ? STAGE : VBYTES + PKBYTES;
   static constexpr int R1 = 2 * TR_T * TR_KQS;
 };
 
-template <int KC, bool RP>
+template <int KC, bool RP, int NH>
 __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   constexpr int KM = KC > 0 ? KC : 8;
-  using LY = TreeLds<KM>;
+  using LY = TreeLds<KM, NH>;
   constexpr int XR = LY::XR;
+  constexpr int ROWB = LY::ROWB;
+  constexpr int NSEG = 2 + NH;  // conv segments: q, k, then v of each head
   static_assert(2 * TR_T * TR_B2S <= LY::R1, "[Ti;M2] operand fits in the K/Q space");
-  static_assert(LY::R1 + LY::R2 + 3 * TR_D * KM * 4 + TR_T * (48 + 4 * KM) <= 160 * 1024,
+  static_assert(LY::R1 + LY::R2 + NSEG * TR_D * KM * 4 + TR_T * (40 + 12 * NH + 4 * KM) <= 160 * 1024,
                 "LDS budget");
 
   __shared__ __align__(16) unsigned char s_r1[LY::R1];  // pre-split [K;Q], later [Ti;M2]
   __shared__ __align__(16) unsigned char s_r2[LY::R2];  // raw staging, later V/RHS + packed
-  __shared__ __align__(16) float s_w[3 * TR_D * KM];    // conv weights [channel][tap]
+  __shared__ __align__(16) float s_w[NSEG * TR_D * KM]; // conv weights [channel][tap]
   __shared__ unsigned long long s_anc[TR_T];            // proper-ancestor masks
   __shared__ int s_par[TR_T], s_dep[TR_T], s_off[TR_T];
   __shared__ __align__(16) int s_widx[TR_T * KM];       // conv window: staging byte offsets
-  __shared__ float s_ga[TR_T], s_gb[TR_T], s_gam[TR_T];
+  __shared__ float s_ga[NH * TR_T], s_gb[NH * TR_T], s_gam[NH * TR_T];  // per head
   __shared__ int s_bad, s_maxd;
   // previous round's accepted path (replay variant): tape entry of step i,
   // w_i = prod_{i<j<pn} g_j (zero for i >= pn), gamma = prod_{j<pn} g_j
   __shared__ int s_ppath[RP ? TR_T : 1];
-  __shared__ float s_pw[RP ? TR_T : 1];
-  __shared__ float s_pgam;
+  __shared__ float s_pw[RP ? NH * TR_T : 1];
+  __shared__ float s_pgam[NH];
   __shared__ int s_pbad;
 
   float* s_v = reinterpret_cast<float*>(s_r2);            // [row of S][node]
@@ -128,14 +138,14 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
 
   const int G = p.Hv / p.Hk;
   const int n_units = p.L * p.B * p.Hk;
-  const UnitSub us = xcd_unit_sub(blockIdx.x, G);
+  const UnitSub us = xcd_unit_sub(blockIdx.x, G / NH);
   if (us.unit >= n_units) return;
   const int hk = us.unit % p.Hk;
   const size_t lb = us.unit / p.Hk;  // l * B + b
   const int bb = static_cast<int>(lb % p.B);
   const int l = static_cast<int>(lb / p.B);
-  const int g = us.sub;
-  const int hv = hk * G + g;
+  const int g = us.sub * NH;
+  const int hv = hk * G + g;  // first v-head of this workgroup (heads hv .. hv + NH - 1)
   const int T = p.T;
   const int K = KC > 0 ? KC : p.K;
   const uint16_t* x = static_cast<const uint16_t*>(p.x);
@@ -154,15 +164,19 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   const int tq = lane < T ? lane : 0;
   const int par_raw = p.parent[static_cast<size_t>(bb) * T + tq];
   const size_t gi = (lb * T + tq) * p.Hv + hv;
-  const float ga_ld = ld_in(static_cast<const uint16_t*>(p.a), gi);
-  const float gb_ld = ld_in(static_cast<const uint16_t*>(p.b), gi);
+  float ga_ld[NH], gb_ld[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    ga_ld[h] = ld_in(static_cast<const uint16_t*>(p.a), gi + h);
+    gb_ld[h] = ld_in(static_cast<const uint16_t*>(p.b), gi + h);
+  }
   // local channel c in [q | k | v-rows] -> qkv channel
   auto chan = [&](int c) {
     return c < TR_D ? hk * TR_D + c
                     : (c < 2 * TR_D ? p.Hk * TR_D + hk * TR_D + (c - TR_D)
                                     : 2 * p.Hk * TR_D + hv * TR_D + (c - 2 * TR_D));
   };
-  constexpr int CPR = TR_ROWB / 16;                     // 16-byte chunks per raw row (48)
+  constexpr int CPR = ROWB / 16;                        // 16-byte chunks per raw row
   constexpr int NRAW = (XR * CPR + TR_NT - 1) / TR_NT;  // per thread
   const int nrows = K - 1 + T;
   const uint16_t* xcol = x + lb * T * p.C;
@@ -179,13 +193,13 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   }
   // conv weights of the 384 channels, zero beyond the kernel width
   const float* cw = p.conv_w + static_cast<size_t>(l) * p.C * K;
-  constexpr int NWL = (3 * TR_D * KM + TR_NT - 1) / TR_NT;
+  constexpr int NWL = (NSEG * TR_D * KM + TR_NT - 1) / TR_NT;
   float wv[NWL];
 #pragma unroll
   for (int q = 0; q < NWL; ++q) {
     const int e = tid + q * TR_NT;
     const int c = e / KM, j = e % KM;
-    const bool ok = e < 3 * TR_D * KM && j < K;
+    const bool ok = e < NSEG * TR_D * KM && j < K;
     const float v = cw[static_cast<size_t>(chan(ok ? c : 0)) * K + (ok ? j : 0)];
     wv[q] = ok ? v : 0.f;
   }
@@ -202,12 +216,18 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
         s_bad = 1;
         pv = -1;
       }
-      s_ga[t] = ga_ld;
-      s_gb[t] = gb_ld;
-      p.tg[(lb * T + t) * p.Hv + hv] = ga_ld;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        s_ga[h * TR_T + t] = ga_ld[h];
+        s_gb[h * TR_T + t] = gb_ld[h];
+        p.tg[(lb * T + t) * p.Hv + hv + h] = ga_ld[h];
+      }
     } else {
-      s_ga[t] = 1.f;
-      s_gb[t] = 0.f;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        s_ga[h * TR_T + t] = 1.f;
+        s_gb[h * TR_T + t] = 0.f;
+      }
     }
     s_par[t] = pv;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -215,19 +235,24 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
     // ancestors, depth, path product of a, conv window (node, then upward)
     unsigned long long m = 0ull;
     int d = 0;
-    float gm = 1.f;
+    float gm[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) gm[h] = 1.f;
     if (t < T) {
-      gm = s_ga[t];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) gm[h] = s_ga[h * TR_T + t];
       d = 1;
       for (int c = s_par[t]; c >= 0; c = s_par[c]) {
         m |= 1ull << c;
-        gm *= s_ga[c];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) gm[h] *= s_ga[h * TR_T + c];
         ++d;
       }
     }
     s_anc[t] = m;
     s_dep[t] = d;
-    s_gam[t] = gm;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) s_gam[h * TR_T + t] = gm[h];
     {
       int cur = t < T ? t : -1, old = 0;
 #pragma unroll
@@ -241,7 +266,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
             w = --old;
           }
         }
-        s_widx[t * KM + j] = (w + K - 1) * TR_ROWB;
+        s_widx[t * KM + j] = (w + K - 1) * ROWB;
       }
     }
     // packed row offsets: exclusive prefix sum of depths over nodes
@@ -267,22 +292,23 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
         bad = pp < 0 || pp >= p.pT;
       }
       pp = lane < pn && !bad ? pp : 0;
-      const float gv = lane < pn ? p.ptg[(lb * p.pT + pp) * p.Hv + hv] : 1.f;
-      float x_s = gv;  // inclusive suffix product prod_{j >= lane} g_j
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_down(x_s, o, 64);
-        if (lane + o < 64) x_s *= y;
+      for (int h = 0; h < NH; ++h) {
+        const float gv = lane < pn ? p.ptg[(lb * p.pT + pp) * p.Hv + hv + h] : 1.f;
+        float x_s = gv;  // inclusive suffix product prod_{j >= lane} g_j
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const float y = __shfl_down(x_s, o, 64);
+          if (lane + o < 64) x_s *= y;
+        }
+        float w = __shfl_down(x_s, 1, 64);
+        if (lane == 63) w = 1.f;
+        s_pw[h * TR_T + lane] = lane < pn ? w : 0.f;
+        if (lane == 0) s_pgam[h] = x_s;
       }
-      float w = __shfl_down(x_s, 1, 64);
-      if (lane == 63) w = 1.f;
       s_ppath[lane] = pp;
-      s_pw[lane] = lane < pn ? w : 0.f;
       const unsigned long long anybad = __ballot(bad);
-      if (lane == 0) {
-        s_pgam = x_s;
-        s_pbad = anybad != 0ull;
-      }
+      if (lane == 0) s_pbad = anybad != 0ull;
     }
   }
   // raw rows and weights into LDS
@@ -295,7 +321,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
 #pragma unroll
   for (int q = 0; q < NWL; ++q) {
     const int e = tid + q * TR_NT;
-    if (e < 3 * TR_D * KM) s_w[e] = wv[q];
+    if (e < NSEG * TR_D * KM) s_w[e] = wv[q];
   }
   __syncthreads();  // (B_a) staging, weights, node structure
   if constexpr (RP) {
@@ -305,35 +331,48 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
     }
   }
 
-  // Replay operands of the first PRE steps, straight from the previous tape
+  // Replay operands of the first 4 PRE steps, straight from the previous tape
   // into registers: lane (c16, kk) takes k_{p_i}[16m + c16] (A) and
   // u_{p_i}[16 wave + c16] (B) for i = 4 st + kk; longer paths load the
   // remaining steps as they go.  Steps with 4 st >= pn are skipped (pn is
   // uniform).
-  constexpr int PRE = 4;
+  constexpr int PRE = NH > 1 ? 2 : 4;  // groups of four steps preloaded
   float kt[RP ? PRE : 1][RP ? TR_D / 16 : 1];
-  float ut[RP ? PRE : 1];
-  auto load_step = [&](int st, float* ka, float& ua) {
+  float ut[NH][RP ? PRE : 1];
+  auto load_step = [&](int st, float* ka, float* ua) {
     const int i = 4 * st + kk;
     const size_t e = lb * p.pT + s_ppath[i < pn ? i : 0];
     const float* kr = p.ptk + (e * p.Hk + hk) * TR_D + c16;
 #pragma unroll
     for (int m = 0; m < TR_D / 16; ++m) ka[m] = kr[16 * m];
-    ua = p.ptu[(e * p.Hv + hv) * TR_D + wave * 16 + c16];
-  };
-  if constexpr (RP) {
 #pragma unroll
-    for (int st = 0; st < PRE; ++st)
-      if (4 * st < pn) load_step(st, kt[st], ut[st]);
-  }
-  floatx4 sreg[TR_D / 16];
+    for (int h = 0; h < NH; ++h) ua[h] = p.ptu[(e * p.Hv + hv + h) * TR_D + wave * 16 + c16];
+  };
+  auto preload_steps = [&]() {
+    if constexpr (RP) {
+#pragma unroll
+      for (int st = 0; st < PRE; ++st) {
+        if (4 * st < pn) {
+          float ua[NH];
+          load_step(st, kt[st], ua);
+#pragma unroll
+          for (int h = 0; h < NH; ++h) ut[h][st] = ua[h];
+        }
+      }
+    }
+  };
+  // one head: the operands load under the conv; two heads: after it (held
+  // through the longer conv they would spill)
+  if constexpr (NH == 1) preload_steps();
+  // state tiles of this wave, one per head
+  floatx4 sreg[NH][TR_D / 16];
   const float* srow = p.S + (lb * p.Hv + hv) * static_cast<size_t>(TR_D * TR_D) +
                       static_cast<size_t>(wave * 16 + c16) * TR_D + 4 * kk;
   // S <- gamma S + sum_i w_i u_{p_i} k_{p_i}^T on this wave's tile, as
   // transposed 16x16 fp32 MFMA tiles D[j][r] = sum_i k_i[16m + j] (w_i u_i)[r]
   // (lane (c16, kk) of D holds exactly sreg[m]); the rolled tile is written
   // back in place.
-  auto replay = [&]() {
+  auto replay = [&](int h) {
     if constexpr (RP) {
       floatx4 acc[TR_D / 16];
 #pragma unroll
@@ -342,33 +381,36 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
       for (int st = 0; st < PRE; ++st) {
         if (4 * st < pn) {
           const int i = 4 * st + kk;
-          const float bu = i < pn ? ut[st] * s_pw[i] : 0.f;
+          const float bu = i < pn ? ut[h][st] * s_pw[h * TR_T + i] : 0.f;
 #pragma unroll
           for (int m = 0; m < TR_D / 16; ++m)
             acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[st][m], bu, acc[m], 0, 0, 0);
         }
       }
       for (int st = PRE; 4 * st < pn; ++st) {
-        float ka[TR_D / 16], ua;
+        float ka[TR_D / 16], ua[NH];
         load_step(st, ka, ua);
         const int i = 4 * st + kk;
-        const float bu = i < pn ? ua * s_pw[i] : 0.f;
+        const float bu = i < pn ? ua[h] * s_pw[h * TR_T + i] : 0.f;
 #pragma unroll
         for (int m = 0; m < TR_D / 16; ++m)
           acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m], bu, acc[m], 0, 0, 0);
       }
-      const float gam = s_pgam;
+      const float gam = s_pgam[h];
 #pragma unroll
-      for (int m = 0; m < TR_D / 16; ++m) sreg[m] = sreg[m] * gam + acc[m];
+      for (int m = 0; m < TR_D / 16; ++m) sreg[h][m] = sreg[h][m] * gam + acc[m];
     }
   };
-  // the rolled tile back to the live state
+  // the rolled tiles back to the live state
   auto store_replayed = [&]() {
     if constexpr (RP) {
-      float* wrow = p.S_out + (lb * p.Hv + hv) * static_cast<size_t>(TR_D * TR_D) +
-                    static_cast<size_t>(wave * 16 + c16) * TR_D + 4 * kk;
 #pragma unroll
-      for (int m = 0; m < TR_D / 16; ++m) *reinterpret_cast<floatx4*>(wrow + 16 * m) = sreg[m];
+      for (int h = 0; h < NH; ++h) {
+        float* wrow = p.S_out + (lb * p.Hv + hv + h) * static_cast<size_t>(TR_D * TR_D) +
+                      static_cast<size_t>(wave * 16 + c16) * TR_D + 4 * kk;
+#pragma unroll
+        for (int m = 0; m < TR_D / 16; ++m) *reinterpret_cast<floatx4*>(wrow + 16 * m) = sreg[h][m];
+      }
     }
   };
 
@@ -376,16 +418,21 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
     if (tid == 0 && p.dev_err) atomicOr(p.dev_err, GDN_DEV_ERR_PARENT);
     // the previous round's replay is still owed to the state
     if (RP && pn > 0) {
+      if constexpr (NH > 1) preload_steps();
 #pragma unroll
-      for (int m = 0; m < TR_D / 16; ++m) sreg[m] = *reinterpret_cast<const floatx4*>(srow + 16 * m);
-      replay();
+      for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int m = 0; m < TR_D / 16; ++m)
+          sreg[h][m] = *reinterpret_cast<const floatx4*>(srow + h * TR_D * TR_D + 16 * m);
+        replay(h);
+      }
       store_replayed();
     }
     return;
   }
   if (p.conv_win && l == 0 && hk == 0 && g == 0) {
     for (int e = tid; e < T * K; e += TR_NT)
-      p.conv_win[static_cast<size_t>(bb) * T * K + e] = s_widx[(e / K) * KM + (e % K)] / TR_ROWB - (K - 1);
+      p.conv_win[static_cast<size_t>(bb) * T * K + e] = s_widx[(e / K) * KM + (e % K)] / ROWB - (K - 1);
   }
 
   // The state tile of this wave: lane (c16, kk) holds row 16w + c16, columns
@@ -397,15 +444,17 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   // 16-lane group gr handles (segment, node) items gr + 32 r; lane li holds
   // channels 8 li .. 8 li + 7 of the segment.
   const int gr = tid >> 4, li = tid & 15;
-  float vout[2][8];
+  float vout[2 * NH][8];
 #pragma unroll
-  for (int r = 0; r < 6; ++r) {
-    if (r < TR_D / 32) {
-      sreg[2 * r] = *reinterpret_cast<const floatx4*>(srow + 32 * r);
-      sreg[2 * r + 1] = *reinterpret_cast<const floatx4*>(srow + 32 * r + 16);
+  for (int r = 0; r < 2 * NSEG; ++r) {
+    if (r < NH * TR_D / 32) {
+      // head r / 4, columns 32 (r % 4) .. +31
+      const float* sr = srow + (r / 4) * TR_D * TR_D + 32 * (r % 4);
+      sreg[r / 4][2 * (r % 4)] = *reinterpret_cast<const floatx4*>(sr);
+      sreg[r / 4][2 * (r % 4) + 1] = *reinterpret_cast<const floatx4*>(sr + 16);
     }
     const int item = gr + 32 * r;
-    const int sg = item / TR_T;  // 0 q, 1 k, 2 v (uniform per round)
+    const int sg = item / TR_T;  // 0 q, 1 k, 2.. v of each head (uniform per round)
     const int t = item % TR_T;
     const int4 wa = *reinterpret_cast<const int4*>(s_widx + t * KM);
     int wi[KM];
@@ -468,7 +517,9 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
       for (int e = 0; e < 8; ++e) vout[r - 4][e] = y[e];
     }
   }
+  if constexpr (NH > 1) __builtin_amdgcn_sched_barrier(0);  // finish the conv here
   __syncthreads();  // (B_b) staging consumed
+  if constexpr (NH > 1) preload_steps();
   // V rows into [row of S][node] (over the staging space)
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -517,11 +568,16 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
         if ((rm[r] >> tc) & 1ull) dst[ro[r] + slot] = acc[r];
     }
   }
-  if (RP && pn > 0) replay();
+  if (RP && pn > 0) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) replay(h);
+  }
   __syncthreads();  // (B_c) packed Gram rows, V rows
 
   // --------------- wave 0: packed Ti and M2 rows; waves 1..7: S0 [K;Q]^T --
-  auto solve_rows = [&]() {
+  auto solve_rows = [&](int h) {
+    const float* s_gah = s_ga + h * TR_T;
+    const float* s_gbh = s_gb + h * TR_T;
     const int t = lane;
     if (t >= T) return;
     const int d = s_dep[t];
@@ -540,8 +596,8 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
       }
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        pa[m] = s_ga[pn[m]];
-        pb[m] = s_gb[pn[m]];
+        pa[m] = s_gah[pn[m]];
+        pb[m] = s_gbh[pn[m]];
         po[m] = s_off[pn[m]];
       }
       float kv[8][8];
@@ -596,8 +652,8 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
         for (int j = i + 1; j < d; ++j) {
           const int v = __builtin_ctzll(mm);
           mm &= mm - 1ull;
-          gmm *= s_ga[v];
-          acc = fmaf(s_TI[off + j] * s_gb[v] * gmm, s_KK[s_off[v] + i], acc);
+          gmm *= s_gah[v];
+          acc = fmaf(s_TI[off + j] * s_gbh[v] * gmm, s_KK[s_off[v] + i], acc);
         }
         s_TI[off + i] = -acc;
       }
@@ -610,45 +666,119 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
           const int v = 63 - __builtin_clzll(mm);
           mm ^= 1ull << v;
           acc = fmaf(gmm * s_QK[off + j], s_TI[s_off[v] + i], acc);
-          gmm *= s_ga[v];
+          gmm *= s_gah[v];
         }
         s_M2[off + i] = acc;
       }
     }
   };
   if (wave == 0) {
-    solve_rows();
+    solve_rows(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // S0 [K;Q]^T: A = this wave's tile, B = pre-split k rows then q rows.
-  floatx4 acc1[8];
+  // S0 [K;Q]^T: A = this wave's tile of head h, B = pre-split k rows then q rows.
+  auto s0_product = [&](int h, floatx4* acc) {
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) acc1[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < 8; ++cb) acc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bf16x8 ahi, alo;
-    split_bf16x8(sreg[2 * s], sreg[2 * s + 1], ahi, alo);
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 ahi, alo;
+      split_bf16x8(sreg[h][2 * s], sreg[h][2 * s + 1], ahi, alo);
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_KQS + kk * 32 + s * 128;
+        const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(br);
+        const bf16x8 blo = *reinterpret_cast<const bf16x8*>(br + 16);
+        acc[cb] = mfma_bf16x3(ahi, alo, bhi, blo, acc[cb]);
+      }
+    }
+  };
+  // RHS_t[i] = b_t (v_t[i] - gamma_t (S0 k_t)[i]) in place of v (own rows).
+  auto form_rhs = [&](int h, const floatx4* acc) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int t = cb * 16 + c16;
+      const float bt = s_gb[h * TR_T + t];
+      const float gm = s_gam[h * TR_T + t];
+      float* col = s_v + (wave * 16 + 4 * kk) * TR_VLD + (t ^ vsw(wave * 16 + 4 * kk));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) col[r * TR_VLD] = bt * (col[r * TR_VLD] - gm * acc[cb][r]);
+    }
+  };
+  // packed Ti and M2 rows expanded to a dense pre-split [Ti; M2] operand in
+  // the K/Q space
+  auto dense_operand = [&]() {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid + q * TR_NT;  // (row n, step st, lane group kg)
+      const int n = e / 8, st = (e / 4) % 2, kg = e % 4;
+      const int nn = n % TR_T;
+      const bool m2 = n >= TR_T;
+      const unsigned long long mask = nn < T ? (s_anc[nn] | (1ull << nn)) : 0ull;
+      const int off = s_off[nn];
+      const float* src = m2 ? s_M2 : s_TI;
+      float vv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int sidx = 32 * st + 8 * kg + i;
+        const bool on = (mask >> sidx) & 1ull;
+        const float val = src[on ? off + s_dep[sidx] - 1 : 0];
+        vv[i] = on ? val : 0.f;
+      }
+      uint2 h0, l0, h1, l1;
+      split4(vv, h0, l0);
+      split4(vv + 4, h1, l1);
+      unsigned char* dst = s_r1 + n * TR_B2S + (st * 4 + kg) * 32;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(l0.x, l0.y, l1.x, l1.y);
+    }
+  };
+  // RHS^T [Ti; M2]^T on bf16x3 MFMA; u and o of head h from registers
+  // (o adds gamma_t (S0 q_t) from the first product's q columns)
+  auto second_product = [&](int h, const floatx4* acc1) {
+    floatx4 acc2[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) acc2[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const float* ar = s_v + (wave * 16 + c16) * TR_VLD + ((32 * st + 8 * kk) ^ vsw(wave * 16 + c16));
+      bf16x8 ahi, alo;
+      split_bf16x8(*reinterpret_cast<const floatx4*>(ar), *reinterpret_cast<const floatx4*>(ar + 4), ahi, alo);
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_B2S + (st * 4 + kk) * 32;
+        const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(br);
+        const bf16x8 blo = *reinterpret_cast<const bf16x8*>(br + 16);
+        acc2[cb] = mfma_bf16x3(ahi, alo, bhi, blo, acc2[cb]);
+      }
+    }
+    const int i0 = wave * 16 + 4 * kk;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
-      const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_KQS + kk * 32 + s * 128;
-      const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(br);
-      const bf16x8 blo = *reinterpret_cast<const bf16x8*>(br + 16);
-      acc1[cb] = mfma_bf16x3(ahi, alo, bhi, blo, acc1[cb]);
+      const int t = (cb * 16 + c16) % TR_T;
+      if (t < T) {
+        const size_t oi = ((lb * T + t) * p.Hv + hv + h) * TR_D + i0;
+        floatx4 val = acc2[cb];
+        if (cb >= 4) val += s_gam[h * TR_T + t] * acc1[cb];
+        // regular stores: the other 64 bytes of each 128-byte line come from
+        // the neighbouring wave and are merged in L2 before the line is written
+        *reinterpret_cast<floatx4*>((cb < 4 ? p.tu : p.o) + oi) = val;
+      }
     }
-  }
-  // RHS_t[i] = b_t (v_t[i] - gamma_t (S0 k_t)[i]) in place of v (own rows).
-  float gam_c[8];
-#pragma unroll
-  for (int cb = 0; cb < 8; ++cb) gam_c[cb] = s_gam[(cb * 16 + c16) % TR_T];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int t = cb * 16 + c16;
-    const float bt = s_gb[t];
-    float* col = s_v + (wave * 16 + 4 * kk) * TR_VLD + (t ^ vsw(wave * 16 + 4 * kk));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) col[r * TR_VLD] = bt * (col[r * TR_VLD] - gam_c[cb] * acc1[cb][r]);
+  };
+
+  floatx4 acc1[8];
+  s0_product(0, acc1);
+  form_rhs(0, acc1);
+  // the second head's product runs while K/Q are still in LDS; its RHS waits
+  // for the V space
+  floatx4 acc1b[NH > 1 ? 8 : 1];
+  if constexpr (NH > 1) {
+    // one head's product at a time (interleaving the two spills registers)
+    __builtin_amdgcn_sched_barrier(0);
+    s0_product(1, acc1b);
   }
   // The rolled tiles go back to the live state where the stores cost least:
   // waves 1..7 while they wait for wave 0's solve at the barrier below,
@@ -657,62 +787,30 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   __syncthreads();  // (B_d) packed Ti, M2; RHS; K/Q space free
   if (RP && pn > 0 && wave == 0) store_replayed();
 
-  // ----------------------- dense pre-split [Ti; M2] in the K/Q space --
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = tid + q * TR_NT;  // (row n, step st, lane group kg)
-    const int n = e / 8, st = (e / 4) % 2, kg = e % 4;
-    const int nn = n % TR_T;
-    const bool m2 = n >= TR_T;
-    const unsigned long long mask = nn < T ? (s_anc[nn] | (1ull << nn)) : 0ull;
-    const int off = s_off[nn];
-    const float* src = m2 ? s_M2 : s_TI;
-    float vv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int sidx = 32 * st + 8 * kg + i;
-      const bool on = (mask >> sidx) & 1ull;
-      const float val = src[on ? off + s_dep[sidx] - 1 : 0];
-      vv[i] = on ? val : 0.f;
-    }
-    uint2 h0, l0, h1, l1;
-    split4(vv, h0, l0);
-    split4(vv + 4, h1, l1);
-    unsigned char* dst = s_r1 + n * TR_B2S + (st * 4 + kg) * 32;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(h0.x, h0.y, h1.x, h1.y);
-    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(l0.x, l0.y, l1.x, l1.y);
-  }
+  dense_operand();
   __syncthreads();  // (B_e)
-
-  // ------------------------------- RHS^T [Ti; M2]^T, outputs from registers --
-  floatx4 acc2[8];
-#pragma unroll
-  for (int cb = 0; cb < 8; ++cb) acc2[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const float* ar = s_v + (wave * 16 + c16) * TR_VLD + ((32 * st + 8 * kk) ^ vsw(wave * 16 + c16));
-    bf16x8 ahi, alo;
-    split_bf16x8(*reinterpret_cast<const floatx4*>(ar), *reinterpret_cast<const floatx4*>(ar + 4), ahi, alo);
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_B2S + (st * 4 + kk) * 32;
-      const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(br);
-      const bf16x8 blo = *reinterpret_cast<const bf16x8*>(br + 16);
-      acc2[cb] = mfma_bf16x3(ahi, alo, bhi, blo, acc2[cb]);
+  if constexpr (NH > 1) {
+    if (wave == 0) {
+      // the second head's packed rows (the first head's are expanded)
+      solve_rows(1);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
-  const int i0 = wave * 16 + 4 * kk;
+  second_product(0, acc1);
+  if constexpr (NH > 1) {
+    __syncthreads();  // (B_f) head 0 done with V / RHS and [Ti; M2]; head 1 rows solved
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) {
-    const int t = (cb * 16 + c16) % TR_T;
-    if (t < T) {
-      const size_t oi = ((lb * T + t) * p.Hv + hv) * TR_D + i0;
-      floatx4 val = acc2[cb];
-      if (cb >= 4) val += gam_c[cb] * acc1[cb];
-      // regular stores: the other 64 bytes of each 128-byte line come from
-      // the neighbouring wave and are merged in L2 before the line is written
-      *reinterpret_cast<floatx4*>((cb < 4 ? p.tu : p.o) + oi) = val;
+    for (int r = 0; r < 2; ++r) {
+      const int t = (gr + 32 * (4 + r)) % TR_T;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_v[(8 * li + e) * TR_VLD + (t ^ vsw(8 * li))] = vout[2 + r][e];
     }
+    __syncthreads();  // (B_g) head 1's V rows
+    form_rhs(1, acc1b);
+    dense_operand();
+    __syncthreads();  // (B_h)
+    second_product(1, acc1b);
   }
 }
 
@@ -721,17 +819,25 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s) {
   const int G = a.Hv / a.Hk;
   const int n_units = a.L * a.B * a.Hk;
-  const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
+  // both v-heads of a k-head in one workgroup (q/k conv, norms and Gram done
+  // once) where the layout fits: two v-heads per k-head, conv width 4
+  const int nh = (G == 2 && a.K == 4) ? 2 : 1;
+  const long long grid =
+      static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * (G / nh);
   if (grid > 0x7fffffffLL || a.T > TR_T || a.T <= 32) return hipErrorInvalidValue;
   const bool rp = a.prev_n_keep != nullptr;
   if (rp && (a.pT < 1 || a.pT > TR_T || !a.ptu || !a.ptk || !a.ptg || !a.S_out))
     return hipErrorInvalidValue;
-  if (a.K == 4) {
-    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
-    else hipLaunchKernelGGL((k_verify_tree<4, false>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
+  const dim3 gd(static_cast<int>(grid)), bd(TR_NT);
+  if (nh == 2) {
+    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 2>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_tree<4, false, 2>), gd, bd, 0, s, a);
+  } else if (a.K == 4) {
+    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 1>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_tree<4, false, 1>), gd, bd, 0, s, a);
   } else {
-    if (rp) hipLaunchKernelGGL((k_verify_tree<0, true>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
-    else hipLaunchKernelGGL((k_verify_tree<0, false>), dim3(static_cast<int>(grid)), dim3(TR_NT), 0, s, a);
+    if (rp) hipLaunchKernelGGL((k_verify_tree<0, true, 1>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_tree<0, false, 1>), gd, bd, 0, s, a);
   }
   return hipGetLastError();
 }
