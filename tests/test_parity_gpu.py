@@ -378,6 +378,52 @@ def test_fused_tree_replay_bad_inputs_flag():
     assert rel_fro(S[:, 0].cpu().double().numpy(), S_ref[:, 0].cpu().double().numpy()) <= 1e-5
 
 
+@pytest.mark.parametrize("Hk,Hv,K,T", [(2, 4, 4, 48), (2, 2, 4, 64), (1, 4, 3, 40)])
+def test_tree_replay_long_previous_paths(Hk, Hv, K, T):
+    """gdn_tree_verify_replay with previous paths of 0, 9, 20 and 64 steps
+    (beyond the operands preloaded into registers): the state equals the
+    oracle's tape_rollback along the path and the outputs its tree_verify from
+    that state.  The cases cover two v-heads per workgroup and the one-head
+    form (one v-head per k-head; conv width 3)."""
+    _need_gpu()
+    from round_ref import oshape
+    cfg = W.CONFIGS[5].with_(L=1, B=4, Hk=Hk, Hv=Hv, K=K, T=T, V=97)
+    inp = W.layer_inputs(cfg, 3, "cpu")
+    parent = W.tree_accept_inputs(cfg, 3, "cpu")["parent"]
+    sh, osh = gshape(cfg), oshape(cfg)
+    pT = 64
+    gen = torch.Generator().manual_seed(55 + Hv + K)
+    pu = torch.randn((1, cfg.B, pT, Hv, cfg.Dv), generator=gen) * 0.2
+    pk = torch.nn.functional.normalize(torch.randn((1, cfg.B, pT, Hk, cfg.Dk), generator=gen),
+                                       dim=-1)
+    pg = 0.6 + 0.4 * torch.rand((1, cfg.B, pT, Hv), generator=gen)
+    nk = torch.tensor([0, 9, 20, 64], dtype=torch.int32)
+    path = torch.full((cfg.B, pT), -1, dtype=torch.int32)
+    for bb in range(cfg.B):
+        path[bb, :int(nk[bb])] = torch.randperm(pT, generator=gen)[:int(nk[bb])].to(torch.int32)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    S = d["S0"].clone()
+    o = torch.empty((1, cfg.B, T, Hv, cfg.Dv), device=DEV)
+    tape = gb.Tape.empty(sh, T, DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print("tree replay long paths", Hk, Hv, K, T, flush=True)
+    gb.gdn_tree_verify_replay(sh, parent.to(DEV), d["x"], d["conv_state"], d["conv_w"], d["a"],
+                              d["b"], S, o, tape, gb.Tape(pu.to(DEV), pk.to(DEV), pg.to(DEV)),
+                              nk.to(DEV), prev_path=path.to(DEV), dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    f = {k: W.to_f64(v) for k, v in inp.items()}
+    S_rep = oracle.tape_rollback(osh, f["S0"], pu.double().numpy(), pk.double().numpy(),
+                                 pg.double().numpy(), nk.numpy(), path.numpy())
+    assert rel_fro(S.cpu().double().numpy(), S_rep) <= 1e-5
+    assert torch.equal(S[:, 0].cpu(), inp["S0"][:, 0])
+    ref = oracle.tree_verify(osh, parent.numpy(), f["x"], f["conv_state"], f["conv_w"], f["a"],
+                             f["b"], S_rep)
+    for name, got in (("o", o), ("u", tape.u), ("k", tape.k)):
+        e = rel_fro(got.cpu().double().numpy(), ref[name])
+        assert e <= 1e-4, (name, e)
+
+
 def test_fused_replay_bad_prev_n_keep_flags():
     """An accepted length outside [0, prev_T] sets GDN_DEV_ERR_N_KEEP and
     that sequence is verified from its state unchanged."""
