@@ -161,10 +161,13 @@ gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* par
   v.conv_win = conv_win;
   v.dev_err = dev_err;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool tree_kernel =
+      T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128;
   if (shape->gate_per_key)
-    return launch_status(gdn::launch_verify_vg_tree(v, shape->d_k, shape->d_v, shape->in_dtype, s));
-  if (T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128)
-    return launch_status(gdn::launch_verify_tree(v, s));
+    return launch_status(tree_kernel ? gdn::launch_verify_tree_vg(v, s)
+                                     : gdn::launch_verify_vg_tree(v, shape->d_k, shape->d_v,
+                                                                  shape->in_dtype, s));
+  if (tree_kernel) return launch_status(gdn::launch_verify_tree(v, s));
   return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype, s));
 }
 

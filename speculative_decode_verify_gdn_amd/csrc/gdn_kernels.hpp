@@ -111,6 +111,9 @@ hipError_t launch_verify_wy(const VerifyArgs& a, int dk, int dv, int dtype, hipS
 hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
 // Trees of 33..64 nodes, 128-dim heads, bf16 inputs (per-node path solve).
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s);
+// Trees of 33..64 nodes (bf16, 128-dim heads) with the per-key-channel gate,
+// on the MFMA tree kernel (no replay).
+hipError_t launch_verify_tree_vg(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream_t s);
 // The state and conv-window rollbacks of a round in one launch.
 hipError_t launch_round_rollback(const RollbackArgs& r, const ConvRollbackArgs& c, int dk, int dv,

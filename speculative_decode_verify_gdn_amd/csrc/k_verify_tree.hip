@@ -98,8 +98,9 @@ struct TreeLds {
   static constexpr int R1 = 2 * TR_T * TR_KQS;
 };
 
-template <int KC, bool RP, int NH>
+template <int KC, bool RP, int NH, bool VG>
 __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
+  static_assert(!VG || (NH == 1 && !RP), "the per-key-channel gate runs one head, no replay");
   constexpr int KM = KC > 0 ? KC : 8;
   using LY = TreeLds<KM, NH>;
   constexpr int XR = LY::XR;
@@ -167,8 +168,19 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   float ga_ld[NH], gb_ld[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    ga_ld[h] = ld_in(static_cast<const uint16_t*>(p.a), gi + h);
+    // per-key-channel gates enter through the operands instead (below)
+    ga_ld[h] = VG ? 1.f : ld_in(static_cast<const uint16_t*>(p.a), gi + h);
     gb_ld[h] = ld_in(static_cast<const uint16_t*>(p.b), gi + h);
+  }
+  // per-key-channel gates of the head, [node][channel]: thread tid holds node
+  // tid / 8, channels 16 (tid % 8) .. +15
+  u32x4 avr[VG ? 2 : 1];
+  if constexpr (VG) {
+    const int tn = tid / 8;
+    const uint16_t* ap = static_cast<const uint16_t*>(p.a) +
+                         ((lb * T + (tn < T ? tn : 0)) * p.Hv + hv) * TR_D + 16 * (tid % 8);
+    avr[0] = *reinterpret_cast<const u32x4*>(ap);
+    avr[1] = *reinterpret_cast<const u32x4*>(ap + 8);
   }
   // local channel c in [q | k | v-rows] -> qkv channel
   auto chan = [&](int c) {
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
       for (int h = 0; h < NH; ++h) {
         s_ga[h * TR_T + t] = ga_ld[h];
         s_gb[h * TR_T + t] = gb_ld[h];
-        p.tg[(lb * T + t) * p.Hv + hv + h] = ga_ld[h];
+        if (!VG) p.tg[(lb * T + t) * p.Hv + hv + h] = ga_ld[h];
       }
     } else {
 #pragma unroll
@@ -520,6 +532,125 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   if constexpr (NH > 1) __builtin_amdgcn_sched_barrier(0);  // finish the conv here
   __syncthreads();  // (B_b) staging consumed
   if constexpr (NH > 1) preload_steps();
+  if constexpr (VG) {
+    // Per-key-channel gate: node v's parent state applied to a_v * k_v is
+    // S0 (gamma_v * k_v) + sum_i u_i c_{v,i} over v's proper ancestors i, with
+    // c_{v,i} = sum_c k_i[c] w_{v,i}[c] k_v[c], w_{v,i} the product of a over
+    // the path nodes below i down to v and gamma_v the product over the whole
+    // path; o_v = S0 (gamma_v * q_v) + sum_i u_i d_{v,i} + u_v (k_v . q_v).
+    // This is the scalar algebra with A[v,i] = b_v c_{v,i}, Oc[v,i] = d_{v,i}
+    // and gamma folded into the K/Q operand rows: c and d go into the packed
+    // Gram rows, the gates used by the scalar path stay 1, and each node's
+    // operand rows are scaled by gamma_v.
+    float* s_av = s_v;  // gates [node][channel] over the V space, until the V rows
+    {
+      const int tn = tid / 8, c0 = 16 * (tid % 8);
+      float av[16];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          av[8 * q + 2 * w] = __uint_as_float(avr[q][w] << 16);
+          av[8 * q + 2 * w + 1] = __uint_as_float(avr[q][w] & 0xffff0000u);
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 v4 = {av[4 * q], av[4 * q + 1], av[4 * q + 2], av[4 * q + 3]};
+        *reinterpret_cast<floatx4*>(s_av + tn * TR_D + c0 + 4 * q) = v4;
+        if (tn < T)
+          *reinterpret_cast<floatx4*>(p.tg + ((lb * T + tn) * p.Hv + hv) * TR_D + c0 + 4 * q) = v4;
+      }
+    }
+    // the 8 channels 8 li .. 8 li + 7 of pre-split operand row n, and back
+    auto read8 = [&](int n, float* y) {
+      const unsigned char* row = s_r1 + n * TR_KQS + (li / 4) * 128 + ((li % 4) / 2) * 8;
+      const int kg = 2 * (li % 2);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + (kg + hf) * 32);
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + (kg + hf) * 32 + 16);
+        y[4 * hf] = __uint_as_float(hi.x << 16) + __uint_as_float(lo.x << 16);
+        y[4 * hf + 1] = __uint_as_float(hi.x & 0xffff0000u) + __uint_as_float(lo.x & 0xffff0000u);
+        y[4 * hf + 2] = __uint_as_float(hi.y << 16) + __uint_as_float(lo.y << 16);
+        y[4 * hf + 3] = __uint_as_float(hi.y & 0xffff0000u) + __uint_as_float(lo.y & 0xffff0000u);
+      }
+    };
+    auto write8 = [&](int n, const float* y) {
+      unsigned char* row = s_r1 + n * TR_KQS + (li / 4) * 128 + ((li % 4) / 2) * 8;
+      const int kg = 2 * (li % 2);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint2 hi, lo;
+        split4(y + 4 * hf, hi, lo);
+        *reinterpret_cast<uint2*>(row + (kg + hf) * 32) = hi;
+        *reinterpret_cast<uint2*>(row + (kg + hf) * 32 + 16) = lo;
+      }
+    };
+    __syncthreads();  // gates in LDS
+    // the path walk: 16-lane group gr takes nodes gr and gr + 32
+    float gam[2][8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int v = gr + 32 * j;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gam[j][e] = 0.f;
+      if (v < T) {
+        float kv[8], qv[8], w[8];
+        read8(v, kv);
+        read8(TR_T + v, qv);
+        const floatx4 w0 = *reinterpret_cast<const floatx4*>(s_av + v * TR_D + 8 * li);
+        const floatx4 w1 = *reinterpret_cast<const floatx4*>(s_av + v * TR_D + 8 * li + 4);
+        float kq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          w[e] = e < 4 ? w0[e] : w1[e - 4];
+          kq = fmaf(kv[e], qv[e], kq);
+        }
+        const int off = s_off[v];
+        for (int i = s_par[v]; i >= 0; i = s_par[i]) {
+          float ki[8];
+          read8(i, ki);
+          const floatx4 a0 = *reinterpret_cast<const floatx4*>(s_av + i * TR_D + 8 * li);
+          const floatx4 a1 = *reinterpret_cast<const floatx4*>(s_av + i * TR_D + 8 * li + 4);
+          float cc = 0.f, dd = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float kw = ki[e] * w[e];
+            cc = fmaf(kw, kv[e], cc);
+            dd = fmaf(kw, qv[e], dd);
+            w[e] *= e < 4 ? a0[e] : a1[e - 4];
+          }
+          cc = sum16(cc);
+          dd = sum16(dd);
+          if (li == 0) {
+            const int slot = s_dep[i] - 1;
+            s_KK[off + slot] = cc;
+            s_QK[off + slot] = dd;
+          }
+        }
+        kq = sum16(kq);
+        if (li == 0) s_QK[off + s_dep[v] - 1] = kq;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gam[j][e] = w[e];
+      }
+    }
+    __syncthreads();  // every walk has read the unscaled rows and the gates
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int v = gr + 32 * j;
+      if (v < T) {
+        float y[8];
+        read8(v, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] *= gam[j][e];
+        write8(v, y);
+        read8(TR_T + v, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] *= gam[j][e];
+        write8(TR_T + v, y);
+      }
+    }
+  }
   // V rows into [row of S][node] (over the staging space)
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -529,7 +660,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   }
 
   // -------------------------- Gram [K;Q] K^T, ancestor-or-self entries only --
-  {
+  if constexpr (!VG) {
     const int rb = wave;           // 16-row block of [K;Q]
     const bool isq = rb >= 4;
     const int nb = rb % 4;         // node block of the rows
@@ -830,15 +961,26 @@ hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const dim3 gd(static_cast<int>(grid)), bd(TR_NT);
   if (nh == 2) {
-    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 2>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((k_verify_tree<4, false, 2>), gd, bd, 0, s, a);
+    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 2, false>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_tree<4, false, 2, false>), gd, bd, 0, s, a);
   } else if (a.K == 4) {
-    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 1>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((k_verify_tree<4, false, 1>), gd, bd, 0, s, a);
+    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 1, false>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_tree<4, false, 1, false>), gd, bd, 0, s, a);
   } else {
-    if (rp) hipLaunchKernelGGL((k_verify_tree<0, true, 1>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((k_verify_tree<0, false, 1>), gd, bd, 0, s, a);
+    if (rp) hipLaunchKernelGGL((k_verify_tree<0, true, 1, false>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_tree<0, false, 1, false>), gd, bd, 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_tree_vg(const VerifyArgs& a, hipStream_t s) {
+  const int G = a.Hv / a.Hk;
+  const int n_units = a.L * a.B * a.Hk;
+  const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
+  if (grid > 0x7fffffffLL || a.T > TR_T || a.T <= 32 || a.prev_n_keep) return hipErrorInvalidValue;
+  const dim3 gd(static_cast<int>(grid)), bd(TR_NT);
+  if (a.K == 4) hipLaunchKernelGGL((k_verify_tree<4, false, 1, true>), gd, bd, 0, s, a);
+  else hipLaunchKernelGGL((k_verify_tree<0, false, 1, true>), gd, bd, 0, s, a);
   return hipGetLastError();
 }
 

@@ -837,38 +837,52 @@ def test_vgate_rollback_matches_oracle(D, with_path):
     assert torch.equal(S[:, 0].cpu(), S0[:, 0])  # n = 0: untouched
 
 
-def test_vgate_chained_rounds():
+@pytest.mark.parametrize("tree", [False, True])
+def test_vgate_chained_rounds(tree):
     """Plain rounds (verify, greedy accept, per-key rollback, conv rollback)
-    with a per-key-channel gate, four rounds chained, against the oracle."""
+    with a per-key-channel gate, four rounds chained, against the oracle:
+    8-token chains, and 64-node trees on the MFMA tree kernel."""
     _need_gpu()
-    cfg = W.CONFIGS[3].with_(L=2, B=4, T=8, V=257)
+    cfg = (W.CONFIGS[5].with_(L=2, B=3, T=64, V=257) if tree
+           else W.CONFIGS[3].with_(L=2, B=4, T=8, V=257))
     gsh, osh = _vg_shapes(cfg)
     inp0 = _vg_inputs(cfg, 0)
     oS, ocs = W.to_f64(inp0["S0"]), W.to_f64(inp0["conv_state"])
     rb = None
     for r in range(4):
         inp = _vg_inputs(cfg, r)
-        acc = W.chain_accept_inputs(cfg, r, "cpu")
+        acc = (W.tree_accept_inputs(cfg, r, "cpu") if tree
+               else W.chain_accept_inputs(cfg, r, "cpu"))
         d = {k: v.to(DEV) for k, v in inp.items()}
+        par = acc["parent"].to(DEV) if tree else None
         if rb is None:
-            rb = spec_round.RoundBuffers(sh=gsh, T=cfg.T, V=cfg.V, tree=False,
+            rb = spec_round.RoundBuffers(sh=gsh, T=cfg.T, V=cfg.V, tree=tree,
                                          S=inp0["S0"].to(DEV), conv_state=inp0["conv_state"].to(DEV),
                                          conv_w=d["conv_w"], x=d["x"], a=d["a"], b=d["b"],
                                          logits=acc["logits"].to(DEV), draft=acc["draft"].to(DEV),
-                                         parent=None)
+                                         parent=par)
         else:
             rb.x, rb.a, rb.b, rb.conv_w = d["x"], d["a"], d["b"], d["conv_w"]
             rb.logits, rb.draft = acc["logits"].to(DEV), acc["draft"].to(DEV)
+            if tree:
+                rb.parent = par
         spec_round.run_round(rb)
         torch.cuda.synchronize()
         f = {k: W.to_f64(v) for k, v in inp.items()}
-        ref = oracle.verify_chunk_vg(osh, f["x"], ocs, f["conv_w"], f["a"], f["b"], oS)
-        n, path, bonus = oracle.accept(acc["draft"].numpy(), W.to_f64(acc["logits"]))
+        parent = acc["parent"].numpy() if tree else None
+        if tree:
+            ref = oracle.tree_verify_vg(osh, parent, f["x"], ocs, f["conv_w"], f["a"], f["b"], oS)
+        else:
+            ref = oracle.verify_chunk_vg(osh, f["x"], ocs, f["conv_w"], f["a"], f["b"], oS)
+        n, path, bonus = oracle.accept(acc["draft"].numpy(), W.to_f64(acc["logits"]), parent)
         np.testing.assert_array_equal(rb.n_keep.cpu().numpy(), n)
         np.testing.assert_array_equal(rb.bonus.cpu().numpy(), bonus)
         assert rel_fro(rb.o.cpu().double().numpy(), ref["o"]) <= 1e-4
-        oS = oracle.tape_rollback_vg(osh, oS, ref["u"], ref["k"], ref["g"], n)
-        ocs, _ = oracle.conv_rollback(osh, ocs, f["x"], n)
+        if tree:
+            np.testing.assert_array_equal(rb.path.cpu().numpy(), path)
+        oS = oracle.tape_rollback_vg(osh, oS, ref["u"], ref["k"], ref["g"], n,
+                                     path if tree else None)
+        ocs, _ = oracle.conv_rollback(osh, ocs, f["x"], n, path if tree else None)
         assert rel_fro(rb.S.cpu().double().numpy(), oS) <= 1e-4
         np.testing.assert_array_equal(rb.conv_state.cpu().double().numpy(), ocs)
     assert int(rb.dev_err.item()) == 0
@@ -910,11 +924,16 @@ def _vg_parents(rng, B, T, depth):
 @pytest.mark.parametrize("T,L,B,Hk,Hv,D,K,dtype,depth", [
     (64, 1, 2, 2, 4, 128, 4, torch.bfloat16, 8), (40, 2, 2, 1, 2, 64, 3, torch.float32, 6),
     (17, 1, 3, 2, 2, 32, 8, torch.bfloat16, 5), (1, 1, 2, 2, 4, 128, 4, torch.bfloat16, 1),
-    (64, 1, 1, 1, 2, 128, 4, torch.float32, 64), (33, 1, 2, 2, 4, 64, 2, torch.bfloat16, 33)])
+    (64, 1, 1, 1, 2, 128, 4, torch.float32, 64), (33, 1, 2, 2, 4, 64, 2, torch.bfloat16, 33),
+    (48, 2, 2, 2, 2, 128, 3, torch.bfloat16, 6), (64, 1, 1, 1, 2, 128, 4, torch.bfloat16, 64),
+    (40, 1, 2, 2, 4, 128, 4, torch.bfloat16, 20), (33, 1, 3, 1, 1, 128, 8, torch.bfloat16, 8)])
 def test_vgate_tree_verify_matches_oracle(T, L, B, Hk, Hv, D, K, dtype, depth):
     """gdn_tree_verify with a per-key-channel gate equals the oracle's
     tree_verify_vg (outputs, tape, conv windows) and leaves S untouched; the
-    depth >= T cases are chains given as parent arrays (the deepest trees)."""
+    depth >= T cases are chains given as parent arrays (the deepest trees).
+    bf16 trees of 33..64 nodes with 128-dim heads run the MFMA tree kernel
+    (conv widths 3, 4 and 8; depths up to 64), the rest the closed-form
+    per-key kernel."""
     _need_gpu()
     cfg = W.CONFIGS[2].with_(L=L, B=B, Hk=Hk, Hv=Hv, Dk=D, Dv=D, K=K, T=T, dtype=dtype)
     inp = _vg_inputs(cfg, 5)
