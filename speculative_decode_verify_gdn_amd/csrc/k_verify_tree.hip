@@ -803,6 +803,85 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
       }
     }
   };
+  // The second head's rows for trees of depth <= 8, solved by wave 1 next to
+  // wave 0's first-head solve, in registers (ancestors' Ti rows come from
+  // their lanes); written to the packed rows once the first head's are
+  // expanded.
+  auto solve_rows_reg = [&](int h, float* xs, float* m2) {
+    const float* s_gah = s_ga + h * TR_T;
+    const float* s_gbh = s_gb + h * TR_T;
+    const int t = lane;
+    const int d = t < T ? s_dep[t] : 0;
+    const int off = s_off[t];
+    const unsigned long long mask = t < T ? (s_anc[t] | (1ull << t)) : 0ull;
+    int pn[8], po[8];
+    float pa[8], pb[8];
+    unsigned long long mm = mask;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int v = mm ? __builtin_ctzll(mm) : 0;
+      mm &= mm - 1ull;
+      pn[m] = v;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      pa[m] = s_gah[pn[m]];
+      pb[m] = s_gbh[pn[m]];
+      po[m] = s_off[pn[m]];
+    }
+    float kv[8][8];
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < j; ++i) kv[j][i] = (j < d) ? s_KK[po[j] + i] : 0.f;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      float acc = 0.f, gmm = 1.f;
+#pragma unroll
+      for (int j = i + 1; j < 8; ++j) {
+        gmm *= pa[j];
+        acc = fmaf(xs[j] * pb[j] * gmm, kv[j][i], acc);
+      }
+      xs[i] = (i == d - 1) ? 1.f : (i < d - 1 ? -acc : 0.f);
+    }
+    float oc[8];
+    {
+      float gmm = 1.f;
+#pragma unroll
+      for (int j = 7; j >= 0; --j) {
+        oc[j] = (j < d) ? gmm * s_QK[off + j] : 0.f;
+        if (j < d) gmm *= pa[j];
+      }
+    }
+    // Ti[p_j][i] is slot i of lane p_j's row (every lane takes part)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = i; j < 8; ++j) {
+        const float tv = __shfl(xs[i], pn[j], 64);
+        acc = fmaf(oc[j], (j < d) ? tv : 0.f, acc);
+      }
+      m2[i] = acc;
+    }
+  };
+  auto store_rows_reg = [&](const float* xs, const float* m2) {
+    const int t = lane;
+    if (t < T) {
+      const int d = s_dep[t], off = s_off[t];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < d) {
+          s_TI[off + i] = xs[i];
+          s_M2[off + i] = m2[i];
+        }
+    }
+  };
+  float xs1[NH > 1 ? 8 : 1], m21[NH > 1 ? 8 : 1];
+  const bool early1 = NH > 1 && s_maxd <= 8;
+  if constexpr (NH > 1) {
+    if (wave == 1 && early1) solve_rows_reg(1, xs1, m21);
+  }
   if (wave == 0) {
     solve_rows(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -921,8 +1000,10 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   dense_operand();
   __syncthreads();  // (B_e)
   if constexpr (NH > 1) {
-    if (wave == 0) {
-      // the second head's packed rows (the first head's are expanded)
+    // the second head's packed rows (the first head's are expanded)
+    if (early1) {
+      if (wave == 1) store_rows_reg(xs1, m21);
+    } else if (wave == 0) {
       solve_rows(1);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
