@@ -980,16 +980,34 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   };
 
   floatx4 acc1[8];
-  s0_product(0, acc1);
-  form_rhs(0, acc1);
-  // the second head's product runs while K/Q are still in LDS; its RHS waits
-  // for the V space
+  // the second head's product runs while K/Q are still in LDS, on the same
+  // operand fragments as the first's; its RHS waits for the V space
   floatx4 acc1b[NH > 1 ? 8 : 1];
   if constexpr (NH > 1) {
-    // one head's product at a time (interleaving the two spills registers)
-    __builtin_amdgcn_sched_barrier(0);
-    s0_product(1, acc1b);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      acc1[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      acc1b[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 ahi0, alo0, ahi1, alo1;
+      split_bf16x8(sreg[0][2 * s], sreg[0][2 * s + 1], ahi0, alo0);
+      split_bf16x8(sreg[1][2 * s], sreg[1][2 * s + 1], ahi1, alo1);
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_KQS + kk * 32 + s * 128;
+        const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(br);
+        const bf16x8 blo = *reinterpret_cast<const bf16x8*>(br + 16);
+        acc1[cb] = mfma_bf16x3(ahi0, alo0, bhi, blo, acc1[cb]);
+        acc1b[cb] = mfma_bf16x3(ahi1, alo1, bhi, blo, acc1b[cb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    s0_product(0, acc1);
   }
+  form_rhs(0, acc1);
   // The rolled tiles go back to the live state where the stores cost least:
   // waves 1..7 while they wait for wave 0's solve at the barrier below,
   // wave 0 once past it (its stores then drain under the dense operand).
