@@ -192,7 +192,8 @@ gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* par
  * unchanged.  A malformed parent array sets GDN_DEV_ERR_PARENT and leaves the
  * sequence's outputs unwritten, but the replay is still applied to S.  Both
  * steps run in one kernel for trees of 33..64 nodes with bf16 inputs and
- * 128-dim heads; otherwise as the two calls in sequence.
+ * 128-dim heads, and for any tree with the per-key-channel gate; otherwise
+ * as the two calls in sequence.
  * Source: GDN page s4 (restore the snapshot and replay the accepted steps),
  * applied at the start of the next verify of the same layer; s2.2 and s8
  * (tree-aware verify).
