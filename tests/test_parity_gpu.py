@@ -626,6 +626,84 @@ def test_full_size_sampled(cfg_id):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("cfg_id", [4, 5])
+def test_full_size_fused_rounds_sampled(cfg_id):
+    """The round form the benchmark times for configurations 4 and 5, at full
+    size: two fused rounds, the second replaying the first's accepted
+    prefixes (paths) inside its verify.  Sampled (layer, sequence) units of
+    the second round's outputs, tape, accepted lengths, paths and conv
+    window, and of the state it leaves (one accepted prefix behind), against
+    the oracle's plain rounds."""
+    _need_gpu()
+    cfg = W.CONFIGS[cfg_id]
+    tree = cfg.is_tree
+    torch.cuda.empty_cache()
+    ls = [0, cfg.L // 2, cfg.L - 1]
+    bs = [0, cfg.B // 3, cfg.B - 1]
+
+    def host(inp):
+        f = {}
+        for k, v in inp.items():
+            t = v[ls]
+            if k != "conv_w":
+                t = t[:, bs]
+            f[k] = W.to_f64(t)
+        return f
+
+    accs = [W.tree_accept_inputs(cfg, r, DEV) if tree else W.chain_accept_inputs(cfg, r, DEV)
+            for r in (0, 1)]
+    inp0 = W.layer_inputs(cfg, 0, DEV)
+    f0 = host(inp0)
+    print("full-size fused rounds", cfg_id, flush=True)
+    fr = spec_round.FusedRound(make_buffers(cfg, inp0, accs[0]))
+    rb = fr.rb
+    fr.round(0, first=True)
+    torch.cuda.synchronize()
+    inp1 = W.layer_inputs(cfg, 1, DEV)
+    f1 = host(inp1)
+    del inp1["S0"], inp1["conv_state"]  # the round goes on from the live state and window
+    rb.x, rb.a, rb.b, rb.conv_w = inp1["x"], inp1["a"], inp1["b"], inp1["conv_w"]
+    rb.logits, rb.draft = accs[1]["logits"], accs[1]["draft"]
+    if tree:
+        rb.parent = accs[1]["parent"]
+    fr.round(1)
+    torch.cuda.synchronize()
+
+    def pick(t, has_l=True):
+        return (t[ls][:, bs] if has_l else t[bs]).detach().cpu()
+
+    tape = fr.tapes[1]
+    got = dict(o=pick(rb.o), u=pick(tape.u), k=pick(tape.k), g=pick(tape.g),
+               S=pick(rb.S), cs=pick(rb.conv_state), n_keep=pick(fr.n_keeps[1], False),
+               path=pick(fr.paths[1], False), bonus=pick(rb.bonus, False),
+               win_idx=pick(rb.win_idx, False))
+    np.testing.assert_array_equal(got["n_keep"].numpy(), np.asarray(accs[1]["n_planted"])[bs])
+    assert int(rb.dev_err.item()) == 0
+
+    def ref_round(f, acc):
+        par = acc["parent"][bs].cpu().numpy() if tree else None
+        return oracle_round(cfg, f, acc["draft"][bs].cpu().numpy(), W.to_f64(acc["logits"][bs]),
+                            par, L=len(ls), B=len(bs))
+
+    ref0 = ref_round(f0, accs[0])
+    f1["S0"], f1["conv_state"] = ref0["S_new"], ref0["cs_new"]
+    ref1 = ref_round(f1, accs[1])
+    for key in ("n_keep", "bonus", "win_idx"):
+        np.testing.assert_array_equal(got[key].numpy(), np.asarray(ref1[key]), err_msg=key)
+    if tree:
+        np.testing.assert_array_equal(got["path"].numpy(), ref1["path"])
+        np.testing.assert_array_equal(rb.conv_win[bs].cpu().numpy(), ref1["conv_win"])
+    np.testing.assert_array_equal(got["cs"].double().numpy(), ref1["cs_new"])
+    for key in ("o", "u", "k"):
+        e = rel_fro(got[key].double().numpy(), ref1[key])
+        assert e <= 1e-4, (key, e)
+    np.testing.assert_array_equal(got["g"].double().numpy(), ref1["g"])
+    e = rel_fro(got["S"].double().numpy(), ref0["S_new"])
+    assert e <= 1e-4, ("S after the replay", e)
+    del fr, rb, inp0, inp1, accs
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------- sampling accept --
 
 def _sample_inputs(B, T, V, tau, dtype, seed, p_lo=0.05, p_hi=0.95):
