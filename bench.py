@@ -413,7 +413,9 @@ def vgate_pass(cfg, stream, steps):
             "verify_hbm_frac": vb / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "rollback_state_and_conv_ms": t_plain[2],
             "kernel": (("k_verify_tree (per-key gate)" if 32 < cfg.T <= 64 and cfg.dtype == torch.bfloat16
-                        and cfg.Dk == cfg.Dv == 128 else "k_verify_vgt") if tree else "k_verify_vg"),
+                        and cfg.Dk == cfg.Dv == 128 else "k_verify_vgt") if tree else
+                       ("k_verify_chain (per-key gate)" if cfg.T <= 16 and cfg.dtype == torch.bfloat16
+                        and cfg.Dk == cfg.Dv == 128 else "k_verify_vg")),
             "fused": {"round_ms": t_fround, "value": cfg.B * cfg.T / (t_fround * 1e-3),
                       "verify_per_layer_ms": t_fverify / cfg.L, "kernel": "k_verify_vgt"}}
 

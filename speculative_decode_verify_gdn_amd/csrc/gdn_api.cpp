@@ -101,8 +101,11 @@ gdn_status gdn_verify_chunk(const gdn_shape* shape, int32_t T, const void* x,
   if (!verify_ptrs_ok(x, conv_state, conv_w, a, b, S, o, tape)) return GDN_ERR_INVALID_ARG;
   VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (shape->gate_per_key)
+  if (shape->gate_per_key) {
+    if (T <= 16 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128)
+      return launch_status(gdn::launch_verify_chain_vg(v, s));
     return launch_status(gdn::launch_verify_vg(v, shape->d_k, shape->d_v, shape->in_dtype, s));
+  }
   if (T <= 16) return launch_status(gdn::launch_verify_chain(v, shape->d_k, shape->d_v, shape->in_dtype, s));
   return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype, s));
 }

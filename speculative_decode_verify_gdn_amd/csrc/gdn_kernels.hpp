@@ -109,6 +109,9 @@ hipError_t launch_sample(const SampleArgs& a, int dtype, hipStream_t s);
 hipError_t launch_verify_wy(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
 // Chains of at most 16 tokens (wave-specialised kernel).
 hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
+// Chains of <= 16 tokens with the per-key-channel gate (bf16, 128-dim heads),
+// on the MFMA chain kernel (no replay).
+hipError_t launch_verify_chain_vg(const VerifyArgs& a, hipStream_t s);
 // Trees of 33..64 nodes, 128-dim heads, bf16 inputs (per-node path solve).
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s);
 // Trees of 33..64 nodes (bf16, 128-dim heads) with the per-key-channel gate,

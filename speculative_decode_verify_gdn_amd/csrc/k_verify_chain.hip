@@ -64,6 +64,15 @@ __device__ __forceinline__ void split_pair(float y0, float y1, uint32_t& hi, uin
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
+// Sum over aligned groups of 16 lanes (DPP; every lane gets its group's sum).
+__device__ __forceinline__ float sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
 __device__ __forceinline__ float silu_f(float y) {
   return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
 }
@@ -113,9 +122,11 @@ struct ChainLayout {
   static_assert(ALD == GLD, "A and Oc overwrite the Gram rows in place");
 };
 
-template <int DK, int DV, int TMAX, int KC, typename TIn, bool RP>
+template <int DK, int DV, int TMAX, int KC, typename TIn, bool RP, bool VG = false>
 __global__ __launch_bounds__(chain_threads<DV>())
 __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
+  static_assert(!VG || (!RP && DK == 128 && DV == 128 && sizeof(TIn) == 2),
+                "the per-key-channel gate runs 128-dim heads, bf16 inputs, no replay");
   constexpr int KM = KC > 0 ? KC : 8;
   using LY = ChainLayout<DK, DV, TMAX, KM, TIn>;
   using PR = Pair<TIn>;
@@ -134,6 +145,8 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
   float* const s_B = s_kf;                                 // rows: Ti, then M2
   __shared__ float s_rn[NKQ], s_ga[TMAX], s_gb[TMAX];
   __shared__ float s_ck[TMAX], s_cq[TMAX], s_cb[TMAX];
+  // per-key-channel gates [token][channel], bf16 as given
+  __shared__ __align__(16) uint16_t s_av[VG ? TMAX * DK : 8];
   // previous round's accepted prefix: w_i = prod_{i<j<pn} g_j (zero for
   // i >= pn) and gamma = prod_{j<pn} g_j
   constexpr int PM = 16;
@@ -221,8 +234,23 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
     // Gates (clamped, unconditional loads).
     const int tq = lane < T ? lane : 0;
     const size_t gi = lb * p.ab_ld + static_cast<size_t>(tq) * p.Hv + hv;
-    const float ga_ld = ld_in(static_cast<const TIn*>(p.a), gi);
+    // (the per-key-channel gate enters through the operands instead)
+    const float ga_ld = VG ? 1.f : ld_in(static_cast<const TIn*>(p.a), gi);
     const float gb_ld = ld_in(static_cast<const TIn*>(p.b), gi);
+    // per-key-channel gates: lane takes 16-byte chunks lane + 64 j, chunk q
+    // holding channels 8 (q % 16) .. +7 of token q / 16
+    constexpr int NAV = VG ? (TMAX * DK / 8 + 63) / 64 : 1;
+    u32x4 avr[NAV];
+    if constexpr (VG) {
+#pragma unroll
+      for (int j = 0; j < NAV; ++j) {
+        const int q = lane + 64 * j;
+        const int t = q / (DK / 8);
+        const uint16_t* ap = static_cast<const uint16_t*>(p.a) +
+                             ((lb * T + (t < T ? t : 0)) * p.Hv + hv) * DK + 8 * (q % (DK / 8));
+        avr[j] = *reinterpret_cast<const u32x4*>(ap);
+      }
+    }
     const float pg_ld = RP && lane < pn ? p.ptg[(lb * p.pT + lane) * p.Hv + hv] : 1.f;
 
     auto load_pair = [&](int j, typename PR::raw* xr, float* w0, float* w1) {
@@ -327,7 +355,28 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
     if (lane < TMAX) {
       s_ga[lane] = lane < T ? ga_ld : 1.f;
       s_gb[lane] = lane < T ? gb_ld : 0.f;
-      if (lane < T) p.tg[(lb * T + lane) * p.Hv + hv] = ga_ld;
+      if (lane < T && !VG) p.tg[(lb * T + lane) * p.Hv + hv] = ga_ld;
+    }
+    if constexpr (VG) {
+#pragma unroll
+      for (int j = 0; j < NAV; ++j) {
+        const int q = lane + 64 * j;
+        const int t = q / (DK / 8), c0 = 8 * (q % (DK / 8));
+        if (t < TMAX) *reinterpret_cast<u32x4*>(s_av + t * DK + c0) = avr[j];
+        if (t < T) {
+          floatx4 v0, v1;
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            v0[2 * w] = __uint_as_float(avr[j][w] << 16);
+            v0[2 * w + 1] = __uint_as_float(avr[j][w] & 0xffff0000u);
+            v1[2 * w] = __uint_as_float(avr[j][2 + w] << 16);
+            v1[2 * w + 1] = __uint_as_float(avr[j][2 + w] & 0xffff0000u);
+          }
+          floatx4* tgp = reinterpret_cast<floatx4*>(p.tg + ((lb * T + t) * p.Hv + hv) * DK + c0);
+          tgp[0] = v0;
+          tgp[1] = v1;
+        }
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -372,32 +421,143 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
       }
     }
 
+    if constexpr (VG) {
+      // Per-key-channel gate: token t's state before it, applied to a_t * k_t,
+      // is S0 (gamma_t * k_t) + sum_{i<t} u_i c_{t,i} with c_{t,i} =
+      // sum_c k_i[c] w_{t,i}[c] k_t[c], w_{t,i} the product of a_j over
+      // i < j <= t and gamma_t over j <= t; o_t adds d_{t,i} (q_t in place of
+      // k_t) and u_t (k_t . q_t).  So A[t,i] = b_t c_{t,i} and Oc[t,i] =
+      // d_{t,i}, found by walking back from t (only forward gate products),
+      // and the operand rows become gamma_t * k_t and gamma_t * q_t
+      // (normalised), leaving the per-token scales at b_t and 1.
+      for (int e = lane; e < 2 * TMAX * ALD; e += 64) s_G[e] = 0.f;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int gq = lane >> 4, li = lane & 15;
+      auto read_pre = [&](int n, float* y) {  // channels 8 li .. +7 of pre-split row n
+        const unsigned char* row = s_kq + n * KQS + (li / 4) * 128 + ((li % 4) / 2) * 8;
+        const int kg = 2 * (li % 2);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint2 hi = *reinterpret_cast<const uint2*>(row + (kg + hf) * 32);
+          const uint2 lo = *reinterpret_cast<const uint2*>(row + (kg + hf) * 32 + 16);
+          y[4 * hf] = __uint_as_float(hi.x << 16) + __uint_as_float(lo.x << 16);
+          y[4 * hf + 1] = __uint_as_float(hi.x & 0xffff0000u) + __uint_as_float(lo.x & 0xffff0000u);
+          y[4 * hf + 2] = __uint_as_float(hi.y << 16) + __uint_as_float(lo.y << 16);
+          y[4 * hf + 3] = __uint_as_float(hi.y & 0xffff0000u) + __uint_as_float(lo.y & 0xffff0000u);
+        }
+      };
+      auto write_pre = [&](int n, const float* y) {
+        unsigned char* row = s_kq + n * KQS + (li / 4) * 128 + ((li % 4) / 2) * 8;
+        const int kg = 2 * (li % 2);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          uint32_t h0, l0, h1, l1;
+          split_pair(y[4 * hf], y[4 * hf + 1], h0, l0);
+          split_pair(y[4 * hf + 2], y[4 * hf + 3], h1, l1);
+          *reinterpret_cast<uint2*>(row + (kg + hf) * 32) = make_uint2(h0, h1);
+          *reinterpret_cast<uint2*>(row + (kg + hf) * 32 + 16) = make_uint2(l0, l1);
+        }
+      };
+      auto gates8 = [&](int t, float* a) {
+        const u32x4 r = *reinterpret_cast<const u32x4*>(s_av + t * DK + 8 * li);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          a[2 * w] = __uint_as_float(r[w] << 16);
+          a[2 * w + 1] = __uint_as_float(r[w] & 0xffff0000u);
+        }
+      };
+      auto kn8 = [&](int t, float* k) {  // normalised k of token t
+        const floatx4 k0 = *reinterpret_cast<const floatx4*>(s_kf + t * DK + 8 * li);
+        const floatx4 k1 = *reinterpret_cast<const floatx4*>(s_kf + t * DK + 8 * li + 4);
+        const float r = s_rn[t];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k[e] = k0[e] * r;
+          k[4 + e] = k1[e] * r;
+        }
+      };
+      // 16-lane group gq takes tokens paired for equal walks
+#pragma unroll
+      for (int j = 0; j < TMAX / 4; ++j) {
+        const int t = (j % 2 == 0) ? 8 * (j / 2) + gq : 8 * (j / 2) + 7 - gq;
+        if (t < T) {
+          float kv[8], qv[8], w[8];
+          kn8(t, kv);
+          read_pre(TMAX + t, qv);
+          const float rq = s_rn[TMAX + t];
+          float kq = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            qv[e] *= rq;
+            kq = fmaf(kv[e], qv[e], kq);
+          }
+          gates8(t, w);
+          const float bt = s_gb[t];
+          for (int i = t - 1; i >= 0; --i) {
+            float ki[8], ai[8];
+            kn8(i, ki);
+            gates8(i, ai);
+            float cc = 0.f, dd = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float kw = ki[e] * w[e];
+              cc = fmaf(kw, kv[e], cc);
+              dd = fmaf(kw, qv[e], dd);
+              w[e] *= ai[e];
+            }
+            cc = sum16(cc);
+            dd = sum16(dd);
+            if (li == 0) {
+              s_A[t * ALD + i] = bt * cc;
+              s_Oc[t * ALD + i] = dd;
+            }
+          }
+          kq = sum16(kq);
+          if (li == 0) s_Oc[t * ALD + t] = kq;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kv[e] *= w[e];
+            qv[e] *= w[e];
+          }
+          write_pre(t, kv);
+          write_pre(TMAX + t, qv);
+        }
+      }
+      if (lane < TMAX) {
+        const bool live = lane < T;
+        s_ck[lane] = live ? s_gb[lane] : 0.f;
+        s_cq[lane] = live ? 1.f : 0.f;
+        s_cb[lane] = live ? s_gb[lane] : 0.f;
+      }
+    } else {
     // T x T coefficients, (t, i) pairs over the lanes, each written in place
-    // of the Gram entries it reads.
-    float ga[TMAX];
+      // of the Gram entries it reads.
+      float ga[TMAX];
 #pragma unroll
-    for (int s = 0; s < TMAX; ++s) ga[s] = s_ga[s];
+      for (int s = 0; s < TMAX; ++s) ga[s] = s_ga[s];
 #pragma unroll
-    for (int q = 0; q < TMAX * TMAX / 64; ++q) {
-      const int e = lane + 64 * q;
-      const int t = e / TMAX, i = e % TMAX;
-      float gm = 1.f;  // Gamma[t,i] = a_{i+1} ... a_t
+      for (int q = 0; q < TMAX * TMAX / 64; ++q) {
+        const int e = lane + 64 * q;
+        const int t = e / TMAX, i = e % TMAX;
+        float gm = 1.f;  // Gamma[t,i] = a_{i+1} ... a_t
 #pragma unroll
-      for (int s = 0; s < TMAX; ++s) gm *= (s > i && s <= t) ? ga[s] : 1.f;
-      const float rki = s_rn[i];
-      const float av = s_gb[t] * gm * s_G[t * GLD + i] * s_rn[t] * rki;
-      const float ov = gm * s_G[(TMAX + t) * GLD + i] * s_rn[TMAX + t] * rki;
-      s_A[t * ALD + i] = (t < T && i < t) ? av : 0.f;
-      s_Oc[t * ALD + i] = (t < T && i <= t) ? ov : 0.f;
-    }
-    if (lane < TMAX) {
-      float gm = 1.f;  // gamma_t = a_0 ... a_t
+        for (int s = 0; s < TMAX; ++s) gm *= (s > i && s <= t) ? ga[s] : 1.f;
+        const float rki = s_rn[i];
+        const float av = s_gb[t] * gm * s_G[t * GLD + i] * s_rn[t] * rki;
+        const float ov = gm * s_G[(TMAX + t) * GLD + i] * s_rn[TMAX + t] * rki;
+        s_A[t * ALD + i] = (t < T && i < t) ? av : 0.f;
+        s_Oc[t * ALD + i] = (t < T && i <= t) ? ov : 0.f;
+      }
+      if (lane < TMAX) {
+        float gm = 1.f;  // gamma_t = a_0 ... a_t
 #pragma unroll
-      for (int s = 0; s < TMAX; ++s) gm *= s <= lane ? ga[s] : 1.f;
-      const bool live = lane < T;
-      s_ck[lane] = live ? s_gb[lane] * gm * s_rn[lane] : 0.f;
-      s_cq[lane] = live ? gm * s_rn[TMAX + lane] : 0.f;
-      s_cb[lane] = live ? s_gb[lane] : 0.f;
+        for (int s = 0; s < TMAX; ++s) gm *= s <= lane ? ga[s] : 1.f;
+        const bool live = lane < T;
+        s_ck[lane] = live ? s_gb[lane] * gm * s_rn[lane] : 0.f;
+        s_cq[lane] = live ? gm * s_rn[TMAX + lane] : 0.f;
+        s_cb[lane] = live ? s_gb[lane] : 0.f;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -578,6 +738,22 @@ hipError_t launch_cd(const VerifyArgs& a, int dk, int dv, hipStream_t s) {
 
 hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s) {
   return dtype == 1 ? launch_cd<uint16_t>(a, dk, dv, s) : launch_cd<float>(a, dk, dv, s);
+}
+
+hipError_t launch_verify_chain_vg(const VerifyArgs& a, hipStream_t s) {
+  const int G = a.Hv / a.Hk;
+  const int n_units = a.L * a.B * a.Hk;
+  const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
+  if (grid > 0x7fffffffLL || a.T > 16 || a.prev_n_keep || a.prev_n_all > 0) return hipErrorInvalidValue;
+  const dim3 gd(static_cast<int>(grid)), bd(chain_threads<128>());
+  if (a.T <= 8) {
+    if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<128, 128, 8, 4, uint16_t, false, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_chain<128, 128, 8, 0, uint16_t, false, true>), gd, bd, 0, s, a);
+  } else {
+    if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<128, 128, 16, 4, uint16_t, false, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_chain<128, 128, 16, 0, uint16_t, false, true>), gd, bd, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace gdn

@@ -861,10 +861,14 @@ def _vg_shapes(cfg):
 @pytest.mark.parametrize("T,L,B,Hk,Hv,D,K,dtype", [
     (1, 1, 2, 2, 4, 128, 4, torch.bfloat16), (8, 2, 2, 2, 4, 128, 4, torch.bfloat16),
     (16, 1, 3, 1, 2, 64, 3, torch.float32), (17, 1, 2, 2, 4, 128, 4, torch.bfloat16),
-    (64, 1, 1, 1, 3, 32, 6, torch.float32), (40, 1, 2, 4, 4, 64, 4, torch.bfloat16)])
+    (64, 1, 1, 1, 3, 32, 6, torch.float32), (40, 1, 2, 4, 4, 64, 4, torch.bfloat16),
+    (16, 2, 3, 2, 4, 128, 4, torch.bfloat16), (12, 1, 2, 2, 2, 128, 3, torch.bfloat16),
+    (5, 1, 3, 1, 2, 128, 8, torch.bfloat16), (16, 1, 2, 1, 1, 128, 2, torch.bfloat16)])
 def test_vgate_verify_matches_oracle(T, L, B, Hk, Hv, D, K, dtype):
-    """gdn_verify_chunk with a per-key-channel gate (sequential kernel) equals
-    the oracle's verify_chunk_vg: outputs and tape; S is left untouched."""
+    """gdn_verify_chunk with a per-key-channel gate equals the oracle's
+    verify_chunk_vg (outputs and tape) and leaves S untouched: bf16 chains of
+    <= 16 tokens with 128-dim heads on the MFMA chain kernel (conv widths 2,
+    3, 4, 8), the rest on the sequential kernel."""
     _need_gpu()
     cfg = W.CONFIGS[2].with_(L=L, B=B, Hk=Hk, Hv=Hv, Dk=D, Dv=D, K=K, T=T, dtype=dtype)
     inp = _vg_inputs(cfg, 3)
