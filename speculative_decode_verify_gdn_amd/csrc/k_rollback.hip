@@ -146,7 +146,7 @@ hipError_t launch_rb(const RollbackArgs& a, hipStream_t s) {
 // w_i[c] = prod_{j>i} g_{p_j}[c] and gamma[c] = prod_j g_{p_j}[c].  One
 // thread per key channel forms the weights backwards along the path and
 // stages k o w for all n <= 64 steps at once; the state pass is as above.
-template <int DK, int DV>
+template <int DK, int DV, int TM>
 __global__ __launch_bounds__(256) void k_tape_rollback_vg(RollbackArgs p) {
   constexpr int NT = 256;
   constexpr int VPT = 4;
@@ -155,7 +155,9 @@ __global__ __launch_bounds__(256) void k_tape_rollback_vg(RollbackArgs p) {
   constexpr int NRBLK = DV / RB;
   constexpr int C4 = DK / 4;
   constexpr int NV = RB * C4;
-  constexpr int TM = 64;
+  // TM: longest tape staged (16 for rounds of up to 16 drafts, else 64); the
+  // k * w staging is sized to it so that short tapes keep more workgroups
+  // resident
   static_assert(DV % RB == 0 && NV <= NT * VPT && DK <= NT, "row blocks");
 
   __shared__ __align__(16) float s_kw[TM * DK];
@@ -251,7 +253,10 @@ hipError_t launch_rb_vg(const RollbackArgs& a, hipStream_t s) {
   constexpr int RB = RB0 < DV ? RB0 : DV;
   const long long grid = static_cast<long long>(a.L) * a.B * a.Hv * (DV / RB);
   if (grid > 0x7fffffffLL || a.T > 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_tape_rollback_vg<DK, DV>), dim3(grid), dim3(256), 0, s, a);
+  if (a.T <= 16)
+    hipLaunchKernelGGL((k_tape_rollback_vg<DK, DV, 16>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_tape_rollback_vg<DK, DV, 64>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
