@@ -294,9 +294,8 @@ def prefill_pass(cfg, n_tokens, stream, reps=3, gate_per_key=False):
     """gdn_prefill of n_tokens through the workload's L layers and B
     sequences (graph replay): time per call, prefilled tokens/s (B x
     n_tokens per call; each layer sees every token) and the HBM fraction of
-    the byte model: per 16-token chunk and (layer, seq) one state read and
-    write, plus per token x, gates, o, and the chunk tape written then read
-    back."""
+    the byte model: per (layer, seq) one state read and write, plus per
+    token x, gates, o, and the chunk tape written then read back."""
     from speculative_decode_verify_gdn_amd import binding as gb
     from speculative_decode_verify_gdn_amd import workload as W
     c = cfg.with_(T=n_tokens)
@@ -329,8 +328,11 @@ def prefill_pass(cfg, n_tokens, stream, reps=3, gate_per_key=False):
     ms = a.elapsed_time(b) / reps
     esz = 2 if c.dtype == torch.bfloat16 else 4
     P = c.Hv * c.Dv * c.Dk * 4
-    # the per-key form runs the recurrence in one pass: one state read and write
-    chunks = 1 if gate_per_key else (n_tokens + 15) // 16
+    # the per-key form and the scalar gate's 128-dim heads keep the state in
+    # registers across the chunks: one state read and write per call; other
+    # shapes read and write it once per 16-token chunk
+    one_pass = gate_per_key or (c.Dk == 128 and c.Dv == 128)
+    chunks = 1 if one_pass else (n_tokens + 15) // 16
     tape_tok = c.Hv * c.Dv * 4 + c.Hk * c.Dk * 4 + c.Hv * 4
     gate = c.Hv * (c.Dk if gate_per_key else 1) * esz + c.Hv * esz
     tape = 0 if gate_per_key else 2 * tape_tok

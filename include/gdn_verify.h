@@ -263,8 +263,10 @@ size_t spec_sample_workspace_bytes(int32_t B, int32_t T, int32_t V);
  * so that S and conv_state end as the state and window after the last token
  * and o holds every token's output.  The tokens go through in chunks of 16:
  * chunk c is verified while the replay of chunk c-1 (every token kept) is
- * folded into the same kernel, the conv window follows each chunk, and the
- * last chunk is committed by a tape replay.  The result is the sequential
+ * folded into the same kernel, and the last chunk is committed by a tape
+ * replay.  With 128-dim heads and the per-v-head gate all chunks run in one
+ * launch that keeps the state in registers; other shapes launch each chunk
+ * and move the conv window after it.  The result is the sequential
  * recurrence of GDN page s2.1 over all T tokens; the chunking is s4's
  * tape replay with nothing rejected.
  *   x [L,B,T,C], a / b [L,B,T,Hv] (in_dtype), conv_w [L,C,K] fp32

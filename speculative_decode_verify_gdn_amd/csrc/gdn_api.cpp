@@ -80,6 +80,7 @@ VerifyArgs verify_args(const gdn_shape* s, int32_t T, const void* x, const void*
   v.x_ld = static_cast<size_t>(T) * v.C;
   v.ab_ld = static_cast<size_t>(T) * v.Hv;
   v.o_ld = static_cast<size_t>(T) * v.Hv * s->d_v;
+  v.cs_ld = static_cast<size_t>(v.K - 1) * v.C;
   return v;
 }
 
@@ -410,6 +411,30 @@ gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* c
     tapes[i].u = base;
     tapes[i].k = base + lbt * Hv * Dv;
     tapes[i].g = tapes[i].k + lbt * shape->n_k_heads * shape->d_k;
+  }
+  if (shape->d_k == 128 && shape->d_v == 128) {
+    // one launch: each workgroup walks its sequence chunk by chunk with the
+    // state in registers, then the window is rolled over all T tokens
+    VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, &tapes[0]);
+    v.S_out = S;
+    v.ptu = tapes[1].u;
+    v.ptk = tapes[1].k;
+    v.ptg = tapes[1].g;
+    v.dev_err = dev_err;
+    st = launch_status(gdn::launch_verify_chain_pf(v, shape->d_k, shape->d_v, shape->in_dtype, s));
+    if (st != GDN_OK) return st;
+    ConvRollbackArgs cr{};
+    cr.conv_state = conv_state;
+    cr.x = x;
+    cr.n_all = T;
+    cr.dev_err = dev_err;
+    cr.L = shape->n_layers;
+    cr.B = shape->batch;
+    cr.K = shape->conv_kernel;
+    cr.T = T;
+    cr.C = C;
+    cr.x_ld = static_cast<size_t>(T) * C;
+    return launch_status(gdn::launch_conv_rollback(cr, shape->in_dtype, s));
   }
   const int nch = (T + kPrefillChunk - 1) / kPrefillChunk;
   int prev_tc = 0;

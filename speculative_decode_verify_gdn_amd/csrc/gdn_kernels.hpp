@@ -44,6 +44,9 @@ struct VerifyArgs {
   // (T*C, T*Hv, T*Hv*Dv for whole chunks; larger when a chunk is a slice of
   // a longer sequence).  Chain kernel only.
   size_t x_ld, ab_ld, o_ld;
+  // Elements between consecutive (layer, seq) slabs of conv_state ((K-1)*C
+  // for a conv-state buffer; x_ld when the window is read in place from x).
+  size_t cs_ld;
 };
 
 // Tape-replay rollback.
@@ -112,6 +115,9 @@ hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, h
 // Chains of <= 16 tokens with the per-key-channel gate (bf16, 128-dim heads),
 // on the MFMA chain kernel (no replay).
 hipError_t launch_verify_chain_vg(const VerifyArgs& a, hipStream_t s);
+// Prefill: one launch over all a.T tokens, chunks of 16 with the state in
+// registers; tu/tk/tg and ptu/ptk/ptg are two one-chunk tape slots.
+hipError_t launch_verify_chain_pf(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
 // Trees of 33..64 nodes, 128-dim heads, bf16 inputs (per-node path solve).
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s);
 // Trees of 33..64 nodes (bf16, 128-dim heads) with the per-key-channel gate,

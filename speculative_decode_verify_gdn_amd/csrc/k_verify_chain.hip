@@ -122,9 +122,13 @@ struct ChainLayout {
   static_assert(ALD == GLD, "A and Oc overwrite the Gram rows in place");
 };
 
-template <int DK, int DV, int TMAX, int KC, typename TIn, bool RP, bool VG = false>
+// PF (prefill loop) holds the state across the wave-0 prologue: it runs at 3
+// waves per SIMD (168 VGPRs, small spill), measured faster than 2 (no spill)
+// and far faster than 4 (heavy spill).
+template <int DK, int DV, int TMAX, int KC, typename TIn, bool RP, bool VG = false, bool PF = false>
 __global__ __launch_bounds__(chain_threads<DV>())
-__attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
+__attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs p0) {
+  static_assert(!PF || (RP && !VG), "the prefill loop runs the replay form");
   static_assert(!VG || (!RP && DK == 128 && DV == 128 && sizeof(TIn) == 2),
                 "the per-key-channel gate runs 128-dim heads, bf16 inputs, no replay");
   constexpr int KM = KC > 0 ? KC : 8;
@@ -153,21 +157,76 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
   __shared__ float s_pw[RP ? PM : 1];
   __shared__ float s_pgam;
 
-  const int tid = threadIdx.x;
+  const int G = p0.Hv / p0.Hk;
+  const int n_units = p0.L * p0.B * p0.Hk;
+  const UnitSub us = xcd_unit_sub(blockIdx.x, G);
+  if (us.unit >= n_units) return;
+  const int hk = us.unit % p0.Hk;
+  const size_t lb = us.unit / p0.Hk;  // l * B + b
+  const int l = static_cast<int>(lb / p0.B);
+  const int g = us.sub;
+  const int hv = hk * G + g;
+  // This wave's tiles of S0 (tile wave + tt * NW): lane (c16, kk) holds row
+  // c16 of a tile, columns 16m + 4kk .. +3, as MFMA A operands.  The prefill
+  // loop carries them across chunks.
+  typedef floatx4 SregT[TPW][DK / 16];
+  SregT sreg_pf;
+
+  // Prefill (PF): the workgroup runs all T tokens as chunks of TMAX with the
+  // state held in registers.  Chunk c is verified from the state after
+  // chunks 0 .. c-1 and writes its tape to slot c % 2 of the workspace (the
+  // tu/tk/tg and ptu/ptk/ptg pointers); the next chunk first folds it into
+  // the state with the replay update, every token kept.  S is read before the
+  // first chunk and written after the last; the conv window of chunk c > 0 is
+  // the previous chunk's last raw rows, read in place from x.
+  // Without PF the body runs once: the exit test sits at its end, so that the
+  // single pass compiles as straight-line code.
+  const int nch = PF ? (p0.T + TMAX - 1) / TMAX : 1;
+  for (int ch = 0;; ++ch) {
+  VerifyArgs pl = p0;  // this chunk's view (prefill)
+  if constexpr (PF) {
+    // Opaque per-chunk copies of the loop-invariant operands, so that the
+    // compiler rematerialises what derives from them inside each chunk
+    // instead of keeping it live in registers across the whole loop.
+    const float* cw = p0.conv_w;
+    int hkn = p0.Hk, hvn = p0.Hv, cn = p0.C;
+    asm volatile("" : "+s"(cw), "+s"(hkn), "+s"(hvn), "+s"(cn));
+    pl.conv_w = cw;
+    pl.Hk = hkn;
+    pl.Hv = hvn;
+    pl.C = cn;
+    const int c0 = ch * TMAX;
+    const size_t C = p0.C;
+    pl.T = p0.T - c0 < TMAX ? p0.T - c0 : TMAX;
+    pl.x = static_cast<const TIn*>(p0.x) + c0 * C;
+    pl.a = static_cast<const TIn*>(p0.a) + static_cast<size_t>(c0) * p0.Hv;
+    pl.b = static_cast<const TIn*>(p0.b) + static_cast<size_t>(c0) * p0.Hv;
+    pl.o = p0.o + static_cast<size_t>(c0) * p0.Hv * DV;
+    if (ch > 0) {
+      pl.conv_state = static_cast<const TIn*>(p0.x) + (c0 - (KC > 0 ? KC : p0.K) + 1) * C;
+      pl.cs_ld = p0.x_ld;
+    }
+    const bool odd = ch & 1;
+    pl.tu = odd ? const_cast<float*>(p0.ptu) : p0.tu;
+    pl.tk = odd ? const_cast<float*>(p0.ptk) : p0.tk;
+    pl.tg = odd ? const_cast<float*>(p0.ptg) : p0.tg;
+    pl.ptu = odd ? p0.tu : p0.ptu;
+    pl.ptk = odd ? p0.tk : p0.ptk;
+    pl.ptg = odd ? p0.tg : p0.ptg;
+    pl.prev_n_keep = nullptr;
+    pl.prev_n_all = ch > 0 ? TMAX : 0;
+    pl.pT = TMAX;
+  }
+  const VerifyArgs& p = PF ? pl : p0;
+  SregT sreg_own;
+  SregT& sreg = PF ? sreg_pf : sreg_own;
+  int tid_l = threadIdx.x;
+  if constexpr (PF) asm volatile("" : "+v"(tid_l));  // per-chunk lane addressing
+  const int tid = tid_l;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int c16 = lane & 15;
   const int kk = lane >> 4;
-
-  const int G = p.Hv / p.Hk;
-  const int n_units = p.L * p.B * p.Hk;
-  const UnitSub us = xcd_unit_sub(blockIdx.x, G);
-  if (us.unit >= n_units) return;
-  const int hk = us.unit % p.Hk;
-  const size_t lb = us.unit / p.Hk;  // l * B + b
-  const int l = static_cast<int>(lb / p.B);
-  const int g = us.sub;
-  const int hv = hk * G + g;
   const int T = p.T;
   const int K = KC > 0 ? KC : p.K;
   // accepted length of the previous round (replay variant)
@@ -180,9 +239,6 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
       atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
   }
 
-  // This wave's tiles of S0 (tile wave + tt * NW): lane (c16, kk) holds row
-  // c16 of a tile, columns 16m + 4kk .. +3, as MFMA A operands.
-  floatx4 sreg[TPW][DK / 16];
   const float* S_head = p.S + (lb * p.Hv + hv) * static_cast<size_t>(DV * DK);
   float* const S_live = RP ? p.S_out + (lb * p.Hv + hv) * static_cast<size_t>(DV * DK) : nullptr;
   // Replay operands, straight from the previous tape into registers: lane
@@ -209,6 +265,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
     }
   };
   auto load_state = [&]() {
+    if (PF && ch > 0) return;  // the state is in registers
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
       const float* rp = S_head + static_cast<size_t>((wave + tt * NW) * 16 + c16) * DK + 4 * kk;
@@ -223,7 +280,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
     const TIn* cs = static_cast<const TIn*>(p.conv_state);
     const float* cw = p.conv_w + static_cast<size_t>(l) * p.C * K;
     const TIn* xcol = x + lb * p.x_ld;
-    const TIn* ccol = cs + lb * (K - 1) * p.C;
+    const TIn* ccol = cs + lb * (PF ? p.cs_ld : static_cast<size_t>(K - 1) * p.C);
     const int nrows = K - 1 + T;
     // local channel c in [q | k | v-rows] -> qkv channel
     auto chan = [&](int c) {
@@ -616,7 +673,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
           for (int st = 0; st < PM / 4; ++st)
             if (4 * st < pn) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[st][m], bu[st], acc, 0, 0, 0);
           sreg[tt][m] = sreg[tt][m] * gam + acc;
-          *reinterpret_cast<floatx4*>(wp + 16 * m) = sreg[tt][m];
+          if constexpr (!PF) *reinterpret_cast<floatx4*>(wp + 16 * m) = sreg[tt][m];
         }
       }
     }
@@ -693,6 +750,72 @@ __attribute__((amdgpu_waves_per_eu(4))) void k_verify_chain(VerifyArgs p) {
       }
     }
   }
+  if constexpr (PF) {
+    // this chunk's tape stores are visible to every wave of the workgroup
+    // (one CU: no cache write-back needed) and its LDS reads are done before
+    // the next chunk reads the tape and overwrites LDS
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+  if (!PF || ch + 1 >= nch) break;
+  }  // chunks
+
+  if constexpr (PF) {
+    // Fold the last chunk (every token kept) into the state and store it.
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c16 = lane & 15;
+    const int kk = lane >> 4;
+    const int cl = nch - 1;
+    const int Tl = p0.T - cl * TMAX;
+    const bool odd = cl & 1;
+    const float* tu = odd ? p0.ptu : p0.tu;
+    const float* tk = odd ? p0.ptk : p0.tk;
+    const float* tg = odd ? p0.ptg : p0.tg;
+    const size_t base = lb * Tl;
+    const float gl = lane < Tl ? tg[(base + lane) * p0.Hv + hv] : 1.f;
+    float w = 1.f, gam = 1.f;  // w_lane = prod_{lane<j<Tl} g_j, gam = prod_j g_j
+#pragma unroll
+    for (int j = 0; j < TMAX; ++j) {
+      const float gj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), j));
+      gam *= gj;
+      if (j > lane) w *= gj;
+    }
+    float kt[TMAX / 4][DK / 16];
+    float bw[TMAX / 4];
+#pragma unroll
+    for (int st = 0; st < TMAX / 4; ++st) {
+      const int i = 4 * st + kk;
+      const size_t ii = base + (i < Tl ? i : 0);
+      const float* kr = tk + (ii * p0.Hk + hk) * DK + c16;
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m) kt[st][m] = kr[16 * m];
+      const float wi = __shfl(w, i, kWave);
+      bw[st] = i < Tl ? wi : 0.f;
+    }
+    float* const S_dst = p0.S_out + (lb * p0.Hv + hv) * static_cast<size_t>(DV * DK);
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int tile = wave + tt * NW;
+      float bu[TMAX / 4];
+#pragma unroll
+      for (int st = 0; st < TMAX / 4; ++st) {
+        const int i = 4 * st + kk;
+        const size_t ii = base + (i < Tl ? i : 0);
+        bu[st] = tu[(ii * p0.Hv + hv) * DV + tile * 16 + c16] * bw[st];
+      }
+      float* const wp = S_dst + (tile * 16 + c16) * DK + 4 * kk;
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < TMAX / 4; ++st)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[st][m], bu[st], acc, 0, 0, 0);
+        *reinterpret_cast<floatx4*>(wp + 16 * m) = sreg_pf[tt][m] * gam + acc;
+      }
+    }
+  }
 }
 
 template <int DK, int DV, typename TIn, bool RP>
@@ -738,6 +861,24 @@ hipError_t launch_cd(const VerifyArgs& a, int dk, int dv, hipStream_t s) {
 
 hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s) {
   return dtype == 1 ? launch_cd<uint16_t>(a, dk, dv, s) : launch_cd<float>(a, dk, dv, s);
+}
+
+hipError_t launch_verify_chain_pf(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s) {
+  const int G = a.Hv / a.Hk;
+  const int n_units = a.L * a.B * a.Hk;
+  const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
+  if (grid > 0x7fffffffLL || dk != 128 || dv != 128 || a.T < 1 || a.K > 16 || a.prev_n_keep ||
+      !a.S_out || !a.tu || !a.tk || !a.tg || !a.ptu || !a.ptk || !a.ptg)
+    return hipErrorInvalidValue;
+  const dim3 gd(static_cast<int>(grid)), bd(chain_threads<128>());
+  if (dtype == 1) {
+    if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<128, 128, 16, 4, uint16_t, true, false, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_chain<128, 128, 16, 0, uint16_t, true, false, true>), gd, bd, 0, s, a);
+  } else {
+    if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<128, 128, 16, 4, float, true, false, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_chain<128, 128, 16, 0, float, true, false, true>), gd, bd, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_verify_chain_vg(const VerifyArgs& a, hipStream_t s) {

@@ -811,11 +811,13 @@ def test_sample_accept_extremes_and_bad_tokens():
     (1, 1, 2, 2, 4, 128, 4, torch.bfloat16), (5, 1, 2, 2, 4, 128, 4, torch.bfloat16),
     (16, 2, 2, 2, 4, 128, 4, torch.bfloat16), (17, 1, 3, 2, 4, 128, 4, torch.float32),
     (40, 1, 2, 1, 3, 64, 3, torch.bfloat16), (100, 1, 2, 2, 4, 128, 4, torch.bfloat16),
-    (150, 1, 1, 1, 1, 32, 4, torch.float32)])
+    (150, 1, 1, 1, 1, 32, 4, torch.float32), (33, 1, 2, 2, 2, 128, 2, torch.bfloat16),
+    (48, 2, 3, 2, 4, 128, 3, torch.float32), (64, 1, 2, 1, 2, 128, 8, torch.bfloat16)])
 def test_prefill_matches_sequential_oracle(T, L, B, Hk, Hv, D, K, dtype):
     """gdn_prefill (16-token chunks, each chunk's replay folded into the next
-    verify) equals the oracle's sequential recurrence over all T tokens:
-    every output, the final state and the final conv window."""
+    verify; for 128-dim heads all chunks in one launch with the state held
+    in registers) equals the oracle's sequential recurrence over all T
+    tokens: every output, the final state and the final conv window."""
     _need_gpu()
     cfg = W.CONFIGS[2].with_(L=L, B=B, Hk=Hk, Hv=Hv, Dk=D, Dv=D, K=K, T=T, dtype=dtype)
     inp = W.layer_inputs(cfg, 0, "cpu")
