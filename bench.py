@@ -333,9 +333,14 @@ def prefill_pass(cfg, n_tokens, stream, reps=3, gate_per_key=False):
     # shapes read and write it once per 16-token chunk
     one_pass = gate_per_key or (c.Dk == 128 and c.Dv == 128)
     chunks = 1 if one_pass else (n_tokens + 15) // 16
-    tape_tok = c.Hv * c.Dv * 4 + c.Hk * c.Dk * 4 + c.Hv * 4
+    # (the one-pass chunk loop keeps its tape's k rows per v-head)
+    kh = c.Hv if c.Dk == c.Dv == 128 and (not gate_per_key or c.dtype == torch.bfloat16) else c.Hk
+    tape_tok = c.Hv * c.Dv * 4 + kh * c.Dk * 4 + c.Hv * (c.Dk if gate_per_key else 1) * 4
     gate = c.Hv * (c.Dk if gate_per_key else 1) * esz + c.Hv * esz
-    tape = 0 if gate_per_key else 2 * tape_tok
+    # the chain kernel's chunk loop writes each chunk's tape and reads it back;
+    # the per-key sequential kernel (other shapes) keeps no tape
+    chain_loop = not gate_per_key or (c.Dk == c.Dv == 128 and c.dtype == torch.bfloat16)
+    tape = 2 * tape_tok if chain_loop else 0
     per_seq = chunks * 2 * P + n_tokens * (c.C * esz + gate + c.Hv * c.Dv * 4 + tape) \
         + chunks * 2 * (c.K - 1) * c.C * esz
     byts = c.L * c.B * per_seq
@@ -352,8 +357,8 @@ def vgate_pass(cfg, stream, steps):
     (a [L,B,T,Hv,Dk], drawn U(0.05, 1)), in both forms: the plain round
     (verify, accept, rollback) with its verify time per layer, byte model and
     HBM fraction and its rollback time, and the fused round (the rollback
-    folded into the next round's verify, k_verify_vgt replaying the previous
-    accepted prefix or path)."""
+    folded into the next round's verify, which replays the previous accepted
+    prefix or path); value_by_rule is the form spec_round.fused_pays picks."""
     from speculative_decode_verify_gdn_amd import binding as gb
     from speculative_decode_verify_gdn_amd import spec_round as sr
     base, sets = build_sets(cfg, 1, "cuda")
@@ -408,9 +413,12 @@ def vgate_pass(cfg, stream, steps):
     extra = cfg.B * cfg.T * cfg.Hv * (cfg.Dk - 1) * (esz + 4)  # larger gate read and tape g
     vb = verify_bytes_per_launch(cfg, cfg.B) + extra
     v_ms = t_plain[1] / cfg.L
+    pays = sr.fused_pays(sh, cfg.T, tree)
     del rb, fr, base, sets, inp, acc, a, plain, f_round, f_verify
     torch.cuda.empty_cache()
-    return {"round_ms": t_plain[0], "value": cfg.B * cfg.T / (t_plain[0] * 1e-3),
+    return {"round_by_rule": "fused" if pays else "plain",
+            "value_by_rule": cfg.B * cfg.T / ((t_fround if pays else t_plain[0]) * 1e-3),
+            "round_ms": t_plain[0], "value": cfg.B * cfg.T / (t_plain[0] * 1e-3),
             "verify_per_layer_ms": v_ms, "verify_bytes_per_launch": vb,
             "verify_hbm_frac": vb / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "rollback_state_and_conv_ms": t_plain[2],
@@ -419,7 +427,10 @@ def vgate_pass(cfg, stream, steps):
                        ("k_verify_chain (per-key gate)" if cfg.T <= 16 and cfg.dtype == torch.bfloat16
                         and cfg.Dk == cfg.Dv == 128 else "k_verify_vg")),
             "fused": {"round_ms": t_fround, "value": cfg.B * cfg.T / (t_fround * 1e-3),
-                      "verify_per_layer_ms": t_fverify / cfg.L, "kernel": "k_verify_vgt"}}
+                      "verify_per_layer_ms": t_fverify / cfg.L,
+                      "kernel": ("k_verify_chain (per-key gate, replay)"
+                                 if not tree and cfg.T <= 16 and cfg.dtype == torch.bfloat16
+                                 and cfg.Dk == cfg.Dv == 128 else "k_verify_vgt")}}
 
 
 def parse():

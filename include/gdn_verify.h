@@ -264,9 +264,11 @@ size_t spec_sample_workspace_bytes(int32_t B, int32_t T, int32_t V);
  * and o holds every token's output.  The tokens go through in chunks of 16:
  * chunk c is verified while the replay of chunk c-1 (every token kept) is
  * folded into the same kernel, and the last chunk is committed by a tape
- * replay.  With 128-dim heads and the per-v-head gate all chunks run in one
- * launch that keeps the state in registers; other shapes launch each chunk
- * and move the conv window after it.  The result is the sequential
+ * replay.  With 128-dim heads (and bf16 inputs for the per-key-channel
+ * gate) all chunks run in one launch that keeps the state in registers; with
+ * the per-v-head gate other shapes launch each chunk and move the conv window
+ * after it, and with the per-key gate they run the sequential recurrence in
+ * one launch.  The result is the sequential
  * recurrence of GDN page s2.1 over all T tokens; the chunking is s4's
  * tape replay with nothing rejected.
  *   x [L,B,T,C], a / b [L,B,T,Hv] (in_dtype), conv_w [L,C,K] fp32
@@ -294,9 +296,10 @@ gdn_status gdn_round_rollback(const gdn_shape* shape, int32_t T, float* S, const
                               const int32_t* n_keep, int32_t* win_idx, int32_t* dev_err,
                               void* stream);
 
-/* Bytes of device workspace gdn_prefill needs for this shape (any T).  With
- * gate_per_key the prefill runs the recurrence in one launch and needs no
- * workspace (NULL is accepted). */
+/* Bytes of device workspace gdn_prefill needs for this shape (any T): two
+ * 16-token tapes.  Zero (NULL is accepted) where gate_per_key runs the
+ * sequential kernel over all T tokens: heads other than 128-dim, or fp32
+ * inputs. */
 size_t gdn_prefill_workspace_bytes(const gdn_shape* shape);
 
 /*

@@ -135,6 +135,9 @@ gdn_status gdn_verify_chunk_replay(const gdn_shape* shape, int32_t T, const void
     v.ptg = prev_tape->g;
     v.prev_n_keep = prev_n_keep;
     v.pT = prev_T;
+    if (T <= 16 && prev_T <= 16 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 &&
+        shape->d_v == 128)
+      return launch_status(gdn::launch_verify_chain_vg(v, s));
     return launch_status(gdn::launch_verify_vg_tree(v, shape->d_k, shape->d_v, shape->in_dtype, s));
   }
   if (T <= 16 && prev_T <= 16) {
@@ -353,17 +356,29 @@ gdn_status gdn_conv_state_rollback(const gdn_shape* shape, int32_t T, void* conv
 namespace {
 constexpr int kPrefillChunk = 16;  // tokens per chunk (the chain kernel's longest)
 
-size_t tape_floats(const gdn_shape* s, int T) {
+// The one-launch prefill of the chain kernel (128-dim heads; bf16 inputs
+// for the per-key-channel gate).
+bool prefill_one_launch(const gdn_shape* s) {
+  return s->d_k == 128 && s->d_v == 128 && (!s->gate_per_key || s->in_dtype == GDN_BF16);
+}
+
+// k-rows per token of a prefill tape: per v-head in the one-launch loop (each
+// workgroup reads back its own copy), else per k-head.
+size_t prefill_k_heads(const gdn_shape* s) {
+  return prefill_one_launch(s) ? s->n_v_heads : s->n_k_heads;
+}
+
+size_t prefill_tape_floats(const gdn_shape* s, int T) {
   const size_t lbt = static_cast<size_t>(s->n_layers) * s->batch * T;
-  return lbt * (static_cast<size_t>(s->n_v_heads) * s->d_v +
-                static_cast<size_t>(s->n_k_heads) * s->d_k + s->n_v_heads);
+  return lbt * (static_cast<size_t>(s->n_v_heads) * s->d_v + prefill_k_heads(s) * s->d_k +
+                static_cast<size_t>(s->n_v_heads) * (s->gate_per_key ? s->d_k : 1));
 }
 }  // namespace
 
 size_t gdn_prefill_workspace_bytes(const gdn_shape* shape) {
   if (check_shape(shape, kPrefillChunk) != GDN_OK) return 0;
-  if (shape->gate_per_key) return 0;  // one launch, no tape
-  return 2 * ((tape_floats(shape, kPrefillChunk) * sizeof(float) + 255) / 256 * 256);
+  if (shape->gate_per_key && !prefill_one_launch(shape)) return 0;  // sequential kernel, no tape
+  return 2 * ((prefill_tape_floats(shape, kPrefillChunk) * sizeof(float) + 255) / 256 * 256);
 }
 
 gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* conv_state,
@@ -375,7 +390,7 @@ gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* c
   if (!x || !conv_state || !conv_w || !a || !b || !S || !o) return GDN_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int C = channels(shape);
-  if (shape->gate_per_key) {
+  if (shape->gate_per_key && !prefill_one_launch(shape)) {
     // one launch of the sequential kernel over all T tokens, committing the
     // state, then the window; no tape, no workspace
     gdn_tape none{nullptr, nullptr, nullptr};
@@ -410,9 +425,9 @@ gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* c
     const size_t lbt = static_cast<size_t>(shape->n_layers) * shape->batch * kPrefillChunk;
     tapes[i].u = base;
     tapes[i].k = base + lbt * Hv * Dv;
-    tapes[i].g = tapes[i].k + lbt * shape->n_k_heads * shape->d_k;
+    tapes[i].g = tapes[i].k + lbt * prefill_k_heads(shape) * shape->d_k;
   }
-  if (shape->d_k == 128 && shape->d_v == 128) {
+  if (prefill_one_launch(shape)) {
     // one launch: each workgroup walks its sequence chunk by chunk with the
     // state in registers, then the window is rolled over all T tokens
     VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, &tapes[0]);
@@ -421,7 +436,10 @@ gdn_status gdn_prefill(const gdn_shape* shape, int32_t T, const void* x, void* c
     v.ptk = tapes[1].k;
     v.ptg = tapes[1].g;
     v.dev_err = dev_err;
-    st = launch_status(gdn::launch_verify_chain_pf(v, shape->d_k, shape->d_v, shape->in_dtype, s));
+    st = launch_status(shape->gate_per_key
+                           ? gdn::launch_verify_chain_vg_pf(v, s)
+                           : gdn::launch_verify_chain_pf(v, shape->d_k, shape->d_v,
+                                                         shape->in_dtype, s));
     if (st != GDN_OK) return st;
     ConvRollbackArgs cr{};
     cr.conv_state = conv_state;

@@ -113,11 +113,14 @@ hipError_t launch_verify_wy(const VerifyArgs& a, int dk, int dv, int dtype, hipS
 // Chains of at most 16 tokens (wave-specialised kernel).
 hipError_t launch_verify_chain(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
 // Chains of <= 16 tokens with the per-key-channel gate (bf16, 128-dim heads),
-// on the MFMA chain kernel (no replay).
+// on the MFMA chain kernel, with or without the replay of a previous chain of
+// <= 16 tokens (per-channel weights on the k operand of the rank-n update).
 hipError_t launch_verify_chain_vg(const VerifyArgs& a, hipStream_t s);
 // Prefill: one launch over all a.T tokens, chunks of 16 with the state in
 // registers; tu/tk/tg and ptu/ptk/ptg are two one-chunk tape slots.
 hipError_t launch_verify_chain_pf(const VerifyArgs& a, int dk, int dv, int dtype, hipStream_t s);
+// The same with the per-key-channel gate (bf16, 128-dim heads).
+hipError_t launch_verify_chain_vg_pf(const VerifyArgs& a, hipStream_t s);
 // Trees of 33..64 nodes, 128-dim heads, bf16 inputs (per-node path solve).
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s);
 // Trees of 33..64 nodes (bf16, 128-dim heads) with the per-key-channel gate,

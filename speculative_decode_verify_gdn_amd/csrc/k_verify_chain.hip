@@ -122,15 +122,17 @@ struct ChainLayout {
   static_assert(ALD == GLD, "A and Oc overwrite the Gram rows in place");
 };
 
-// PF (prefill loop) holds the state across the wave-0 prologue: it runs at 3
-// waves per SIMD (168 VGPRs, small spill), measured faster than 2 (no spill)
-// and far faster than 4 (heavy spill).
+// Occupancy targets.  PF (prefill loop) holds the state across the wave-0
+// prologue: with the per-head gate it runs at 3 waves per SIMD (168 VGPRs,
+// small spill), measured faster than 2 (no spill) and far faster than 4
+// (heavy spill); with the per-key gate at 2 (no spill), faster than 3
+// (spill).  The per-key replay (VG and RP) runs at 3, spill-free.
 template <int DK, int DV, int TMAX, int KC, typename TIn, bool RP, bool VG = false, bool PF = false>
 __global__ __launch_bounds__(chain_threads<DV>())
-__attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs p0) {
-  static_assert(!PF || (RP && !VG), "the prefill loop runs the replay form");
-  static_assert(!VG || (!RP && DK == 128 && DV == 128 && sizeof(TIn) == 2),
-                "the per-key-channel gate runs 128-dim heads, bf16 inputs, no replay");
+__attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) void k_verify_chain(VerifyArgs p0) {
+  static_assert(!PF || RP, "the prefill loop runs the replay form");
+  static_assert(!VG || (DK == 128 && DV == 128 && sizeof(TIn) == 2),
+                "the per-key-channel gate runs 128-dim heads, bf16 inputs");
   constexpr int KM = KC > 0 ? KC : 8;
   using LY = ChainLayout<DK, DV, TMAX, KM, TIn>;
   using PR = Pair<TIn>;
@@ -156,6 +158,11 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
   constexpr int PM = 16;
   __shared__ float s_pw[RP ? PM : 1];
   __shared__ float s_pgam;
+  // per-key-channel replay: w_{i,c} = prod_{i<j<pn} g_{j,c} (zero for i >= pn)
+  // as [i][c], and gamma_c = prod_{j<pn} g_{j,c}
+  constexpr bool VR = VG && RP;
+  __shared__ float s_pwk[VR ? PM * DK : 1];
+  __shared__ __align__(16) float s_pgk[VR ? DK : 4];
 
   const int G = p0.Hv / p0.Hk;
   const int n_units = p0.L * p0.B * p0.Hk;
@@ -199,7 +206,7 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
     const size_t C = p0.C;
     pl.T = p0.T - c0 < TMAX ? p0.T - c0 : TMAX;
     pl.x = static_cast<const TIn*>(p0.x) + c0 * C;
-    pl.a = static_cast<const TIn*>(p0.a) + static_cast<size_t>(c0) * p0.Hv;
+    pl.a = static_cast<const TIn*>(p0.a) + static_cast<size_t>(c0) * p0.Hv * (VG ? DK : 1);
     pl.b = static_cast<const TIn*>(p0.b) + static_cast<size_t>(c0) * p0.Hv;
     pl.o = p0.o + static_cast<size_t>(c0) * p0.Hv * DV;
     if (ch > 0) {
@@ -254,7 +261,7 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
         if (4 * st < pn) {
           const int i = 4 * st + kk;
           const size_t ii = base + (i < pn ? i : 0);
-          const float* kr = p.ptk + (ii * p.Hk + hk) * DK + c16;
+          const float* kr = p.ptk + (PF ? ii * p.Hv + hv : ii * p.Hk + hk) * DK + c16;
 #pragma unroll
           for (int m = 0; m < DK / 16; ++m) kt[st][m] = kr[16 * m];
           const float* ur = p.ptu + (ii * p.Hv + hv) * DV + c16;
@@ -304,11 +311,13 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
         const int q = lane + 64 * j;
         const int t = q / (DK / 8);
         const uint16_t* ap = static_cast<const uint16_t*>(p.a) +
-                             ((lb * T + (t < T ? t : 0)) * p.Hv + hv) * DK + 8 * (q % (DK / 8));
+                             (lb * p.ab_ld + static_cast<size_t>(t < T ? t : 0) * p.Hv + hv) * DK +
+                             8 * (q % (DK / 8));
         avr[j] = *reinterpret_cast<const u32x4*>(ap);
       }
     }
-    const float pg_ld = RP && lane < pn ? p.ptg[(lb * p.pT + lane) * p.Hv + hv] : 1.f;
+    const float pg_ld = RP && !VG && lane < pn ? p.ptg[(lb * p.pT + lane) * p.Hv + hv] : 1.f;
+
 
     auto load_pair = [&](int j, typename PR::raw* xr, float* w0, float* w1) {
       const int pr = lane + 64 * j;
@@ -398,7 +407,7 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
         conv_pair(j, xr, w0, w1);
       }
     }
-    if constexpr (RP) {
+    if constexpr (RP && !VG) {
       float w = 1.f, gm = 1.f;
 #pragma unroll
       for (int j = 0; j < PM; ++j) {
@@ -468,13 +477,16 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // Tape k: the normalised k rows, once per k-head (before [Ti; M2] takes
-    // their space).
-    if (g == 0) {
+    // their space).  The prefill loop reads its own chunk tapes back while the
+    // k-head's other workgroups run at their own pace, so there every
+    // workgroup keeps its own copy, per v-head.
+    if (PF || g == 0) {
       constexpr int C4 = DK / 4;
       for (int e = lane; e < T * C4; e += 64) {
         const int t = e / C4, c4 = e % C4;
         const floatx4 v = *reinterpret_cast<const floatx4*>(s_kf + t * DK + 4 * c4) * s_rn[t];
-        __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(p.tk + ((lb * T + t) * p.Hk + hk) * DK) + c4);
+        const size_t row = PF ? (lb * T + t) * p.Hv + hv : (lb * T + t) * p.Hk + hk;
+        __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(p.tk + row * DK) + c4);
       }
     }
 
@@ -641,6 +653,29 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
     }
   } else {
     __syncthreads();  // (B0)
+    if constexpr (VR) {
+      // the per-key replay weights, off wave 0's path: wave 1 takes channels
+      // lane and lane + 64 of the previous tape's gates g_{j,c}, j < pn
+      static_assert(NW >= 2, "needs a second wave");
+      if (wave == 1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float gk[PM];
+#pragma unroll
+          for (int j = 0; j < PM; ++j) {
+            const float gv = p.ptg[((lb * p.pT + (j < pn ? j : 0)) * p.Hv + hv) * DK + lane + 64 * h];
+            gk[j] = j < pn ? gv : 1.f;
+          }
+          float w = 1.f;  // suffix product over j > i
+#pragma unroll
+          for (int i = PM - 1; i >= 0; --i) {
+            s_pwk[i * DK + lane + 64 * h] = i < pn ? w : 0.f;
+            w *= gk[i];
+          }
+          s_pgk[lane + 64 * h] = w;
+        }
+      }
+    }
     load_state();
     load_tape();
   }
@@ -658,7 +693,16 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
       const float gam = s_pgam;
       float wv[PM / 4];
 #pragma unroll
-      for (int st = 0; st < PM / 4; ++st) wv[st] = s_pw[4 * st + kk];
+      for (int st = 0; st < PM / 4; ++st) wv[st] = VR ? 1.f : s_pw[4 * st + kk];
+      if constexpr (VR) {
+        // per-key weights go on the k operand: k_i[c] w_{i,c}
+#pragma unroll
+        for (int st = 0; st < PM / 4; ++st)
+          if (4 * st < pn) {
+#pragma unroll
+            for (int m = 0; m < DK / 16; ++m) kt[st][m] *= s_pwk[(4 * st + kk) * DK + 16 * m + c16];
+          }
+      }
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt) {
         const int tile = wave + tt * NW;
@@ -672,7 +716,10 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
 #pragma unroll
           for (int st = 0; st < PM / 4; ++st)
             if (4 * st < pn) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[st][m], bu[st], acc, 0, 0, 0);
-          sreg[tt][m] = sreg[tt][m] * gam + acc;
+          if constexpr (VR)  // columns 16m + 4kk .. +3 decay by their own gamma
+            sreg[tt][m] = sreg[tt][m] * *reinterpret_cast<const floatx4*>(s_pgk + 16 * m + 4 * kk) + acc;
+          else
+            sreg[tt][m] = sreg[tt][m] * gam + acc;
           if constexpr (!PF) *reinterpret_cast<floatx4*>(wp + 16 * m) = sreg[tt][m];
         }
       }
@@ -774,7 +821,29 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
     const float* tk = odd ? p0.ptk : p0.tk;
     const float* tg = odd ? p0.ptg : p0.tg;
     const size_t base = lb * Tl;
-    const float gl = lane < Tl ? tg[(base + lane) * p0.Hv + hv] : 1.f;
+    if constexpr (VG) {
+      // per-key weights of the last chunk, as in the chunk replays
+      if (wave == 1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float gk[TMAX];
+#pragma unroll
+          for (int j = 0; j < TMAX; ++j) {
+            const float gv = tg[((base + (j < Tl ? j : 0)) * p0.Hv + hv) * DK + lane + 64 * h];
+            gk[j] = j < Tl ? gv : 1.f;
+          }
+          float wk = 1.f;
+#pragma unroll
+          for (int i = TMAX - 1; i >= 0; --i) {
+            s_pwk[i * DK + lane + 64 * h] = i < Tl ? wk : 0.f;
+            wk *= gk[i];
+          }
+          s_pgk[lane + 64 * h] = wk;
+        }
+      }
+      __syncthreads();
+    }
+    const float gl = !VG && lane < Tl ? tg[(base + lane) * p0.Hv + hv] : 1.f;
     float w = 1.f, gam = 1.f;  // w_lane = prod_{lane<j<Tl} g_j, gam = prod_j g_j
 #pragma unroll
     for (int j = 0; j < TMAX; ++j) {
@@ -788,11 +857,12 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
     for (int st = 0; st < TMAX / 4; ++st) {
       const int i = 4 * st + kk;
       const size_t ii = base + (i < Tl ? i : 0);
-      const float* kr = tk + (ii * p0.Hk + hk) * DK + c16;
+      const float* kr = tk + (ii * p0.Hv + hv) * DK + c16;  // per-v-head copy
 #pragma unroll
-      for (int m = 0; m < DK / 16; ++m) kt[st][m] = kr[16 * m];
+      for (int m = 0; m < DK / 16; ++m)
+        kt[st][m] = kr[16 * m] * (VG ? s_pwk[i * DK + 16 * m + c16] : 1.f);
       const float wi = __shfl(w, i, kWave);
-      bw[st] = i < Tl ? wi : 0.f;
+      bw[st] = i < Tl ? (VG ? 1.f : wi) : 0.f;
     }
     float* const S_dst = p0.S_out + (lb * p0.Hv + hv) * static_cast<size_t>(DV * DK);
 #pragma unroll
@@ -812,7 +882,11 @@ __attribute__((amdgpu_waves_per_eu(PF ? 3 : 4))) void k_verify_chain(VerifyArgs 
 #pragma unroll
         for (int st = 0; st < TMAX / 4; ++st)
           acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[st][m], bu[st], acc, 0, 0, 0);
-        *reinterpret_cast<floatx4*>(wp + 16 * m) = sreg_pf[tt][m] * gam + acc;
+        if constexpr (VG)
+          *reinterpret_cast<floatx4*>(wp + 16 * m) =
+              sreg_pf[tt][m] * *reinterpret_cast<const floatx4*>(s_pgk + 16 * m + 4 * kk) + acc;
+        else
+          *reinterpret_cast<floatx4*>(wp + 16 * m) = sreg_pf[tt][m] * gam + acc;
       }
     }
   }
@@ -881,12 +955,37 @@ hipError_t launch_verify_chain_pf(const VerifyArgs& a, int dk, int dv, int dtype
   return hipGetLastError();
 }
 
+hipError_t launch_verify_chain_vg_pf(const VerifyArgs& a, hipStream_t s) {
+  const int G = a.Hv / a.Hk;
+  const int n_units = a.L * a.B * a.Hk;
+  const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
+  if (grid > 0x7fffffffLL || a.T < 1 || a.K > 16 || a.prev_n_keep || !a.S_out || !a.tu ||
+      !a.tk || !a.tg || !a.ptu || !a.ptk || !a.ptg)
+    return hipErrorInvalidValue;
+  const dim3 gd(static_cast<int>(grid)), bd(chain_threads<128>());
+  if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<128, 128, 16, 4, uint16_t, true, true, true>), gd, bd, 0, s, a);
+  else hipLaunchKernelGGL((k_verify_chain<128, 128, 16, 0, uint16_t, true, true, true>), gd, bd, 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_verify_chain_vg(const VerifyArgs& a, hipStream_t s) {
   const int G = a.Hv / a.Hk;
   const int n_units = a.L * a.B * a.Hk;
   const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
-  if (grid > 0x7fffffffLL || a.T > 16 || a.prev_n_keep || a.prev_n_all > 0) return hipErrorInvalidValue;
+  if (grid > 0x7fffffffLL || a.T > 16) return hipErrorInvalidValue;
   const dim3 gd(static_cast<int>(grid)), bd(chain_threads<128>());
+  if (a.prev_n_keep || a.prev_n_all > 0) {
+    if (a.pT > 16 || a.prev_n_all > a.pT || !a.S_out || !a.ptu || !a.ptk || !a.ptg)
+      return hipErrorInvalidValue;
+    if (a.T <= 8) {
+      if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<128, 128, 8, 4, uint16_t, true, true>), gd, bd, 0, s, a);
+      else hipLaunchKernelGGL((k_verify_chain<128, 128, 8, 0, uint16_t, true, true>), gd, bd, 0, s, a);
+    } else {
+      if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<128, 128, 16, 4, uint16_t, true, true>), gd, bd, 0, s, a);
+      else hipLaunchKernelGGL((k_verify_chain<128, 128, 16, 0, uint16_t, true, true>), gd, bd, 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (a.T <= 8) {
     if (a.K == 4) hipLaunchKernelGGL((k_verify_chain<128, 128, 8, 4, uint16_t, false, true>), gd, bd, 0, s, a);
     else hipLaunchKernelGGL((k_verify_chain<128, 128, 8, 0, uint16_t, false, true>), gd, bd, 0, s, a);

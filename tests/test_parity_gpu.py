@@ -840,6 +840,46 @@ def test_prefill_matches_sequential_oracle(T, L, B, Hk, Hv, D, K, dtype):
     np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
 
 
+def test_full_size_prefill_sampled():
+    """The benchmark's prefill at full size: 512 tokens through the 30-layer,
+    B = 32 stack of configuration 3 (one launch, state in registers), with
+    sampled (layer, sequence) units of the outputs, the final state and the
+    final conv window against the oracle's sequential recurrence."""
+    _need_gpu()
+    cfg = W.CONFIGS[3].with_(T=512)
+    torch.cuda.empty_cache()
+    inp = W.layer_inputs(cfg, 11, DEV)
+    ls = [0, cfg.L // 2, cfg.L - 1]
+    bs = [0, cfg.B // 3, cfg.B - 1]
+    f = {}
+    for k, v in inp.items():
+        t = v[ls]
+        f[k] = W.to_f64(t if k == "conv_w" else t[:, bs])
+    sh = gshape(cfg)
+    o = torch.empty((cfg.L, cfg.B, cfg.T, cfg.Hv, cfg.Dv), device=DEV)
+    ws = torch.empty((gb.gdn_prefill_workspace_bytes(sh),), device=DEV, dtype=torch.uint8)
+    err = torch.zeros((1,), device=DEV, dtype=torch.int32)
+    S, cs = inp["S0"], inp["conv_state"]
+    print("full-size prefill", cfg.L, cfg.B, cfg.T, flush=True)
+    gb.gdn_prefill(sh, inp["x"], cs, inp["conv_w"], inp["a"], inp["b"], S, o, ws, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got_o = o[ls][:, bs].cpu().double().numpy()
+    got_S = S[ls][:, bs].cpu().double().numpy()
+    got_cs = cs[ls][:, bs].cpu().double().numpy()
+    del inp, o, ws, S, cs
+    torch.cuda.empty_cache()
+    osh = oracle.Shape(L=len(ls), B=len(bs), Hk=cfg.Hk, Hv=cfg.Hv, Dk=cfg.Dk, Dv=cfg.Dv, K=cfg.K,
+                       silu=cfg.silu, eps=cfg.eps)
+    ref = oracle.verify_chunk(osh, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"], f["S0"],
+                              want_final=True)
+    cs_ref, _ = oracle.conv_rollback(osh, f["conv_state"], f["x"],
+                                     np.full(len(bs), cfg.T, np.int32))
+    assert rel_fro(got_o, ref["o"]) <= 1e-4
+    assert rel_fro(got_S, ref["S_final"]) <= 1e-4
+    np.testing.assert_array_equal(got_cs, cs_ref)
+
+
 # ------------------------------------------------ per-key-channel decay gate --
 
 def _vg_inputs(cfg, seed, gate_lo=0.05):
@@ -972,25 +1012,33 @@ def test_vgate_chained_rounds(tree):
     assert int(rb.dev_err.item()) == 0
 
 
-@pytest.mark.parametrize("T,D,dtype", [(5, 128, torch.bfloat16), (70, 64, torch.float32),
-                                       (130, 128, torch.bfloat16)])
-def test_vgate_prefill_matches_oracle(T, D, dtype):
-    """gdn_prefill with a per-key-channel gate (one launch of the sequential
-    kernel, committing the state) equals the oracle's verify_chunk_vg over
-    all T tokens: outputs, final state, final conv window."""
+@pytest.mark.parametrize("T,D,dtype,L,B,Hk,Hv,K", [
+    (5, 128, torch.bfloat16, 1, 2, 2, 4, 4), (70, 64, torch.float32, 1, 2, 2, 4, 4),
+    (130, 128, torch.bfloat16, 1, 2, 2, 4, 4), (33, 128, torch.bfloat16, 2, 3, 2, 2, 3),
+    (48, 128, torch.float32, 1, 2, 1, 2, 4), (16, 128, torch.bfloat16, 1, 2, 1, 2, 2)])
+def test_vgate_prefill_matches_oracle(T, D, dtype, L, B, Hk, Hv, K):
+    """gdn_prefill with a per-key-channel gate equals the oracle's
+    verify_chunk_vg over all T tokens: outputs, final state, final conv
+    window.  bf16 inputs with 128-dim heads run the chain kernel's one-launch
+    chunk loop (a two-tape workspace); other shapes one launch of the
+    sequential kernel (no workspace)."""
     _need_gpu()
-    cfg = W.CONFIGS[2].with_(L=1, B=2, Hk=2, Hv=4, Dk=D, Dv=D, K=4, T=T, dtype=dtype)
+    cfg = W.CONFIGS[2].with_(L=L, B=B, Hk=Hk, Hv=Hv, Dk=D, Dv=D, K=K, T=T, dtype=dtype)
     inp = _vg_inputs(cfg, 5)
     gsh, osh = _vg_shapes(cfg)
     d = {k: v.to(DEV) for k, v in inp.items()}
     S, cs = d["S0"].clone(), d["conv_state"].clone()
-    o = torch.empty((1, 2, T, cfg.Hv, D), device=DEV)
-    assert gb.gdn_prefill_workspace_bytes(gsh) == 0
-    gb.gdn_prefill(gsh, d["x"], cs, d["conv_w"], d["a"], d["b"], S, o, None)
+    o = torch.empty((L, B, T, cfg.Hv, D), device=DEV)
+    need = gb.gdn_prefill_workspace_bytes(gsh)
+    assert (need > 0) == (D == 128 and dtype == torch.bfloat16)
+    ws = torch.empty((need,), device=DEV, dtype=torch.uint8) if need else None
+    err = torch.zeros((1,), device=DEV, dtype=torch.int32)
+    gb.gdn_prefill(gsh, d["x"], cs, d["conv_w"], d["a"], d["b"], S, o, ws, dev_err=err)
     torch.cuda.synchronize()
+    assert int(err.item()) == 0
     f = {k: W.to_f64(v) for k, v in inp.items()}
     ref = oracle.verify_chunk_vg(osh, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"], f["S0"])
-    cs_ref, _ = oracle.conv_rollback(osh, f["conv_state"], f["x"], np.full(2, T, np.int32))
+    cs_ref, _ = oracle.conv_rollback(osh, f["conv_state"], f["x"], np.full(B, T, np.int32))
     assert rel_fro(o.cpu().double().numpy(), ref["o"]) <= 1e-4
     assert rel_fro(S.cpu().double().numpy(), ref["S_final"]) <= 1e-4
     np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
@@ -1057,6 +1105,7 @@ def _vg_prev_tape(cfg, pT, seed):
 
 @pytest.mark.parametrize("tree,T,pT,D,dtype", [
     (False, 8, 8, 128, torch.bfloat16), (False, 16, 12, 64, torch.float32),
+    (False, 16, 16, 128, torch.bfloat16), (False, 5, 13, 128, torch.bfloat16),
     (False, 40, 64, 32, torch.bfloat16), (True, 64, 64, 128, torch.bfloat16),
     (True, 24, 40, 32, torch.float32)])
 def test_vgate_replay_verify_equals_rollback_then_verify(tree, T, pT, D, dtype):
@@ -1164,7 +1213,7 @@ def test_vgate_tree_replay_bad_inputs_flag():
     assert rel_fro(S[:, 1].double().numpy(), S_rep[:, 1]) <= 1e-5
 
 
-@pytest.mark.parametrize("tree,T", [(True, 64), (False, 8)])
+@pytest.mark.parametrize("tree,T", [(True, 64), (False, 8), (False, 16)])
 def test_vgate_fused_rounds(tree, T):
     """Fused rounds (spec_round.FusedRound) with a per-key-channel gate: every
     round's outputs, tape, accepted lengths and paths, conv window, and the
