@@ -304,8 +304,11 @@ def prefill_pass(cfg, n_tokens, stream, reps=3, gate_per_key=False):
                      gate_per_key=gate_per_key)
     if gate_per_key:
         gen = torch.Generator(device="cuda").manual_seed(c.seed ^ 0x3C)
-        inp["a"] = (0.05 + 0.95 * torch.rand(sh.gate_shape(n_tokens), device="cuda",
-                                             generator=gen)).to(c.dtype)
+        gs = sh.gate_shape(n_tokens)
+        a = torch.empty(gs, device="cuda", dtype=c.dtype)
+        for l in range(gs[0]):  # per layer: the fp32 draw of a whole stack can exceed HBM
+            a[l] = 0.05 + 0.95 * torch.rand(gs[1:], device="cuda", generator=gen)
+        inp["a"] = a
     o = torch.empty((c.L, c.B, n_tokens, c.Hv, c.Dv), device="cuda")
     need = gb.gdn_prefill_workspace_bytes(sh)
     ws = torch.empty((need,), device="cuda", dtype=torch.uint8) if need else None
