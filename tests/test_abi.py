@@ -144,6 +144,23 @@ def test_host_validation_before_launch(lib):
     assert pf(100, FAKE, None, wsb) == gb.GDN_ERR_WORKSPACE
     assert lib.gdn_prefill(ctypes.byref(_shape(Dk=96, Dv=96)), 10, FAKE, FAKE, FAKE, FAKE, FAKE,
                            FAKE, FAKE, FAKE, wsb, None, None) == gb.GDN_ERR_UNSUPPORTED
+    # workspace sizes: two 16-token tapes (u, k, g) per (layer, seq); the
+    # one-launch loop (128-dim heads) keeps k rows per v-head, the chunked
+    # form per k-head; the per-key gate's g has Dk entries per v-head, and
+    # the per-key sequential kernel (fp32 inputs, other head sizes) none
+    def wsize(**kw):
+        return gb.lib().gdn_prefill_workspace_bytes(ctypes.byref(_shape(**kw)))
+
+    def tapes(L, B, Hk, Hv, D, gdk, kh):
+        fl = L * B * 16 * (Hv * D + kh * D + Hv * gdk)
+        return 2 * ((fl * 4 + 255) // 256 * 256)
+
+    assert wsize() == tapes(1, 2, 2, 4, 128, 1, 4)
+    assert wsize(Dk=64, Dv=64) == tapes(1, 2, 2, 4, 64, 1, 2)
+    assert wsize(gate_per_key=True) == tapes(1, 2, 2, 4, 128, 128, 4)
+    import torch
+    assert wsize(gate_per_key=True, dtype=torch.float32) == 0
+    assert wsize(gate_per_key=True, Dk=64, Dv=64) == 0
     # accept: missing / short workspace, bad dtype
     assert lib.spec_accept_prefix(2, 4, 100, None, FAKE, FAKE, gb.GDN_BF16, FAKE, FAKE, FAKE,
                                   FAKE, 8, None, None) == gb.GDN_ERR_WORKSPACE
