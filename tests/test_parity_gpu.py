@@ -1015,7 +1015,8 @@ def test_vgate_chained_rounds(tree):
 @pytest.mark.parametrize("T,D,dtype,L,B,Hk,Hv,K", [
     (5, 128, torch.bfloat16, 1, 2, 2, 4, 4), (70, 64, torch.float32, 1, 2, 2, 4, 4),
     (130, 128, torch.bfloat16, 1, 2, 2, 4, 4), (33, 128, torch.bfloat16, 2, 3, 2, 2, 3),
-    (48, 128, torch.float32, 1, 2, 1, 2, 4), (16, 128, torch.bfloat16, 1, 2, 1, 2, 2)])
+    (48, 128, torch.float32, 1, 2, 1, 2, 4), (16, 128, torch.bfloat16, 1, 2, 1, 2, 2),
+    (1, 128, torch.bfloat16, 1, 2, 2, 4, 4), (17, 128, torch.bfloat16, 2, 2, 2, 4, 8)])
 def test_vgate_prefill_matches_oracle(T, D, dtype, L, B, Hk, Hv, K):
     """gdn_prefill with a per-key-channel gate equals the oracle's
     verify_chunk_vg over all T tokens: outputs, final state, final conv
