@@ -433,6 +433,9 @@ def vgate_pass(cfg, stream, steps):
                       "verify_per_layer_ms": t_fverify / cfg.L,
                       "kernel": ("k_verify_chain (per-key gate, replay)"
                                  if not tree and cfg.T <= 16 and cfg.dtype == torch.bfloat16
+                                 and cfg.Dk == cfg.Dv == 128 else
+                                 "k_verify_tree (per-key gate, replay)"
+                                 if tree and 32 < cfg.T <= 64 and cfg.dtype == torch.bfloat16
                                  and cfg.Dk == cfg.Dv == 128 else "k_verify_vgt")}}
 
 

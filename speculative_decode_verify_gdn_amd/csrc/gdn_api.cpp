@@ -207,6 +207,8 @@ gdn_status gdn_tree_verify_replay(const gdn_shape* shape, int32_t T, const int32
     v.prev_n_keep = prev_n_keep;
     v.prev_path = prev_path;
     v.pT = prev_T;
+    if (T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128)
+      return launch_status(gdn::launch_verify_tree_vg(v, s));
     return launch_status(gdn::launch_verify_vg_tree(v, shape->d_k, shape->d_v, shape->in_dtype, s));
   }
   if (T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128) {

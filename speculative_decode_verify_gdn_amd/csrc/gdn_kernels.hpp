@@ -124,7 +124,8 @@ hipError_t launch_verify_chain_vg_pf(const VerifyArgs& a, hipStream_t s);
 // Trees of 33..64 nodes, 128-dim heads, bf16 inputs (per-node path solve).
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s);
 // Trees of 33..64 nodes (bf16, 128-dim heads) with the per-key-channel gate,
-// on the MFMA tree kernel (no replay).
+// on the MFMA tree kernel, with or without the replay of a previous path of
+// <= 64 steps (per-channel weights on the k operand of the rank-n update).
 hipError_t launch_verify_tree_vg(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream_t s);
 // The state and conv-window rollbacks of a round in one launch.

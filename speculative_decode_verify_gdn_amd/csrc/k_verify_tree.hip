@@ -100,7 +100,7 @@ struct TreeLds {
 
 template <int KC, bool RP, int NH, bool VG>
 __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
-  static_assert(!VG || (NH == 1 && !RP), "the per-key-channel gate runs one head, no replay");
+  static_assert(!VG || NH == 1, "the per-key-channel gate runs one head");
   constexpr int KM = KC > 0 ? KC : 8;
   using LY = TreeLds<KM, NH>;
   constexpr int XR = LY::XR;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
       }
       pp = lane < pn && !bad ? pp : 0;
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
+      for (int h = 0; h < (VG ? 0 : NH); ++h) {  // (per-key weights: formed in the replay)
         const float gv = lane < pn ? p.ptg[(lb * p.pT + pp) * p.Hv + hv + h] : 1.f;
         float x_s = gv;  // inclusive suffix product prod_{j >= lane} g_j
 #pragma unroll
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   constexpr int PRE = NH > 1 ? 2 : 4;  // groups of four steps preloaded
   float kt[RP ? PRE : 1][RP ? TR_D / 16 : 1];
   float ut[NH][RP ? PRE : 1];
-  auto load_step = [&](int st, float* ka, float* ua) {
+  auto load_step = [&](int st, float* ka, float* ua) __attribute__((always_inline)) {
     const int i = 4 * st + kk;
     const size_t e = lb * p.pT + s_ppath[i < pn ? i : 0];
     const float* kr = p.ptk + (e * p.Hk + hk) * TR_D + c16;
@@ -384,8 +384,68 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   // transposed 16x16 fp32 MFMA tiles D[j][r] = sum_i k_i[16m + j] (w_i u_i)[r]
   // (lane (c16, kk) of D holds exactly sreg[m]); the rolled tile is written
   // back in place.
-  auto replay = [&](int h) {
-    if constexpr (RP) {
+  // Per-key gate: S <- S diag(gamma) + sum_i u_{p_i} (k_{p_i} o w_i)^T with
+  // w_i[c] = prod_{i<j<pn} g_{p_j}[c] and gamma[c] = prod_{j<pn} g_{p_j}[c].
+  // Step groups go from the last to the first; each lane keeps, for its
+  // channels 16m + c16, the product R[m] of the gates of the groups already
+  // done, and its step 4 st + kk takes R times the gates of the later steps
+  // of its own group on the k operand.
+  auto replay_vg = [&]() __attribute__((always_inline)) {
+    if constexpr (RP && VG) {
+      floatx4 acc[TR_D / 16];
+      float R[TR_D / 16];
+#pragma unroll
+      for (int m = 0; m < TR_D / 16; ++m) {
+        acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+        R[m] = 1.f;
+      }
+      auto group = [&](int st, const float* ka, float ua) __attribute__((always_inline)) {
+        float gq[4][TR_D / 16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = 4 * st + q;
+          const float* gr = p.ptg + ((lb * p.pT + s_ppath[j < pn ? j : 0]) * p.Hv + hv) * TR_D + c16;
+#pragma unroll
+          for (int m = 0; m < TR_D / 16; ++m) {
+            const float gv = gr[16 * m];
+            gq[q][m] = j < pn ? gv : 1.f;
+          }
+        }
+        const int i = 4 * st + kk;
+        const float bu = i < pn ? ua : 0.f;
+#pragma unroll
+        for (int m = 0; m < TR_D / 16; ++m) {
+          float w = R[m];
+#pragma unroll
+          for (int q = 1; q < 4; ++q) w *= q > kk ? gq[q][m] : 1.f;
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m] * w, bu, acc[m], 0, 0, 0);
+          R[m] *= gq[0][m] * gq[1][m] * gq[2][m] * gq[3][m];
+        }
+      };
+      const int ng = (pn + 3) / 4;
+      for (int st = ng - 1; st >= PRE; --st) {
+        float ka[TR_D / 16], ua[NH];
+        load_step(st, ka, ua);
+        group(st, ka, ua[0]);
+      }
+#pragma unroll
+      for (int st = PRE - 1; st >= 0; --st)
+        if (4 * st < pn) group(st, kt[st], ut[0][st]);
+      // columns 16m + 4kk + e decay by gamma of that channel, held by lane 4kk + e
+#pragma unroll
+      for (int m = 0; m < TR_D / 16; ++m) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gm = __shfl(R[m], 4 * kk + e, 64);
+          sreg[0][m][e] = sreg[0][m][e] * gm + acc[m][e];
+        }
+      }
+    }
+  };
+  auto replay = [&](int h) __attribute__((always_inline)) {
+    if constexpr (RP && VG) {
+      replay_vg();
+    } else if constexpr (RP) {
       floatx4 acc[TR_D / 16];
 #pragma unroll
       for (int m = 0; m < TR_D / 16; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1076,10 +1136,18 @@ hipError_t launch_verify_tree_vg(const VerifyArgs& a, hipStream_t s) {
   const int G = a.Hv / a.Hk;
   const int n_units = a.L * a.B * a.Hk;
   const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
-  if (grid > 0x7fffffffLL || a.T > TR_T || a.T <= 32 || a.prev_n_keep) return hipErrorInvalidValue;
+  if (grid > 0x7fffffffLL || a.T > TR_T || a.T <= 32) return hipErrorInvalidValue;
+  const bool rp = a.prev_n_keep != nullptr;
+  if (rp && (a.pT < 1 || a.pT > TR_T || !a.ptu || !a.ptk || !a.ptg || !a.S_out))
+    return hipErrorInvalidValue;
   const dim3 gd(static_cast<int>(grid)), bd(TR_NT);
-  if (a.K == 4) hipLaunchKernelGGL((k_verify_tree<4, false, 1, true>), gd, bd, 0, s, a);
-  else hipLaunchKernelGGL((k_verify_tree<0, false, 1, true>), gd, bd, 0, s, a);
+  if (a.K == 4) {
+    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 1, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_tree<4, false, 1, true>), gd, bd, 0, s, a);
+  } else {
+    if (rp) hipLaunchKernelGGL((k_verify_tree<0, true, 1, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((k_verify_tree<0, false, 1, true>), gd, bd, 0, s, a);
+  }
   return hipGetLastError();
 }
 

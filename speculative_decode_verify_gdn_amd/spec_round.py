@@ -122,19 +122,20 @@ def fused_pays(sh: gb.GdnShape, T: int, tree: bool, device=None) -> bool:
     at most 16 drafts) and 1 for the tree kernel (trees of 33..64 nodes, bf16
     inputs, 128-dim heads); other shapes are not fused by the library.
 
-    With the decay gate per key channel, chains of at most 16 drafts (bf16
-    inputs, 128-dim heads) fuse on the chain kernel under the same rule as
-    the per-head gate.  Other chains and trees of 33..64 nodes with bf16
-    inputs and 128-dim heads (the MFMA tree kernel) would fuse on the
-    closed-form per-key kernel, slower than their plain verify, so they stay
-    plain.  Other trees run the closed-form kernel in both forms, and folding
-    the rollback in saves its state pass."""
+    With the decay gate per key channel, chains of at most 16 drafts and
+    trees of 33..64 nodes (bf16 inputs, 128-dim heads) fuse on the chain and
+    tree kernels under the same rules as the per-head gate.  Other chains
+    would fuse on the closed-form per-key kernel, slower than their plain
+    verify, so they stay plain.  Other trees run the closed-form kernel in
+    both forms, and folding the rollback in saves its state pass."""
     cus = torch.cuda.get_device_properties(device or torch.cuda.current_device()).multi_processor_count
     if sh.gate_per_key:
         mfma = sh.dtype == torch.bfloat16 and sh.Dk == sh.Dv == 128
         if not tree:
             return mfma and T <= 16 and sh.B * sh.Hv >= 2 * 4 * cus
-        return T <= 64 and not (mfma and 32 < T)
+        if mfma and 32 < T <= 64:
+            return sh.B * sh.Hv >= 2 * cus
+        return T <= 64
     if not tree:
         return T <= 16 and sh.B * sh.Hv >= 2 * 4 * cus
     tree_kernel = 32 < T <= 64 and sh.dtype == torch.bfloat16 and sh.Dk == sh.Dv == 128

@@ -1108,6 +1108,7 @@ def _vg_prev_tape(cfg, pT, seed):
     (False, 8, 8, 128, torch.bfloat16), (False, 16, 12, 64, torch.float32),
     (False, 16, 16, 128, torch.bfloat16), (False, 5, 13, 128, torch.bfloat16),
     (False, 40, 64, 32, torch.bfloat16), (True, 64, 64, 128, torch.bfloat16),
+    (True, 40, 23, 128, torch.bfloat16), (True, 33, 5, 128, torch.bfloat16),
     (True, 24, 40, 32, torch.float32)])
 def test_vgate_replay_verify_equals_rollback_then_verify(tree, T, pT, D, dtype):
     """gdn_verify_chunk_replay / gdn_tree_verify_replay with a per-key gate:
@@ -1161,13 +1162,14 @@ def test_vgate_replay_verify_equals_rollback_then_verify(tree, T, pT, D, dtype):
     np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
 
 
-def test_vgate_tree_replay_bad_inputs_flag():
-    """Per-key tree replay: a malformed parent array flags GDN_DEV_ERR_PARENT,
+@pytest.mark.parametrize("T,pT,D", [(24, 8, 64), (40, 8, 128)])
+def test_vgate_tree_replay_bad_inputs_flag(T, pT, D):
+    """Per-key tree replay (the closed-form kernel, and the MFMA tree kernel
+    for 33..64 nodes): a malformed parent array flags GDN_DEV_ERR_PARENT,
     skips that sequence's outputs and still applies its replay; an
     out-of-range accepted length or path entry flags its bit and leaves that
     sequence's state as it was."""
     _need_gpu()
-    T, pT, D = 24, 8, 64
     cfg = W.CONFIGS[2].with_(L=1, B=2, Hk=2, Hv=4, Dk=D, Dv=D, K=4, T=T, dtype=torch.bfloat16)
     gsh, osh = _vg_shapes(cfg)
     inp = _vg_inputs(cfg, 11)
@@ -1214,7 +1216,7 @@ def test_vgate_tree_replay_bad_inputs_flag():
     assert rel_fro(S[:, 1].double().numpy(), S_rep[:, 1]) <= 1e-5
 
 
-@pytest.mark.parametrize("tree,T", [(True, 64), (False, 8), (False, 16)])
+@pytest.mark.parametrize("tree,T", [(True, 64), (True, 40), (False, 8), (False, 16)])
 def test_vgate_fused_rounds(tree, T):
     """Fused rounds (spec_round.FusedRound) with a per-key-channel gate: every
     round's outputs, tape, accepted lengths and paths, conv window, and the
