@@ -900,6 +900,95 @@ def _vg_shapes(cfg):
     return g, o
 
 
+@pytest.mark.parametrize("cfg_id", [4, 5])
+def test_full_size_vgate_fused_rounds_sampled(cfg_id):
+    """The per-key round form the benchmark picks for configurations 4 and 5
+    (fused) at full size, with the decay gate drawn per key channel: two
+    rounds, the second replaying the first's accepted prefixes (paths) inside
+    its verify.  Sampled (layer, sequence) units of the second round's outputs,
+    tape, accepted lengths, paths and conv window, and of the state it leaves
+    (one accepted prefix behind), against the oracle's per-key plain rounds."""
+    _need_gpu()
+    cfg = W.CONFIGS[cfg_id]
+    tree = cfg.is_tree
+    torch.cuda.empty_cache()
+    ls = [0, cfg.L // 2, cfg.L - 1]
+    bs = [0, cfg.B // 3, cfg.B - 1]
+    gsh, _ = _vg_shapes(cfg)
+    osh = oracle.Shape(L=len(ls), B=len(bs), Hk=cfg.Hk, Hv=cfg.Hv, Dk=cfg.Dk, Dv=cfg.Dv,
+                       K=cfg.K, silu=cfg.silu, eps=cfg.eps)
+
+    def inputs(r):
+        inp = W.layer_inputs(cfg, r, DEV)
+        gen = torch.Generator(device=DEV).manual_seed(5000 + r)
+        a = torch.empty(gsh.gate_shape(cfg.T), device=DEV, dtype=cfg.dtype)
+        for l in range(cfg.L):
+            a[l] = 0.05 + 0.95 * torch.rand(a.shape[1:], device=DEV, generator=gen)
+        inp["a"] = a
+        host = {}
+        for k, v in inp.items():
+            t = v[ls]
+            host[k] = W.to_f64(t if k == "conv_w" else t[:, bs])
+        return inp, host
+
+    accs = [W.tree_accept_inputs(cfg, r, DEV) if tree else W.chain_accept_inputs(cfg, r, DEV)
+            for r in (0, 1)]
+    inp0, f0 = inputs(0)
+    print("full-size per-key fused rounds", cfg_id, flush=True)
+    rb = spec_round.RoundBuffers(sh=gsh, T=cfg.T, V=cfg.V, tree=tree, S=inp0["S0"],
+                                 conv_state=inp0["conv_state"], conv_w=inp0["conv_w"],
+                                 x=inp0["x"], a=inp0["a"], b=inp0["b"],
+                                 logits=accs[0]["logits"], draft=accs[0]["draft"],
+                                 parent=accs[0]["parent"] if tree else None)
+    fr = spec_round.FusedRound(rb)
+    fr.round(0, first=True)
+    torch.cuda.synchronize()
+    inp1, f1 = inputs(1)
+    rb.x, rb.a, rb.b, rb.conv_w = inp1["x"], inp1["a"], inp1["b"], inp1["conv_w"]
+    rb.logits, rb.draft = accs[1]["logits"], accs[1]["draft"]
+    if tree:
+        rb.parent = accs[1]["parent"]
+    fr.round(1)
+    torch.cuda.synchronize()
+    assert int(rb.dev_err.item()) == 0
+
+    def pick(t, has_l=True):
+        return (t[ls][:, bs] if has_l else t[bs]).detach().cpu()
+
+    tape = fr.tapes[1]
+    got = dict(o=pick(rb.o), u=pick(tape.u), k=pick(tape.k), g=pick(tape.g), S=pick(rb.S),
+               cs=pick(rb.conv_state), n_keep=pick(fr.n_keeps[1], False),
+               path=pick(fr.paths[1], False))
+
+    def ref_round(f, S, cs, acc):
+        par = acc["parent"][bs].cpu().numpy() if tree else None
+        if tree:
+            ref = oracle.tree_verify_vg(osh, par, f["x"], cs, f["conv_w"], f["a"], f["b"], S)
+        else:
+            ref = oracle.verify_chunk_vg(osh, f["x"], cs, f["conv_w"], f["a"], f["b"], S)
+        n, path, _ = oracle.accept(acc["draft"][bs].cpu().numpy(), W.to_f64(acc["logits"][bs]),
+                                   par)
+        S_new = oracle.tape_rollback_vg(osh, S, ref["u"], ref["k"], ref["g"], n,
+                                        path if tree else None)
+        cs_new, _ = oracle.conv_rollback(osh, cs, f["x"], n, path if tree else None)
+        return ref, n, path, S_new, cs_new
+
+    _, _, _, S1, cs1 = ref_round(f0, f0["S0"], f0["conv_state"], accs[0])
+    ref, n, path, _, cs2 = ref_round(f1, S1, cs1, accs[1])
+    np.testing.assert_array_equal(got["n_keep"].numpy(), n)
+    if tree:
+        np.testing.assert_array_equal(got["path"].numpy(), path)
+    np.testing.assert_array_equal(got["cs"].double().numpy(), cs2)
+    for key in ("o", "u", "k"):
+        e = rel_fro(got[key].double().numpy(), ref[key])
+        assert e <= 1e-4, (key, e)
+    np.testing.assert_array_equal(got["g"].double().numpy(), ref["g"])
+    e = rel_fro(got["S"].double().numpy(), S1)
+    assert e <= 1e-4, ("S after the replay", e)
+    del fr, rb, inp0, inp1, accs
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("T,L,B,Hk,Hv,D,K,dtype", [
     (1, 1, 2, 2, 4, 128, 4, torch.bfloat16), (8, 2, 2, 2, 4, 128, 4, torch.bfloat16),
     (16, 1, 3, 1, 2, 64, 3, torch.float32), (17, 1, 2, 2, 4, 128, 4, torch.bfloat16),
