@@ -628,9 +628,10 @@ def test_full_size_sampled(cfg_id):
 
 @pytest.mark.parametrize("cfg_id", [4, 5])
 def test_full_size_fused_rounds_sampled(cfg_id):
-    """The round form the benchmark times for configurations 4 and 5, at full
-    size: two fused rounds, the second replaying the first's accepted
-    prefixes (paths) inside its verify.  Sampled (layer, sequence) units of
+    """The round form the benchmark times for the B=256 16-draft chain stack
+    and the B=64 64-node tree stack, at full size: two fused rounds, the
+    second replaying the first's accepted prefixes (paths) inside its
+    verify.  Sampled (layer, sequence) units of
     the second round's outputs, tape, accepted lengths, paths and conv
     window, and of the state it leaves (one accepted prefix behind), against
     the oracle's plain rounds."""
@@ -842,7 +843,7 @@ def test_prefill_matches_sequential_oracle(T, L, B, Hk, Hv, D, K, dtype):
 
 def test_full_size_prefill_sampled():
     """The benchmark's prefill at full size: 512 tokens through the 30-layer,
-    B = 32 stack of configuration 3 (one launch, state in registers), with
+    B = 32 stack of 8-draft chains (one launch, state in registers), with
     sampled (layer, sequence) units of the outputs, the final state and the
     final conv window against the oracle's sequential recurrence."""
     _need_gpu()
@@ -902,8 +903,9 @@ def _vg_shapes(cfg):
 
 @pytest.mark.parametrize("cfg_id", [4, 5])
 def test_full_size_vgate_fused_rounds_sampled(cfg_id):
-    """The per-key round form the benchmark picks for configurations 4 and 5
-    (fused) at full size, with the decay gate drawn per key channel: two
+    """The per-key round form the benchmark picks for the B=256 16-draft chain
+    stack and the B=64 64-node tree stack (fused), at full size, with the
+    decay gate drawn per key channel: two
     rounds, the second replaying the first's accepted prefixes (paths) inside
     its verify.  Sampled (layer, sequence) units of the second round's outputs,
     tape, accepted lengths, paths and conv window, and of the state it leaves
