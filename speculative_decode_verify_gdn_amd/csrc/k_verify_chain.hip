@@ -31,7 +31,15 @@
 // the workgroups waiting for a free slot.  (Measured alternatives -- a
 // prologue-only wave with the state on three waves, raised issue priority
 // for the prologue, delaying the state loads -- were no faster.)
-// S0 and the conv window are never written (they stay the snapshot).
+// S0 and the conv window are never written (they stay the snapshot), except
+// by the forms below.
+//
+// Forms (template flags): RP folds the previous round's accepted prefix into
+// S first (the rank-n tape replay on fp32 MFMA, written back in place); VG
+// takes the decay gate per key channel (the walk that forms the A and Oc
+// coefficients from forward gate products, and per-channel weights on the k
+// operand of the replay); PF walks a whole prefill through the workgroup in
+// chunks of TMAX tokens with the state held in registers.
 //
 // Work item: one workgroup per (layer, seq, v-head), all Dv rows of S.
 

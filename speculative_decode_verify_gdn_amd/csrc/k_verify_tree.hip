@@ -39,7 +39,15 @@
 // (K/Q are still in LDS), its v rows wait in registers until the first head
 // has finished with the V space, and wave 0 solves its packed rows while the
 // other waves run the first head's second product.
-// S0 and the conv window are never written (they stay the snapshot).
+// S0 and the conv window are never written (they stay the snapshot), except
+// by the replay form.
+//
+// Forms (template flags): RP first folds the previous round's accepted path
+// into S (the rank-n tape replay on fp32 MFMA, written back in place); VG
+// takes the decay gate per key channel (one head per workgroup: a path walk
+// forms the A and Oc coefficients from forward gate products, the operand
+// rows carry gamma, and the replay puts per-channel path weights, formed
+// backwards along the path in registers, on its k operand).
 
 #include "gdn_common.hpp"
 #include "gdn_kernels.hpp"
