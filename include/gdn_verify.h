@@ -72,6 +72,7 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 #define GDN_DEV_ERR_PARENT 2 /* parent[b][v] outside [-1, v-1] */
 #define GDN_DEV_ERR_PATH 4   /* path entry outside [0, T) or not a child of the previous */
 #define GDN_DEV_ERR_TOKEN 8  /* draft token outside [0, V) (sampling acceptance) */
+#define GDN_DEV_ERR_NAN 16   /* a logits row holds a NaN (greedy acceptance) */
 
 typedef struct {
   int32_t n_layers;    /* L: leading dimension of every per-layer tensor */
@@ -208,7 +209,10 @@ gdn_status gdn_tree_verify_replay(const gdn_shape* shape, int32_t T, const int32
 /*
  * Greedy acceptance.  logits [B,T+1,V] (F32 or BF16): row 0 is the target's
  * distribution after the last committed token, row 1+v after draft token /
- * node v.  argmax takes the lowest index among equal maxima.
+ * node v.  argmax takes the lowest index among equal maxima.  Infinities are
+ * ordinary values (a row of -inf, e.g. fully masked, gives index 0).  NaN is
+ * an input error: it sets GDN_DEV_ERR_NAN, a NaN entry is never the argmax,
+ * and a row holding no number gives index 0; results stay in [0, V).
  *   parent == NULL (chain): n_keep[b] = longest prefix with
  *     draft[b][j] == argmax(row j); path[b] = 0..n-1 then -1.
  *   parent != NULL (tree): from the root, step to the lowest-index child c

@@ -43,8 +43,9 @@
  *  - Tree: parent[v] in [-1, v-1], -1 = virtual root whose state is S0; the
  *    conv window of node v is the last K entries of [old conv rows,
  *    ancestors' x from the root down, x_v].
- *  - Accept: argmax takes the first index of the maximum; tree walk takes the
- *    lowest-index child whose token equals the argmax.
+ *  - Accept: argmax takes the first index of the maximum (NaN entries never
+ *    win; a row with no number gives 0); tree walk takes the lowest-index
+ *    child whose token equals the argmax.
  *  - Conv-window index space: -(K-1)..-1 = old conv_state row (K-1+idx),
  *    0..T-1 = token / node index.
  */
@@ -452,11 +453,16 @@ int oracle_tree_verify_vg(const oshape* sh, int T, const int* parent,
 }
 
 /* First index of the maximum of row[0..V-1]. */
+/* The first index of the largest value.  Infinities are values like any
+ * other (a row of -inf gives 0); a NaN is not a number, so it is never the
+ * maximum; a row holding no number gives 0. */
 static int argmax_first(int V, const double* row) {
-  int best = 0;
-  for (int i = 1; i < V; ++i)
-    if (row[i] > row[best]) best = i;
-  return best;
+  int best = -1;
+  for (int i = 0; i < V; ++i) {
+    if (isnan(row[i])) continue;
+    if (best < 0 || row[i] > row[best]) best = i;
+  }
+  return best < 0 ? 0 : best;
 }
 
 /* ---------------------------------------------------------------------------

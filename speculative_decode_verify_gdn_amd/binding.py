@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH, GDN_ERR_WORKSPACE = range(5)
 GDN_F32, GDN_BF16 = 0, 1
-DEV_ERR_N_KEEP, DEV_ERR_PARENT, DEV_ERR_PATH, DEV_ERR_TOKEN = 1, 2, 4, 8
+DEV_ERR_N_KEEP, DEV_ERR_PARENT, DEV_ERR_PATH, DEV_ERR_TOKEN, DEV_ERR_NAN = 1, 2, 4, 8, 16
 
 EXPORTS = ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
            "gdn_tree_verify_replay", "spec_accept_prefix", "spec_accept_sample",

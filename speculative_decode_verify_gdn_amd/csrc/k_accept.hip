@@ -12,7 +12,11 @@
 // (max value, lowest index).  (2) k_accept_walk: one wave per sequence folds
 // the partials into each row's argmax and walks the chain / tree.  Ties at
 // every level keep the lowest index, so the result equals a plain sequential
-// first-maximum scan.  The walk never leaves the device.
+// first-maximum scan.  Infinities compare as values (a row of -inf gives
+// index 0); a NaN is never the maximum (it loses every comparison, and the
+// "no value yet" seed below loses to any number), so a row with no number
+// gives index 0, and a NaN seen in a row sets GDN_DEV_ERR_NAN.  The walk never
+// leaves the device.
 
 #include "gdn_common.hpp"
 #include "gdn_kernels.hpp"
@@ -24,6 +28,10 @@ struct Best {
   float v;
   int i;
 };
+
+// Seed of every reduction: below or equal to any number, and any number at a
+// real index beats it (equal value, lower index); NaN never does.
+constexpr int kNoIndex = 0x7fffffff;
 
 // Keep the larger value; on equal values the lower index.
 __device__ __forceinline__ Best better(Best a, Best b) {
@@ -49,32 +57,37 @@ __global__ __launch_bounds__(256) void k_argmax_part(AcceptArgs p) {
   constexpr int NT = 256;
   constexpr int EPV = 16 / ESZ;  // elements per 16-byte vector
   __shared__ Best s_best[NT / kWave];
+  __shared__ bool s_nan[NT / kWave];
   const int tid = threadIdx.x;
   const int part = blockIdx.x % p.split;
   const size_t row = blockIdx.x / p.split;
   const size_t V = p.V;
   const int beg = part * p.chunk;
   const int end = min(beg + p.chunk, p.V);
-  Best best{-__builtin_inff(), 0x7fffffff};
+  Best best{-__builtin_inff(), kNoIndex};
+  bool nan = false;
   const char* base = static_cast<const char*>(p.logits) + row * V * ESZ;
   if (((V * ESZ) % 16) == 0 && (beg % EPV) == 0) {
     // vector path: 16-byte loads of EPV consecutive elements
     const uint4* vp = reinterpret_cast<const uint4*>(base);
     const int vbeg = beg / EPV;
     const int vend = end / EPV;  // full vectors
-    // A thread sees its elements in increasing index order, so a strict
-    // greater-than keeps the lowest index among equal values.
+    // A thread sees its elements in increasing index order, so an equal
+    // value replaces the best only while it is still the seed: the lowest
+    // index among equal values is kept.
+    auto take = [&](float v, int i) {
+      nan |= v != v;
+      if (v > best.v || (v == best.v && best.i == kNoIndex)) best = Best{v, i};
+    };
     auto scan = [&](const uint4& w, int i0) {
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         if (ESZ == 2) {
-          const float lo = bf16_lo(ws[h]), hi = bf16_hi(ws[h]);
-          if (lo > best.v) best = Best{lo, i0 + 2 * h};
-          if (hi > best.v) best = Best{hi, i0 + 2 * h + 1};
+          take(bf16_lo(ws[h]), i0 + 2 * h);
+          take(bf16_hi(ws[h]), i0 + 2 * h + 1);
         } else {
-          const float v = __uint_as_float(ws[h]);
-          if (v > best.v) best = Best{v, i0 + h};
+          take(__uint_as_float(ws[h]), i0 + h);
         }
       }
     };
@@ -91,17 +104,23 @@ __global__ __launch_bounds__(256) void k_argmax_part(AcceptArgs p) {
     for (int i = vend * EPV + tid; i < end; i += NT) {  // ragged tail
       const float v = ESZ == 2 ? ld_in(reinterpret_cast<const uint16_t*>(base), i)
                                : ld_in(reinterpret_cast<const float*>(base), i);
+      nan |= v != v;
       best = better(best, Best{v, i});
     }
   } else {
     for (int i = beg + tid; i < end; i += NT) {
       const float v = ESZ == 2 ? ld_in(reinterpret_cast<const uint16_t*>(base), i)
                                : ld_in(reinterpret_cast<const float*>(base), i);
+      nan |= v != v;
       best = better(best, Best{v, i});
     }
   }
   best = wave_best(best);
-  if ((tid & (kWave - 1)) == 0) s_best[tid / kWave] = best;
+  const bool wave_nan = __any(nan);
+  if ((tid & (kWave - 1)) == 0) {
+    s_best[tid / kWave] = best;
+    s_nan[tid / kWave] = wave_nan;
+  }
   __syncthreads();
   if (tid == 0) {
     Best b = s_best[0];
@@ -109,6 +128,10 @@ __global__ __launch_bounds__(256) void k_argmax_part(AcceptArgs p) {
     for (int w = 1; w < NT / kWave; ++w) b = better(b, s_best[w]);
     p.part_val[row * p.split + part] = b.v;
     p.part_idx[row * p.split + part] = b.i;
+    bool any_nan = false;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) any_nan |= s_nan[w];
+    if (any_nan && p.dev_err) atomicOr(p.dev_err, GDN_DEV_ERR_NAN);
   }
 }
 
@@ -120,10 +143,10 @@ __global__ __launch_bounds__(64) void k_accept_walk(AcceptArgs p) {
   const int rows = T + 1;
   for (int r = lane; r < rows; r += kWave) {
     const size_t row = static_cast<size_t>(bb) * rows + r;
-    Best b{-__builtin_inff(), 0x7fffffff};
+    Best b{-__builtin_inff(), kNoIndex};
     for (int s = 0; s < p.split; ++s)
       b = better(b, Best{p.part_val[row * p.split + s], p.part_idx[row * p.split + s]});
-    s_star[r] = b.i;
+    s_star[r] = b.i == kNoIndex ? 0 : b.i;  // a row with no number
   }
   __syncthreads();
   const int* draft = p.draft + static_cast<size_t>(bb) * T;

@@ -120,3 +120,55 @@ def test_generator_plants_requested_tree_paths():
     nk, path, bo = oracle.accept(d["draft"].numpy(), W.to_f64(d["logits"]), d["parent"].numpy())
     np.testing.assert_array_equal(nk, d["n_planted"])
     np.testing.assert_array_equal(path, d["planted_path"])
+
+
+def _nan_rule_argmax(row):
+    """numpy's NaN-skipping first-maximum; a row with no number gives 0."""
+    row = np.asarray(row, dtype=np.float64)
+    return 0 if np.all(np.isnan(row)) else int(np.nanargmax(row))
+
+
+@pytest.mark.parametrize("tree", [False, True])
+def test_infinite_and_nan_logits(tree):
+    """Rows of -inf, -inf padding, +inf entries and NaN entries: the argmax is
+    numpy's NaN-skipping first maximum (np.nanargmax), -inf rows give 0, a row
+    of NaN gives 0; the walk then follows the same rule as for finite rows."""
+    rng = np.random.default_rng(21 if tree else 20)
+    B, T, V = 40, 6, 9
+    logits = rng.integers(-2, 3, size=(B, T + 1, V)).astype(np.float64)
+    kinds = rng.integers(0, 6, size=(B, T + 1))
+    for b in range(B):
+        for r in range(T + 1):
+            k = kinds[b, r]
+            if k == 1:
+                logits[b, r, :] = -np.inf
+            elif k == 2:
+                logits[b, r, rng.integers(1, V):] = -np.inf   # -inf padded tail
+            elif k == 3:
+                logits[b, r, rng.integers(0, V, size=3)] = np.nan
+            elif k == 4:
+                logits[b, r, :] = np.nan
+            elif k == 5:
+                logits[b, r, rng.integers(0, V, size=2)] = np.inf
+    star = np.array([[_nan_rule_argmax(logits[b, r]) for r in range(T + 1)] for b in range(B)])
+    draft = np.where(rng.random((B, T)) < 0.8, star[:, :T], rng.integers(0, V, (B, T)))
+    parent = np.stack([W.random_tree(rng, T, 3, 4) for _ in range(B)]) if tree else None
+    nk, path, bo = oracle.accept(draft, logits, parent)
+    nanfree = np.where(np.isnan(logits), -np.inf, logits)  # NaN never wins
+    for b in range(B):
+        assert all(star[b, r] == (0 if np.all(np.isnan(logits[b, r]))
+                                  else int(np.argmax(nanfree[b, r])))
+                   for r in range(T + 1))
+        if tree:
+            # the brute-force walk with the same argmax rule
+            lg = np.where(np.isnan(logits[b]), -np.inf, logits[b])
+            p, bonus = brute_tree(parent[b], draft[b], lg)
+        else:
+            m = 0
+            while m < T and draft[b, m] == star[b, m]:
+                m += 1
+            p, bonus = list(range(m)), star[b, m]
+        assert nk[b] == len(p) and bo[b] == bonus
+        assert list(path[b, :nk[b]]) == list(p)
+    assert oracle.accept(np.zeros((1, 1), np.int32), np.full((1, 2, 5), -np.inf))[2][0] == 0
+    assert oracle.accept(np.zeros((1, 1), np.int32), np.full((1, 2, 5), np.nan))[2][0] == 0

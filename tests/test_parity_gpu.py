@@ -16,7 +16,7 @@ from speculative_decode_verify_gdn_amd import binding as gb
 from speculative_decode_verify_gdn_amd import spec_round
 from speculative_decode_verify_gdn_amd import workload as W
 
-from round_ref import compare, gpu_outputs, gshape, make_buffers, oracle_round, rel_fro
+from round_ref import check_units, compare, gpu_outputs, gshape, make_buffers, oracle_round
 
 pytestmark = pytest.mark.gpu
 
@@ -73,8 +73,8 @@ def test_cfg1_tiny_prefill_then_chained_rounds():
     gb.gdn_conv_state_rollback(gsh, cs, dev["x"], nk)
     f = {k: W.to_f64(v) for k, v in pre.items()}
     ref = oracle.verify_chunk(sh_o, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"], f["S0"])
-    assert rel_fro(o.cpu().double(), ref["o"]) <= 1e-4
-    assert rel_fro(S.cpu().double(), ref["S_final"]) <= 1e-4
+    check_units("o", o, ref["o"], "tok")
+    check_units("S", S, ref["S_final"], "state")
     oS = ref["S_final"]
     ocs, _ = oracle.conv_rollback(sh_o, f["conv_state"], f["x"], np.array([64], np.int32))
     np.testing.assert_array_equal(cs.cpu().double().numpy(), ocs)
@@ -238,10 +238,9 @@ def test_tree_with_chain_parents_equals_chunk():
                                 d["S0"], o, tape)
         outs.append((o, tape))
     torch.cuda.synchronize()
-    c = lambda t: t.cpu().double().numpy()
-    assert rel_fro(c(outs[1][0]), c(outs[0][0])) <= 1e-4
-    assert rel_fro(c(outs[1][1].u), c(outs[0][1].u)) <= 1e-4
-    assert rel_fro(c(outs[1][1].k), c(outs[0][1].k)) <= 1e-4
+    check_units("o", outs[1][0], outs[0][0], "tok")
+    check_units("u", outs[1][1].u, outs[0][1].u, "tok")
+    check_units("k", outs[1][1].k, outs[0][1].k, "tok")
     assert torch.equal(outs[0][1].g, outs[1][1].g)
 
 
@@ -282,13 +281,12 @@ def test_fused_replay_rounds(cfg_id, L, B, rounds, forced):
         np.testing.assert_array_equal(fr.rb.conv_state.cpu().double().numpy(), ref["cs_new"])
         for name, got, want in (("o", fr.rb.o, ref["o"]), ("u", tape.u, ref["u"]),
                                 ("k", tape.k, ref["k"])):
-            err = rel_fro(got.cpu().double().numpy(), want)
-            assert err <= 1e-4, (r, name, err)
+            check_units("%s, round %d" % (name, r), got, want, "tok")
         np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
         oS, ocs = ref["S_new"], ref["cs_new"]
     fr.finish(rounds - 1)
     torch.cuda.synchronize()
-    assert rel_fro(fr.rb.S.cpu().double().numpy(), oS) <= 1e-4
+    check_units("S", fr.rb.S, oS, "state")
     assert int(fr.rb.dev_err.item()) == 0
 
 
@@ -328,13 +326,12 @@ def test_fused_replay_tree_rounds(L, B, rounds, T):
         np.testing.assert_array_equal(fr.rb.conv_state.cpu().double().numpy(), ref["cs_new"])
         for name, got, want in (("o", fr.rb.o, ref["o"]), ("u", tape.u, ref["u"]),
                                 ("k", tape.k, ref["k"])):
-            err = rel_fro(got.cpu().double().numpy(), want)
-            assert err <= 1e-4, (r, name, err)
+            check_units("%s, round %d" % (name, r), got, want, "tok")
         np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
         oS, ocs = ref["S_new"], ref["cs_new"]
     fr.finish(rounds - 1)
     torch.cuda.synchronize()
-    assert rel_fro(fr.rb.S.cpu().double().numpy(), oS) <= 1e-4
+    check_units("S", fr.rb.S, oS, "state")
     assert int(fr.rb.dev_err.item()) == 0
 
 
@@ -375,7 +372,7 @@ def test_fused_tree_replay_bad_inputs_flag():
     gb.gdn_tape_rollback(sh, S_ref, prev, torch.tensor([3, 0], dtype=torch.int32, device=DEV),
                          path=ppath.clamp(0, cfg.T - 1))
     torch.cuda.synchronize()
-    assert rel_fro(S[:, 0].cpu().double().numpy(), S_ref[:, 0].cpu().double().numpy()) <= 1e-5
+    check_units("S", S[:, 0], S_ref[:, 0], "state", 1e-5)
 
 
 @pytest.mark.parametrize("Hk,Hv,K,T", [(2, 4, 4, 48), (2, 2, 4, 64), (1, 4, 3, 40)])
@@ -415,13 +412,12 @@ def test_tree_replay_long_previous_paths(Hk, Hv, K, T):
     f = {k: W.to_f64(v) for k, v in inp.items()}
     S_rep = oracle.tape_rollback(osh, f["S0"], pu.double().numpy(), pk.double().numpy(),
                                  pg.double().numpy(), nk.numpy(), path.numpy())
-    assert rel_fro(S.cpu().double().numpy(), S_rep) <= 1e-5
+    check_units("S", S, S_rep, "state", 1e-5)
     assert torch.equal(S[:, 0].cpu(), inp["S0"][:, 0])
     ref = oracle.tree_verify(osh, parent.numpy(), f["x"], f["conv_state"], f["conv_w"], f["a"],
                              f["b"], S_rep)
     for name, got in (("o", o), ("u", tape.u), ("k", tape.k)):
-        e = rel_fro(got.cpu().double().numpy(), ref[name])
-        assert e <= 1e-4, (name, e)
+        check_units(name, got, ref[name], "tok")
 
 
 def test_fused_replay_bad_prev_n_keep_flags():
@@ -471,6 +467,61 @@ def test_accept_ties_and_ragged_vocab(dtype, V):
         np.testing.assert_array_equal(nk.cpu().numpy(), n_ref)
         np.testing.assert_array_equal(path.cpu().numpy(), p_ref)
         np.testing.assert_array_equal(bonus.cpu().numpy(), b_ref)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V", [9, 4100, 151936])
+def test_accept_infinite_and_nan_rows(dtype, V):
+    """Rows of -inf (fully masked), -inf-padded rows, rows with +inf entries
+    and rows with NaN entries or only NaN: the accepted lengths, paths and
+    bonus tokens equal the oracle's (NaN never the argmax, a row with no
+    number gives 0), every index stays in [0, V), and GDN_DEV_ERR_NAN is set
+    exactly when some row holds a NaN."""
+    _need_gpu()
+    rng = np.random.default_rng(V + (1 if dtype == torch.float32 else 0))
+    B, T = 12, 5
+    lg = rng.integers(-3, 4, size=(B, T + 1, V)).astype(np.float32)
+    kinds = rng.integers(0, 6, size=(B, T + 1))
+    kinds[0, :] = 1   # a sequence of -inf rows only
+    kinds[1, 0] = 4   # a row of NaN only
+    for bb in range(B):
+        for r in range(T + 1):
+            k = kinds[bb, r]
+            if k == 1:
+                lg[bb, r, :] = -np.inf
+            elif k == 2:
+                lg[bb, r, int(rng.integers(1, V)):] = -np.inf
+            elif k == 3:
+                lg[bb, r, rng.integers(0, V, size=3)] = np.nan
+            elif k == 4:
+                lg[bb, r, :] = np.nan
+            elif k == 5:
+                lg[bb, r, rng.integers(0, V, size=2)] = np.inf
+    lg_t = torch.from_numpy(lg).to(dtype)
+    lg64 = lg_t.double().numpy()
+    clean = np.where(np.isnan(lg64), -np.inf, lg64)
+    star = np.where(np.all(np.isnan(lg64), -1), 0, clean.argmax(-1))
+    draft = np.where(rng.random((B, T)) < 0.8, star[:, :T], rng.integers(0, V, (B, T)))
+    d = torch.from_numpy(draft.astype(np.int32)).to(DEV)
+    for parent in (None, np.stack([W.random_tree(rng, T, 2, 4) for _ in range(B)])):
+        for with_nan in (True, False):
+            x = lg_t if with_nan else torch.from_numpy(np.where(np.isnan(lg), -np.inf, lg)).to(dtype)
+            nk = torch.empty(B, dtype=torch.int32, device=DEV)
+            path = torch.empty((B, T), dtype=torch.int32, device=DEV)
+            bonus = torch.empty(B, dtype=torch.int32, device=DEV)
+            err = torch.zeros(1, dtype=torch.int32, device=DEV)
+            ws = torch.empty(gb.spec_accept_workspace_bytes(B, T, V), dtype=torch.uint8,
+                             device=DEV)
+            par_t = None if parent is None else torch.from_numpy(parent.astype(np.int32)).to(DEV)
+            print("accept inf/nan", V, dtype, parent is not None, with_nan, flush=True)
+            gb.spec_accept_prefix(d, x.to(DEV), nk, path, bonus, ws, parent=par_t, dev_err=err)
+            n_ref, p_ref, b_ref = oracle.accept(draft, x.double().numpy(), parent)
+            np.testing.assert_array_equal(nk.cpu().numpy(), n_ref)
+            np.testing.assert_array_equal(path.cpu().numpy(), p_ref)
+            np.testing.assert_array_equal(bonus.cpu().numpy(), b_ref)
+            assert ((bonus.cpu().numpy() >= 0) & (bonus.cpu().numpy() < V)).all()
+            assert bool(int(err.item()) & gb.DEV_ERR_NAN) == with_nan
+            assert int(err.item()) & ~gb.DEV_ERR_NAN == 0
 
 
 # ------------------------------------------------ one-launch round rollback -
@@ -523,7 +574,7 @@ def test_round_rollback_equals_the_two_calls(K, dtype, tree):
     pnp = None if path is None else path.numpy()
     ref = oracle.tape_rollback(osh, S0.double().numpy(), u.double().numpy(), k.double().numpy(),
                                g.double().numpy(), nk.numpy(), pnp)
-    assert rel_fro(outs[0][0].double().numpy(), ref) <= 1e-5
+    check_units("S", outs[0][0], ref, "state", 1e-5)
     cs_ref, wi_ref = oracle.conv_rollback(osh, W.to_f64(cs0), W.to_f64(x), nk.numpy(), pnp)
     np.testing.assert_array_equal(outs[0][1].double().numpy(), cs_ref)
     np.testing.assert_array_equal(outs[0][2].numpy(), wi_ref)
@@ -696,11 +747,9 @@ def test_full_size_fused_rounds_sampled(cfg_id):
         np.testing.assert_array_equal(rb.conv_win[bs].cpu().numpy(), ref1["conv_win"])
     np.testing.assert_array_equal(got["cs"].double().numpy(), ref1["cs_new"])
     for key in ("o", "u", "k"):
-        e = rel_fro(got[key].double().numpy(), ref1[key])
-        assert e <= 1e-4, (key, e)
+        check_units(key, got[key], ref1[key], "tok")
     np.testing.assert_array_equal(got["g"].double().numpy(), ref1["g"])
-    e = rel_fro(got["S"].double().numpy(), ref0["S_new"])
-    assert e <= 1e-4, ("S after the replay", e)
+    check_units("S after the replay", got["S"], ref0["S_new"], "state")
     del fr, rb, inp0, inp1, accs
     torch.cuda.empty_cache()
 
@@ -836,8 +885,8 @@ def test_prefill_matches_sequential_oracle(T, L, B, Hk, Hv, D, K, dtype):
                               want_final=True)
     cs_ref, _ = oracle.conv_rollback(osh, f["conv_state"], f["x"], np.full(B, T, np.int32))
     assert int(err.item()) == 0
-    assert rel_fro(o.cpu().double().numpy(), ref["o"]) <= 1e-4
-    assert rel_fro(S.cpu().double().numpy(), ref["S_final"]) <= 1e-4
+    check_units("o", o, ref["o"], "tok")
+    check_units("S", S, ref["S_final"], "state")
     np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
 
 
@@ -876,8 +925,8 @@ def test_full_size_prefill_sampled():
                               want_final=True)
     cs_ref, _ = oracle.conv_rollback(osh, f["conv_state"], f["x"],
                                      np.full(len(bs), cfg.T, np.int32))
-    assert rel_fro(got_o, ref["o"]) <= 1e-4
-    assert rel_fro(got_S, ref["S_final"]) <= 1e-4
+    check_units("o", got_o, ref["o"], "tok")
+    check_units("S", got_S, ref["S_final"], "state")
     np.testing.assert_array_equal(got_cs, cs_ref)
 
 
@@ -982,11 +1031,9 @@ def test_full_size_vgate_fused_rounds_sampled(cfg_id):
         np.testing.assert_array_equal(got["path"].numpy(), path)
     np.testing.assert_array_equal(got["cs"].double().numpy(), cs2)
     for key in ("o", "u", "k"):
-        e = rel_fro(got[key].double().numpy(), ref[key])
-        assert e <= 1e-4, (key, e)
+        check_units(key, got[key], ref[key], "tok")
     np.testing.assert_array_equal(got["g"].double().numpy(), ref["g"])
-    e = rel_fro(got["S"].double().numpy(), S1)
-    assert e <= 1e-4, ("S after the replay", e)
+    check_units("S after the replay", got["S"], S1, "state")
     del fr, rb, inp0, inp1, accs
     torch.cuda.empty_cache()
 
@@ -1015,8 +1062,7 @@ def test_vgate_verify_matches_oracle(T, L, B, Hk, Hv, D, K, dtype):
     f = {k: W.to_f64(v) for k, v in inp.items()}
     ref = oracle.verify_chunk_vg(osh, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"], f["S0"])
     for name, got in (("o", o), ("u", tape.u), ("k", tape.k)):
-        err = rel_fro(got.cpu().double().numpy(), ref[name])
-        assert err <= 1e-4, (name, err)
+        check_units(name, got, ref[name], "tok")
     np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
     assert torch.equal(d["S0"], S0)
 
@@ -1048,7 +1094,7 @@ def test_vgate_rollback_matches_oracle(D, with_path):
     ref = oracle.tape_rollback_vg(osh, S0.double().numpy(), u.double().numpy(),
                                   k.double().numpy(), g.double().numpy(), nk.numpy(),
                                   None if path is None else path.numpy())
-    assert rel_fro(S.cpu().double().numpy(), ref) <= 1e-5
+    check_units("S", S, ref, "state", 1e-5)
     assert torch.equal(S[:, 0].cpu(), S0[:, 0])  # n = 0: untouched
 
 
@@ -1092,13 +1138,13 @@ def test_vgate_chained_rounds(tree):
         n, path, bonus = oracle.accept(acc["draft"].numpy(), W.to_f64(acc["logits"]), parent)
         np.testing.assert_array_equal(rb.n_keep.cpu().numpy(), n)
         np.testing.assert_array_equal(rb.bonus.cpu().numpy(), bonus)
-        assert rel_fro(rb.o.cpu().double().numpy(), ref["o"]) <= 1e-4
+        check_units("o", rb.o, ref["o"], "tok")
         if tree:
             np.testing.assert_array_equal(rb.path.cpu().numpy(), path)
         oS = oracle.tape_rollback_vg(osh, oS, ref["u"], ref["k"], ref["g"], n,
                                      path if tree else None)
         ocs, _ = oracle.conv_rollback(osh, ocs, f["x"], n, path if tree else None)
-        assert rel_fro(rb.S.cpu().double().numpy(), oS) <= 1e-4
+        check_units("S", rb.S, oS, "state")
         np.testing.assert_array_equal(rb.conv_state.cpu().double().numpy(), ocs)
     assert int(rb.dev_err.item()) == 0
 
@@ -1131,8 +1177,8 @@ def test_vgate_prefill_matches_oracle(T, D, dtype, L, B, Hk, Hv, K):
     f = {k: W.to_f64(v) for k, v in inp.items()}
     ref = oracle.verify_chunk_vg(osh, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"], f["S0"])
     cs_ref, _ = oracle.conv_rollback(osh, f["conv_state"], f["x"], np.full(B, T, np.int32))
-    assert rel_fro(o.cpu().double().numpy(), ref["o"]) <= 1e-4
-    assert rel_fro(S.cpu().double().numpy(), ref["S_final"]) <= 1e-4
+    check_units("o", o, ref["o"], "tok")
+    check_units("S", S, ref["S_final"], "state")
     np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
 
 
@@ -1177,8 +1223,7 @@ def test_vgate_tree_verify_matches_oracle(T, L, B, Hk, Hv, D, K, dtype, depth):
     ref = oracle.tree_verify_vg(osh, parent, f["x"], f["conv_state"], f["conv_w"], f["a"], f["b"],
                                 f["S0"])
     for name, got in (("o", o), ("u", tape.u), ("k", tape.k)):
-        e = rel_fro(got.cpu().double().numpy(), ref[name])
-        assert e <= 1e-4, (name, e)
+        check_units(name, got, ref[name], "tok")
     np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
     np.testing.assert_array_equal(win.cpu().numpy(), ref["conv_win"])
     assert int(err.item()) == 0
@@ -1245,11 +1290,10 @@ def test_vgate_replay_verify_equals_rollback_then_verify(tree, T, pT, D, dtype):
                                      S_rep)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
-    assert rel_fro(S.cpu().double().numpy(), S_rep) <= 1e-5
+    check_units("S", S, S_rep, "state", 1e-5)
     assert torch.equal(S[:, 0].cpu(), inp["S0"][:, 0])  # n = 0: untouched
     for name, got in (("o", o), ("u", tape.u), ("k", tape.k)):
-        e = rel_fro(got.cpu().double().numpy(), ref[name])
-        assert e <= 1e-4, (name, e)
+        check_units(name, got, ref[name], "tok")
     np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
 
 
@@ -1292,19 +1336,19 @@ def test_vgate_tree_replay_bad_inputs_flag(T, pT, D):
     S, o, err = run(bad_par, nk, good_path)
     assert err & gb.DEV_ERR_PARENT
     assert torch.all(o[:, 1] == 7.0)
-    assert rel_fro(S.double().numpy(), S_rep) <= 1e-5  # replay applied to both sequences
+    check_units("S", S, S_rep, "state", 1e-5)  # replay applied to both sequences
     print("vgate bad n_keep", flush=True)
     S, o, err = run(parent, torch.tensor([pT + 1, 2], dtype=torch.int32), good_path)
     assert err & gb.DEV_ERR_N_KEEP
     assert torch.equal(S[:, 0], inp["S0"][:, 0])
-    assert rel_fro(S[:, 1].double().numpy(), S_rep[:, 1]) <= 1e-5
+    check_units("S", S[:, 1], S_rep[:, 1], "state", 1e-5)
     print("vgate bad path", flush=True)
     bad_path = good_path.clone()
     bad_path[0, 1] = pT
     S, o, err = run(parent, nk, bad_path)
     assert err & gb.DEV_ERR_PATH
     assert torch.equal(S[:, 0], inp["S0"][:, 0])
-    assert rel_fro(S[:, 1].double().numpy(), S_rep[:, 1]) <= 1e-5
+    check_units("S", S[:, 1], S_rep[:, 1], "state", 1e-5)
 
 
 @pytest.mark.parametrize("tree,T", [(True, 64), (True, 40), (False, 8), (False, 16)])
@@ -1355,8 +1399,7 @@ def test_vgate_fused_rounds(tree, T):
         tape = fr.tapes[r % 2]
         for name, got, want in (("o", rb.o, ref["o"]), ("u", tape.u, ref["u"]),
                                 ("k", tape.k, ref["k"])):
-            e = rel_fro(got.cpu().double().numpy(), want)
-            assert e <= 1e-4, (r, name, e)
+            check_units("%s, round %d" % (name, r), got, want, "tok")
         np.testing.assert_array_equal(tape.g.cpu().double().numpy(), ref["g"])
         oS = oracle.tape_rollback_vg(osh, oS, ref["u"], ref["k"], ref["g"], n,
                                      path if tree else None)
@@ -1364,5 +1407,5 @@ def test_vgate_fused_rounds(tree, T):
         np.testing.assert_array_equal(rb.conv_state.cpu().double().numpy(), ocs)
     fr.finish(3)
     torch.cuda.synchronize()
-    assert rel_fro(fr.rb.S.cpu().double().numpy(), oS) <= 1e-4
+    check_units("S", fr.rb.S, oS, "state")
     assert int(fr.rb.dev_err.item()) == 0
