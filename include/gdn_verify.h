@@ -55,14 +55,15 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef enum {
   GDN_OK = 0,
   GDN_ERR_INVALID_ARG = 1, /* NULL pointer, bad size or inconsistent shape */
   GDN_ERR_UNSUPPORTED = 2, /* valid but not instantiated (e.g. d_k = 96) */
   GDN_ERR_LAUNCH = 3,      /* the HIP runtime rejected a launch */
-  GDN_ERR_WORKSPACE = 4    /* workspace missing or smaller than required */
+  GDN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  GDN_ERR_SCRATCH = 5      /* input too large for the library's static scratch */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -230,6 +231,27 @@ gdn_status spec_accept_prefix(int32_t B, int32_t T, int32_t V, const int32_t* pa
 
 /* Bytes of device workspace spec_accept_prefix needs for (B, T, V). */
 size_t spec_accept_workspace_bytes(int32_t B, int32_t T, int32_t V);
+
+/* Size of the static device scratch behind spec_accept_prefix_noalloc. */
+#define GDN_ACCEPT_SCRATCH_BYTES (1u << 20)
+
+/*
+ * spec_accept_prefix for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, results and errors, without the workspace.
+ * The argmax partials live in a static device array of
+ * GDN_ACCEPT_SCRATCH_BYTES that each GPU holds from library load until the
+ * process ends; the call allocates nothing.  Limit: it returns
+ * GDN_ERR_SCRATCH, before any launch, when spec_accept_workspace_bytes(B, T,
+ * V) exceeds GDN_ACCEPT_SCRATCH_BYTES, i.e. when B*(T+1) > 131040 rows.
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one
+ * GPU (different streams without ordering, or different host threads) race;
+ * calls ordered on one stream do not.
+ */
+gdn_status spec_accept_prefix_noalloc(int32_t B, int32_t T, int32_t V, const int32_t* parent,
+                                      const int32_t* draft, const void* logits,
+                                      int32_t logits_dtype, int32_t* n_keep, int32_t* path,
+                                      int32_t* bonus, int32_t* dev_err, void* stream);
 
 /*
  * Rejection-sampling acceptance of a draft chain (sampling at temperature

@@ -18,12 +18,15 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
 
-GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH, GDN_ERR_WORKSPACE = range(5)
+(GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_LAUNCH, GDN_ERR_WORKSPACE,
+ GDN_ERR_SCRATCH) = range(6)
+ACCEPT_SCRATCH_BYTES = 1 << 20  # GDN_ACCEPT_SCRATCH_BYTES
 GDN_F32, GDN_BF16 = 0, 1
 DEV_ERR_N_KEEP, DEV_ERR_PARENT, DEV_ERR_PATH, DEV_ERR_TOKEN, DEV_ERR_NAN = 1, 2, 4, 8, 16
 
 EXPORTS = ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
-           "gdn_tree_verify_replay", "spec_accept_prefix", "spec_accept_sample",
+           "gdn_tree_verify_replay", "spec_accept_prefix", "spec_accept_prefix_noalloc",
+           "spec_accept_sample",
            "spec_sample_workspace_bytes", "gdn_prefill", "gdn_prefill_workspace_bytes",
            "gdn_round_rollback",
            "spec_accept_workspace_bytes", "gdn_tape_rollback", "gdn_conv_state_rollback",
@@ -101,6 +104,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_tree_verify_replay.argtypes = [SP, I32, P, P, P, P, P, P, P, P, TP, P, I32, TP, P,
                                              P, P, P]
         L.spec_accept_prefix.argtypes = [I32, I32, I32, P, P, P, I32, P, P, P, P, SZ, P, P]
+        L.spec_accept_prefix_noalloc.argtypes = [I32, I32, I32, P, P, P, I32, P, P, P, P, P]
         L.spec_accept_workspace_bytes.argtypes = [I32, I32, I32]
         L.spec_accept_workspace_bytes.restype = SZ
         L.spec_accept_sample.argtypes = [I32, I32, I32, P, P, I32, ctypes.c_float, P, P, P, P, P,
@@ -117,7 +121,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
         for name in ("gdn_verify_chunk", "gdn_verify_chunk_replay", "gdn_tree_verify",
-                     "gdn_tree_verify_replay", "spec_accept_prefix", "spec_accept_sample",
+                     "gdn_tree_verify_replay", "spec_accept_prefix",
+                     "spec_accept_prefix_noalloc", "spec_accept_sample",
                      "gdn_prefill", "gdn_round_rollback",
                      "gdn_tape_rollback", "gdn_conv_state_rollback", "gdn_abi_version"):
             getattr(L, name).restype = I32
@@ -323,6 +328,28 @@ def spec_accept_prefix(draft, logits, n_keep, path, bonus, workspace, parent=Non
                                     GDN_BF16 if logits.dtype == torch.bfloat16 else GDN_F32,
                                     *args, workspace.data_ptr(), workspace.numel(), de,
                                     _stream(stream)), "spec_accept_prefix")
+
+
+def spec_accept_prefix_noalloc(draft, logits, n_keep, path, bonus, parent=None, dev_err=None,
+                               stream=None):
+    """spec_accept_prefix with the library's static scratch instead of a
+    workspace (no device allocation anywhere in the call)."""
+    B, T = int(draft.shape[0]), int(draft.shape[1])
+    V = int(logits.shape[-1])
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("logits must be float32 or bfloat16")
+    lp = _need(logits, "logits", logits.dtype, (B, T + 1, V))
+    dp = _need(draft, "draft", torch.int32, (B, T), 4)
+    pp = _opt(parent, "parent", torch.int32, (B, T))
+    args = [_need(n_keep, "n_keep", torch.int32, (B,), 4),
+            _need(path, "path", torch.int32, (B, T), 4),
+            _need(bonus, "bonus", torch.int32, (B,), 4)]
+    de = _opt(dev_err, "dev_err", torch.int32, (1,))
+    _dev(draft.device, logits, n_keep, path, bonus, parent, dev_err)
+    _check(lib().spec_accept_prefix_noalloc(B, T, V, pp, dp, lp,
+                                            GDN_BF16 if logits.dtype == torch.bfloat16
+                                            else GDN_F32, *args, de, _stream(stream)),
+           "spec_accept_prefix_noalloc")
 
 
 def spec_sample_workspace_bytes(B: int, T: int, V: int) -> int:

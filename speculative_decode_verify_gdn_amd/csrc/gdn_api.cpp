@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -276,16 +277,33 @@ size_t spec_accept_workspace_bytes(int32_t B, int32_t T, int32_t V) {
   return rows * split * (sizeof(float) + sizeof(int32_t)) + 256;
 }
 
-gdn_status spec_accept_prefix(int32_t B, int32_t T, int32_t V, const int32_t* parent,
-                              const int32_t* draft, const void* logits, int32_t logits_dtype,
-                              int32_t* n_keep, int32_t* path, int32_t* bonus, void* workspace,
-                              size_t workspace_bytes, int32_t* dev_err, void* stream) {
+}  // extern "C"
+
+// Static scratch of spec_accept_prefix_noalloc: the argmax partials.  Each
+// GPU holds its own copy at its own address, kept until the process ends.
+// In host code `scratch` only names the symbol, so kernels take the device
+// address that hipGetSymbolAddress reports for the current device, looked up
+// once per device and kept in `g_scratch` below.
+static __device__ __align__(256) unsigned char scratch[GDN_ACCEPT_SCRATCH_BYTES];
+
+namespace {
+
+gdn_status accept_check(int32_t B, int32_t T, int32_t V, const int32_t* draft,
+                        const void* logits, int32_t logits_dtype, const int32_t* n_keep,
+                        const int32_t* path, const int32_t* bonus) {
   if (B < 1 || T < 1 || V < 1) return GDN_ERR_INVALID_ARG;
   if (logits_dtype != GDN_F32 && logits_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   if (!draft || !logits || !n_keep || !path || !bonus) return GDN_ERR_INVALID_ARG;
   if (T > kMaxT) return GDN_ERR_UNSUPPORTED;
-  const size_t need = spec_accept_workspace_bytes(B, T, V);
-  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  return GDN_OK;
+}
+
+// Launch the two accept kernels with their partial results in `workspace`
+// (spec_accept_workspace_bytes(B, T, V) bytes, any alignment).
+gdn_status accept_launch(int32_t B, int32_t T, int32_t V, const int32_t* parent,
+                         const int32_t* draft, const void* logits, int32_t logits_dtype,
+                         int32_t* n_keep, int32_t* path, int32_t* bonus, void* workspace,
+                         int32_t* dev_err, void* stream) {
   gdn::AcceptArgs a{};
   a.logits = logits;
   a.parent = parent;
@@ -304,6 +322,54 @@ gdn_status spec_accept_prefix(int32_t B, int32_t T, int32_t V, const int32_t* pa
   a.part_val = reinterpret_cast<float*>(base);
   a.part_idx = reinterpret_cast<int32_t*>(base + n * sizeof(float));
   return launch_status(gdn::launch_accept(a, logits_dtype, static_cast<hipStream_t>(stream)));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's address of `scratch`, or nullptr if it cannot be had.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status spec_accept_prefix(int32_t B, int32_t T, int32_t V, const int32_t* parent,
+                              const int32_t* draft, const void* logits, int32_t logits_dtype,
+                              int32_t* n_keep, int32_t* path, int32_t* bonus, void* workspace,
+                              size_t workspace_bytes, int32_t* dev_err, void* stream) {
+  const gdn_status st = accept_check(B, T, V, draft, logits, logits_dtype, n_keep, path, bonus);
+  if (st != GDN_OK) return st;
+  const size_t need = spec_accept_workspace_bytes(B, T, V);
+  if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  return accept_launch(B, T, V, parent, draft, logits, logits_dtype, n_keep, path, bonus,
+                       workspace, dev_err, stream);
+}
+
+gdn_status spec_accept_prefix_noalloc(int32_t B, int32_t T, int32_t V, const int32_t* parent,
+                                      const int32_t* draft, const void* logits,
+                                      int32_t logits_dtype, int32_t* n_keep, int32_t* path,
+                                      int32_t* bonus, int32_t* dev_err, void* stream) {
+  const gdn_status st = accept_check(B, T, V, draft, logits, logits_dtype, n_keep, path, bonus);
+  if (st != GDN_OK) return st;
+  if (spec_accept_workspace_bytes(B, T, V) > GDN_ACCEPT_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
+  void* ws = scratch_ptr();
+  if (!ws) return GDN_ERR_LAUNCH;
+  // every partial is written by the first kernel before the second reads it,
+  // so the buffer needs no clearing between calls
+  return accept_launch(B, T, V, parent, draft, logits, logits_dtype, n_keep, path, bonus, ws,
+                       dev_err, stream);
 }
 
 gdn_status gdn_tape_rollback(const gdn_shape* shape, int32_t T, float* S, const gdn_tape* tape,
@@ -560,6 +626,7 @@ const char* gdn_status_string(int32_t status) {
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
     case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH";
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+    case GDN_ERR_SCRATCH: return "GDN_ERR_SCRATCH";
     default: return "GDN_UNKNOWN_STATUS";
   }
 }

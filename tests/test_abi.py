@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gb.abi_version() == 7
+    assert gb.abi_version() == 8
     assert gb.status_string(0) == "GDN_OK"
     assert gb.status_string(1) == "GDN_ERR_INVALID_ARG"
     assert gb.status_string(4) == "GDN_ERR_WORKSPACE"
@@ -180,3 +180,20 @@ def test_binding_rejects_mismatched_tensors():
         gb._need(x, "x", torch.bfloat16, (1, 1, 4, sh.C))
     with pytest.raises(ValueError):  # host tensor
         gb._need(x, "x", torch.float32, (1, 1, 4, sh.C))
+
+
+def test_noalloc_accept_rejects_oversize_before_launch(lib):
+    """spec_accept_prefix_noalloc refuses, on the host, inputs whose partials
+    exceed the static scratch (B*(T+1) > 131040 rows), and takes the
+    ordinary argument checks first."""
+    P = ctypes.c_void_p
+    call = lambda B, T, V, d=FAKE: lib.spec_accept_prefix_noalloc(
+        B, T, V, None, d, FAKE, gb.GDN_BF16, FAKE, FAKE, FAKE, None, None)
+    assert call(2100, 63, 7) == gb.GDN_ERR_SCRATCH
+    assert call(2017, 64, 7) == gb.GDN_ERR_SCRATCH      # 131105 rows
+    assert gb.spec_accept_workspace_bytes(2017, 64, 7) > gb.ACCEPT_SCRATCH_BYTES
+    assert gb.spec_accept_workspace_bytes(2016, 64, 7) == gb.ACCEPT_SCRATCH_BYTES  # 131040 rows
+    assert call(2, 4, 7, d=None) == gb.GDN_ERR_INVALID_ARG
+    assert call(2, 65, 7) == gb.GDN_ERR_UNSUPPORTED
+    assert gb.status_string(gb.GDN_ERR_SCRATCH) == "GDN_ERR_SCRATCH"
+    del P
