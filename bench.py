@@ -28,6 +28,13 @@ Workloads (seeded synthetic, Qwen3.6-shaped GDN layers: 16 q/k heads and
   --config 4            30 layers, batch 256, N=16 chain, acceptance 0.85
   --config 5            30 layers, batch 64, 64-node draft trees
   --config 1 / 2        tiny and one-layer cases (launch-bound; parity cases)
+`value` is the --config workload's; the run also times the workloads named by
+--also (default 4 and 5) and reports each under other_workloads with the same
+fields.  Every chain workload also reports rejection-sampling acceptance, and
+every workload a rollback sweep (each sequence forced to n accepted steps,
+chain prefixes or tree paths) with its fit t(n) = c0 [n >= 1] + c1 n.  The
+line ends with a measured device-to-device copy rate and the fp64 oracle's
+throughput on the host cores (all threads and one core).
 """
 from __future__ import annotations
 
@@ -65,20 +72,30 @@ def measured_traffic(workload: str):
             h.update(g.read())
     if not w.get("sources") or h.hexdigest() != w.get("source_sha256"):
         return None
-    return w["traffic_bytes"], w["algorithmic_bytes"]
+    return w["traffic_bytes"], w["algorithmic_bytes"], w["source_sha256"]
 
 
 def rollback_sweep(cfg, rb, stream, reps=10):
-    """Rollback time (tape replay + conv window) with every sequence forced
-    to the same accepted length n = 0..T; least-squares fit of
-    t(n) = c0 [n >= 1] + c1 n over n >= 1."""
+    """Rollback time (tape replay + conv window, one gdn_round_rollback over
+    the stack) with every sequence forced to the same accepted length n;
+    least-squares fit of t(n) = c0 [n >= 1] + c1 n over n >= 1.  Chains
+    sweep n = 0..T.  Trees replay along a path of n tape entries (a fixed
+    random order of each sequence's nodes, so the replay gathers its
+    entries), n = 0..8 (the deepest accepted path) and 16, 32, 64."""
     ev = lambda: torch.cuda.Event(enable_timing=True)
     from speculative_decode_verify_gdn_amd import spec_round as sr
+    if cfg.is_tree:
+        gen = torch.Generator(device=rb.path.device).manual_seed(cfg.seed ^ 0x5B)
+        perm = torch.argsort(torch.rand(rb.path.shape, device=rb.path.device, generator=gen), 1)
+        rb.path.copy_(perm.to(torch.int32))
+        ns = [n for n in list(range(9)) + [16, 32, 64] if n <= cfg.T]
+    else:
+        ns = list(range(cfg.T + 1))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         sr.rollback(rb, stream)
     us = []
-    for n in range(cfg.T + 1):
+    for n in ns:
         rb.n_keep.fill_(n)
         for _ in range(2):
             g.replay()
@@ -89,16 +106,22 @@ def rollback_sweep(cfg, rb, stream, reps=10):
         b.record(stream)
         torch.cuda.synchronize()
         us.append(a.elapsed_time(b) / reps * 1e3)
-    ns = np.arange(1, cfg.T + 1)
-    A = np.stack([np.ones_like(ns), ns], 1).astype(np.float64)
-    y = np.array(us[1:])
+    n1 = np.array([n for n in ns if n >= 1], dtype=np.float64)
+    A = np.stack([np.ones_like(n1), n1], 1)
+    y = np.array([t for n, t in zip(ns, us) if n >= 1])
     coef, *_ = np.linalg.lstsq(A, y, rcond=None)
     pred = A @ coef
     r2 = 1.0 - float(np.sum((y - pred) ** 2) / max(np.sum((y - y.mean()) ** 2), 1e-30))
     tape_tok = cfg.Hv * cfg.Dv * 4 + cfg.Hk * cfg.Dk * 4 + cfg.Hv * 4
-    return {"n": list(range(cfg.T + 1)), "us": us, "c0_us": float(coef[0]),
-            "c1_us_per_token": float(coef[1]), "r2": r2,
-            "tape_bytes_per_token_per_stack": cfg.L * cfg.B * tape_tok}
+    tape_stack = cfg.L * cfg.B * tape_tok
+    esz = 2 if cfg.dtype == torch.bfloat16 else 4
+    state_pass = cfg.L * cfg.B * (2 * cfg.Hv * cfg.Dv * cfg.Dk * 4 + 2 * (cfg.K - 1) * cfg.C * esz)
+    return {"path": "tree path (gathered tape entries)" if cfg.is_tree else "chain prefix",
+            "n": ns, "us": us, "t0_us": us[0] if ns[0] == 0 else None,
+            "c0_us": float(coef[0]), "c1_us_per_token": float(coef[1]), "r2": r2,
+            "tape_bytes_per_token_per_stack": tape_stack,
+            "c1_bound_us_at_peak": tape_stack / (HBM_PEAK_GBS * 1e3),
+            "c0_bound_us_at_peak": state_pass / (HBM_PEAK_GBS * 1e3)}
 
 
 def fused_pass(cfg, rbs, shared, stream, steps, warmup, eager):
@@ -181,19 +204,36 @@ def fused_pass(cfg, rbs, shared, stream, steps, warmup, eager):
 
 def sample_accept_pass(cfg, rb, stream, reps, oracle_seqs=2):
     """Rejection-sampling acceptance (spec_accept_sample, temperature 1) on
-    the round's logits and drafts with seeded uniforms: mean time per call of
-    a replayed graph, its algorithmic bytes (every logits row read once, the
-    drawn chunk re-read, partials written and read), and the fp64 oracle's
-    time on `oracle_seqs` sequences scaled to the batch."""
+    the round's drafts and a copy of its logits in which each draft token's
+    logit is reset so that its probability is a seeded draw from U(0.05,
+    0.95) (before bf16 rounding), so drafts are kept and rejected at rates
+    like a real draft model's and both branches (keep, and resample with
+    the rejected token removed) run; seeded uniforms.  Reports the mean time
+    per call of a replayed graph, its algorithmic bytes (every logits row
+    read once, the drawn chunk re-read, partials written and read), the mean
+    kept length, and the fp64 oracle's time on `oracle_seqs` sequences scaled
+    to the batch."""
     from speculative_decode_verify_gdn_amd import binding as gb
     B, T, V = cfg.B, cfg.T, cfg.V
     dev = rb.S.device
     gen = torch.Generator(device=dev).manual_seed(cfg.seed ^ 0x5A)
     uni = torch.rand((B, T + 1), device=dev, generator=gen)
+    p_draft = 0.05 + 0.9 * torch.rand((B, T), device=dev, generator=gen)
+    logits = rb.logits.clone()
+    d = rb.draft.to(torch.int64).unsqueeze(-1)
+    for b0 in range(0, B, 16):  # bounded fp32 temporaries
+        z = logits[b0:b0 + 16, :T].float()
+        lse = torch.logsumexp(z, -1)
+        zd = z.gather(-1, d[b0:b0 + 16]).squeeze(-1)
+        lse_others = lse + torch.log1p(-torch.exp(zd - lse).clamp(max=1 - 1e-7))
+        p = p_draft[b0:b0 + 16]
+        new = (lse_others + torch.log(p / (1 - p))).to(logits.dtype)
+        logits[b0:b0 + 16, :T].scatter_(-1, d[b0:b0 + 16], new.unsqueeze(-1))
+        del z
     i32 = dict(device=dev, dtype=torch.int32)
     n, path, tok = torch.empty((B,), **i32), torch.empty((B, T), **i32), torch.empty((B,), **i32)
     ws = torch.empty((gb.spec_sample_workspace_bytes(B, T, V),), device=dev, dtype=torch.uint8)
-    call = lambda: gb.spec_accept_sample(rb.draft, rb.logits, 1.0, uni, n, path, tok, ws,
+    call = lambda: gb.spec_accept_sample(rb.draft, logits, 1.0, uni, n, path, tok, ws,
                                          dev_err=rb.dev_err)
     ev = lambda: torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
@@ -210,13 +250,13 @@ def sample_accept_pass(cfg, rb, stream, reps, oracle_seqs=2):
         b.record(stream)
         torch.cuda.synchronize()
     us = a.elapsed_time(b) / reps * 1e3
-    esz = 2 if rb.logits.dtype == torch.bfloat16 else 4
+    esz = 2 if logits.dtype == torch.bfloat16 else 4
     split = (V + 4095) // 4096
     byts = B * (T + 1) * V * esz + B * 4096 * esz + 2 * B * (T + 1) * split * 8 \
         + B * T * (4 + esz) + B * (T + 1) * 4 + B * (T + 2) * 4
     import oracle
     k = min(oracle_seqs, B)
-    lg = rb.logits[:k].double().cpu().numpy()
+    lg = logits[:k].double().cpu().numpy()
     dr = rb.draft[:k].cpu().numpy()
     un = uni[:k].double().cpu().numpy()
     t0 = time.perf_counter()
@@ -225,6 +265,7 @@ def sample_accept_pass(cfg, rb, stream, reps, oracle_seqs=2):
     gbs = byts / (us * 1e-6) / 1e9
     return {"us_per_round": us, "algorithmic_bytes": byts, "achieved_GBps": gbs,
             "frac": gbs / HBM_PEAK_GBS, "mean_kept": float(n.float().mean().item()),
+            "draft_probability": "U(0.05, 0.95) per draft position",
             "oracle_us_per_round": o_us, "oracle_sample_sequences": k, "temperature": 1.0}
 
 
@@ -464,8 +505,12 @@ def parse():
     ap.add_argument("--draft-sweep", action="store_true",
                     help="also time rounds at N = 1, 2, 4, 8, 16 drafts and report the draft "
                          "length the host policy picks (chain workloads)")
-    ap.add_argument("--sweep-n", action="store_true",
-                    help="also time rollback with every sequence forced to n = 0..T")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the rollback sweeps (every sequence forced to n accepted steps)")
+    ap.add_argument("--also", default="4,5",
+                    help="comma-separated further workloads timed in the same run and reported "
+                         "under other_workloads (default: the 256-sequence 16-draft stack and "
+                         "the 64-node tree stack; empty for none)")
     return ap.parse_args()
 
 
@@ -507,6 +552,9 @@ def roofline(kernel: str, bytes_per_launch: float, ms_per_launch: float, traffic
             "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
             "traffic": None if traffic is None else traffic[0],
             "traffic_algorithmic_bytes": None if traffic is None else traffic[1],
+            "traffic_source": None if traffic is None else
+            "profiles/verify_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE per launch, "
+            "scaled by a plain copy's counters; sources sha256 %s" % traffic[2][:16],
             "bytes_per_launch": bytes_per_launch}
 
 
@@ -620,35 +668,50 @@ def oracle_baseline(cfg, seconds: float) -> dict:
     del sample
     t = float(np.mean(times))
     t_round = t * (cfg.L * cfg.B) / (L_s * B_s)
+    # the same round on one core: one layer of one sequence, about a fifth of
+    # the time budget
+    oracle.set_num_threads(1)
+    try:
+        one = prepare(1, 1)
+        t1 = [run(one)]
+        while sum(t1) < seconds / 5:
+            t1.append(run(one))
+        del one
+    finally:
+        oracle.set_num_threads(nthr)
+    t1m = float(np.mean(t1))
+    t1_round = t1m * cfg.L * cfg.B
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": cfg.B * cfg.T / t_round, "unit": "tokens/s", "cores": nthr,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": "fp64 oracle round (verify, accept, tape and conv rollback) on %d layers x "
                       "%d sequences of the %d x %d workload, %d repetitions in %.1f s (mean "
                       "%.2f s), scaled by unit count to %.1f s per round"
-                      % (L_s, B_s, cfg.L, cfg.B, len(times), sum(times), t, t_round)}
+                      % (L_s, B_s, cfg.L, cfg.B, len(times), sum(times), t, t_round),
+            "one_core": {"value": cfg.B * cfg.T / t1_round, "unit": "tokens/s", "cores": 1,
+                         "sample": "the same round on 1 layer x 1 sequence, %d repetitions in "
+                                   "%.1f s (mean %.3f s), scaled by unit count to %.1f s per "
+                                   "round" % (len(t1), sum(t1), t1m, t1_round)}}
 
 
 # ------------------------------------------------------------------- main --
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        sys.stderr.write("bench.py measures one GPU only: this build runs on a single MI355X "
-                         "and has no multi-GPU path (got --gpus %d)\n" % args.gpus)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        sys.stderr.write("bench.py needs a GPU\n")
-        sys.exit(2)
-    if args.calib_copy:
-        calib_copy()
-        return
-
+def measure_workload(cfg, args, stream, extras: bool):
+    """Time the workload's rounds (plain, and fused where the library fuses)
+    as replayed HIP graphs, plus per-phase kernel times.  Returns a dict of
+    the round forms with their values, kernel times, byte models and the
+    dominant kernel's roofline, the form the library's rule picks, and (when
+    `extras`) the sampling-acceptance and rollback-sweep measurements."""
     from speculative_decode_verify_gdn_amd import binding as gb
     from speculative_decode_verify_gdn_amd import spec_round as sr
-    from speculative_decode_verify_gdn_amd import workload as W
-    gb.lib()  # fail loudly if the HIP library is missing
-
-    cfg = W.CONFIGS[args.config]
     dev = "cuda"
     torch.cuda.empty_cache()
     base, sets = build_sets(cfg, args.input_sets, dev)
@@ -669,7 +732,6 @@ def main():
         if shared is None:
             shared = rb
         rbs.append(rb)
-    stream = torch.cuda.Stream()
     n_hist = torch.zeros((args.steps, cfg.B), dtype=torch.int32, device=dev)
 
     graphs = []
@@ -736,6 +798,7 @@ def main():
             s1.record(stream)
             r_ms.append((s0, s1))
         torch.cuda.synchronize()
+        del phase_graphs, graphs
     verify_ms = float(np.mean([a.elapsed_time(b) for a, b in v_ms])) / cfg.L
     accept_ms = float(np.mean([a.elapsed_time(b) for a, b in a_ms]))
     rollback_ms = float(np.mean([a.elapsed_time(b) for a, b in r_ms]))
@@ -745,48 +808,29 @@ def main():
     mode = args.round if args.round != "auto" else ("fused" if pays else "plain")
     fusable = fused_kernel(cfg)
     if mode == "fused" and not fusable:
-        sys.stderr.write("the library fuses chains of at most 16 drafts and trees of 33..64 "
-                         "nodes (bf16, 128-dim heads) only\n")
-        sys.exit(2)
+        raise SystemExit("the library fuses chains of at most 16 drafts and trees of 33..64 "
+                         "nodes (bf16, 128-dim heads) only")
     fused = None
     if fusable:
         fused = fused_pass(cfg, rbs, shared, stream, args.steps, args.warmup, args.eager)
 
-    sampled = None
-    if not cfg.is_tree:
-        sampled = sample_accept_pass(cfg, rbs[0], stream, args.steps)
-
-    pre = prefill_pass(cfg, args.prefill, stream) if args.prefill > 0 else None
-    pre_vg = (prefill_pass(cfg, args.prefill, stream, gate_per_key=True)
-              if args.prefill > 0 and args.gate_per_key and not cfg.is_tree else None)
-    vgate = vgate_pass(cfg, stream, args.steps) if args.gate_per_key else None
-
-    dsweep = None
-    if args.draft_sweep and not cfg.is_tree:
-        dsweep = draft_sweep(cfg, stream)
-
-    sweep = None
-    if args.sweep_n and not cfg.is_tree:
-        with torch.cuda.stream(stream):
-            sweep = rollback_sweep(cfg, rbs[0], stream)
-
     B, T = cfg.B, cfg.T
     vb = verify_bytes_per_launch(cfg, B)
-    # plain round: L verifies, accept, state + conv rollback
     ms = total_ms / args.steps
     n_keep = n_hist.cpu().numpy()
     plain_bytes = float(np.mean([cfg.L * vb + accept_bytes(cfg, B) + rollback_bytes(cfg, n_keep[i])
                                  + conv_rollback_bytes(cfg, n_keep[i]) for i in range(args.steps)]))
+    rb_bytes = float(np.mean([rollback_bytes(cfg, n_keep[i]) + conv_rollback_bytes(cfg, n_keep[i])
+                              for i in range(args.steps)]))
     rounds = {"plain": {
         "value": B * T / (ms * 1e-3), "ms_per_step": ms, "n_keep": n_keep,
         "round_bytes": plain_bytes,
         "kernel_ms": {"verify_per_layer": verify_ms, "accept": accept_ms,
                       "rollback_state_and_conv": rollback_ms},
+        "rollback_hbm_frac": rb_bytes / (rollback_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": roofline(verify_kernel_name(cfg), vb, verify_ms,
                              measured_traffic(cfg.name))}}
     if fused is not None:
-        # fused round: L verifies that each replay the previous round's prefix,
-        # accept, conv rollback
         fms = fused["ms"]
         nk, npv = fused["n_keep"], fused["n_prev"]
         fvb = float(np.mean([fused_verify_bytes(cfg, B, npv[i]) for i in range(args.steps)]))
@@ -799,52 +843,151 @@ def main():
                           "accept_and_conv_rollback": fused["accept_conv_ms"]},
             "roofline": roofline(verify_kernel_name(cfg, fused=True), fvb, fused["verify_replay_ms"],
                                  measured_traffic(cfg.name + "_fused"))}
+    res = {"cfg": cfg, "rounds": rounds, "mode": mode, "input_sets": len(rbs)}
+    if extras:
+        if not cfg.is_tree:
+            res["sample_accept"] = sample_accept_pass(cfg, rbs[0], stream, args.steps)
+        if not args.no_sweep:
+            with torch.cuda.stream(stream):
+                res["rollback_sweep"] = rollback_sweep(cfg, rbs[0], stream)
+    del rbs, shared, sets, base, S, cs, conv_w
+    torch.cuda.empty_cache()
+    return res
+
+
+def summary(res, steps) -> dict:
+    """The bench line's fields for one workload: the timed form's value and
+    round time, both forms, accepted / committed rates and roofline."""
+    cfg, rounds, mode = res["cfg"], res["rounds"], res["mode"]
     r = rounds[mode]
     ms = r["ms_per_step"]
-    acc_tok = float(r["n_keep"].sum()) / args.steps
+    acc_tok = float(r["n_keep"].sum()) / steps
+    unit = "nodes" if cfg.is_tree else "tokens"
+    return {
+        "value": r["value"], "unit": unit + "/s", "ms_per_step": ms, "round": mode,
+        "accepted_tokens_per_s": acc_tok / (ms * 1e-3),
+        "committed_tokens_per_s": (acc_tok + cfg.B) / (ms * 1e-3),
+        "round_hbm_frac": r["round_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "round_algorithmic_bytes": r["round_bytes"],
+        "kernel_ms": r["kernel_ms"],
+        "roofline": r["roofline"],
+        "rounds": {k: dict({"value": v["value"], "ms_per_step": v["ms_per_step"],
+                            "kernel_ms": v["kernel_ms"],
+                            "verify_kernel": v["roofline"]["kernel"],
+                            "verify_bytes_per_launch": v["roofline"]["bytes_per_launch"],
+                            "verify_roofline_frac": v["roofline"]["frac"],
+                            "round_hbm_frac": v["round_bytes"] / (v["ms_per_step"] * 1e-3) / 1e9
+                            / HBM_PEAK_GBS},
+                           **({"rollback_hbm_frac": v["rollback_hbm_frac"]}
+                              if "rollback_hbm_frac" in v else {}))
+                   for k, v in rounds.items()},
+    }
+
+
+def config_fields(cfg, args, mode, n_sets) -> dict:
+    return {"workload": cfg.name, "layers": cfg.L, "batch": cfg.B,
+            "drafts" if not cfg.is_tree else "tree_nodes": cfg.T,
+            "acceptance": (cfg.p_accept if cfg.law == "bernoulli" else cfg.law),
+            "k_heads": cfg.Hk, "v_heads": cfg.Hv, "d_k": cfg.Dk, "d_v": cfg.Dv,
+            "conv_kernel": cfg.K, "inputs": "bf16" if cfg.dtype == torch.bfloat16 else "f32",
+            "state": "f32", "vocab": cfg.V, "hip_graph": not args.eager,
+            "input_sets": n_sets, "round": mode}
+
+
+def copy_bandwidth(n_bytes=1 << 30, reps=10) -> dict:
+    """Device-to-device copy rate (read + write bytes / time), median of reps."""
+    a = torch.empty(n_bytes // 4, device="cuda", dtype=torch.float32).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    del a, b
+    torch.cuda.empty_cache()
+    gbs = 2 * n_bytes / (ms * 1e-3) / 1e9
+    return {"bytes_copied": n_bytes, "ms": ms, "GBps_read_plus_write": gbs,
+            "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU only: this build runs on a single MI355X "
+                         "and has no multi-GPU path (got --gpus %d)\n" % args.gpus)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py needs a GPU\n")
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+
+    from speculative_decode_verify_gdn_amd import binding as gb
+    from speculative_decode_verify_gdn_amd import workload as W
+    gb.lib()  # fail loudly if the HIP library is missing
+
+    cfg = W.CONFIGS[args.config]
+    stream = torch.cuda.Stream()
+    res = measure_workload(cfg, args, stream, extras=True)
+    head = summary(res, args.steps)
     out = {
         "metric": "verified draft tokens/s per 30-layer GDN stack",
-        "value": r["value"],
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "layers": cfg.L, "batch": B,
-                   "drafts" if not cfg.is_tree else "tree_nodes": T,
-                   "acceptance": (cfg.p_accept if cfg.law == "bernoulli" else cfg.law),
-                   "k_heads": cfg.Hk, "v_heads": cfg.Hv, "d_k": cfg.Dk, "d_v": cfg.Dv,
-                   "conv_kernel": cfg.K, "inputs": "bf16" if cfg.dtype == torch.bfloat16 else "f32",
-                   "state": "f32", "vocab": cfg.V, "hip_graph": not args.eager,
-                   "input_sets": len(rbs), "round": mode},
-        "accepted_tokens_per_s": acc_tok / (ms * 1e-3),
-        "committed_tokens_per_s": (acc_tok + B) / (ms * 1e-3),
-        "round_hbm_frac": r["round_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "round_algorithmic_bytes": r["round_bytes"],
-        "kernel_ms": r["kernel_ms"],
-        "roofline": r["roofline"],
-        "rounds": {k: {"value": v["value"], "ms_per_step": v["ms_per_step"],
-                       "kernel_ms": v["kernel_ms"],
-                       "verify_bytes_per_launch": v["roofline"]["bytes_per_launch"],
-                       "verify_roofline_frac": v["roofline"]["frac"]} for k, v in rounds.items()},
+        "config": config_fields(cfg, args, res["mode"], res["input_sets"]),
     }
-    if sampled is not None:
-        out["sample_accept"] = sampled
-    if pre is not None:
-        out["prefill"] = pre
-    if pre_vg is not None:
-        out["prefill_per_key_gate"] = pre_vg
-    if vgate is not None:
-        out["per_key_gate"] = vgate
-    if dsweep is not None:
-        out["draft_policy"] = dsweep
-    if sweep is not None:
-        out["rollback_sweep"] = sweep
+    out.update({k: v for k, v in head.items()
+                if k not in ("value", "unit", "ms_per_step", "round")})
+    for k in ("sample_accept", "rollback_sweep"):
+        if k in res:
+            out[k] = res[k]
+    del res
+
+    others = {}
+    for cid in [int(c) for c in args.also.split(",") if c.strip()]:
+        if cid == args.config:
+            continue
+        ocfg = W.CONFIGS[cid]
+        print("bench: %s" % ocfg.name, file=sys.stderr, flush=True)
+        ores = measure_workload(ocfg, args, stream, extras=not args.no_sweep)
+        o = summary(ores, args.steps)
+        o["config"] = config_fields(ocfg, args, ores["mode"], ores["input_sets"])
+        if "rollback_sweep" in ores:
+            o["rollback_sweep"] = ores["rollback_sweep"]
+        if "sample_accept" in ores:
+            o["sample_accept"] = ores["sample_accept"]
+        others[ocfg.name] = o
+        del ores
+    if others:
+        out["other_workloads"] = others
+
+    if args.prefill > 0:
+        out["prefill"] = prefill_pass(cfg, args.prefill, stream)
+        if args.gate_per_key and not cfg.is_tree:
+            out["prefill_per_key_gate"] = prefill_pass(cfg, args.prefill, stream,
+                                                       gate_per_key=True)
+    if args.gate_per_key:
+        out["per_key_gate"] = vgate_pass(cfg, stream, args.steps)
+    if args.draft_sweep and not cfg.is_tree:
+        out["draft_policy"] = draft_sweep(cfg, stream)
+    out["copy_bandwidth"] = copy_bandwidth()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = oracle_baseline(cfg, args.cpu_seconds)
     print(json.dumps(out), flush=True)

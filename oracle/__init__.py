@@ -124,6 +124,8 @@ def _load():
         lib.oracle_conv_rollback.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
+        lib.oracle_set_num_threads.argtypes = [I]
+        lib.oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -153,6 +155,11 @@ def _check(rc: int, what: str):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Worker threads of later oracle calls (used to time it on one core)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def conv_chain(state, x, w, silu: bool = True) -> np.ndarray:

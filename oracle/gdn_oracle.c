@@ -636,6 +636,15 @@ int oracle_conv_rollback(const oshape* sh, int T, double* conv_state,
   return ORACLE_OK;
 }
 
+/* Set the number of worker threads of later OpenMP regions (timing only). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Number of worker threads an OpenMP region would use (1 without OpenMP). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP
