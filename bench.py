@@ -91,21 +91,23 @@ def rollback_sweep(cfg, rb, stream, reps=10):
         ns = [n for n in list(range(9)) + [16, 32, 64] if n <= cfg.T]
     else:
         ns = list(range(cfg.T + 1))
+    # `reps` calls in one graph, so that a short call is timed on the GPU
+    # and not by the host's graph-launch rate
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
-        sr.rollback(rb, stream)
+        for _ in range(reps):
+            sr.rollback(rb, stream)
     us = []
     for n in ns:
         rb.n_keep.fill_(n)
-        for _ in range(2):
-            g.replay()
+        g.replay()
         a, b = ev(), ev()
         a.record(stream)
-        for _ in range(reps):
+        for _ in range(2):
             g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        us.append(a.elapsed_time(b) / reps * 1e3)
+        us.append(a.elapsed_time(b) / (2 * reps) * 1e3)
     n1 = np.array([n for n in ns if n >= 1], dtype=np.float64)
     A = np.stack([np.ones_like(n1), n1], 1)
     y = np.array([t for n, t in zip(ns, us) if n >= 1])

@@ -11,8 +11,12 @@
 // touching the state, so the cost is one state pass plus O(n) tape bytes.
 //
 // Layout: one 256-thread workgroup per (layer, seq, v-head, RB-row block);
-// every thread owns 4 float4 of the block, read and written fully coalesced.
-// The block's n tape rows (k: n x Dk, w-scaled u: n x RB) are staged in LDS.
+// every thread owns 4 float4 of the block, read and written fully coalesced
+// (whole cache lines), and many small workgroups per CU keep the state
+// streaming.  The block's n tape rows (k: n x Dk, w-scaled u: n x RB) are
+// staged in LDS, the rank-n update U = sum_i w_i u_i k_i^T is formed on fp32
+// MFMA (four steps per instruction), and it reaches the threads' layout
+// through LDS: S_n = gamma S0 + U.
 //
 // Conv window: new row j = row n+j of [old window; x[p_0]; ...; x[p_{n-1}]],
 // copied 16 bytes per thread; all sources are loaded before any store, so
@@ -37,8 +41,18 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
   constexpr int TM = 64;                  // longest tape
   static_assert(DV % RB == 0 && NV <= NT * VPT, "row blocks");
 
-  __shared__ __align__(16) float s_k[CH * DK];
-  __shared__ float s_u[CH * RB];
+  // the rank-n update on fp32 MFMA: 16x16 tiles of the RB x DK block, TPW
+  // per wave; the tiles go to the thread layout of the state through LDS
+  constexpr int NRT = RB / 16, NCT = DK / 16, TPW = NRT * NCT / 4;
+  constexpr int ULD = DK + 4;  // padded row stride of the update in LDS
+  constexpr int NSTAGE = CH * DK + CH * RB;
+  constexpr int NBUF = NSTAGE > RB * ULD ? NSTAGE : RB * ULD;
+  static_assert(NRT * NCT % 4 == 0, "tiles per wave");
+  // staged tape (k rows, w-scaled u slice); reused for the update once the
+  // products are done
+  __shared__ __align__(16) float s_buf[NBUF];
+  float* const s_k = s_buf;
+  float* const s_u = s_buf + CH * DK;
   __shared__ float s_w[TM];
   __shared__ int s_pi[TM];
   __shared__ int s_bad;
@@ -88,9 +102,14 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
   }
   __syncthreads();
   const float gam = s_w[0] * p.tg[(lb * T + s_pi[0]) * p.Hv + hv];
-  floatx4 acc[VPT];
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int c16 = lane & 15, kk = lane >> 4;
+  // U = sum_i (w_i u_i) k_i^T as transposed tiles D[j][r] = sum_i k_i[j]
+  // (w_i u_i)[r] on mfma_f32_16x16x4f32 (four steps per instruction): lane
+  // (c16, kk) of tile (rt, ct) ends holding U[16 rt + c16][16 ct + 4 kk .. +3]
+  floatx4 ut[TPW];
 #pragma unroll
-  for (int v = 0; v < VPT; ++v) acc[v] = sv[v] * gam;
+  for (int m = 0; m < TPW; ++m) ut[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   for (int i0 = 0; i0 < n; i0 += CH) {
     const int nc = n - i0 < CH ? n - i0 : CH;
@@ -105,29 +124,39 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
       s_u[e] = s_w[i0 + i] * p.tu[((lb * T + s_pi[i0 + i]) * p.Hv + hv) * DV + r0 + r];
     }
     __syncthreads();
+    for (int s4 = 0; s4 < nc; s4 += 4) {
+      const int i = s4 + kk;  // this lane's step; steps past the chunk add zero
+      const bool on = i < nc;
+      const int ii = on ? i : 0;
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const int e = tid + v * NT;
-      const int r = (e % NV) / C4, c = (e % C4) * 4;
-      for (int i = 0; i < nc; ++i) {
-        const float u = s_u[i * RB + r];
-        const floatx4 k = *reinterpret_cast<const floatx4*>(s_k + i * DK + c);
-        acc[v][0] = fmaf(u, k[0], acc[v][0]);
-        acc[v][1] = fmaf(u, k[1], acc[v][1]);
-        acc[v][2] = fmaf(u, k[2], acc[v][2]);
-        acc[v][3] = fmaf(u, k[3], acc[v][3]);
+      for (int m = 0; m < TPW; ++m) {
+        const int j = wave * TPW + m;
+        const int rt = j / NCT, ct = j % NCT;
+        const float a = s_k[ii * DK + 16 * ct + c16];
+        const float b = s_u[ii * RB + 16 * rt + c16];
+        ut[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(on ? a : 0.f, on ? b : 0.f, ut[m], 0, 0, 0);
       }
     }
   }
+  __syncthreads();  // every wave is done with the staged tape
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int j = wave * TPW + m;
+    const int rt = j / NCT, ct = j % NCT;
+    *reinterpret_cast<floatx4*>(s_buf + (16 * rt + c16) * ULD + 16 * ct + 4 * kk) = ut[m];
+  }
+  __syncthreads();
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int e = tid + v * NT;
-    if (e < NV) reinterpret_cast<floatx4*>(Sblk)[e] = acc[v];
+    const int r = (e % NV) / C4, c = (e % C4) * 4;
+    const floatx4 acc = sv[v] * gam + *reinterpret_cast<const floatx4*>(s_buf + r * ULD + c);
+    if (e < NV) reinterpret_cast<floatx4*>(Sblk)[e] = acc;
   }
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_tape_rollback(RollbackArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_tape_rollback(RollbackArgs p) {
   tape_rollback_body<DK, DV>(p, blockIdx.x);
 }
 
@@ -355,7 +384,7 @@ namespace {
 // the conv-window ones, which fill the tail of the state pass.  Built for
 // the common conv width (K = 4); other widths take the two launches.
 template <int DK, int DV, int ESZ>
-__global__ __launch_bounds__(256) void k_round_rollback(RollbackArgs r, ConvRollbackArgs c,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_round_rollback(RollbackArgs r, ConvRollbackArgs c,
                                                         int n_state, int conv_y) {
   const int bid = blockIdx.x;
   if (bid < n_state) {

@@ -580,6 +580,56 @@ def test_round_rollback_equals_the_two_calls(K, dtype, tree):
     np.testing.assert_array_equal(outs[0][2].numpy(), wi_ref)
 
 
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("tree", [False, True])
+def test_rollback_every_accepted_length(D, tree):
+    """gdn_tape_rollback and gdn_round_rollback with sequence b replaying
+    n = b steps of a 64-entry tape, for every n in 0..64 (chains, and paths
+    in a random order of tape entries): the state equals the oracle's
+    tape_rollback per (layer, seq, v-head), the conv window and its indices
+    the oracle's conv_rollback exactly."""
+    _need_gpu()
+    T, B, L = 64, 65, 2
+    sh = gb.GdnShape(L, B, 2, 4, D, D, 4, True, 1e-6, torch.bfloat16)
+    gen = torch.Generator().manual_seed(400 + D + tree)
+    S0 = torch.randn((L, B, 4, D, D), generator=gen) * 0.1
+    u = torch.randn((L, B, T, 4, D), generator=gen)
+    k = torch.nn.functional.normalize(torch.randn((L, B, T, 2, D), generator=gen), dim=-1)
+    g = 0.6 + 0.4 * torch.rand((L, B, T, 4), generator=gen)
+    cs0 = torch.randn((L, B, 3, sh.C), generator=gen).to(torch.bfloat16)
+    x = torch.randn((L, B, T, sh.C), generator=gen).to(torch.bfloat16)
+    nk = torch.arange(B, dtype=torch.int32)
+    path = None
+    if tree:
+        path = torch.full((B, T), -1, dtype=torch.int32)
+        for bb in range(B):
+            path[bb, :bb] = torch.randperm(T, generator=gen)[:bb].to(torch.int32)
+    tape = gb.Tape(u.to(DEV), k.to(DEV), g.to(DEV))
+    pd = None if path is None else path.to(DEV)
+    osh = oracle.Shape(L=L, B=B, Hk=2, Hv=4, Dk=D, Dv=D, K=4, silu=True, eps=1e-6)
+    pnp = None if path is None else path.numpy()
+    ref = oracle.tape_rollback(osh, S0.double().numpy(), u.double().numpy(), k.double().numpy(),
+                               g.double().numpy(), nk.numpy(), pnp)
+    cs_ref, wi_ref = oracle.conv_rollback(osh, W.to_f64(cs0), W.to_f64(x), nk.numpy(), pnp)
+    print("rollback every n", D, tree, flush=True)
+    S = S0.to(DEV).clone()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_tape_rollback(sh, S, tape, nk.to(DEV), path=pd, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    check_units("S (tape rollback)", S, ref, "state", 1e-5)
+    assert torch.equal(S[:, 0].cpu(), S0[:, 0])  # n = 0: untouched
+    S, cs = S0.to(DEV).clone(), cs0.to(DEV).clone()
+    wi = torch.full((B, 3), -9, dtype=torch.int32, device=DEV)
+    gb.gdn_round_rollback(sh, S, tape, cs, x.to(DEV), nk.to(DEV), path=pd, win_idx=wi,
+                          dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    check_units("S (round rollback)", S, ref, "state", 1e-5)
+    np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
+    np.testing.assert_array_equal(wi.cpu().numpy(), wi_ref)
+
+
 # ------------------------------------------------------- device-side errors -
 
 def test_dev_err_bad_n_keep_leaves_state():
