@@ -91,16 +91,21 @@ __global__ __launch_bounds__(256) void k_argmax_part(AcceptArgs p) {
         }
       }
     };
-    constexpr int U = 4;  // vectors in flight per thread
-    int q = vbeg + tid;
-    for (; q + (U - 1) * NT < vend; q += U * NT) {
+    constexpr int U = 8;  // vectors in flight per thread (a whole bf16 chunk in one batch)
+    // Every load of a batch is issued before any is scanned; a load past
+    // the chunk reads the batch's first vector (a valid address) and is not
+    // scanned.
+    for (int q = vbeg + tid; q < vend; q += U * NT) {
       uint4 w[U];
 #pragma unroll
-      for (int j = 0; j < U; ++j) w[j] = vp[q + j * NT];
+      for (int j = 0; j < U; ++j) {
+        const int qj = q + j * NT;
+        w[j] = vp[qj < vend ? qj : q];
+      }
 #pragma unroll
-      for (int j = 0; j < U; ++j) scan(w[j], (q + j * NT) * EPV);
+      for (int j = 0; j < U; ++j)
+        if (q + j * NT < vend) scan(w[j], (q + j * NT) * EPV);
     }
-    for (; q < vend; q += NT) scan(vp[q], q * EPV);
     for (int i = vend * EPV + tid; i < end; i += NT) {  // ragged tail
       const float v = ESZ == 2 ? ld_in(reinterpret_cast<const uint16_t*>(base), i)
                                : ld_in(reinterpret_cast<const float*>(base), i);
@@ -206,9 +211,12 @@ __global__ __launch_bounds__(64) void k_accept_walk(AcceptArgs p) {
 
 void accept_split(int B, int T, int V, int* split, int* chunk) {
   const long long rows = static_cast<long long>(B) * (T + 1);
-  // Aim for ~2048 workgroups in flight, chunks of at least 4096 elements,
+  // At least ~2048 workgroups, and chunks of at most 16384 elements (one
+  // batch of eight 16-byte loads per thread for bf16), but of at least 4096;
   // chunk a multiple of 8 so vector loads stay aligned.
   long long sp = (2048 + rows - 1) / rows;
+  const long long min_sp = (V + 16383) / 16384;
+  if (sp < min_sp) sp = min_sp;
   const long long max_sp = (V + 4095) / 4096;
   if (sp > max_sp) sp = max_sp;
   if (sp < 1) sp = 1;
