@@ -56,6 +56,8 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
   __shared__ float s_w[TM];
   __shared__ int s_pi[TM];
   __shared__ int s_bad;
+  __shared__ float s_gam;
+  static_assert(TM == kWave, "one lane per tape step");
 
   const int tid = threadIdx.x;
   const int rblk = bid % NRBLK;
@@ -95,13 +97,24 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
     if (tid == 0 && p.dev_err && l == 0 && hv == 0 && rblk == 0) atomicOr(p.dev_err, GDN_DEV_ERR_PATH);
     return;
   }
-  if (tid < n) {  // w_i = prod_{j>i} g_{p_j}
-    float w = 1.f;
-    for (int j = tid + 1; j < n; ++j) w *= p.tg[(lb * T + s_pi[j]) * p.Hv + hv];
-    s_w[tid] = w;
+  if (tid < kWave) {
+    // wave 0, one lane per step: every gate load in flight at once, then
+    // w_i = prod_{j>i} g_{p_j} by a suffix-product scan (shuffles on every
+    // lane) and gamma = prod_j g_{p_j}
+    const float gv = tid < n ? p.tg[(lb * T + s_pi[tid]) * p.Hv + hv] : 1.f;
+    float xs = gv;  // inclusive suffix product prod_{j >= lane} g_j
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float y = __shfl_down(xs, o, kWave);
+      if (tid + o < kWave) xs *= y;
+    }
+    float w = __shfl_down(xs, 1, kWave);
+    if (tid == kWave - 1) w = 1.f;
+    if (tid < n) s_w[tid] = w;
+    if (tid == 0) s_gam = xs;
   }
   __syncthreads();
-  const float gam = s_w[0] * p.tg[(lb * T + s_pi[0]) * p.Hv + hv];
+  const float gam = s_gam;
   const int wave = tid / kWave, lane = tid % kWave;
   const int c16 = lane & 15, kk = lane >> 4;
   // U = sum_i (w_i u_i) k_i^T as transposed tiles D[j][r] = sum_i k_i[j]
