@@ -120,7 +120,9 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
 
   __shared__ __align__(16) unsigned char s_r1[LY::R1];  // pre-split [K;Q], later [Ti;M2]
   __shared__ __align__(16) unsigned char s_r2[LY::R2];  // raw staging, later V/RHS + packed
-  __shared__ __align__(16) float s_w[NSEG * TR_D * KM]; // conv weights [channel][tap]
+  // conv weights [segment][e][li][tap] for channel 8 li + e of the segment:
+  // the conv's 16-lane groups read them as consecutive 16-byte chunks
+  __shared__ __align__(16) float s_w[NSEG * TR_D * KM];
   __shared__ unsigned long long s_anc[TR_T];            // proper-ancestor masks
   __shared__ int s_par[TR_T], s_dep[TR_T], s_off[TR_T];
   __shared__ __align__(16) int s_widx[TR_T * KM];       // conv window: staging byte offsets
@@ -341,7 +343,11 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
 #pragma unroll
   for (int q = 0; q < NWL; ++q) {
     const int e = tid + q * TR_NT;
-    if (e < NSEG * TR_D * KM) s_w[e] = wv[q];
+    if (e < NSEG * TR_D * KM) {
+      const int c = e / KM, j = e % KM;  // loaded as [channel][tap]
+      const int sg = c / TR_D, cc = c % TR_D;
+      s_w[((sg * 8 + cc % 8) * 16 + cc / 8) * KM + j] = wv[q];
+    }
   }
   __syncthreads();  // (B_a) staging, weights, node structure
   if constexpr (RP) {
@@ -554,7 +560,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
     for (int j = 0; j < KM; ++j)
       xv[j] = *reinterpret_cast<const u32x4*>(s_r2 + wi[j] + sg * 256 + li * 16);
     float y[8];
-    const float* wrow = s_w + (sg * TR_D + 8 * li) * KM;
+    const float* wrow = s_w + (sg * TR_D + li) * KM;  // + 16 KM per channel step e
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float acc = 0.f;
@@ -562,7 +568,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
       for (int j = 0; j < KM; ++j) {
         const uint32_t wd = xv[j][e / 2];
         const float xe = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
-        acc = fmaf(wrow[e * KM + j], xe, acc);
+        acc = fmaf(wrow[e * 16 * KM + j], xe, acc);
       }
       if (p.silu) acc = silu_t(acc);
       y[e] = t < T ? acc : 0.f;
