@@ -28,7 +28,10 @@
 namespace gdn {
 namespace {
 
-template <int DK, int DV>
+// LT (tapes longer than 16 steps, several staging chunks): each chunk's
+// loads all go out together, at a lower occupancy; shorter tapes keep one
+// load per thread in flight and eight waves per SIMD.
+template <int DK, int DV, bool LT>
 __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bid) {
   constexpr int NT = 256;
   constexpr int VPT = 4;                  // float4 per thread
@@ -60,10 +63,25 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
   static_assert(TM == kWave, "one lane per tape step");
 
   const int tid = threadIdx.x;
-  const int rblk = bid % NRBLK;
-  const int rest = bid / NRBLK;
-  const int hv = rest % p.Hv;
-  const size_t lb = rest / p.Hv;
+  int rblk, hv;
+  size_t lb;
+  if constexpr (LT) {
+    // long tapes: the G v-heads x NRBLK row blocks of one (layer, seq,
+    // k-head) read the same k rows n times over; they take consecutive slots
+    // of one XCD (workgroup i runs on XCD i mod 8) so the rows come from
+    // that XCD's L2 after the first read
+    const int G = p.Hv / p.Hk;
+    const UnitSub us = xcd_unit_sub(bid, G * NRBLK);
+    if (us.unit >= p.L * p.B * p.Hk) return;
+    rblk = us.sub % NRBLK;
+    hv = (us.unit % p.Hk) * G + us.sub / NRBLK;
+    lb = us.unit / p.Hk;
+  } else {
+    rblk = bid % NRBLK;
+    const int rest = bid / NRBLK;
+    hv = rest % p.Hv;
+    lb = rest / p.Hv;
+  }
   const int bb = static_cast<int>(lb % p.B);
   const int l = static_cast<int>(lb / p.B);
   const int T = p.T;
@@ -127,14 +145,45 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
   for (int i0 = 0; i0 < n; i0 += CH) {
     const int nc = n - i0 < CH ? n - i0 : CH;
     if (i0 > 0) __syncthreads();  // previous chunk consumed
-    for (int e = tid; e < nc * C4; e += NT) {
-      const int i = e / C4, c4 = e % C4;
-      reinterpret_cast<floatx4*>(s_k)[e] =
-          reinterpret_cast<const floatx4*>(p.tk + ((lb * T + s_pi[i0 + i]) * p.Hk + hk) * DK)[c4];
-    }
-    for (int e = tid; e < nc * RB; e += NT) {
-      const int i = e / RB, r = e % RB;
-      s_u[e] = s_w[i0 + i] * p.tu[((lb * T + s_pi[i0 + i]) * p.Hv + hv) * DV + r0 + r];
+    if constexpr (LT) {
+      // every load of the chunk first (clamped, valid addresses), then the
+      // LDS stores
+      constexpr int KPT = (CH * C4 + NT - 1) / NT;  // k float4 per thread
+      constexpr int UPT = (CH * RB + NT - 1) / NT;  // u floats per thread
+      floatx4 kr[KPT];
+      float ur[UPT];
+#pragma unroll
+      for (int q = 0; q < KPT; ++q) {
+        const int e = tid + q * NT;
+        const int i = e < nc * C4 ? e / C4 : nc - 1, c4 = e % C4;
+        kr[q] = reinterpret_cast<const floatx4*>(p.tk + ((lb * T + s_pi[i0 + i]) * p.Hk + hk) * DK)[c4];
+      }
+#pragma unroll
+      for (int q = 0; q < UPT; ++q) {
+        const int e = tid + q * NT;
+        const int i = e < nc * RB ? e / RB : nc - 1, r = e % RB;
+        ur[q] = s_w[i0 + i] * p.tu[((lb * T + s_pi[i0 + i]) * p.Hv + hv) * DV + r0 + r];
+      }
+#pragma unroll
+      for (int q = 0; q < KPT; ++q) {
+        const int e = tid + q * NT;
+        if (e < nc * C4) reinterpret_cast<floatx4*>(s_k)[e] = kr[q];
+      }
+#pragma unroll
+      for (int q = 0; q < UPT; ++q) {
+        const int e = tid + q * NT;
+        if (e < nc * RB) s_u[e] = ur[q];
+      }
+    } else {
+      for (int e = tid; e < nc * C4; e += NT) {
+        const int i = e / C4, c4 = e % C4;
+        reinterpret_cast<floatx4*>(s_k)[e] =
+            reinterpret_cast<const floatx4*>(p.tk + ((lb * T + s_pi[i0 + i]) * p.Hk + hk) * DK)[c4];
+      }
+      for (int e = tid; e < nc * RB; e += NT) {
+        const int i = e / RB, r = e % RB;
+        s_u[e] = s_w[i0 + i] * p.tu[((lb * T + s_pi[i0 + i]) * p.Hv + hv) * DV + r0 + r];
+      }
     }
     __syncthreads();
     for (int s4 = 0; s4 < nc; s4 += 4) {
@@ -168,18 +217,29 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
   }
 }
 
+// Workgroups of the state rollback: one per (layer, seq, v-head, row block);
+// with long tapes the (layer, seq, k-head) units are rounded up to a
+// multiple of the XCD count.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_tape_rollback(RollbackArgs p) {
-  tape_rollback_body<DK, DV>(p, blockIdx.x);
+long long state_grid(const RollbackArgs& a) {
+  constexpr int RB0 = 256 * 4 * 4 / DK;
+  constexpr int NRBLK = DV / (RB0 < DV ? RB0 : DV);
+  const long long units = static_cast<long long>(a.L) * a.B * a.Hk;
+  const long long padded = a.T > 16 ? (units + kNumXcd - 1) / kNumXcd * kNumXcd : units;
+  return padded * (a.Hv / a.Hk) * NRBLK;
+}
+
+template <int DK, int DV, bool LT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LT ? 7 : 8))) void k_tape_rollback(RollbackArgs p) {
+  tape_rollback_body<DK, DV, LT>(p, blockIdx.x);
 }
 
 template <int DK, int DV>
 hipError_t launch_rb(const RollbackArgs& a, hipStream_t s) {
-  constexpr int RB0 = 256 * 4 * 4 / DK;
-  constexpr int RB = RB0 < DV ? RB0 : DV;
-  const long long grid = static_cast<long long>(a.L) * a.B * a.Hv * (DV / RB);
+  const long long grid = state_grid<DK, DV>(a);
   if (grid > 0x7fffffffLL || a.T > 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_tape_rollback<DK, DV>), dim3(grid), dim3(256), 0, s, a);
+  if (a.T > 16) hipLaunchKernelGGL((k_tape_rollback<DK, DV, true>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_tape_rollback<DK, DV, false>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -396,12 +456,12 @@ namespace {
 // Both rollbacks of a round in one launch: the state workgroups first, then
 // the conv-window ones, which fill the tail of the state pass.  Built for
 // the common conv width (K = 4); other widths take the two launches.
-template <int DK, int DV, int ESZ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_round_rollback(RollbackArgs r, ConvRollbackArgs c,
+template <int DK, int DV, int ESZ, bool LT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LT ? 7 : 8))) void k_round_rollback(RollbackArgs r, ConvRollbackArgs c,
                                                         int n_state, int conv_y) {
   const int bid = blockIdx.x;
   if (bid < n_state) {
-    tape_rollback_body<DK, DV>(r, bid);
+    tape_rollback_body<DK, DV, LT>(r, bid);
   } else {
     const int q = bid - n_state;
     conv_rollback_body<ESZ, 3>(c, static_cast<size_t>(q / conv_y), q % conv_y);
@@ -410,19 +470,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k
 
 template <int DK, int DV>
 hipError_t launch_rr(const RollbackArgs& r, const ConvRollbackArgs& c, int dtype, hipStream_t s) {
-  constexpr int RB0 = 256 * 4 * 4 / DK;
-  constexpr int RB = RB0 < DV ? RB0 : DV;
-  const long long n_state = static_cast<long long>(r.L) * r.B * r.Hv * (DV / RB);
+  const long long n_state = state_grid<DK, DV>(r);
   const int esz = dtype == 1 ? 2 : 4;
   const int conv_y = (c.C * esz / 16 + 255) / 256;
   const long long grid = n_state + static_cast<long long>(c.L) * c.B * conv_y;
   if (grid > 0x7fffffffLL || r.T > 64 || c.K != 4) return hipErrorInvalidValue;
-  if (dtype == 1)
-    hipLaunchKernelGGL((k_round_rollback<DK, DV, 2>), dim3(grid), dim3(256), 0, s, r, c,
-                       static_cast<int>(n_state), conv_y);
-  else
-    hipLaunchKernelGGL((k_round_rollback<DK, DV, 4>), dim3(grid), dim3(256), 0, s, r, c,
-                       static_cast<int>(n_state), conv_y);
+  const int ns = static_cast<int>(n_state);
+  if (r.T > 16) {
+    if (dtype == 1) hipLaunchKernelGGL((k_round_rollback<DK, DV, 2, true>), dim3(grid), dim3(256), 0, s, r, c, ns, conv_y);
+    else hipLaunchKernelGGL((k_round_rollback<DK, DV, 4, true>), dim3(grid), dim3(256), 0, s, r, c, ns, conv_y);
+  } else {
+    if (dtype == 1) hipLaunchKernelGGL((k_round_rollback<DK, DV, 2, false>), dim3(grid), dim3(256), 0, s, r, c, ns, conv_y);
+    else hipLaunchKernelGGL((k_round_rollback<DK, DV, 4, false>), dim3(grid), dim3(256), 0, s, r, c, ns, conv_y);
+  }
   return hipGetLastError();
 }
 
