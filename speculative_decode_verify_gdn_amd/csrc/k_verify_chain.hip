@@ -107,6 +107,35 @@ struct Pair<float> {
   static __device__ __forceinline__ float hi(raw r) { return r[1]; }
 };
 
+// Sequence at position q of the order that lists first the sequences with a
+// previous prefix to replay (1 <= prev_n_keep[b] <= pT), then the others,
+// each group in index order.  Every lane of the wave takes part; the result
+// is wave-uniform.
+__device__ __forceinline__ int writers_first_seq(const int32_t* pnk, int B, int pT, int q) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int W = 0;
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int b = c0 + lane;
+    const int v = b < B ? pnk[b] : 0;
+    W += __popcll(__ballot(b < B && v >= 1 && v <= pT));
+  }
+  const bool want = q < W;
+  int target = want ? q : q - W;
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int b = c0 + lane;
+    const int v = b < B ? pnk[b] : 0;
+    const bool wr = v >= 1 && v <= pT;
+    unsigned long long m = __ballot(b < B && wr == want);
+    const int cnt = __popcll(m);
+    if (target < cnt) {
+      for (int k = 0; k < target; ++k) m &= m - 1ull;
+      return c0 + __builtin_ctzll(m);
+    }
+    target -= cnt;
+  }
+  return q;  // not reached for q < B
+}
+
 template <int DK, int DV, int TMAX, int KM, typename TIn>
 struct ChainLayout {
   static constexpr int NW = chain_waves<DV>();
@@ -177,8 +206,17 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
   const UnitSub us = xcd_unit_sub(blockIdx.x, G);
   if (us.unit >= n_units) return;
   const int hk = us.unit % p0.Hk;
-  const size_t lb = us.unit / p0.Hk;  // l * B + b
+  size_t lb = us.unit / p0.Hk;  // l * B + b
   const int l = static_cast<int>(lb / p0.B);
+  if constexpr (RP && !PF) {
+    // The sequences that replay (and write their state back) go first, so
+    // that one pass of workgroups over the CUs (workgroup i on CU i mod the
+    // CU count) spreads them evenly instead of letting a CU draw several.
+    if (p0.prev_n_keep) {
+      const int q = static_cast<int>(lb % p0.B);
+      lb = static_cast<size_t>(l) * p0.B + writers_first_seq(p0.prev_n_keep, p0.B, p0.pT, q);
+    }
+  }
   const int g = us.sub;
   const int hv = hk * G + g;
   // This wave's tiles of S0 (tile wave + tt * NW): lane (c16, kk) holds row
