@@ -243,7 +243,9 @@ size_t spec_accept_workspace_bytes(int32_t B, int32_t T, int32_t V);
  * GDN_ACCEPT_SCRATCH_BYTES that each GPU holds from library load until the
  * process ends; the call allocates nothing.  Limit: it returns
  * GDN_ERR_SCRATCH, before any launch, when spec_accept_workspace_bytes(B, T,
- * V) exceeds GDN_ACCEPT_SCRATCH_BYTES, i.e. when B*(T+1) > 131040 rows.
+ * V) exceeds GDN_ACCEPT_SCRATCH_BYTES: for V <= 16384 when B*(T+1) > 131040
+ * logits rows, for V = 151936 when B*(T+1) > 13104 (each row then takes ten
+ * partials).
  * Every call on one GPU shares that GPU's array, so calls that overlap on one
  * GPU (different streams without ordering, or different host threads) race;
  * calls ordered on one stream do not.

@@ -184,8 +184,8 @@ def test_binding_rejects_mismatched_tensors():
 
 def test_noalloc_accept_rejects_oversize_before_launch(lib):
     """spec_accept_prefix_noalloc refuses, on the host, inputs whose partials
-    exceed the static scratch (B*(T+1) > 131040 rows), and takes the
-    ordinary argument checks first."""
+    exceed the static scratch (B*(T+1) > 131040 rows for small vocabularies,
+    > 13104 at V = 151936), and takes the ordinary argument checks first."""
     P = ctypes.c_void_p
     call = lambda B, T, V, d=FAKE: lib.spec_accept_prefix_noalloc(
         B, T, V, None, d, FAKE, gb.GDN_BF16, FAKE, FAKE, FAKE, None, None)
@@ -193,6 +193,9 @@ def test_noalloc_accept_rejects_oversize_before_launch(lib):
     assert call(2017, 64, 7) == gb.GDN_ERR_SCRATCH      # 131105 rows
     assert gb.spec_accept_workspace_bytes(2017, 64, 7) > gb.ACCEPT_SCRATCH_BYTES
     assert gb.spec_accept_workspace_bytes(2016, 64, 7) == gb.ACCEPT_SCRATCH_BYTES  # 131040 rows
+    # at the full vocabulary every row takes ten partials: 13104 rows fit
+    assert gb.spec_accept_workspace_bytes(6552, 1, 151936) == gb.ACCEPT_SCRATCH_BYTES
+    assert call(6553, 1, 151936) == gb.GDN_ERR_SCRATCH   # 13106 rows
     assert call(2, 4, 7, d=None) == gb.GDN_ERR_INVALID_ARG
     assert call(2, 65, 7) == gb.GDN_ERR_UNSUPPORTED
     assert gb.status_string(gb.GDN_ERR_SCRATCH) == "GDN_ERR_SCRATCH"
