@@ -106,8 +106,10 @@ struct TreeLds {
   static constexpr int R1 = 2 * TR_T * TR_KQS;
 };
 
+// One (layer, seq, k-head or v-head) unit; bid plays the role of the block
+// index.  All threads leave together.
 template <int KC, bool RP, int NH, bool VG>
-__global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
+__device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
   static_assert(!VG || NH == 1, "the per-key-channel gate runs one head");
   constexpr int KM = KC > 0 ? KC : 8;
   using LY = TreeLds<KM, NH>;
@@ -141,7 +143,12 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   float* s_TI = s_QK + TR_PK;
   float* s_M2 = s_TI + TR_PK;
 
-  const int tid = threadIdx.x;
+  // an opaque copy of the lane index per unit, so that the compiler
+  // recomputes lane-dependent addresses inside the unit loop instead of
+  // keeping them live across it
+  int tid_l = threadIdx.x;
+  asm volatile("" : "+v"(tid_l));
+  const int tid = tid_l;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int c16 = lane & 15;
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
 
   const int G = p.Hv / p.Hk;
   const int n_units = p.L * p.B * p.Hk;
-  const UnitSub us = xcd_unit_sub(blockIdx.x, G / NH);
+  const UnitSub us = xcd_unit_sub(bid, G / NH);
   if (us.unit >= n_units) return;
   const int hk = us.unit % p.Hk;
   const size_t lb = us.unit / p.Hk;  // l * B + b
@@ -1118,6 +1125,38 @@ __global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p) {
   }
 }
 
+// Without the replay, one workgroup per CU (the LDS allows no more) walks
+// the units bid = blockIdx.x, blockIdx.x + gridDim.x, ...: the next unit's
+// loads start right after the barrier instead of after a new workgroup's
+// dispatch.  The grid is a multiple of the XCD count, so a workgroup's units
+// all map to its own XCD.  The replay forms run one unit per workgroup: they
+// sit at the register limit, and the loop made them spill.
+template <int KC, bool RP, int NH, bool VG>
+__global__ __launch_bounds__(TR_NT) void k_verify_tree(VerifyArgs p, int nbid) {
+  if constexpr (RP) {
+    tree_unit<KC, RP, NH, VG>(p, blockIdx.x);
+  } else {
+    for (int bid = blockIdx.x; bid < nbid; bid += gridDim.x) {
+      tree_unit<KC, RP, NH, VG>(p, bid);
+      __syncthreads();  // every wave is done with this unit's LDS
+    }
+  }
+}
+
+// Workgroups of a persistent tree launch: one per CU of the current device.
+int tree_grid(long long nbid) {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return static_cast<int>(nbid);
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      return static_cast<int>(nbid);
+    cus[dev] = (n + kNumXcd - 1) / kNumXcd * kNumXcd;
+  }
+  return static_cast<int>(nbid < cus[dev] ? nbid : cus[dev]);
+}
+
 }  // namespace
 
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s) {
@@ -1132,16 +1171,17 @@ hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s) {
   const bool rp = a.prev_n_keep != nullptr;
   if (rp && (a.pT < 1 || a.pT > TR_T || !a.ptu || !a.ptk || !a.ptg || !a.S_out))
     return hipErrorInvalidValue;
-  const dim3 gd(static_cast<int>(grid)), bd(TR_NT);
+  const int nbid = static_cast<int>(grid);
+  const dim3 gd(rp ? nbid : tree_grid(grid)), bd(TR_NT);
   if (nh == 2) {
-    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 2, false>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((k_verify_tree<4, false, 2, false>), gd, bd, 0, s, a);
+    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 2, false>), gd, bd, 0, s, a, nbid);
+    else hipLaunchKernelGGL((k_verify_tree<4, false, 2, false>), gd, bd, 0, s, a, nbid);
   } else if (a.K == 4) {
-    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 1, false>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((k_verify_tree<4, false, 1, false>), gd, bd, 0, s, a);
+    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 1, false>), gd, bd, 0, s, a, nbid);
+    else hipLaunchKernelGGL((k_verify_tree<4, false, 1, false>), gd, bd, 0, s, a, nbid);
   } else {
-    if (rp) hipLaunchKernelGGL((k_verify_tree<0, true, 1, false>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((k_verify_tree<0, false, 1, false>), gd, bd, 0, s, a);
+    if (rp) hipLaunchKernelGGL((k_verify_tree<0, true, 1, false>), gd, bd, 0, s, a, nbid);
+    else hipLaunchKernelGGL((k_verify_tree<0, false, 1, false>), gd, bd, 0, s, a, nbid);
   }
   return hipGetLastError();
 }
@@ -1154,13 +1194,14 @@ hipError_t launch_verify_tree_vg(const VerifyArgs& a, hipStream_t s) {
   const bool rp = a.prev_n_keep != nullptr;
   if (rp && (a.pT < 1 || a.pT > TR_T || !a.ptu || !a.ptk || !a.ptg || !a.S_out))
     return hipErrorInvalidValue;
-  const dim3 gd(static_cast<int>(grid)), bd(TR_NT);
+  const int nbid = static_cast<int>(grid);
+  const dim3 gd(rp ? nbid : tree_grid(grid)), bd(TR_NT);
   if (a.K == 4) {
-    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 1, true>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((k_verify_tree<4, false, 1, true>), gd, bd, 0, s, a);
+    if (rp) hipLaunchKernelGGL((k_verify_tree<4, true, 1, true>), gd, bd, 0, s, a, nbid);
+    else hipLaunchKernelGGL((k_verify_tree<4, false, 1, true>), gd, bd, 0, s, a, nbid);
   } else {
-    if (rp) hipLaunchKernelGGL((k_verify_tree<0, true, 1, true>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((k_verify_tree<0, false, 1, true>), gd, bd, 0, s, a);
+    if (rp) hipLaunchKernelGGL((k_verify_tree<0, true, 1, true>), gd, bd, 0, s, a, nbid);
+    else hipLaunchKernelGGL((k_verify_tree<0, false, 1, true>), gd, bd, 0, s, a, nbid);
   }
   return hipGetLastError();
 }
