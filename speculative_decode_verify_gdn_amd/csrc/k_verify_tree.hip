@@ -31,14 +31,16 @@
 //     lane; q and k rows are L2-normalised with a 16-lane reduction, written
 //     as pre-split bf16 hi/lo MFMA operands, and k goes to the tape;
 //   Gram [K;Q] K^T on bf16x3 MFMA, keeping only ancestor-or-self entries;
-//   wave 0 solves the packed Ti and M2 rows while the other waves run
-//   S0 [K;Q]^T (bf16x3 MFMA) and form RHS in LDS;
+//   the packed Ti and M2 rows are solved (trees of depth <= 8: in registers
+//   on waves 2 and 3, one head each; deeper trees: on wave 0) while the
+//   other waves run S0 [K;Q]^T (bf16x3 MFMA) and form RHS in LDS;
 //   [Ti; M2] is expanded to a dense pre-split operand in the space of K/Q;
 //   RHS [Ti; M2]^T (bf16x3 MFMA); u and o are stored from registers.
 // With two heads the second head's S0 [K;Q]^T runs right after the first's
 // (K/Q are still in LDS), its v rows wait in registers until the first head
-// has finished with the V space, and wave 0 solves its packed rows while the
-// other waves run the first head's second product.
+// has finished with the V space, and its packed rows (solved beside the
+// first head's, or on wave 0 during the first head's second product for
+// trees deeper than 8) are written once the first head's are expanded.
 // S0 and the conv window are never written (they stay the snapshot), except
 // by the replay form.
 //
@@ -884,10 +886,9 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
       }
     }
   };
-  // The second head's rows for trees of depth <= 8, solved by wave 1 next to
-  // wave 0's first-head solve, in registers (ancestors' Ti rows come from
-  // their lanes); written to the packed rows once the first head's are
-  // expanded.
+  // A head's rows for trees of depth <= 8, solved by one wave in registers
+  // (ancestors' Ti rows come from their lanes by shuffle) and written to the
+  // packed rows by store_rows_reg.
   auto solve_rows_reg = [&](int h, float* xs, float* m2) {
     const float* s_gah = s_ga + h * TR_T;
     const float* s_gbh = s_gb + h * TR_T;
@@ -958,12 +959,23 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
         }
     }
   };
+  // Trees of depth <= 8 solve in registers on waves 2 (head 0, rows stored
+  // at once) and 3 (head 1, rows stored once head 0's are expanded): the
+  // waves that finish their share of the first products earliest, so the
+  // solves leave the barrier's critical path.  Deeper trees solve on wave 0.
   float xs1[NH > 1 ? 8 : 1], m21[NH > 1 ? 8 : 1];
-  const bool early1 = NH > 1 && s_maxd <= 8;
-  if constexpr (NH > 1) {
-    if (wave == 1 && early1) solve_rows_reg(1, xs1, m21);
-  }
-  if (wave == 0) {
+  const bool early = s_maxd <= 8;
+  const bool early1 = NH > 1 && early;
+  if (early) {
+    if (wave == 2) {
+      float xs0[8], m20[8];
+      solve_rows_reg(0, xs0, m20);
+      store_rows_reg(xs0, m20);
+    }
+    if constexpr (NH > 1) {
+      if (wave == 3) solve_rows_reg(1, xs1, m21);
+    }
+  } else if (wave == 0) {
     solve_rows(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1101,7 +1113,7 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
   if constexpr (NH > 1) {
     // the second head's packed rows (the first head's are expanded)
     if (early1) {
-      if (wave == 1) store_rows_reg(xs1, m21);
+      if (wave == 3) store_rows_reg(xs1, m21);
     } else if (wave == 0) {
       solve_rows(1);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
