@@ -74,6 +74,14 @@ __device__ __forceinline__ float silu_t(float y) {
   return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
 }
 
+// x moved across lanes by the DPP control CTRL into the rows of ROW_MASK;
+// lanes without a source (and rows outside the mask) get 1.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+
 // Sum over aligned groups of 16 lanes (DPP; every lane gets its group's sum).
 __device__ __forceinline__ float sum16(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -789,7 +797,101 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
   __syncthreads();  // (B_c) packed Gram rows, V rows
 
   // --------------- wave 0: packed Ti and M2 rows; waves 1..7: S0 [K;Q]^T --
-  auto solve_rows = [&](int h) {
+  // Trees deeper than 24 (one whole wave).  Lane c owns column c of Ti and M2.
+  // Rows go in topological order from Ti = I - A Ti: row t is
+  // e_t - sum_{k in anc(t)} A[t][k] Ti[k], A[t][k] = b_t Gamma(t,k) kk(t,k),
+  // and row t of M2 is sum_{k in path(t)} Gamma(t,k) qk(t,k) Ti[k] with
+  // Gamma(t,t) = 1.  Column c is nonzero only for c on t's path, at slot
+  // dep(c) - 1, so lane c reads back only entries it wrote itself.  Per row,
+  // lane 63 - j first finds the ancestor p_j at slot j (the j-th set bit of
+  // t's ancestor mask), Gamma(t, p_j) by a DPP prefix product over the lanes
+  // (deeper slots sit on lower lanes) and both coefficients; the row's sum
+  // then takes them by readlane, with the Ti[p_j][c] reads going out eight at
+  // a time.
+  auto rlf = [](float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+  };
+  auto solve_cols = [&](int h) {
+    const float* s_gah = s_ga + h * TR_T;
+    const float* s_gbh = s_gb + h * TR_T;
+    const int c = lane;
+    const bool live = c < T;
+    const int dc = live ? s_dep[c] : 0;
+    const int dm1 = live ? dc - 1 : TR_T;  // lowest ancestor slot that reaches column c
+    const int jl = kWave - 1 - lane;       // the slot this lane prepares
+    for (int t = 0; t < T; ++t) {
+      const unsigned long long anc = s_anc[t];  // same address on every lane
+      const int dt = s_dep[t], offt = s_off[t];
+      const float at = s_gah[t], bt = s_gbh[t];
+      const bool cpath = live && (c == t || ((anc >> c) & 1ull));
+      // p_j, the j-th lowest set bit of anc, for j = jl < dt - 1
+      const bool onj = jl < dt - 1;
+      int r = onj ? jl : 0, pos = 0;
+      unsigned w = static_cast<unsigned>(anc);
+      {
+        const int lo = __builtin_popcount(w);
+        if (r >= lo) {
+          r -= lo;
+          pos = 32;
+          w = static_cast<unsigned>(anc >> 32);
+        }
+      }
+#pragma unroll
+      for (int sh = 16; sh >= 1; sh >>= 1) {
+        const int n = __builtin_popcount(w & ((1u << sh) - 1u));
+        if (r >= n) {
+          r -= n;
+          pos += sh;
+          w >>= sh;
+        }
+      }
+      const int pj = onj ? pos : 0;
+      const float aj = onj ? s_gah[pj] : 1.f;
+      const int offj = s_off[pj];
+      const float kkj = s_KK[offt + (onj ? jl : 0)];
+      const float qkj = s_QK[offt + (jl < dt ? jl : 0)];
+      // inclusive prefix product over lanes 0..lane (slots jl..63), then
+      // shifted one lane: Gamma(t, p_j) / a_t = prod_{j < m < dt-1} a(p_m)
+      float xs = aj;
+      xs *= dpp_move<0x111, 0xF>(xs);  // row_shr:1
+      xs *= dpp_move<0x112, 0xF>(xs);  // row_shr:2
+      xs *= dpp_move<0x114, 0xF>(xs);  // row_shr:4
+      xs *= dpp_move<0x118, 0xF>(xs);  // row_shr:8
+      xs *= dpp_move<0x142, 0xA>(xs);  // row_bcast:15 into rows 1 and 3
+      xs *= dpp_move<0x143, 0xC>(xs);  // row_bcast:31 into rows 2 and 3
+      const float gj = at * dpp_move<0x138, 0xF>(xs);  // wave_shr:1
+      const float cA = gj * kkj, cM = gj * qkj;
+      float acc = 0.f, mac = 0.f;
+      for (int j0 = 0; j0 < dt - 1; j0 += 8) {
+        float xk[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = j0 + u < dt - 1 ? j0 + u : dt - 2;
+          const int ok = __builtin_amdgcn_readlane(offj, kWave - 1 - j);
+          xk[u] = s_TI[j >= dm1 ? ok + dc - 1 : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = j0 + u < dt - 1 ? j0 + u : dt - 2;
+          const float x = (j0 + u < dt - 1 && j >= dm1) ? xk[u] : 0.f;
+          acc = fmaf(rlf(cA, kWave - 1 - j), x, acc);
+          mac = fmaf(rlf(cM, kWave - 1 - j), x, mac);
+        }
+      }
+      const float xt = (c == t ? 1.f : 0.f) - bt * acc;
+      if (cpath) {
+        s_TI[offt + dc - 1] = xt;
+        s_M2[offt + dc - 1] = fmaf(rlf(qkj, kWave - dt), xt, mac);
+      }
+    }
+  };
+  // Depths 9 to 24: lane t solves its own row along its path, backward for
+  // Ti and forward for M2, walking the path from the ancestor mask.  The
+  // rows run side by side, so the cost grows with the square of the deepest
+  // path; deeper trees take the column form above, whose cost follows the
+  // summed path lengths (on 64-node trees with one long chain the two meet
+  // near depth 24; a 64-node chain runs 3.1x faster in the column form).
+  auto solve_path = [&](int h) {
     const float* s_gah = s_ga + h * TR_T;
     const float* s_gbh = s_gb + h * TR_T;
     const int t = lane;
@@ -797,94 +899,38 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
     const int d = s_dep[t];
     const int off = s_off[t];
     const unsigned long long mask = s_anc[t] | (1ull << t);
-    if (s_maxd <= 8) {
-      // Registers: path nodes, gates and the strictly-lower path entries of A.
-      int pn[8], po[8];
-      float pa[8], pb[8];
+    s_TI[off + d - 1] = 1.f;
+    for (int i = d - 2; i >= 0; --i) {
       unsigned long long mm = mask;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int v = mm ? __builtin_ctzll(mm) : 0;
+      for (int c = 0; c <= i; ++c) mm &= mm - 1ull;  // drop p_0 .. p_i
+      float acc = 0.f, gmm = 1.f;
+      for (int j = i + 1; j < d; ++j) {
+        const int v = __builtin_ctzll(mm);
         mm &= mm - 1ull;
-        pn[m] = v;
+        gmm *= s_gah[v];
+        acc = fmaf(s_TI[off + j] * s_gbh[v] * gmm, s_KK[s_off[v] + i], acc);
       }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        pa[m] = s_gah[pn[m]];
-        pb[m] = s_gbh[pn[m]];
-        po[m] = s_off[pn[m]];
-      }
-      float kv[8][8];
-#pragma unroll
-      for (int j = 1; j < 8; ++j)
-#pragma unroll
-        for (int i = 0; i < j; ++i) kv[j][i] = (j < d) ? s_KK[po[j] + i] : 0.f;
-      // Row t of Ti: x_{d-1} = 1, x_i = -sum_{j>i} x_j b_j Gamma(j,i) kk(j,i)
-      float xs[8];
-#pragma unroll
-      for (int i = 7; i >= 0; --i) {
-        float acc = 0.f, gmm = 1.f;
-#pragma unroll
-        for (int j = i + 1; j < 8; ++j) {
-          gmm *= pa[j];
-          acc = fmaf(xs[j] * pb[j] * gmm, kv[j][i], acc);
-        }
-        xs[i] = (i == d - 1) ? 1.f : (i < d - 1 ? -acc : 0.f);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < d) s_TI[off + i] = xs[i];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // Row t of M2: sum_{j>=i} Gamma(d-1,j) qk(t,p_j) Ti[p_j][p_i]
-      float oc[8];
-      {
-        float gmm = 1.f;
-#pragma unroll
-        for (int j = 7; j >= 0; --j) {
-          oc[j] = (j < d) ? gmm * s_QK[off + j] : 0.f;
-          if (j < d) gmm *= pa[j];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float acc = 0.f;
-#pragma unroll
-        for (int j = i; j < 8; ++j) {
-          const float tv = (j < d) ? s_TI[po[j] + i] : 0.f;
-          acc = fmaf(oc[j], tv, acc);
-        }
-        if (i < d) s_M2[off + i] = acc;
-      }
-    } else {
-      // Any depth: the same recurrences with the path walked from the mask.
-      s_TI[off + d - 1] = 1.f;
-      for (int i = d - 2; i >= 0; --i) {
-        unsigned long long mm = mask;
-        for (int c = 0; c <= i; ++c) mm &= mm - 1ull;  // drop p_0 .. p_i
-        float acc = 0.f, gmm = 1.f;
-        for (int j = i + 1; j < d; ++j) {
-          const int v = __builtin_ctzll(mm);
-          mm &= mm - 1ull;
-          gmm *= s_gah[v];
-          acc = fmaf(s_TI[off + j] * s_gbh[v] * gmm, s_KK[s_off[v] + i], acc);
-        }
-        s_TI[off + i] = -acc;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int i = 0; i < d; ++i) {
-        unsigned long long mm = mask;
-        float acc = 0.f, gmm = 1.f;
-        for (int j = d - 1; j >= i; --j) {
-          const int v = 63 - __builtin_clzll(mm);
-          mm ^= 1ull << v;
-          acc = fmaf(gmm * s_QK[off + j], s_TI[s_off[v] + i], acc);
-          gmm *= s_gah[v];
-        }
-        s_M2[off + i] = acc;
-      }
+      s_TI[off + i] = -acc;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = 0; i < d; ++i) {
+      unsigned long long mm = mask;
+      float acc = 0.f, gmm = 1.f;
+      for (int j = d - 1; j >= i; --j) {
+        const int v = 63 - __builtin_clzll(mm);
+        mm ^= 1ull << v;
+        acc = fmaf(gmm * s_QK[off + j], s_TI[s_off[v] + i], acc);
+        gmm *= s_gah[v];
+      }
+      s_M2[off + i] = acc;
+    }
+  };
+  auto solve_rows = [&](int h) {
+    if (s_maxd > 24)
+      solve_cols(h);
+    else
+      solve_path(h);
   };
   // A head's rows for trees of depth <= 8, solved by one wave in registers
   // (ancestors' Ti rows come from their lanes by shuffle) and written to the

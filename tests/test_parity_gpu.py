@@ -205,7 +205,8 @@ def test_all_rejected_and_all_accepted(n):
 
 
 @pytest.mark.parametrize("T,branching,depth", [(1, 4, 8), (5, 4, 8), (37, 4, 8), (64, 4, 8),
-                                               (64, 64, 1), (64, 1, 64), (40, 2, 20)])
+                                               (64, 64, 1), (64, 1, 64), (40, 2, 20),
+                                               (33, 1, 33), (64, 3, 16)])
 def test_tree_shapes(T, branching, depth):
     _need_gpu()
     cfg = W.CONFIGS[5].with_(L=1, B=3, Hk=2, Hv=4, T=T, V=700, branching=branching,
@@ -375,16 +376,50 @@ def test_fused_tree_replay_bad_inputs_flag():
     check_units("S", S[:, 0], S_ref[:, 0], "state", 1e-5)
 
 
-@pytest.mark.parametrize("Hk,Hv,K,T", [(2, 4, 4, 48), (2, 2, 4, 64), (1, 4, 3, 40)])
-def test_tree_replay_long_previous_paths(Hk, Hv, K, T):
+@pytest.mark.parametrize("Hk,Hv,chain", [(2, 4, 24), (2, 4, 25), (2, 4, 40), (2, 2, 25),
+                                         (2, 2, 64)])
+def test_tree_verify_long_chain_with_branches(Hk, Hv, chain):
+    """64-node trees made of a chain of `chain` nodes with the others hung
+    at random below it: the deepest path lies on either side of the depth at
+    which the packed solve switches from one row per lane to one column per
+    lane.  Outputs and tape against the oracle's tree_verify."""
+    _need_gpu()
+    from round_ref import oshape
+    cfg = W.CONFIGS[5].with_(L=1, B=3, Hk=Hk, Hv=Hv, T=64, V=97)
+    inp = W.layer_inputs(cfg, 7, "cpu")
+    rng = np.random.default_rng(chain)
+    parent = torch.tensor([[t - 1 for t in range(chain)] +
+                           [int(rng.integers(0, t)) for t in range(chain, cfg.T)]
+                           for _ in range(cfg.B)], dtype=torch.int32)
+    sh, osh = gshape(cfg), oshape(cfg)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    o = torch.empty((1, cfg.B, cfg.T, Hv, cfg.Dv), device=DEV)
+    tape = gb.Tape.empty(sh, cfg.T, DEV)
+    print("tree long chain", Hk, Hv, chain, flush=True)
+    gb.gdn_tree_verify(sh, parent.to(DEV), d["x"], d["conv_state"], d["conv_w"], d["a"], d["b"],
+                       d["S0"], o, tape)
+    torch.cuda.synchronize()
+    f = {k: W.to_f64(v) for k, v in inp.items()}
+    ref = oracle.tree_verify(osh, parent.numpy(), f["x"], f["conv_state"], f["conv_w"], f["a"],
+                             f["b"], f["S0"])
+    for name, got in (("o", o), ("u", tape.u), ("k", tape.k)):
+        check_units(name, got, ref[name], "tok")
+
+
+@pytest.mark.parametrize("Hk,Hv,K,T,branching,depth", [
+    (2, 4, 4, 48, 4, 8), (2, 2, 4, 64, 4, 8), (1, 4, 3, 40, 4, 8),
+    (2, 4, 4, 64, 1, 64), (2, 4, 4, 48, 2, 20), (1, 4, 4, 64, 1, 64)])
+def test_tree_replay_long_previous_paths(Hk, Hv, K, T, branching, depth):
     """gdn_tree_verify_replay with previous paths of 0, 9, 20 and 64 steps
     (beyond the operands preloaded into registers): the state equals the
     oracle's tape_rollback along the path and the outputs its tree_verify from
     that state.  The cases cover two v-heads per workgroup and the one-head
-    form (one v-head per k-head; conv width 3)."""
+    form (one v-head per k-head; conv width 3), and trees deeper than the
+    register solve: a 64-node chain and depth 20."""
     _need_gpu()
     from round_ref import oshape
-    cfg = W.CONFIGS[5].with_(L=1, B=4, Hk=Hk, Hv=Hv, K=K, T=T, V=97)
+    cfg = W.CONFIGS[5].with_(L=1, B=4, Hk=Hk, Hv=Hv, K=K, T=T, V=97, branching=branching,
+                             max_depth=depth)
     inp = W.layer_inputs(cfg, 3, "cpu")
     parent = W.tree_accept_inputs(cfg, 3, "cpu")["parent"]
     sh, osh = gshape(cfg), oshape(cfg)
@@ -403,7 +438,7 @@ def test_tree_replay_long_previous_paths(Hk, Hv, K, T):
     o = torch.empty((1, cfg.B, T, Hv, cfg.Dv), device=DEV)
     tape = gb.Tape.empty(sh, T, DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    print("tree replay long paths", Hk, Hv, K, T, flush=True)
+    print("tree replay long paths", Hk, Hv, K, T, branching, depth, flush=True)
     gb.gdn_tree_verify_replay(sh, parent.to(DEV), d["x"], d["conv_state"], d["conv_w"], d["a"],
                               d["b"], S, o, tape, gb.Tape(pu.to(DEV), pk.to(DEV), pg.to(DEV)),
                               nk.to(DEV), prev_path=path.to(DEV), dev_err=err)
