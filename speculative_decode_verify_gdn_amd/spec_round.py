@@ -114,17 +114,24 @@ def fused_pays(sh: gb.GdnShape, T: int, tree: bool, device=None) -> bool:
     The fused verify writes the replayed state back from inside the verify.
     When the verify grid fits the chip in about one pass, every workgroup
     streams its state at once and the kernel is latency bound: the extra
-    writes land on that critical path and cost more than the separate
+    writes land on that critical path.  The chain kernel (chains of at most
+    16 drafts) puts the sequences that replay first in its workgroup order,
+    so that one pass spreads them evenly over the CUs; with that, the fused
+    round is faster at one pass too (30-layer stack, B = 32, 8 drafts:
+    0.865 against 0.879 ms per round), and from two passes of workgroups on
+    the writes overlap other workgroups' loads anyway.  The tree kernel
+    (trees of 33..64 nodes, bf16 inputs, 128-dim heads) takes one workgroup
+    per CU per pass and fuses from two passes on: below that, the separate
     rollback, a single launch over all layers that streams at a much higher
-    fraction of HBM bandwidth.  From two passes of workgroups on, the writes
-    overlap other workgroups' loads and the fused round saves the rollback's
-    state read.  A pass is 4 workgroups per CU for the chain kernel (chains of
-    at most 16 drafts) and 1 for the tree kernel (trees of 33..64 nodes, bf16
-    inputs, 128-dim heads); other shapes are not fused by the library.
+    fraction of HBM bandwidth, costs less than the writes on the verify's
+    critical path.  Other shapes are not fused by the library.
 
-    With the decay gate per key channel, chains of at most 16 drafts and
-    trees of 33..64 nodes (bf16 inputs, 128-dim heads) fuse on the chain and
-    tree kernels under the same rules as the per-head gate.  Other chains
+    With the decay gate per key channel, chains of at most 16 drafts (bf16
+    inputs, 128-dim heads) fuse from two passes of workgroups on: at one pass
+    the per-key replay's gate products keep the verify at 34 against 22 us
+    per layer and the fused round is the slower one (1.065 against 0.964 ms
+    at B = 32, 8 drafts).  Trees of 33..64 nodes follow the per-head tree
+    rule.  Other chains
     would fuse on the closed-form per-key kernel, slower than their plain
     verify, so they stay plain.  Other trees run the closed-form kernel in
     both forms, and folding the rollback in saves its state pass."""
@@ -137,7 +144,8 @@ def fused_pays(sh: gb.GdnShape, T: int, tree: bool, device=None) -> bool:
             return sh.B * sh.Hv >= 2 * cus
         return T <= 64
     if not tree:
-        return T <= 16 and sh.B * sh.Hv >= 2 * 4 * cus
+        # the replaying sequences go first only for batches of at most 256
+        return T <= 16 and (sh.B <= 256 or sh.B * sh.Hv >= 2 * 4 * cus)
     tree_kernel = 32 < T <= 64 and sh.dtype == torch.bfloat16 and sh.Dk == sh.Dv == 128
     return tree_kernel and sh.B * sh.Hv >= 2 * cus
 
