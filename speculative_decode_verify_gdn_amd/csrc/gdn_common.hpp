@@ -12,8 +12,24 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Split 8 fp32 values into bf16 high parts and bf16 residuals, x ~ hi + lo
-// with |x - hi - lo| <= 2^-18 |x| (both roundings to nearest even).
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Split two fp32 values into packed bf16 high parts and bf16 residuals,
+// x ~ hi + lo with |x - hi - lo| <= 2^-18 |x| (both roundings to nearest
+// even).  Each pair takes one packed conversion for the highs and one for
+// the residuals; the highs widen back exactly by a shift or a mask.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){a, b}, bf16x2));
+  const float ra = a - __uint_as_float(h << 16);
+  const float rb = b - __uint_as_float(h & 0xffff0000u);
+  hi = h;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){ra, rb}, bf16x2));
+}
+
+// The same for 8 values: hi and lo hold a[0..3] then b[0..3].  One
+// conversion per value; it keeps fewer values live than the paired form
+// below, which kernels near their register limit need.
 __device__ __forceinline__ void split_bf16x8(const floatx4& a, const floatx4& b, bf16x8& hi,
                                              bf16x8& lo) {
 #pragma unroll
@@ -25,6 +41,19 @@ __device__ __forceinline__ void split_bf16x8(const floatx4& a, const floatx4& b,
     lo[e] = static_cast<__bf16>(a[e] - static_cast<float>(ha));
     lo[e + 4] = static_cast<__bf16>(b[e] - static_cast<float>(hb));
   }
+}
+
+// The same split by packed conversions of pairs (split_pair): bit-identical
+// results in about half the instructions.
+__device__ __forceinline__ void split_bf16x8_pk(const floatx4& a, const floatx4& b, bf16x8& hi,
+                                                bf16x8& lo) {
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split_pair(a[0], a[1], h0, l0);
+  split_pair(a[2], a[3], h1, l1);
+  split_pair(b[0], b[1], h2, l2);
+  split_pair(b[2], b[3], h3, l3);
+  hi = __builtin_bit_cast(bf16x8, (u32x4){h0, h1, h2, h3});
+  lo = __builtin_bit_cast(bf16x8, (u32x4){l0, l1, l2, l3});
 }
 
 // fp32-accurate product on bf16 MFMA (16x16x32): acc += A B with each

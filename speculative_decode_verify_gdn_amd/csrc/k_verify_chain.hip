@@ -49,8 +49,6 @@
 namespace gdn {
 namespace {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 template <int DV>
 constexpr int chain_waves() {
@@ -61,8 +59,10 @@ constexpr int chain_threads() {
   return 64 * chain_waves<DV>();
 }
 
-// Split two fp32 values into packed bf16 high parts and residuals.
-__device__ __forceinline__ void split_pair(float y0, float y1, uint32_t& hi, uint32_t& lo) {
+// Split two fp32 values into packed bf16 high parts and residuals, one
+// conversion per value: fewer values live than the paired split, which the
+// prefill loop needs at its register limit.
+__device__ __forceinline__ void split_pair_each(float y0, float y1, uint32_t& hi, uint32_t& lo) {
   const __bf16 h0 = static_cast<__bf16>(y0);
   const __bf16 h1 = static_cast<__bf16>(y1);
   bf16x2 h = {h0, h1};
@@ -424,7 +424,7 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
           const int s = c / 32, h = (c % 32) / 16, kg = (c % 16) / 4, e = c % 4;
           unsigned char* row = s_kq + n * KQS + s * 128 + kg * 32 + (h * 4 + e) * 2;
           uint32_t hi, lo;
-          split_pair(y0, y1, hi, lo);
+          split_pair_each(y0, y1, hi, lo);
           *reinterpret_cast<uint32_t*>(row) = hi;
           *reinterpret_cast<uint32_t*>(row + 16) = lo;
           if (!isq) *reinterpret_cast<floatx2*>(s_kf + t * DK + c) = floatx2{y0, y1};
@@ -569,8 +569,8 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           uint32_t h0, l0, h1, l1;
-          split_pair(y[4 * hf], y[4 * hf + 1], h0, l0);
-          split_pair(y[4 * hf + 2], y[4 * hf + 3], h1, l1);
+          split_pair_each(y[4 * hf], y[4 * hf + 1], h0, l0);
+          split_pair_each(y[4 * hf + 2], y[4 * hf + 3], h1, l1);
           *reinterpret_cast<uint2*>(row + (kg + hf) * 32) = make_uint2(h0, h1);
           *reinterpret_cast<uint2*>(row + (kg + hf) * 32 + 16) = make_uint2(l0, l1);
         }
@@ -792,7 +792,12 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       bf16x8 ahi, alo;
-      split_bf16x8(sreg[tt][2 * s], sreg[tt][2 * s + 1], ahi, alo);
+      // 16-token chunks sit at the register limit: the one-value-at-a-time
+      // split keeps them from spilling
+      if constexpr (TMAX > 8)
+        split_bf16x8(sreg[tt][2 * s], sreg[tt][2 * s + 1], ahi, alo);
+      else
+        split_bf16x8_pk(sreg[tt][2 * s], sreg[tt][2 * s + 1], ahi, alo);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const unsigned char* br = s_kq + (cb * 16 + c16) * KQS + kk * 32 + s * 128;

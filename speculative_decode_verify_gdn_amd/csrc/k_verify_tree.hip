@@ -93,16 +93,8 @@ __device__ __forceinline__ float sum16(float v) {
 
 // Pack four fp32 values as bf16 high parts and bf16 residuals (8 bytes each).
 __device__ __forceinline__ void split4(const float* y, uint2& hi, uint2& lo) {
-  uint32_t h[4], r[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const __bf16 bh = static_cast<__bf16>(y[e]);
-    const __bf16 bl = static_cast<__bf16>(y[e] - static_cast<float>(bh));
-    h[e] = __builtin_bit_cast(uint16_t, bh);
-    r[e] = __builtin_bit_cast(uint16_t, bl);
-  }
-  hi = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  lo = make_uint2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
+  split_pair(y[0], y[1], hi.x, lo.x);
+  split_pair(y[2], y[3], hi.y, lo.y);
 }
 
 template <int KM, int NH>
@@ -1034,7 +1026,7 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 ahi, alo;
-      split_bf16x8(sreg[h][2 * s], sreg[h][2 * s + 1], ahi, alo);
+      split_bf16x8_pk(sreg[h][2 * s], sreg[h][2 * s + 1], ahi, alo);
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
         const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_KQS + kk * 32 + s * 128;
@@ -1094,7 +1086,7 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
     for (int st = 0; st < 2; ++st) {
       const float* ar = s_v + (wave * 16 + c16) * TR_VLD + ((32 * st + 8 * kk) ^ vsw(wave * 16 + c16));
       bf16x8 ahi, alo;
-      split_bf16x8(*reinterpret_cast<const floatx4*>(ar), *reinterpret_cast<const floatx4*>(ar + 4), ahi, alo);
+      split_bf16x8_pk(*reinterpret_cast<const floatx4*>(ar), *reinterpret_cast<const floatx4*>(ar + 4), ahi, alo);
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
         const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_B2S + (st * 4 + kk) * 32;
@@ -1131,8 +1123,8 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 ahi0, alo0, ahi1, alo1;
-      split_bf16x8(sreg[0][2 * s], sreg[0][2 * s + 1], ahi0, alo0);
-      split_bf16x8(sreg[1][2 * s], sreg[1][2 * s + 1], ahi1, alo1);
+      split_bf16x8_pk(sreg[0][2 * s], sreg[0][2 * s + 1], ahi0, alo0);
+      split_bf16x8_pk(sreg[1][2 * s], sreg[1][2 * s + 1], ahi1, alo1);
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
         const unsigned char* br = s_r1 + (cb * 16 + c16) * TR_KQS + kk * 32 + s * 128;
