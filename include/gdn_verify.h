@@ -42,8 +42,10 @@
  *    by OR-ing bits into *dev_err (when dev_err != NULL); the affected
  *    sequence is left untouched.
  *  - Supported: d_k, d_v in {32, 64, 128}; conv_kernel in 2..8; T in 1..64;
- *    n_v_heads % n_k_heads == 0; in_dtype F32 or BF16 (x, conv_state, a, b).
- *    conv_w, S, o and the tape are always fp32.
+ *    n_v_heads % n_k_heads == 0; in_dtype F32 or BF16 (x, conv_state, a, b);
+ *    n_layers * batch * n_v_heads <= 2^26 and C <= 2^28 channels (grids and
+ *    channel offsets stay within 32 bits; larger shapes return
+ *    GDN_ERR_UNSUPPORTED).  conv_w, S, o and the tape are always fp32.
  */
 #ifndef GDN_VERIFY_H_
 #define GDN_VERIFY_H_

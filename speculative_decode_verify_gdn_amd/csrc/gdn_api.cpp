@@ -42,6 +42,9 @@ gdn_status check_shape(const gdn_shape* s, int32_t T) {
   // are 32-bit: keep L*B*Hv within range.
   const long long heads = static_cast<long long>(s->n_layers) * s->batch * s->n_v_heads;
   if (heads > (1LL << 26)) return GDN_ERR_UNSUPPORTED;
+  // channel counts and channel offsets are 32-bit inside the kernels
+  const long long C = 2LL * s->n_k_heads * s->d_k + static_cast<long long>(s->n_v_heads) * s->d_v;
+  if (C > (1LL << 28)) return GDN_ERR_UNSUPPORTED;
   return GDN_OK;
 }
 

@@ -73,6 +73,10 @@ def test_host_validation_before_launch(lib):
     assert _verify(_shape(Dk=64, Dv=128)) == gb.GDN_ERR_UNSUPPORTED
     assert _verify(_shape(K=9)) == gb.GDN_ERR_UNSUPPORTED
     assert _verify(_shape(B=0)) == gb.GDN_ERR_INVALID_ARG
+    # sizes whose grids or channel offsets would leave 32 bits
+    assert _verify(_shape(L=64, B=1 << 12, Hk=64, Hv=512)) == gb.GDN_ERR_UNSUPPORTED
+    assert _verify(_shape(Hk=1, Hv=1 << 22)) == gb.GDN_ERR_UNSUPPORTED
+    assert _verify(_shape(Hk=1 << 21, Hv=1 << 21, B=1)) == gb.GDN_ERR_UNSUPPORTED
     # fused replay: previous tape missing, aliasing the current one, bad prev_T
     cur = gb._CTape(0x1000, 0x2000, 0x3000)
     prev = gb._CTape(0x4000, 0x5000, 0x6000)
