@@ -1140,11 +1140,13 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
   }
   form_rhs(0, acc1);
   // The rolled tiles go back to the live state where the stores cost least:
-  // waves 1..7 while they wait for wave 0's solve at the barrier below,
-  // wave 0 once past it (its stores then drain under the dense operand).
-  if (RP && pn > 0 && wave != 0) store_replayed();
+  // the other waves while they wait for the solving waves at the barrier
+  // below, the solving waves (2 and 3, or 0 for deep trees) once past it
+  // (their stores then drain under the dense operand).
+  const bool solver = early ? (wave == 2 || (NH > 1 && wave == 3)) : wave == 0;
+  if (RP && pn > 0 && !solver) store_replayed();
   __syncthreads();  // (B_d) packed Ti, M2; RHS; K/Q space free
-  if (RP && pn > 0 && wave == 0) store_replayed();
+  if (RP && pn > 0 && solver) store_replayed();
 
   dense_operand();
   __syncthreads();  // (B_e)
