@@ -131,3 +131,38 @@ def test_fused_rounds_graph_replays_match_eager(cfg_id, kw):
         fg.finish(4, stream=st)
     torch.cuda.synchronize()
     assert torch.equal(gr.S, ref.S)
+
+
+@pytest.mark.parametrize("cfg_id,kw", CFGS)
+def test_two_streams_at_once_match_one_at_a_time(cfg_id, kw):
+    """Two independent stacks (different seeded draws) run three fused rounds
+    each on two streams with no synchronisation between them; each ends bit
+    for bit where the same rounds run alone on one stream end (no state is
+    shared between calls)."""
+    _need_gpu()
+    cfg = W.CONFIGS[cfg_id].with_(**kw)
+    alone = [_buffers(cfg, 4), _buffers(cfg, 5)]
+    both = [_buffers(cfg, 4), _buffers(cfg, 5)]
+    s0 = torch.cuda.Stream()
+    print("two streams", cfg_id, flush=True)
+    frs = [sr.FusedRound(rb) for rb in alone]
+    for fr in frs:
+        with torch.cuda.stream(s0):
+            for r in range(3):
+                fr.round(r, stream=s0, first=(r == 0))
+            fr.finish(2, stream=s0)
+        s0.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    fbs = [sr.FusedRound(rb) for rb in both]
+    for r in range(3):
+        for fb, st in zip(fbs, streams):
+            with torch.cuda.stream(st):
+                fb.round(r, stream=st, first=(r == 0))
+    for fb, st in zip(fbs, streams):
+        with torch.cuda.stream(st):
+            fb.finish(2, stream=st)
+    torch.cuda.synchronize()
+    for i in range(2):
+        _same(_state(both[i], {"n_keep": fbs[i].n_keeps[0], "path": fbs[i].paths[0]}),
+              _state(alone[i], {"n_keep": frs[i].n_keeps[0], "path": frs[i].paths[0]}),
+              ("two streams", cfg_id, i))
