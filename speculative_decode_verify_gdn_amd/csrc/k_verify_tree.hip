@@ -918,7 +918,77 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
       s_M2[off + i] = acc;
     }
   };
+  // Depths 9 to 16 in the replay forms (one whole wave): lane t solves its
+  // own row with the path's offsets and gates in registers; each row step's
+  // Gram entries are read from LDS together.  The Ti rows go out first, and
+  // M2 then reads the ancestors' Ti rows back from LDS (a wave's LDS accesses
+  // run in order).  The plain two-head form would spill with it.
+  auto solve_rows16 = [&](int h) {
+    const float* s_gah = s_ga + h * TR_T;
+    const float* s_gbh = s_gb + h * TR_T;
+    const int t = lane;
+    const int d = t < T ? s_dep[t] : 0;
+    const int off = s_off[t];
+    int po[16];
+    float pa[16], pb[16];
+    {
+      unsigned long long mm = t < T ? (s_anc[t] | (1ull << t)) : 0ull;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const int v = mm ? __builtin_ctzll(mm) : 0;
+        mm &= mm - 1ull;
+        pa[m] = s_gah[v];
+        pb[m] = s_gbh[v];
+        po[m] = m < d ? s_off[v] : 0;
+      }
+    }
+    // Row t of Ti: x_{d-1} = 1, x_i = -sum_{j>i} x_j b_j Gamma(j,i) kk(j,i)
+    float xs[16];
+#pragma unroll
+    for (int i = 15; i >= 0; --i) {
+      float kv[16];
+#pragma unroll
+      for (int j = i + 1; j < 16; ++j) kv[j] = s_KK[po[j] + i];
+      float acc = 0.f, gmm = 1.f;
+#pragma unroll
+      for (int j = i + 1; j < 16; ++j) {
+        gmm *= pa[j];
+        acc = fmaf(xs[j] * pb[j] * gmm, j < d ? kv[j] : 0.f, acc);
+      }
+      xs[i] = (i == d - 1) ? 1.f : (i < d - 1 ? -acc : 0.f);
+      __builtin_amdgcn_sched_barrier(0);  // one row step's reads at a time
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (t < T && i < d) s_TI[off + i] = xs[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Row t of M2: sum_{j>=i} Gamma(t,p_j) qk(t,p_j) Ti[p_j][i]
+    float oc[16];
+    {
+      float gmm = 1.f;
+#pragma unroll
+      for (int j = 15; j >= 0; --j) {
+        oc[j] = (j < d) ? gmm * s_QK[off + j] : 0.f;
+        if (j < d) gmm *= pa[j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = i; j < 16; ++j) acc = fmaf(oc[j], j < d ? s_TI[po[j] + i] : 0.f, acc);
+      if (t < T && i < d) s_M2[off + i] = acc;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto solve_rows = [&](int h) {
+    if constexpr (RP) {
+      if (s_maxd <= 16) {
+        solve_rows16(h);
+        return;
+      }
+    }
     if (s_maxd > 24)
       solve_cols(h);
     else
