@@ -788,7 +788,7 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
   }
   __syncthreads();  // (B_c) packed Gram rows, V rows
 
-  // --------------- wave 0: packed Ti and M2 rows; waves 1..7: S0 [K;Q]^T --
+  // ---------- packed Ti and M2 rows on one or two waves; the others: S0 [K;Q]^T --
   // Trees deeper than 24 (one whole wave).  Lane c owns column c of Ti and M2.
   // Rows go in topological order from Ti = I - A Ti: row t is
   // e_t - sum_{k in anc(t)} A[t][k] Ti[k], A[t][k] = b_t Gamma(t,k) kk(t,k),
@@ -877,7 +877,8 @@ __device__ __forceinline__ void tree_unit(const VerifyArgs& p, const int bid) {
       }
     }
   };
-  // Depths 9 to 24: lane t solves its own row along its path, backward for
+  // Depths 9 to 24 (17 to 24 in the replay forms, which solve 9 to 16 in
+  // registers below): lane t solves its own row along its path, backward for
   // Ti and forward for M2, walking the path from the ancestor mask.  The
   // rows run side by side, so the cost grows with the square of the deepest
   // path; deeper trees take the column form above, whose cost follows the
