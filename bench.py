@@ -564,7 +564,7 @@ def fused_kernel(cfg) -> bool:
     """Whether the library runs the replay and the verify as one kernel."""
     if not cfg.is_tree:
         return cfg.T <= 16
-    return 32 < cfg.T <= 64 and cfg.dtype == torch.bfloat16 and cfg.Dk == cfg.Dv == 128
+    return 16 < cfg.T <= 64 and cfg.dtype == torch.bfloat16 and cfg.Dk == cfg.Dv == 128
 
 
 def verify_kernel_name(cfg, fused: bool = False) -> str:
@@ -575,8 +575,8 @@ def verify_kernel_name(cfg, fused: bool = False) -> str:
         return "k_verify_chain, replay variant (gdn_verify_chunk_replay, one layer)"
     if not cfg.is_tree and cfg.T <= 16:
         return "k_verify_chain (gdn_verify_chunk, chains of <= 16 tokens, one layer)"
-    if cfg.is_tree and cfg.T > 32 and cfg.dtype == torch.bfloat16 and cfg.Dk == cfg.Dv == 128:
-        return "k_verify_tree (gdn_tree_verify, trees of 33..64 nodes, one layer)"
+    if cfg.is_tree and cfg.T > 16 and cfg.dtype == torch.bfloat16 and cfg.Dk == cfg.Dv == 128:
+        return "k_verify_tree (gdn_tree_verify, trees of 17..64 nodes, one layer)"
     return "k_verify_wy (%s, one layer)" % ("gdn_tree_verify" if cfg.is_tree else "gdn_verify_chunk")
 
 
@@ -810,7 +810,7 @@ def measure_workload(cfg, args, stream, extras: bool):
     mode = args.round if args.round != "auto" else ("fused" if pays else "plain")
     fusable = fused_kernel(cfg)
     if mode == "fused" and not fusable:
-        raise SystemExit("the library fuses chains of at most 16 drafts and trees of 33..64 "
+        raise SystemExit("the library fuses chains of at most 16 drafts and trees of 17..64 "
                          "nodes (bf16, 128-dim heads) only")
     fused = None
     if fusable:

@@ -195,7 +195,7 @@ gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* par
  * [0, prev_T) sets GDN_DEV_ERR_PATH; that sequence is verified from S
  * unchanged.  A malformed parent array sets GDN_DEV_ERR_PARENT and leaves the
  * sequence's outputs unwritten, but the replay is still applied to S.  Both
- * steps run in one kernel for trees of 33..64 nodes with bf16 inputs and
+ * steps run in one kernel for trees of 17..64 nodes with bf16 inputs and
  * 128-dim heads, and for any tree with the per-key-channel gate; otherwise
  * as the two calls in sequence.
  * Source: GDN page s4 (restore the snapshot and replay the accepted steps),

@@ -48,6 +48,14 @@ gdn_status check_shape(const gdn_shape* s, int32_t T) {
   return GDN_OK;
 }
 
+// Trees the MFMA tree kernel serves (bf16 inputs, 128-dim heads): 17..64
+// nodes with the per-v-head gate (measured faster than the chunked WY kernel
+// from 17 nodes on, slower at 16), 33..64 with the per-key-channel gate.
+bool tree_kernel_serves(const gdn_shape* s, int32_t T) {
+  return T > (s->gate_per_key ? 32 : 16) && s->in_dtype == GDN_BF16 && s->d_k == 128 &&
+         s->d_v == 128;
+}
+
 int channels(const gdn_shape* s) {
   return 2 * s->n_k_heads * s->d_k + s->n_v_heads * s->d_v;
 }
@@ -172,13 +180,12 @@ gdn_status gdn_tree_verify(const gdn_shape* shape, int32_t T, const int32_t* par
   v.conv_win = conv_win;
   v.dev_err = dev_err;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool tree_kernel =
-      T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128;
   if (shape->gate_per_key)
-    return launch_status(tree_kernel ? gdn::launch_verify_tree_vg(v, s)
-                                     : gdn::launch_verify_vg_tree(v, shape->d_k, shape->d_v,
-                                                                  shape->in_dtype, s));
-  if (tree_kernel) return launch_status(gdn::launch_verify_tree(v, s));
+    return launch_status(tree_kernel_serves(shape, T) ? gdn::launch_verify_tree_vg(v, s)
+                                                      : gdn::launch_verify_vg_tree(
+                                                            v, shape->d_k, shape->d_v,
+                                                            shape->in_dtype, s));
+  if (tree_kernel_serves(shape, T)) return launch_status(gdn::launch_verify_tree(v, s));
   return launch_status(gdn::launch_verify_wy(v, shape->d_k, shape->d_v, shape->in_dtype, s));
 }
 
@@ -211,11 +218,10 @@ gdn_status gdn_tree_verify_replay(const gdn_shape* shape, int32_t T, const int32
     v.prev_n_keep = prev_n_keep;
     v.prev_path = prev_path;
     v.pT = prev_T;
-    if (T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128)
-      return launch_status(gdn::launch_verify_tree_vg(v, s));
+    if (tree_kernel_serves(shape, T)) return launch_status(gdn::launch_verify_tree_vg(v, s));
     return launch_status(gdn::launch_verify_vg_tree(v, shape->d_k, shape->d_v, shape->in_dtype, s));
   }
-  if (T > 32 && shape->in_dtype == GDN_BF16 && shape->d_k == 128 && shape->d_v == 128) {
+  if (tree_kernel_serves(shape, T)) {
     VerifyArgs v = verify_args(shape, T, x, conv_state, conv_w, a, b, S, o, tape);
     v.parent = parent;
     v.conv_win = conv_win;

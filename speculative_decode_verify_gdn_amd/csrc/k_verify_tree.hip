@@ -1,4 +1,4 @@
-// k_verify_tree.hip -- verify of a draft tree of 33..64 nodes through one GDN
+// k_verify_tree.hip -- verify of a draft tree of up to 64 nodes through one GDN
 // layer (128-dim heads, bf16 inputs), for gfx950.
 //
 // Per node v with parent p (p = -1: the committed state S0), the gated delta
@@ -1290,7 +1290,7 @@ hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t s) {
   const int nh = (G == 2 && a.K == 4) ? 2 : 1;
   const long long grid =
       static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * (G / nh);
-  if (grid > 0x7fffffffLL || a.T > TR_T || a.T <= 32) return hipErrorInvalidValue;
+  if (grid > 0x7fffffffLL || a.T > TR_T || a.T < 1) return hipErrorInvalidValue;
   const bool rp = a.prev_n_keep != nullptr;
   if (rp && (a.pT < 1 || a.pT > TR_T || !a.ptu || !a.ptk || !a.ptg || !a.S_out))
     return hipErrorInvalidValue;
@@ -1313,7 +1313,7 @@ hipError_t launch_verify_tree_vg(const VerifyArgs& a, hipStream_t s) {
   const int G = a.Hv / a.Hk;
   const int n_units = a.L * a.B * a.Hk;
   const long long grid = static_cast<long long>((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
-  if (grid > 0x7fffffffLL || a.T > TR_T || a.T <= 32) return hipErrorInvalidValue;
+  if (grid > 0x7fffffffLL || a.T > TR_T || a.T < 1) return hipErrorInvalidValue;
   const bool rp = a.prev_n_keep != nullptr;
   if (rp && (a.pT < 1 || a.pT > TR_T || !a.ptu || !a.ptk || !a.ptg || !a.S_out))
     return hipErrorInvalidValue;

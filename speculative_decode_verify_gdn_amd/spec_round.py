@@ -120,7 +120,7 @@ def fused_pays(sh: gb.GdnShape, T: int, tree: bool, device=None) -> bool:
     round is faster at one pass too (30-layer stack, B = 32, 8 drafts:
     0.865 against 0.879 ms per round), and from two passes of workgroups on
     the writes overlap other workgroups' loads anyway.  The tree kernel
-    (trees of 33..64 nodes, bf16 inputs, 128-dim heads) takes one workgroup
+    (trees of 17..64 nodes, bf16 inputs, 128-dim heads) takes one workgroup
     per CU per pass and fuses from two passes on: below that, the separate
     rollback, a single launch over all layers that streams at a much higher
     fraction of HBM bandwidth, costs less than the writes on the verify's
@@ -130,8 +130,8 @@ def fused_pays(sh: gb.GdnShape, T: int, tree: bool, device=None) -> bool:
     inputs, 128-dim heads) fuse from two passes of workgroups on: at one pass
     the per-key replay's gate products keep the verify at 34 against 22 us
     per layer and the fused round is the slower one (1.065 against 0.964 ms
-    at B = 32, 8 drafts).  Trees of 33..64 nodes follow the per-head tree
-    rule.  Other chains
+    at B = 32, 8 drafts).  Trees of 33..64 nodes (the per-key form of the
+    tree kernel) follow the per-head tree rule.  Other chains
     would fuse on the closed-form per-key kernel, slower than their plain
     verify, so they stay plain.  Other trees run the closed-form kernel in
     both forms, and folding the rollback in saves its state pass."""
@@ -146,7 +146,7 @@ def fused_pays(sh: gb.GdnShape, T: int, tree: bool, device=None) -> bool:
     if not tree:
         # the replaying sequences go first only for batches of at most 256
         return T <= 16 and (sh.B <= 256 or sh.B * sh.Hv >= 2 * 4 * cus)
-    tree_kernel = 32 < T <= 64 and sh.dtype == torch.bfloat16 and sh.Dk == sh.Dv == 128
+    tree_kernel = 16 < T <= 64 and sh.dtype == torch.bfloat16 and sh.Dk == sh.Dv == 128
     return tree_kernel and sh.B * sh.Hv >= 2 * cus
 
 

@@ -204,7 +204,8 @@ def test_all_rejected_and_all_accepted(n):
         assert torch.equal(got["cs_new"], inp["conv_state"])
 
 
-@pytest.mark.parametrize("T,branching,depth", [(1, 4, 8), (5, 4, 8), (37, 4, 8), (64, 4, 8),
+@pytest.mark.parametrize("T,branching,depth", [(1, 4, 8), (5, 4, 8), (16, 4, 8), (17, 4, 8),
+                                               (24, 2, 12), (32, 4, 8), (37, 4, 8), (64, 4, 8),
                                                (64, 64, 1), (64, 1, 64), (40, 2, 20),
                                                (33, 1, 33), (64, 3, 16)])
 def test_tree_shapes(T, branching, depth):
@@ -291,11 +292,12 @@ def test_fused_replay_rounds(cfg_id, L, B, rounds, forced):
     assert int(fr.rb.dev_err.item()) == 0
 
 
-@pytest.mark.parametrize("L,B,rounds,T", [(2, 3, 4, 64), (1, 2, 3, 40), (1, 2, 3, 24)])
+@pytest.mark.parametrize("L,B,rounds,T", [(2, 3, 4, 64), (1, 2, 3, 40), (1, 2, 3, 24),
+                                          (1, 2, 3, 17), (1, 2, 3, 12)])
 def test_fused_replay_tree_rounds(L, B, rounds, T):
     """Tree rounds with the rollback folded into the next verify
     (gdn_tree_verify_replay) give the oracle's plain tree rounds every round
-    and after finish(); T = 24 runs the library's two-call form."""
+    and after finish(); T = 12 runs the library's two-call form."""
     _need_gpu()
     cfg = W.CONFIGS[5].with_(L=L, B=B, T=T, V=311)
     inp0 = W.layer_inputs(cfg, 0, "cpu")
