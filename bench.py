@@ -468,7 +468,7 @@ def vgate_pass(cfg, stream, steps):
             "verify_per_layer_ms": v_ms, "verify_bytes_per_launch": vb,
             "verify_hbm_frac": vb / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "rollback_state_and_conv_ms": t_plain[2],
-            "kernel": (("k_verify_tree (per-key gate)" if 32 < cfg.T <= 64 and cfg.dtype == torch.bfloat16
+            "kernel": (("k_verify_tree (per-key gate)" if 12 < cfg.T <= 64 and cfg.dtype == torch.bfloat16
                         and cfg.Dk == cfg.Dv == 128 else "k_verify_vgt") if tree else
                        ("k_verify_chain (per-key gate)" if cfg.T <= 16 and cfg.dtype == torch.bfloat16
                         and cfg.Dk == cfg.Dv == 128 else "k_verify_vg")),
@@ -478,7 +478,7 @@ def vgate_pass(cfg, stream, steps):
                                  if not tree and cfg.T <= 16 and cfg.dtype == torch.bfloat16
                                  and cfg.Dk == cfg.Dv == 128 else
                                  "k_verify_tree (per-key gate, replay)"
-                                 if tree and 32 < cfg.T <= 64 and cfg.dtype == torch.bfloat16
+                                 if tree and 12 < cfg.T <= 64 and cfg.dtype == torch.bfloat16
                                  and cfg.Dk == cfg.Dv == 128 else "k_verify_vgt")}}
 
 

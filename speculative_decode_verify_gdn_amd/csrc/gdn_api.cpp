@@ -50,9 +50,10 @@ gdn_status check_shape(const gdn_shape* s, int32_t T) {
 
 // Trees the MFMA tree kernel serves (bf16 inputs, 128-dim heads): 17..64
 // nodes with the per-v-head gate (measured faster than the chunked WY kernel
-// from 17 nodes on, slower at 16), 33..64 with the per-key-channel gate.
+// from 17 nodes on, slower at 16), 13..64 with the per-key-channel gate
+// (faster than the closed-form kernel from 16 nodes on, level at 12).
 bool tree_kernel_serves(const gdn_shape* s, int32_t T) {
-  return T > (s->gate_per_key ? 32 : 16) && s->in_dtype == GDN_BF16 && s->d_k == 128 &&
+  return T > (s->gate_per_key ? 12 : 16) && s->in_dtype == GDN_BF16 && s->d_k == 128 &&
          s->d_v == 128;
 }
 

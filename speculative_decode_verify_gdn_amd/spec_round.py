@@ -130,7 +130,7 @@ def fused_pays(sh: gb.GdnShape, T: int, tree: bool, device=None) -> bool:
     inputs, 128-dim heads) fuse from two passes of workgroups on: at one pass
     the per-key replay's gate products keep the verify at 34 against 22 us
     per layer and the fused round is the slower one (1.065 against 0.964 ms
-    at B = 32, 8 drafts).  Trees of 33..64 nodes (the per-key form of the
+    at B = 32, 8 drafts).  Trees of 13..64 nodes (the per-key form of the
     tree kernel) follow the per-head tree rule.  Other chains
     would fuse on the closed-form per-key kernel, slower than their plain
     verify, so they stay plain.  Other trees run the closed-form kernel in
@@ -140,7 +140,7 @@ def fused_pays(sh: gb.GdnShape, T: int, tree: bool, device=None) -> bool:
         mfma = sh.dtype == torch.bfloat16 and sh.Dk == sh.Dv == 128
         if not tree:
             return mfma and T <= 16 and sh.B * sh.Hv >= 2 * 4 * cus
-        if mfma and 32 < T <= 64:
+        if mfma and 12 < T <= 64:
             return sh.B * sh.Hv >= 2 * cus
         return T <= 64
     if not tree:

@@ -1283,12 +1283,14 @@ def _vg_parents(rng, B, T, depth):
     (17, 1, 3, 2, 2, 32, 8, torch.bfloat16, 5), (1, 1, 2, 2, 4, 128, 4, torch.bfloat16, 1),
     (64, 1, 1, 1, 2, 128, 4, torch.float32, 64), (33, 1, 2, 2, 4, 64, 2, torch.bfloat16, 33),
     (48, 2, 2, 2, 2, 128, 3, torch.bfloat16, 6), (64, 1, 1, 1, 2, 128, 4, torch.bfloat16, 64),
-    (40, 1, 2, 2, 4, 128, 4, torch.bfloat16, 20), (33, 1, 3, 1, 1, 128, 8, torch.bfloat16, 8)])
+    (40, 1, 2, 2, 4, 128, 4, torch.bfloat16, 20), (33, 1, 3, 1, 1, 128, 8, torch.bfloat16, 8),
+    (13, 1, 2, 2, 4, 128, 4, torch.bfloat16, 6), (24, 1, 2, 1, 2, 128, 4, torch.bfloat16, 24),
+    (12, 1, 2, 2, 4, 128, 4, torch.bfloat16, 8)])
 def test_vgate_tree_verify_matches_oracle(T, L, B, Hk, Hv, D, K, dtype, depth):
     """gdn_tree_verify with a per-key-channel gate equals the oracle's
     tree_verify_vg (outputs, tape, conv windows) and leaves S untouched; the
     depth >= T cases are chains given as parent arrays (the deepest trees).
-    bf16 trees of 33..64 nodes with 128-dim heads run the MFMA tree kernel
+    bf16 trees of 13..64 nodes with 128-dim heads run the MFMA tree kernel
     (conv widths 3, 4 and 8; depths up to 64), the rest the closed-form
     per-key kernel."""
     _need_gpu()
@@ -1332,7 +1334,8 @@ def _vg_prev_tape(cfg, pT, seed):
     (False, 16, 16, 128, torch.bfloat16), (False, 5, 13, 128, torch.bfloat16),
     (False, 40, 64, 32, torch.bfloat16), (True, 64, 64, 128, torch.bfloat16),
     (True, 40, 23, 128, torch.bfloat16), (True, 33, 5, 128, torch.bfloat16),
-    (True, 24, 40, 32, torch.float32)])
+    (True, 24, 40, 32, torch.float32), (True, 16, 9, 128, torch.bfloat16),
+    (True, 13, 64, 128, torch.bfloat16), (True, 12, 12, 128, torch.bfloat16)])
 def test_vgate_replay_verify_equals_rollback_then_verify(tree, T, pT, D, dtype):
     """gdn_verify_chunk_replay / gdn_tree_verify_replay with a per-key gate:
     the state afterwards is the oracle's tape_rollback_vg of the previous tape
@@ -1387,7 +1390,7 @@ def test_vgate_replay_verify_equals_rollback_then_verify(tree, T, pT, D, dtype):
 @pytest.mark.parametrize("T,pT,D", [(24, 8, 64), (40, 8, 128)])
 def test_vgate_tree_replay_bad_inputs_flag(T, pT, D):
     """Per-key tree replay (the closed-form kernel, and the MFMA tree kernel
-    for 33..64 nodes): a malformed parent array flags GDN_DEV_ERR_PARENT,
+    for 13..64 nodes): a malformed parent array flags GDN_DEV_ERR_PARENT,
     skips that sequence's outputs and still applies its replay; an
     out-of-range accepted length or path entry flags its bit and leaves that
     sequence's state as it was."""
@@ -1438,7 +1441,8 @@ def test_vgate_tree_replay_bad_inputs_flag(T, pT, D):
     check_units("S", S[:, 1], S_rep[:, 1], "state", 1e-5)
 
 
-@pytest.mark.parametrize("tree,T", [(True, 64), (True, 40), (False, 8), (False, 16)])
+@pytest.mark.parametrize("tree,T", [(True, 64), (True, 40), (True, 24), (True, 12), (False, 8),
+                                    (False, 16)])
 def test_vgate_fused_rounds(tree, T):
     """Fused rounds (spec_round.FusedRound) with a per-key-channel gate: every
     round's outputs, tape, accepted lengths and paths, conv window, and the
