@@ -793,8 +793,9 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
     for (int s = 0; s < KSTEPS; ++s) {
       bf16x8 ahi, alo;
       // 16-token chunks sit at the register limit: the one-value-at-a-time
-      // split keeps them from spilling
-      if constexpr (TMAX > 8)
+      // split keeps them from spilling (the prefill loop, which spills a
+      // little either way, spills less with the paired split)
+      if constexpr (TMAX > 8 && !PF)
         split_bf16x8(sreg[tt][2 * s], sreg[tt][2 * s + 1], ahi, alo);
       else
         split_bf16x8_pk(sreg[tt][2 * s], sreg[tt][2 * s + 1], ahi, alo);
