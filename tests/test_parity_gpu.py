@@ -410,14 +410,15 @@ def test_tree_verify_long_chain_with_branches(Hk, Hv, chain):
 
 @pytest.mark.parametrize("Hk,Hv,K,T,branching,depth", [
     (2, 4, 4, 48, 4, 8), (2, 2, 4, 64, 4, 8), (1, 4, 3, 40, 4, 8),
-    (2, 4, 4, 64, 1, 64), (2, 4, 4, 48, 2, 20), (1, 4, 4, 64, 1, 64)])
+    (2, 4, 4, 64, 1, 64), (2, 4, 4, 48, 2, 20), (1, 4, 4, 64, 1, 64), (2, 4, 4, 20, 4, 8)])
 def test_tree_replay_long_previous_paths(Hk, Hv, K, T, branching, depth):
     """gdn_tree_verify_replay with previous paths of 0, 9, 20 and 64 steps
     (beyond the operands preloaded into registers): the state equals the
     oracle's tape_rollback along the path and the outputs its tree_verify from
     that state.  The cases cover two v-heads per workgroup and the one-head
-    form (one v-head per k-head; conv width 3), and trees deeper than the
-    register solve: a 64-node chain and depth 20."""
+    form (one v-head per k-head; conv width 3), trees deeper than the
+    register solve (a 64-node chain and depth 20), and a 20-node tree after
+    a 64-entry previous path."""
     _need_gpu()
     from round_ref import oshape
     cfg = W.CONFIGS[5].with_(L=1, B=4, Hk=Hk, Hv=Hv, K=K, T=T, V=97, branching=branching,
