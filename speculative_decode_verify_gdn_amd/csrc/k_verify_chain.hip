@@ -159,9 +159,9 @@ struct ChainLayout {
   static_assert(ALD == GLD, "A and Oc overwrite the Gram rows in place");
 };
 
-// Occupancy targets.  PF (prefill loop) holds the state across the wave-0
-// prologue: with the per-head gate it runs at 3 waves per SIMD (168 VGPRs,
-// small spill), measured faster than 2 (no spill) and far faster than 4
+// Occupancy targets.  PF (prefill loop) holds the state across the
+// prologue: with the per-head gate it runs at 3 waves per SIMD (166 VGPRs,
+// no spill at conv width 4), measured faster than 2 and far faster than 4
 // (heavy spill); with the per-key gate at 2 (no spill), faster than 3
 // (spill).  The per-key replay (VG and RP) runs at 3, spill-free.
 template <int DK, int DV, int TMAX, int KC, typename TIn, bool RP, bool VG = false, bool PF = false>
@@ -328,20 +328,93 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
     }
   };
 
+  // Conv helpers (prologue).  Wave 0 runs every channel pair in the verify
+  // forms; the prefill loop shares the pairs out over the waves, since from
+  // its second chunk on the state waves have no loads to queue.
+  const TIn* x = static_cast<const TIn*>(p.x);
+  const TIn* cs = static_cast<const TIn*>(p.conv_state);
+  const float* cw = p.conv_w + static_cast<size_t>(l) * p.C * K;
+  const TIn* xcol = x + lb * p.x_ld;
+  const TIn* ccol = cs + lb * (PF ? p.cs_ld : static_cast<size_t>(K - 1) * p.C);
+  const int nrows = K - 1 + T;
+  // local channel c in [q | k | v-rows] -> qkv channel
+  auto chan = [&](int c) {
+    return c < DK ? hk * DK + c
+                  : (c < 2 * DK ? p.Hk * DK + hk * DK + (c - DK)
+                                : 2 * p.Hk * DK + hv * DV + (c - 2 * DK));
+  };
+  auto load_pair = [&](int j, typename PR::raw* xr, float* w0, float* w1) {
+    const int pr = lane + 64 * j;
+    const int c0 = 2 * (pr < NPAIR ? pr : NPAIR - 1);
+    const int ch = chan(c0);
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+      const int rr = r < nrows ? r : nrows - 1;
+      const TIn* base = rr < K - 1 ? ccol + static_cast<size_t>(rr) * p.C
+                                   : xcol + static_cast<size_t>(rr - (K - 1)) * p.C;
+      xr[r] = PR::load(base + ch);
+    }
+    if (KC == 4) {
+      const floatx4 a0 = *reinterpret_cast<const floatx4*>(cw + static_cast<size_t>(ch) * 4);
+      const floatx4 a1 = *reinterpret_cast<const floatx4*>(cw + static_cast<size_t>(ch) * 4 + 4);
+#pragma unroll
+      for (int jj = 0; jj < KM; ++jj) {
+        w0[jj] = a0[jj % 4];
+        w1[jj] = a1[jj % 4];
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < KM; ++jj) {
+        const int q = jj < K ? jj : 0;
+        const float v0 = cw[static_cast<size_t>(ch) * K + q];
+        const float v1 = cw[static_cast<size_t>(ch + 1) * K + q];
+        w0[jj] = jj < K ? v0 : 0.f;
+        w1[jj] = jj < K ? v1 : 0.f;
+      }
+    }
+  };
+  // conv + SiLU of one channel pair over the chunk; results to LDS.
+  auto conv_pair = [&](int j, const typename PR::raw* xr, const float* w0, const float* w1) {
+    const int pr = lane + 64 * j;
+    if (pr >= NPAIR) return;
+    const int c0 = 2 * pr;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < KM; ++jj) {
+        if (t + jj < XR) {
+          y0 = fmaf(w0[jj], PR::lo(xr[t + jj]), y0);
+          y1 = fmaf(w1[jj], PR::hi(xr[t + jj]), y1);
+        }
+      }
+      if (p.silu) {
+        y0 = silu_f(y0);
+        y1 = silu_f(y1);
+      }
+      if (t >= T) y0 = y1 = 0.f;
+      if (c0 < 2 * DK) {
+        const int isq = c0 < DK;
+        const int c = isq ? c0 : c0 - DK;
+        const int n = isq ? TMAX + t : t;
+        // element c -> 32-column step s, half h, lane group kg, slot e
+        const int s = c / 32, h = (c % 32) / 16, kg = (c % 16) / 4, e = c % 4;
+        unsigned char* row = s_kq + n * KQS + s * 128 + kg * 32 + (h * 4 + e) * 2;
+        uint32_t hi, lo;
+        split_pair_each(y0, y1, hi, lo);
+        *reinterpret_cast<uint32_t*>(row) = hi;
+        *reinterpret_cast<uint32_t*>(row + 16) = lo;
+        if (!isq) *reinterpret_cast<floatx2*>(s_kf + t * DK + c) = floatx2{y0, y1};
+      } else {
+        const int i = c0 - 2 * DK;
+        s_rhs[i * RT_LD + t] = y0;
+        s_rhs[(i + 1) * RT_LD + t] = y1;
+      }
+    }
+  };
+
   if (wave == 0) {
     // ---------------------------------------------------------- prologue --
-    const TIn* x = static_cast<const TIn*>(p.x);
-    const TIn* cs = static_cast<const TIn*>(p.conv_state);
-    const float* cw = p.conv_w + static_cast<size_t>(l) * p.C * K;
-    const TIn* xcol = x + lb * p.x_ld;
-    const TIn* ccol = cs + lb * (PF ? p.cs_ld : static_cast<size_t>(K - 1) * p.C);
-    const int nrows = K - 1 + T;
-    // local channel c in [q | k | v-rows] -> qkv channel
-    auto chan = [&](int c) {
-      return c < DK ? hk * DK + c
-                    : (c < 2 * DK ? p.Hk * DK + hk * DK + (c - DK)
-                                  : 2 * p.Hk * DK + hv * DV + (c - 2 * DK));
-    };
     // Gates (clamped, unconditional loads).
     const int tq = lane < T ? lane : 0;
     const size_t gi = lb * p.ab_ld + static_cast<size_t>(tq) * p.Hv + hv;
@@ -366,77 +439,17 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
     const float pg_ld = RP && !VG && lane < pn ? p.ptg[(lb * p.pT + lane) * p.Hv + hv] : 1.f;
 
 
-    auto load_pair = [&](int j, typename PR::raw* xr, float* w0, float* w1) {
-      const int pr = lane + 64 * j;
-      const int c0 = 2 * (pr < NPAIR ? pr : NPAIR - 1);
-      const int ch = chan(c0);
-#pragma unroll
-      for (int r = 0; r < XR; ++r) {
-        const int rr = r < nrows ? r : nrows - 1;
-        const TIn* base = rr < K - 1 ? ccol + static_cast<size_t>(rr) * p.C
-                                     : xcol + static_cast<size_t>(rr - (K - 1)) * p.C;
-        xr[r] = PR::load(base + ch);
+    if constexpr (PF) {
+      // this wave's share of the channel pairs, then (B0') every wave's
+      // conv results are in LDS
+      for (int j = 0; j < PPL; j += NW) {
+        typename PR::raw xr[XR];
+        float w0[KM], w1[KM];
+        load_pair(j, xr, w0, w1);
+        conv_pair(j, xr, w0, w1);
       }
-      if (KC == 4) {
-        const floatx4 a0 = *reinterpret_cast<const floatx4*>(cw + static_cast<size_t>(ch) * 4);
-        const floatx4 a1 = *reinterpret_cast<const floatx4*>(cw + static_cast<size_t>(ch) * 4 + 4);
-#pragma unroll
-        for (int jj = 0; jj < KM; ++jj) {
-          w0[jj] = a0[jj % 4];
-          w1[jj] = a1[jj % 4];
-        }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < KM; ++jj) {
-          const int q = jj < K ? jj : 0;
-          const float v0 = cw[static_cast<size_t>(ch) * K + q];
-          const float v1 = cw[static_cast<size_t>(ch + 1) * K + q];
-          w0[jj] = jj < K ? v0 : 0.f;
-          w1[jj] = jj < K ? v1 : 0.f;
-        }
-      }
-    };
-    // conv + SiLU of one channel pair over the chunk; results to LDS.
-    auto conv_pair = [&](int j, const typename PR::raw* xr, const float* w0, const float* w1) {
-      const int pr = lane + 64 * j;
-      if (pr >= NPAIR) return;
-      const int c0 = 2 * pr;
-#pragma unroll
-      for (int t = 0; t < TMAX; ++t) {
-        float y0 = 0.f, y1 = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < KM; ++jj) {
-          if (t + jj < XR) {
-            y0 = fmaf(w0[jj], PR::lo(xr[t + jj]), y0);
-            y1 = fmaf(w1[jj], PR::hi(xr[t + jj]), y1);
-          }
-        }
-        if (p.silu) {
-          y0 = silu_f(y0);
-          y1 = silu_f(y1);
-        }
-        if (t >= T) y0 = y1 = 0.f;
-        if (c0 < 2 * DK) {
-          const int isq = c0 < DK;
-          const int c = isq ? c0 : c0 - DK;
-          const int n = isq ? TMAX + t : t;
-          // element c -> 32-column step s, half h, lane group kg, slot e
-          const int s = c / 32, h = (c % 32) / 16, kg = (c % 16) / 4, e = c % 4;
-          unsigned char* row = s_kq + n * KQS + s * 128 + kg * 32 + (h * 4 + e) * 2;
-          uint32_t hi, lo;
-          split_pair_each(y0, y1, hi, lo);
-          *reinterpret_cast<uint32_t*>(row) = hi;
-          *reinterpret_cast<uint32_t*>(row + 16) = lo;
-          if (!isq) *reinterpret_cast<floatx2*>(s_kf + t * DK + c) = floatx2{y0, y1};
-        } else {
-          const int i = c0 - 2 * DK;
-          s_rhs[i * RT_LD + t] = y0;
-          s_rhs[(i + 1) * RT_LD + t] = y1;
-        }
-      }
-    };
-
-    if constexpr (LY::LOAD_ALL) {
+      __syncthreads();  // (B0')
+    } else if constexpr (LY::LOAD_ALL) {
       typename PR::raw xr[PPL][XR];
       float w0[PPL][KM], w1[PPL][KM];
 #pragma unroll
@@ -699,7 +712,19 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
       }
     }
   } else {
-    __syncthreads();  // (B0)
+    if constexpr (PF) {
+      load_state();  // the first chunk queues the state first; later ones hold it
+#pragma unroll 1
+      for (int j = wave; j < PPL; j += NW) {
+        typename PR::raw xr[XR];
+        float w0[KM], w1[KM];
+        load_pair(j, xr, w0, w1);
+        conv_pair(j, xr, w0, w1);
+      }
+      __syncthreads();  // (B0')
+    } else {
+      __syncthreads();  // (B0)
+    }
     if constexpr (VR) {
       // the per-key replay weights, off wave 0's path: wave 1 takes channels
       // lane and lane + 64 of the previous tape's gates g_{j,c}, j < pn
@@ -723,7 +748,7 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
         }
       }
     }
-    load_state();
+    if constexpr (!PF) load_state();
     load_tape();
   }
   __syncthreads();  // (B1) prologue results in LDS
