@@ -200,6 +200,10 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
   constexpr bool VR = VG && RP;
   __shared__ float s_pwk[VR ? PM * DK : 1];
   __shared__ __align__(16) float s_pgk[VR ? DK : 4];
+  // prefill loop, bf16 and conv width 4: the next chunk's raw conv rows,
+  // [row][channel pair], fetched by the last wave while wave 0 solves
+  constexpr bool PFX = PF && sizeof(TIn) == 2 && KC == 4;
+  __shared__ typename PR::raw s_raw[PFX ? XR * NPAIR : 1];
 
   const int G = p0.Hv / p0.Hk;
   const int n_units = p0.L * p0.B * p0.Hk;
@@ -343,6 +347,7 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
                   : (c < 2 * DK ? p.Hk * DK + hk * DK + (c - DK)
                                 : 2 * p.Hk * DK + hv * DV + (c - 2 * DK));
   };
+  const bool raw_lds = PFX && ch > 0;  // rows fetched ahead into s_raw
   auto load_pair = [&](int j, typename PR::raw* xr, float* w0, float* w1) {
     const int pr = lane + 64 * j;
     const int c0 = 2 * (pr < NPAIR ? pr : NPAIR - 1);
@@ -352,7 +357,7 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
       const int rr = r < nrows ? r : nrows - 1;
       const TIn* base = rr < K - 1 ? ccol + static_cast<size_t>(rr) * p.C
                                    : xcol + static_cast<size_t>(rr - (K - 1)) * p.C;
-      xr[r] = PR::load(base + ch);
+      xr[r] = raw_lds ? s_raw[r * NPAIR + c0 / 2] : PR::load(base + ch);
     }
     if (KC == 4) {
       const floatx4 a0 = *reinterpret_cast<const floatx4*>(cw + static_cast<size_t>(ch) * 4);
@@ -550,6 +555,9 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
       }
     }
 
+    // prefill loop, per-head gate: this lane's A and Oc entries (see below)
+    constexpr int NQ = TMAX * TMAX / 64;
+    float cav[VG || !PF ? 1 : NQ], cov[VG || !PF ? 1 : NQ];
     if constexpr (VG) {
       // Per-key-channel gate: token t's state before it, applied to a_t * k_t,
       // is S0 (gamma_t * k_t) + sum_{i<t} u_i c_{t,i} with c_{t,i} =
@@ -660,8 +668,9 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
         s_cb[lane] = live ? s_gb[lane] : 0.f;
       }
     } else {
-    // T x T coefficients, (t, i) pairs over the lanes, each written in place
-      // of the Gram entries it reads.
+      // T x T coefficients, (t, i) pairs over the lanes, each written in
+      // place of the Gram entries it reads (prefill loop: entry e = t TMAX + i
+      // of A and Oc stays in register e / 64 of lane e % 64).
       float ga[TMAX];
 #pragma unroll
       for (int s = 0; s < TMAX; ++s) ga[s] = s_ga[s];
@@ -675,8 +684,13 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
         const float rki = s_rn[i];
         const float av = s_gb[t] * gm * s_G[t * GLD + i] * s_rn[t] * rki;
         const float ov = gm * s_G[(TMAX + t) * GLD + i] * s_rn[TMAX + t] * rki;
-        s_A[t * ALD + i] = (t < T && i < t) ? av : 0.f;
-        s_Oc[t * ALD + i] = (t < T && i <= t) ? ov : 0.f;
+        if constexpr (PF) {
+          cav[q] = (t < T && i < t) ? av : 0.f;
+          cov[q] = (t < T && i <= t) ? ov : 0.f;
+        } else {
+          s_A[t * ALD + i] = (t < T && i < t) ? av : 0.f;
+          s_Oc[t * ALD + i] = (t < T && i <= t) ? ov : 0.f;
+        }
       }
       if (lane < TMAX) {
         float gm = 1.f;  // gamma_t = a_0 ... a_t
@@ -692,23 +706,54 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // Ti = (I + A)^-1 and M2 = Oc Ti, column j per lane, in registers.
-    if (lane < TMAX) {
+    if constexpr (VG || !PF) {
+      if (lane < TMAX) {
+        const int j = lane;
+        float xc[TMAX];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+          float v = (t == j) ? 1.f : 0.f;
+#pragma unroll
+          for (int a = 0; a < t; ++a) v = fmaf(-s_A[t * ALD + a], xc[a], v);
+          xc[t] = (t < T && j < T) ? v : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+          float m = 0.f;
+#pragma unroll
+          for (int a = 0; a <= t; ++a) m = fmaf(s_Oc[t * ALD + a], xc[a], m);
+          s_B[t * BLD + j] = xc[t];
+          s_B[(TMAX + t) * BLD + j] = m;
+        }
+      }
+    } else {
+      // Prefill loop: the solve sits on every chunk's critical path, so the
+      // coefficients come from the lanes that formed them by readlane
+      // (scalar operands), not one LDS read each (2.1 against 3.0 us per
+      // chunk).  Every lane runs the substitution (lanes past TMAX form zero
+      // columns); lanes j < TMAX store theirs.
+      auto coef = [&](const float* r, int t, int a) {
+        const int e = t * TMAX + a;
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r[e / 64]), e % 64));
+      };
       const int j = lane;
       float xc[TMAX];
 #pragma unroll
       for (int t = 0; t < TMAX; ++t) {
         float v = (t == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int a = 0; a < t; ++a) v = fmaf(-s_A[t * ALD + a], xc[a], v);
+        for (int a = 0; a < t; ++a) v = fmaf(-coef(cav, t, a), xc[a], v);
         xc[t] = (t < T && j < T) ? v : 0.f;
       }
 #pragma unroll
       for (int t = 0; t < TMAX; ++t) {
         float m = 0.f;
 #pragma unroll
-        for (int a = 0; a <= t; ++a) m = fmaf(s_Oc[t * ALD + a], xc[a], m);
-        s_B[t * BLD + j] = xc[t];
-        s_B[(TMAX + t) * BLD + j] = m;
+        for (int a = 0; a <= t; ++a) m = fmaf(coef(cov, t, a), xc[a], m);
+        if (j < TMAX) {
+          s_B[t * BLD + j] = xc[t];
+          s_B[(TMAX + t) * BLD + j] = m;
+        }
       }
     }
   } else {
@@ -749,6 +794,30 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
       }
     }
     if constexpr (!PF) load_state();
+    if constexpr (PFX) {
+      // The last wave (no conv share) fetches the next chunk's raw rows
+      // while wave 0 solves, before its replay operands (fewer live
+      // registers): x rows c0' - (K - 1) .. of chunk c' = ch + 1,
+      // clamped at its end as in load_pair.  This chunk's conv has read
+      // s_raw before (B0'); the next one reads it after the chunk barrier.
+      if (wave == NW - 1 && ch + 1 < nch) {
+        const int c0n = (ch + 1) * TMAX;
+        const int nrn = K - 1 + (p0.T - c0n < TMAX ? p0.T - c0n : TMAX);
+        const TIn* xb = static_cast<const TIn*>(p0.x) + lb * p0.x_ld;
+#pragma unroll 1
+        for (int pr = lane; pr < NPAIR; pr += 64) {
+          const int chn = chan(2 * pr);
+          typename PR::raw v[XR];
+#pragma unroll
+          for (int r = 0; r < XR; ++r) {
+            const int rr = r < nrn ? r : nrn - 1;
+            v[r] = PR::load(xb + static_cast<size_t>(c0n - (K - 1) + rr) * p0.C + chn);
+          }
+#pragma unroll
+          for (int r = 0; r < XR; ++r) s_raw[r * NPAIR + pr] = v[r];
+        }
+      }
+    }
     load_tape();
   }
   __syncthreads();  // (B1) prologue results in LDS
