@@ -60,6 +60,7 @@ struct RollbackArgs {
   int32_t* dev_err;
   int L, B, Hk, Hv, T;
   int n_all;
+  int lpw;  // short tapes: layers per workgroup (set by the launcher)
 };
 
 // Conv-window rollback.

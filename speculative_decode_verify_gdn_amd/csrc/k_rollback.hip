@@ -63,8 +63,7 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
   static_assert(TM == kWave, "one lane per tape step");
 
   const int tid = threadIdx.x;
-  int rblk, hv;
-  size_t lb;
+  int rblk, hv, bb, l0, l1;
   if constexpr (LT) {
     // long tapes: the G v-heads x NRBLK row blocks of one (layer, seq,
     // k-head) read the same k rows n times over; they take consecutive slots
@@ -75,33 +74,46 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
     if (us.unit >= p.L * p.B * p.Hk) return;
     rblk = us.sub % NRBLK;
     hv = (us.unit % p.Hk) * G + us.sub / NRBLK;
-    lb = us.unit / p.Hk;
+    const int lb0 = us.unit / p.Hk;
+    bb = lb0 % p.B;
+    l0 = lb0 / p.B;
+    l1 = l0 + 1;
   } else {
+    // short tapes: layers l0 .. l0 + lpw - 1 of one (seq, v-head, row
+    // block), in turn.  The accepted length is read once, so a sequence
+    // that accepted nothing costs one workgroup per lpw layers.
+    const int lpw = p.lpw > 0 ? p.lpw : 1;
     rblk = bid % NRBLK;
-    const int rest = bid / NRBLK;
+    int rest = bid / NRBLK;
     hv = rest % p.Hv;
-    lb = rest / p.Hv;
+    rest /= p.Hv;
+    bb = rest % p.B;
+    l0 = (rest / p.B) * lpw;
+    l1 = l0 + lpw < p.L ? l0 + lpw : p.L;
   }
-  const int bb = static_cast<int>(lb % p.B);
-  const int l = static_cast<int>(lb / p.B);
   const int T = p.T;
   const int n = p.n_keep ? p.n_keep[bb] : p.n_all;
+  const bool reporter = l0 == 0 && hv == 0 && rblk == 0;
   if (n == 0) return;
   if (n < 0 || n > T) {
-    if (tid == 0 && p.dev_err && l == 0 && hv == 0 && rblk == 0) atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
+    if (tid == 0 && p.dev_err && reporter) atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
     return;
   }
   const int hk = hv / (p.Hv / p.Hk);
   const int r0 = rblk * RB;
-  float* Sblk = p.S + ((lb * p.Hv + hv) * DV + r0) * static_cast<size_t>(DK);
+  float* Sblk = nullptr;
 
   // Snapshot loads first (unconditional: every thread owns VPT float4).
   floatx4 sv[VPT];
+  auto load_sv = [&](size_t lb, int t) {
+    Sblk = p.S + ((lb * p.Hv + hv) * DV + r0) * static_cast<size_t>(DK);
 #pragma unroll
-  for (int v = 0; v < VPT; ++v) {
-    const int e = tid + v * NT;
-    sv[v] = reinterpret_cast<const floatx4*>(Sblk)[e < NV ? e : 0];
-  }
+    for (int v = 0; v < VPT; ++v) {
+      const int e = t + v * NT;
+      sv[v] = reinterpret_cast<const floatx4*>(Sblk)[e < NV ? e : 0];
+    }
+  };
+  load_sv(static_cast<size_t>(l0) * p.B + bb, tid);
 
   if (tid == 0) s_bad = 0;
   __syncthreads();
@@ -112,9 +124,17 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
   }
   __syncthreads();
   if (s_bad) {
-    if (tid == 0 && p.dev_err && l == 0 && hv == 0 && rblk == 0) atomicOr(p.dev_err, GDN_DEV_ERR_PATH);
+    if (tid == 0 && p.dev_err && reporter) atomicOr(p.dev_err, GDN_DEV_ERR_PATH);
     return;
   }
+  for (int l = l0; l < l1; ++l) {
+  const size_t lb = static_cast<size_t>(l) * p.B + bb;
+  // short tapes: an opaque copy of the lane index per layer, so that
+  // lane-dependent addresses are formed inside the loop rather than held
+  // across it (long tapes run one layer)
+  int tid = threadIdx.x;
+  if constexpr (!LT) asm volatile("" : "+v"(tid));
+  if (l > l0) load_sv(lb, tid);
   if (tid < kWave) {
     // wave 0, one lane per step: every gate load in flight at once, then
     // w_i = prod_{j>i} g_{p_j} by a suffix-product scan (shuffles on every
@@ -215,18 +235,40 @@ __device__ __forceinline__ void tape_rollback_body(const RollbackArgs& p, int bi
     const floatx4 acc = sv[v] * gam + *reinterpret_cast<const floatx4*>(s_buf + r * ULD + c);
     if (e < NV) reinterpret_cast<floatx4*>(Sblk)[e] = acc;
   }
+  }  // layers
 }
 
-// Workgroups of the state rollback: one per (layer, seq, v-head, row block);
-// with long tapes the (layer, seq, k-head) units are rounded up to a
-// multiple of the XCD count.
+// Short tapes: layers per workgroup.  As few workgroups as keep the chip
+// streaming when every sequence replays (about 16K), since each launched
+// workgroup costs its dispatch and one load even when its sequence accepted
+// nothing.
 template <int DK, int DV>
-long long state_grid(const RollbackArgs& a) {
+int rb_layers(const RollbackArgs& a) {
   constexpr int RB0 = 256 * 4 * 4 / DK;
   constexpr int NRBLK = DV / (RB0 < DV ? RB0 : DV);
-  const long long units = static_cast<long long>(a.L) * a.B * a.Hk;
-  const long long padded = a.T > 16 ? (units + kNumXcd - 1) / kNumXcd * kNumXcd : units;
-  return padded * (a.Hv / a.Hk) * NRBLK;
+  const long long units = static_cast<long long>(a.L) * a.B * a.Hv * NRBLK;
+  const long long lpw = (units + 16383) / 16384;
+  return static_cast<int>(lpw < 1 ? 1 : (lpw > a.L ? a.L : lpw));
+}
+
+// Workgroups of the state rollback: short tapes, one per (lpw layers, seq,
+// v-head, row block); long tapes, one per (layer, seq, v-head, row block),
+// the (layer, seq, k-head) units rounded up to a multiple of the XCD count.
+// The returned args carry the layers per workgroup.
+template <int DK, int DV>
+long long state_grid(const RollbackArgs& a, RollbackArgs* out = nullptr) {
+  constexpr int RB0 = 256 * 4 * 4 / DK;
+  constexpr int NRBLK = DV / (RB0 < DV ? RB0 : DV);
+  if (out) *out = a;
+  if (a.T > 16) {
+    const long long units = static_cast<long long>(a.L) * a.B * a.Hk;
+    const long long padded = (units + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (out) out->lpw = 1;
+    return padded * (a.Hv / a.Hk) * NRBLK;
+  }
+  const int lpw = rb_layers<DK, DV>(a);
+  if (out) out->lpw = lpw;
+  return static_cast<long long>((a.L + lpw - 1) / lpw) * a.B * a.Hv * NRBLK;
 }
 
 template <int DK, int DV, bool LT>
@@ -235,8 +277,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LT ? 7 : 8)
 }
 
 template <int DK, int DV>
-hipError_t launch_rb(const RollbackArgs& a, hipStream_t s) {
-  const long long grid = state_grid<DK, DV>(a);
+hipError_t launch_rb(const RollbackArgs& a0, hipStream_t s) {
+  RollbackArgs a;
+  const long long grid = state_grid<DK, DV>(a0, &a);
   if (grid > 0x7fffffffLL || a.T > 64) return hipErrorInvalidValue;
   if (a.T > 16) hipLaunchKernelGGL((k_tape_rollback<DK, DV, true>), dim3(grid), dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_tape_rollback<DK, DV, false>), dim3(grid), dim3(256), 0, s, a);
@@ -469,8 +512,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LT ? 7 : 8)
 }
 
 template <int DK, int DV>
-hipError_t launch_rr(const RollbackArgs& r, const ConvRollbackArgs& c, int dtype, hipStream_t s) {
-  const long long n_state = state_grid<DK, DV>(r);
+hipError_t launch_rr(const RollbackArgs& r0, const ConvRollbackArgs& c, int dtype, hipStream_t s) {
+  RollbackArgs r;
+  const long long n_state = state_grid<DK, DV>(r0, &r);
   const int esz = dtype == 1 ? 2 : 4;
   const int conv_y = (c.C * esz / 16 + 255) / 256;
   const long long grid = n_state + static_cast<long long>(c.L) * c.B * conv_y;
