@@ -10,10 +10,12 @@
 // tape, and one write -- no products with the state.  n = 0 returns before
 // touching the state, so the cost is one state pass plus O(n) tape bytes.
 //
-// Layout: one 256-thread workgroup per (layer, seq, v-head, RB-row block);
-// every thread owns 4 float4 of the block, read and written fully coalesced
-// (whole cache lines), and many small workgroups per CU keep the state
-// streaming.  The block's n tape rows (k: n x Dk, w-scaled u: n x RB) are
+// Layout: one 256-thread workgroup per (layer, seq, v-head, RB-row block)
+// -- for tapes of at most 16 steps, per (several layers, seq, v-head, row
+// block), walked in turn, so that a sequence that accepted nothing costs
+// few workgroups; every thread owns 4 float4 of the block, read and written
+// fully coalesced (whole cache lines), and many small workgroups per CU keep
+// the state streaming.  The block's n tape rows (k: n x Dk, w-scaled u: n x RB) are
 // staged in LDS, the rank-n update U = sum_i w_i u_i k_i^T is formed on fp32
 // MFMA (four steps per instruction), and it reaches the threads' layout
 // through LDS: S_n = gamma S0 + U.
