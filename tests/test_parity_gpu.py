@@ -668,6 +668,51 @@ def test_rollback_every_accepted_length(D, tree):
     np.testing.assert_array_equal(wi.cpu().numpy(), wi_ref)
 
 
+@pytest.mark.parametrize("D,B", [(32, 600), (128, 160)])
+def test_rollback_layer_walk_ragged(D, B):
+    """Short tapes: at this size each workgroup of the state rollback walks
+    several layers (at most ~16K workgroups), and L = 7 leaves a shorter last
+    group.  Sequences that accepted nothing sit between ones that did; the
+    state equals the oracle's tape_rollback per (layer, seq, v-head) and the
+    idle sequences' state is untouched, in both rollback calls."""
+    _need_gpu()
+    T, L, Hk, Hv = 16, 7, 2, 4
+    rows = min(256 * 16 // D, D)
+    units = L * B * Hv * (D // rows)
+    lpw = -(-units // 16384)
+    assert 1 < lpw < L and L % lpw != 0  # several layers per workgroup, ragged
+    sh = gb.GdnShape(L, B, Hk, Hv, D, D, 4, True, 1e-6, torch.bfloat16)
+    gen = torch.Generator().manual_seed(700 + D)
+    S0 = torch.randn((L, B, Hv, D, D), generator=gen) * 0.1
+    u = torch.randn((L, B, T, Hv, D), generator=gen)
+    k = torch.nn.functional.normalize(torch.randn((L, B, T, Hk, D), generator=gen), dim=-1)
+    g = 0.6 + 0.4 * torch.rand((L, B, T, Hv), generator=gen)
+    nk = torch.randint(0, T + 1, (B,), generator=gen, dtype=torch.int32)
+    nk[::3] = 0
+    nk[1] = T
+    cs0 = torch.randn((L, B, 3, sh.C), generator=gen).to(torch.bfloat16)
+    x = torch.randn((L, B, T, sh.C), generator=gen).to(torch.bfloat16)
+    tape = gb.Tape(u.to(DEV), k.to(DEV), g.to(DEV))
+    osh = oracle.Shape(L=L, B=B, Hk=Hk, Hv=Hv, Dk=D, Dv=D, K=4, silu=True, eps=1e-6)
+    ref = oracle.tape_rollback(osh, S0.double().numpy(), u.double().numpy(), k.double().numpy(),
+                               g.double().numpy(), nk.numpy(), None)
+    idle = (nk == 0).nonzero().flatten()
+    print("rollback layer walk", D, B, "lpw", lpw, flush=True)
+    S = S0.to(DEV).clone()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gb.gdn_tape_rollback(sh, S, tape, nk.to(DEV), dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    check_units("S (tape rollback, layer walk)", S, ref, "state", 1e-5)
+    assert torch.equal(S[:, idle].cpu(), S0[:, idle])
+    S, cs = S0.to(DEV).clone(), cs0.to(DEV).clone()
+    gb.gdn_round_rollback(sh, S, tape, cs, x.to(DEV), nk.to(DEV), dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    check_units("S (round rollback, layer walk)", S, ref, "state", 1e-5)
+    assert torch.equal(S[:, idle].cpu(), S0[:, idle])
+
+
 # ------------------------------------------------------- device-side errors -
 
 def test_dev_err_bad_n_keep_leaves_state():
