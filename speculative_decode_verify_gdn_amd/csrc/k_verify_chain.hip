@@ -418,6 +418,97 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
     }
   };
 
+  // Per-key gate: the walk that forms row t of A and Oc (see the per-key
+  // block of the prologue) for one token, on one 16-lane group (channels
+  // 8 li .. 8 li + 7 per lane).  A token's walk writes only its own rows.
+    const int gq = lane >> 4, li = lane & 15;
+    auto read_pre = [&](int n, float* y) {  // channels 8 li .. +7 of pre-split row n
+      const unsigned char* row = s_kq + n * KQS + (li / 4) * 128 + ((li % 4) / 2) * 8;
+      const int kg = 2 * (li % 2);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + (kg + hf) * 32);
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + (kg + hf) * 32 + 16);
+        y[4 * hf] = __uint_as_float(hi.x << 16) + __uint_as_float(lo.x << 16);
+        y[4 * hf + 1] = __uint_as_float(hi.x & 0xffff0000u) + __uint_as_float(lo.x & 0xffff0000u);
+        y[4 * hf + 2] = __uint_as_float(hi.y << 16) + __uint_as_float(lo.y << 16);
+        y[4 * hf + 3] = __uint_as_float(hi.y & 0xffff0000u) + __uint_as_float(lo.y & 0xffff0000u);
+      }
+    };
+    auto write_pre = [&](int n, const float* y) {
+      unsigned char* row = s_kq + n * KQS + (li / 4) * 128 + ((li % 4) / 2) * 8;
+      const int kg = 2 * (li % 2);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint32_t h0, l0, h1, l1;
+        split_pair_each(y[4 * hf], y[4 * hf + 1], h0, l0);
+        split_pair_each(y[4 * hf + 2], y[4 * hf + 3], h1, l1);
+        *reinterpret_cast<uint2*>(row + (kg + hf) * 32) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(row + (kg + hf) * 32 + 16) = make_uint2(l0, l1);
+      }
+    };
+    auto gates8 = [&](int t, float* a) {
+      const u32x4 r = *reinterpret_cast<const u32x4*>(s_av + t * DK + 8 * li);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        a[2 * w] = __uint_as_float(r[w] << 16);
+        a[2 * w + 1] = __uint_as_float(r[w] & 0xffff0000u);
+      }
+    };
+    auto kn8 = [&](int t, float* k) {  // normalised k of token t
+      const floatx4 k0 = *reinterpret_cast<const floatx4*>(s_kf + t * DK + 8 * li);
+      const floatx4 k1 = *reinterpret_cast<const floatx4*>(s_kf + t * DK + 8 * li + 4);
+      const float r = s_rn[t];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k[e] = k0[e] * r;
+        k[4 + e] = k1[e] * r;
+      }
+    };
+  auto walk_token = [&](int t) {
+    if (t < T) {
+      float kv[8], qv[8], w[8];
+      kn8(t, kv);
+      read_pre(TMAX + t, qv);
+      const float rq = s_rn[TMAX + t];
+      float kq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qv[e] *= rq;
+        kq = fmaf(kv[e], qv[e], kq);
+      }
+      gates8(t, w);
+      const float bt = s_gb[t];
+      for (int i = t - 1; i >= 0; --i) {
+        float ki[8], ai[8];
+        kn8(i, ki);
+        gates8(i, ai);
+        float cc = 0.f, dd = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kw = ki[e] * w[e];
+          cc = fmaf(kw, kv[e], cc);
+          dd = fmaf(kw, qv[e], dd);
+          w[e] *= ai[e];
+        }
+        cc = sum16(cc);
+        dd = sum16(dd);
+        if (li == 0) {
+          s_A[t * ALD + i] = bt * cc;
+          s_Oc[t * ALD + i] = dd;
+        }
+      }
+      kq = sum16(kq);
+      if (li == 0) s_Oc[t * ALD + t] = kq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kv[e] *= w[e];
+        qv[e] *= w[e];
+      }
+      write_pre(t, kv);
+      write_pre(TMAX + t, qv);
+    }
+  };
   if (wave == 0) {
     // ---------------------------------------------------------- prologue --
     // Gates (clamped, unconditional loads).
@@ -570,96 +661,19 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
       for (int e = lane; e < 2 * TMAX * ALD; e += 64) s_G[e] = 0.f;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int gq = lane >> 4, li = lane & 15;
-      auto read_pre = [&](int n, float* y) {  // channels 8 li .. +7 of pre-split row n
-        const unsigned char* row = s_kq + n * KQS + (li / 4) * 128 + ((li % 4) / 2) * 8;
-        const int kg = 2 * (li % 2);
+      if constexpr (PF) {
+        // the prefill loop shares the walks out over the waves (the other
+        // waves have no state to load): wave w's groups take tokens w,
+        // 7 - w, 8 + w and 15 - w, pairs of equal total length
+        static_assert(!PF || (TMAX == 16 && NW == 4), "four tokens per wave");
+        __syncthreads();  // (B_w0) norms, gates and zeroed A/Oc in LDS
+        walk_token(gq == 0 ? 0 : (gq == 1 ? 7 : (gq == 2 ? 8 : 15)));
+        __syncthreads();  // (B_w1) every token's walk is done
+      } else {
+        // 16-lane group gq takes tokens paired for equal walks
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const uint2 hi = *reinterpret_cast<const uint2*>(row + (kg + hf) * 32);
-          const uint2 lo = *reinterpret_cast<const uint2*>(row + (kg + hf) * 32 + 16);
-          y[4 * hf] = __uint_as_float(hi.x << 16) + __uint_as_float(lo.x << 16);
-          y[4 * hf + 1] = __uint_as_float(hi.x & 0xffff0000u) + __uint_as_float(lo.x & 0xffff0000u);
-          y[4 * hf + 2] = __uint_as_float(hi.y << 16) + __uint_as_float(lo.y << 16);
-          y[4 * hf + 3] = __uint_as_float(hi.y & 0xffff0000u) + __uint_as_float(lo.y & 0xffff0000u);
-        }
-      };
-      auto write_pre = [&](int n, const float* y) {
-        unsigned char* row = s_kq + n * KQS + (li / 4) * 128 + ((li % 4) / 2) * 8;
-        const int kg = 2 * (li % 2);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          uint32_t h0, l0, h1, l1;
-          split_pair_each(y[4 * hf], y[4 * hf + 1], h0, l0);
-          split_pair_each(y[4 * hf + 2], y[4 * hf + 3], h1, l1);
-          *reinterpret_cast<uint2*>(row + (kg + hf) * 32) = make_uint2(h0, h1);
-          *reinterpret_cast<uint2*>(row + (kg + hf) * 32 + 16) = make_uint2(l0, l1);
-        }
-      };
-      auto gates8 = [&](int t, float* a) {
-        const u32x4 r = *reinterpret_cast<const u32x4*>(s_av + t * DK + 8 * li);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          a[2 * w] = __uint_as_float(r[w] << 16);
-          a[2 * w + 1] = __uint_as_float(r[w] & 0xffff0000u);
-        }
-      };
-      auto kn8 = [&](int t, float* k) {  // normalised k of token t
-        const floatx4 k0 = *reinterpret_cast<const floatx4*>(s_kf + t * DK + 8 * li);
-        const floatx4 k1 = *reinterpret_cast<const floatx4*>(s_kf + t * DK + 8 * li + 4);
-        const float r = s_rn[t];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k[e] = k0[e] * r;
-          k[4 + e] = k1[e] * r;
-        }
-      };
-      // 16-lane group gq takes tokens paired for equal walks
-#pragma unroll
-      for (int j = 0; j < TMAX / 4; ++j) {
-        const int t = (j % 2 == 0) ? 8 * (j / 2) + gq : 8 * (j / 2) + 7 - gq;
-        if (t < T) {
-          float kv[8], qv[8], w[8];
-          kn8(t, kv);
-          read_pre(TMAX + t, qv);
-          const float rq = s_rn[TMAX + t];
-          float kq = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            qv[e] *= rq;
-            kq = fmaf(kv[e], qv[e], kq);
-          }
-          gates8(t, w);
-          const float bt = s_gb[t];
-          for (int i = t - 1; i >= 0; --i) {
-            float ki[8], ai[8];
-            kn8(i, ki);
-            gates8(i, ai);
-            float cc = 0.f, dd = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float kw = ki[e] * w[e];
-              cc = fmaf(kw, kv[e], cc);
-              dd = fmaf(kw, qv[e], dd);
-              w[e] *= ai[e];
-            }
-            cc = sum16(cc);
-            dd = sum16(dd);
-            if (li == 0) {
-              s_A[t * ALD + i] = bt * cc;
-              s_Oc[t * ALD + i] = dd;
-            }
-          }
-          kq = sum16(kq);
-          if (li == 0) s_Oc[t * ALD + t] = kq;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            kv[e] *= w[e];
-            qv[e] *= w[e];
-          }
-          write_pre(t, kv);
-          write_pre(TMAX + t, qv);
-        }
+        for (int j = 0; j < TMAX / 4; ++j)
+          walk_token((j % 2 == 0) ? 8 * (j / 2) + gq : 8 * (j / 2) + 7 - gq);
       }
       if (lane < TMAX) {
         const bool live = lane < T;
@@ -792,6 +806,11 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
           s_pgk[lane + 64 * h] = w;
         }
       }
+    }
+    if constexpr (PF && VG) {
+      __syncthreads();  // (B_w0)
+      walk_token(gq == 0 ? wave : (gq == 1 ? 7 - wave : (gq == 2 ? 8 + wave : 15 - wave)));
+      __syncthreads();  // (B_w1)
     }
     if constexpr (!PF) load_state();
     if constexpr (PFX) {
