@@ -465,7 +465,10 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
         k[4 + e] = k1[e] * r;
       }
     };
-  auto walk_token = [&](int t) {
+  // Rows i in [lo, hi) of token t (hi <= t): the rows above hi only
+  // advance the gate product.  `last` also finishes the token: its diagonal
+  // Oc entry and the gamma-scaled operand rows.
+  auto walk_part = [&](int t, int lo, int hi, bool last) {
     if (t < T) {
       float kv[8], qv[8], w[8];
       kn8(t, kv);
@@ -479,7 +482,13 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
       }
       gates8(t, w);
       const float bt = s_gb[t];
-      for (int i = t - 1; i >= 0; --i) {
+      for (int i = t - 1; i >= hi; --i) {
+        float ai[8];
+        gates8(i, ai);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] *= ai[e];
+      }
+      for (int i = hi - 1; i >= lo; --i) {
         float ki[8], ai[8];
         kn8(i, ki);
         gates8(i, ai);
@@ -498,16 +507,25 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
           s_Oc[t * ALD + i] = dd;
         }
       }
-      kq = sum16(kq);
-      if (li == 0) s_Oc[t * ALD + t] = kq;
+      if (last) {
+        kq = sum16(kq);
+        if (li == 0) s_Oc[t * ALD + t] = kq;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kv[e] *= w[e];
-        qv[e] *= w[e];
+        for (int e = 0; e < 8; ++e) {
+          kv[e] *= w[e];
+          qv[e] *= w[e];
+        }
+        write_pre(t, kv);
+        write_pre(TMAX + t, qv);
       }
-      write_pre(t, kv);
-      write_pre(TMAX + t, qv);
     }
+  };
+  // The prefill loop's share for 16-lane group g = 4 wave + gq: the upper
+  // half of token g's walk and the lower half of token 15 - g's (at most 8
+  // full steps a group; the walk of token t has t).
+  auto walk_share = [&](int g) {
+    walk_part(g, (g + 1) / 2, g, false);
+    walk_part(15 - g, 0, (16 - g) / 2, true);
   };
   if (wave == 0) {
     // ---------------------------------------------------------- prologue --
@@ -663,17 +681,19 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       if constexpr (PF) {
         // the prefill loop shares the walks out over the waves (the other
-        // waves have no state to load): wave w's groups take tokens w,
-        // 7 - w, 8 + w and 15 - w, pairs of equal total length
+        // waves have no state to load), halves of two tokens per group
         static_assert(!PF || (TMAX == 16 && NW == 4), "four tokens per wave");
         __syncthreads();  // (B_w0) norms, gates and zeroed A/Oc in LDS
-        walk_token(gq == 0 ? 0 : (gq == 1 ? 7 : (gq == 2 ? 8 : 15)));
+        walk_share(gq);
         __syncthreads();  // (B_w1) every token's walk is done
       } else {
         // 16-lane group gq takes tokens paired for equal walks
 #pragma unroll
         for (int j = 0; j < TMAX / 4; ++j)
-          walk_token((j % 2 == 0) ? 8 * (j / 2) + gq : 8 * (j / 2) + 7 - gq);
+        {
+          const int t = (j % 2 == 0) ? 8 * (j / 2) + gq : 8 * (j / 2) + 7 - gq;
+          walk_part(t, 0, t, true);
+        }
       }
       if (lane < TMAX) {
         const bool live = lane < T;
@@ -809,7 +829,7 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
     }
     if constexpr (PF && VG) {
       __syncthreads();  // (B_w0)
-      walk_token(gq == 0 ? wave : (gq == 1 ? 7 - wave : (gq == 2 ? 8 + wave : 15 - wave)));
+      walk_share(4 * wave + gq);
       __syncthreads();  // (B_w1)
     }
     if constexpr (!PF) load_state();
