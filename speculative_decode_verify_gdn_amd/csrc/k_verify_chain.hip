@@ -216,8 +216,11 @@ __attribute__((amdgpu_waves_per_eu(PF && VG ? 2 : (PF || (VG && RP) ? 3 : 4)))) 
     // The sequences that replay (and write their state back) go first, so
     // that one pass of workgroups over the CUs (workgroup i on CU i mod the
     // CU count) spreads them evenly instead of letting a CU draw several.
-    // Larger batches run many passes, which even out by themselves.
-    if (p0.prev_n_keep && p0.B <= 256) {
+    // Larger batches run many passes, which even out by themselves.  The
+    // per-key form keeps index order: at three waves per SIMD its rounds run
+    // several passes at every batch size, and the reordering measured slower
+    // there (256 sequences: 356 against 327 us per layer).
+    if (!VG && p0.prev_n_keep && p0.B <= 256) {
       const int q = static_cast<int>(lb % p0.B);
       lb = static_cast<size_t>(l) * p0.B + writers_first_seq(p0.prev_n_keep, p0.B, p0.pT, q);
     }
