@@ -21,8 +21,8 @@
 // through LDS: S_n = gamma S0 + U.
 //
 // Conv window: new row j = row n+j of [old window; x[p_0]; ...; x[p_{n-1}]],
-// copied 16 bytes per thread; all sources are loaded before any store, so
-// the in-place update is safe.
+// copied 16 bytes per thread by one workgroup per (several layers, seq);
+// all sources are loaded before any store, so the in-place update is safe.
 
 #include "gdn_common.hpp"
 #include "gdn_kernels.hpp"
@@ -407,16 +407,21 @@ hipError_t launch_rb_vg(const RollbackArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 16-byte chunks of channels per thread; KM1 = K-1 window rows.
+// One workgroup per (lpw layers, seq): the window indices depend on the
+// sequence only, so they are formed once; then every layer's rows are copied
+// 16 bytes of channels per thread, CB chunks' loads in flight together.
+// KM1 = K-1 window rows.
 template <int ESZ, int KM1>
-__device__ __forceinline__ void conv_rollback_body(const ConvRollbackArgs& p, size_t lb, int by) {
+__device__ __forceinline__ void conv_rollback_body(const ConvRollbackArgs& p, int bid, int lpw) {
   constexpr int EPC = 16 / ESZ;  // elements per chunk
+  constexpr int CB = KM1 <= 4 ? 8 / KM1 : 1;  // at most 8 rows of loads in flight (64 VGPRs)
   const int tid = threadIdx.x;
-  const int bb = static_cast<int>(lb % p.B);
-  const int l = static_cast<int>(lb / p.B);
+  const int bb = bid % p.B;
+  const int l0 = (bid / p.B) * lpw;
+  const int l1 = l0 + lpw < p.L ? l0 + lpw : p.L;
   const int n = p.n_keep ? p.n_keep[bb] : p.n_all;
   const int T = p.T;
-  const bool first_block = (l == 0 && by == 0);
+  const bool first_block = l0 == 0;
   if (n < 0 || n > T) {
     if (first_block && tid == 0 && p.dev_err) atomicOr(p.dev_err, GDN_DEV_ERR_N_KEEP);
     return;
@@ -444,41 +449,71 @@ __device__ __forceinline__ void conv_rollback_body(const ConvRollbackArgs& p, si
     for (int j = 0; j < KM1; ++j) p.win_idx[static_cast<size_t>(bb) * KM1 + j] = idx[j];
   }
   if (n == 0) return;  // window unchanged
-  const size_t chunk = static_cast<size_t>(by) * 256 + tid;
-  const size_t row_chunks = static_cast<size_t>(p.C) / EPC;
-  if (chunk >= row_chunks) return;
-  const uint4* xs = static_cast<const uint4*>(p.x);
-  uint4* cs = static_cast<uint4*>(p.conv_state);
-  // sources first (a select of addresses, so every load is unconditional)
-  const uint4* src[KM1];
+  const int row_chunks = p.C / EPC;
+  const u32x4* xs = static_cast<const u32x4*>(p.x);
+  u32x4* cs = static_cast<u32x4*>(p.conv_state);
+  for (int l = l0; l < l1; ++l) {
+    const size_t lb = static_cast<size_t>(l) * p.B + bb;
+    u32x4* crow = cs + lb * KM1 * row_chunks;
+    // each new row's source row (a select of addresses, so every load is
+    // unconditional)
+    const u32x4* src[KM1];
 #pragma unroll
-  for (int j = 0; j < KM1; ++j) {
-    const int id = idx[j];
-    src[j] = id < 0 ? cs + (lb * KM1 + (KM1 + id)) * row_chunks + chunk
-                    : xs + lb * (p.x_ld / EPC) + id * row_chunks + chunk;
+    for (int j = 0; j < KM1; ++j) {
+      const int id = idx[j];
+      src[j] = id < 0 ? crow + (KM1 + id) * row_chunks
+                      : xs + lb * (p.x_ld / EPC) + static_cast<size_t>(id) * row_chunks;
+    }
+    // whole batches of CB chunks: every source first, then the stores; a
+    // chunk's new rows come from its own old rows, so the in-place update
+    // is safe
+    int c0 = 0;
+    for (; c0 + CB * 256 <= row_chunks; c0 += CB * 256) {
+      u32x4 v[CB * KM1];
+#pragma unroll
+      for (int q = 0; q < CB; ++q)
+#pragma unroll
+        for (int j = 0; j < KM1; ++j) v[q * KM1 + j] = src[j][c0 + q * 256 + tid];
+#pragma unroll
+      for (int q = 0; q < CB; ++q)
+#pragma unroll
+        for (int j = 0; j < KM1; ++j) crow[j * row_chunks + c0 + q * 256 + tid] = v[q * KM1 + j];
+    }
+    // the rest, one chunk per thread
+    for (int ch = c0 + tid; ch < row_chunks; ch += 256) {
+      u32x4 v[KM1];
+#pragma unroll
+      for (int j = 0; j < KM1; ++j) v[j] = src[j][ch];
+#pragma unroll
+      for (int j = 0; j < KM1; ++j) crow[j * row_chunks + ch] = v[j];
+    }
   }
-  uint4 v[KM1];
-#pragma unroll
-  for (int j = 0; j < KM1; ++j) v[j] = *src[j];
-#pragma unroll
-  for (int j = 0; j < KM1; ++j) cs[(lb * KM1 + j) * row_chunks + chunk] = v[j];
+}
+
+// Layers per conv workgroup: as few as leave about 2K workgroups, so that a
+// round in which few sequences accepted anything launches few of them.
+inline int conv_layers(const ConvRollbackArgs& a) {
+  const long long lpw = (static_cast<long long>(a.L) * a.B + 2047) / 2048;
+  return static_cast<int>(lpw < 1 ? 1 : (lpw > a.L ? a.L : lpw));
 }
 
 template <int ESZ, int KM1>
-__global__ __launch_bounds__(256) void k_conv_rollback(ConvRollbackArgs p) {
-  conv_rollback_body<ESZ, KM1>(p, blockIdx.x, blockIdx.y);
+__global__ __launch_bounds__(256) void k_conv_rollback(ConvRollbackArgs p, int lpw) {
+  conv_rollback_body<ESZ, KM1>(p, blockIdx.x, lpw);
 }
 
 template <int ESZ>
-hipError_t launch_crb(const ConvRollbackArgs& a, dim3 grid, hipStream_t s) {
+hipError_t launch_crb(const ConvRollbackArgs& a, hipStream_t s) {
+  const int lpw = conv_layers(a);
+  const dim3 grid(static_cast<unsigned>((a.L + lpw - 1) / lpw) * a.B);
   switch (a.K) {
-    case 2: hipLaunchKernelGGL((k_conv_rollback<ESZ, 1>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_conv_rollback<ESZ, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_conv_rollback<ESZ, 3>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((k_conv_rollback<ESZ, 4>), grid, dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((k_conv_rollback<ESZ, 5>), grid, dim3(256), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((k_conv_rollback<ESZ, 6>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_conv_rollback<ESZ, 7>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_conv_rollback<ESZ, 1>), grid, dim3(256), 0, s, a, lpw); break;
+    case 3: hipLaunchKernelGGL((k_conv_rollback<ESZ, 2>), grid, dim3(256), 0, s, a, lpw); break;
+    case 4: hipLaunchKernelGGL((k_conv_rollback<ESZ, 3>), grid, dim3(256), 0, s, a, lpw); break;
+    case 5: hipLaunchKernelGGL((k_conv_rollback<ESZ, 4>), grid, dim3(256), 0, s, a, lpw); break;
+    case 6: hipLaunchKernelGGL((k_conv_rollback<ESZ, 5>), grid, dim3(256), 0, s, a, lpw); break;
+    case 7: hipLaunchKernelGGL((k_conv_rollback<ESZ, 6>), grid, dim3(256), 0, s, a, lpw); break;
+    case 8: hipLaunchKernelGGL((k_conv_rollback<ESZ, 7>), grid, dim3(256), 0, s, a, lpw); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -498,18 +533,18 @@ hipError_t launch_tape_rollback(const RollbackArgs& a, int dk, int dv, hipStream
 
 namespace {
 
-// Both rollbacks of a round in one launch: the state workgroups first, then
-// the conv-window ones, which fill the tail of the state pass.  Built for
-// the common conv width (K = 4); other widths take the two launches.
+// Both rollbacks of a round in one launch: the conv-window workgroups first
+// (few, each walking its layers, so they overlap the state pass), then the
+// state ones.  Built for the common conv width (K = 4); other widths take
+// the two launches.
 template <int DK, int DV, int ESZ, bool LT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LT ? 7 : 8))) void k_round_rollback(RollbackArgs r, ConvRollbackArgs c,
-                                                        int n_state, int conv_y) {
+                                                        int n_conv, int conv_lpw) {
   const int bid = blockIdx.x;
-  if (bid < n_state) {
-    tape_rollback_body<DK, DV, LT>(r, bid);
+  if (bid < n_conv) {
+    conv_rollback_body<ESZ, 3>(c, bid, conv_lpw);
   } else {
-    const int q = bid - n_state;
-    conv_rollback_body<ESZ, 3>(c, static_cast<size_t>(q / conv_y), q % conv_y);
+    tape_rollback_body<DK, DV, LT>(r, bid - n_conv);
   }
 }
 
@@ -517,17 +552,17 @@ template <int DK, int DV>
 hipError_t launch_rr(const RollbackArgs& r0, const ConvRollbackArgs& c, int dtype, hipStream_t s) {
   RollbackArgs r;
   const long long n_state = state_grid<DK, DV>(r0, &r);
-  const int esz = dtype == 1 ? 2 : 4;
-  const int conv_y = (c.C * esz / 16 + 255) / 256;
-  const long long grid = n_state + static_cast<long long>(c.L) * c.B * conv_y;
+  const int conv_lpw = conv_layers(c);
+  const long long n_conv = static_cast<long long>((c.L + conv_lpw - 1) / conv_lpw) * c.B;
+  const long long grid = n_conv + n_state;
   if (grid > 0x7fffffffLL || r.T > 64 || c.K != 4) return hipErrorInvalidValue;
-  const int ns = static_cast<int>(n_state);
+  const int nc = static_cast<int>(n_conv);
   if (r.T > 16) {
-    if (dtype == 1) hipLaunchKernelGGL((k_round_rollback<DK, DV, 2, true>), dim3(grid), dim3(256), 0, s, r, c, ns, conv_y);
-    else hipLaunchKernelGGL((k_round_rollback<DK, DV, 4, true>), dim3(grid), dim3(256), 0, s, r, c, ns, conv_y);
+    if (dtype == 1) hipLaunchKernelGGL((k_round_rollback<DK, DV, 2, true>), dim3(grid), dim3(256), 0, s, r, c, nc, conv_lpw);
+    else hipLaunchKernelGGL((k_round_rollback<DK, DV, 4, true>), dim3(grid), dim3(256), 0, s, r, c, nc, conv_lpw);
   } else {
-    if (dtype == 1) hipLaunchKernelGGL((k_round_rollback<DK, DV, 2, false>), dim3(grid), dim3(256), 0, s, r, c, ns, conv_y);
-    else hipLaunchKernelGGL((k_round_rollback<DK, DV, 4, false>), dim3(grid), dim3(256), 0, s, r, c, ns, conv_y);
+    if (dtype == 1) hipLaunchKernelGGL((k_round_rollback<DK, DV, 2, false>), dim3(grid), dim3(256), 0, s, r, c, nc, conv_lpw);
+    else hipLaunchKernelGGL((k_round_rollback<DK, DV, 4, false>), dim3(grid), dim3(256), 0, s, r, c, nc, conv_lpw);
   }
   return hipGetLastError();
 }
@@ -556,10 +591,7 @@ hipError_t launch_round_rollback(const RollbackArgs& r, const ConvRollbackArgs& 
 }
 
 hipError_t launch_conv_rollback(const ConvRollbackArgs& a, int dtype, hipStream_t s) {
-  const int esz = dtype == 1 ? 2 : 4;
-  const int chunks = a.C * esz / 16;
-  dim3 grid(static_cast<unsigned>(a.L) * a.B, (chunks + 255) / 256);
-  return dtype == 1 ? launch_crb<2>(a, grid, s) : launch_crb<4>(a, grid, s);
+  return dtype == 1 ? launch_crb<2>(a, s) : launch_crb<4>(a, s);
 }
 
 }  // namespace gdn

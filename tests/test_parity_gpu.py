@@ -711,6 +711,57 @@ def test_rollback_layer_walk_ragged(D, B):
     assert int(err.item()) == 0
     check_units("S (round rollback, layer walk)", S, ref, "state", 1e-5)
     assert torch.equal(S[:, idle].cpu(), S0[:, idle])
+    cs_ref, _ = oracle.conv_rollback(osh, W.to_f64(cs0), W.to_f64(x), nk.numpy())
+    np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
+
+
+@pytest.mark.parametrize("entry", ["conv", "round"])
+def test_conv_rollback_walk_batches(entry):
+    """The conv window rollback with 4,800 bf16 channels (600 16-byte
+    chunks per row: one whole batch of two chunks per thread, then a tail of
+    88), against the oracle's conv_rollback, exactly.  The standalone call at
+    5 layers x 420 sequences walks two layers per workgroup with a shorter
+    last group; the round call (state and window in one launch) runs a small
+    stack, its state checked too.  Sequences that accepted nothing keep
+    their window."""
+    _need_gpu()
+    D, H, T = 32, 50, 4
+    L, B = (5, 420) if entry == "conv" else (2, 8)
+    sh = gb.GdnShape(L, B, H, H, D, D, 4, True, 1e-6, torch.bfloat16)
+    assert sh.C == 4800
+    if entry == "conv":
+        lpw = -(-(L * B) // 2048)
+        assert lpw == 2 and L % lpw != 0
+    gen = torch.Generator().manual_seed(811 + L)
+    nk = torch.randint(0, T + 1, (B,), generator=gen, dtype=torch.int32)
+    nk[::4] = 0
+    nk[1] = T
+    cs0 = torch.randn((L, B, 3, sh.C), generator=gen).to(torch.bfloat16)
+    x = torch.randn((L, B, T, sh.C), generator=gen).to(torch.bfloat16)
+    osh = oracle.Shape(L=L, B=B, Hk=H, Hv=H, Dk=D, Dv=D, K=4, silu=True, eps=1e-6)
+    cs_ref, wi_ref = oracle.conv_rollback(osh, W.to_f64(cs0), W.to_f64(x), nk.numpy())
+    print("conv rollback walk", entry, L, B, flush=True)
+    cs = cs0.to(DEV).clone()
+    wi = torch.full((B, 3), -5, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    if entry == "conv":
+        gb.gdn_conv_state_rollback(sh, cs, x.to(DEV), nk.to(DEV), win_idx=wi, dev_err=err)
+    else:
+        S0 = torch.randn((L, B, H, D, D), generator=gen) * 0.1
+        u = torch.randn((L, B, T, H, D), generator=gen)
+        k = torch.nn.functional.normalize(torch.randn((L, B, T, H, D), generator=gen), dim=-1)
+        g = 0.6 + 0.4 * torch.rand((L, B, T, H), generator=gen)
+        S = S0.to(DEV).clone()
+        gb.gdn_round_rollback(sh, S, gb.Tape(u.to(DEV), k.to(DEV), g.to(DEV)), cs, x.to(DEV),
+                              nk.to(DEV), win_idx=wi, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    np.testing.assert_array_equal(cs.cpu().double().numpy(), cs_ref)
+    np.testing.assert_array_equal(wi.cpu().numpy(), wi_ref)
+    if entry == "round":
+        ref = oracle.tape_rollback(osh, S0.double().numpy(), u.double().numpy(),
+                                   k.double().numpy(), g.double().numpy(), nk.numpy(), None)
+        check_units("S (round rollback)", S, ref, "state", 1e-5)
 
 
 # ------------------------------------------------------- device-side errors -
